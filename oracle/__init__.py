@@ -1,0 +1,14 @@
+"""CPU oracle of the flow-matching action-expert denoise loop.
+
+TEST INFRASTRUCTURE ONLY: a plain, slow numpy (fp64) definition of what the
+denoise loop computes.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+benchmark's CPU-baseline leg may import it.  The HIP library never calls it,
+and the two share no code; both consume the seeded inputs of ``synth``.
+
+Pins (what fixes each function independently of itself) live in
+``tests/test_oracle_pins.py``.  Parity unpinned: the end-to-end output at the
+real model sizes rests only on the definitions here plus those pins, since the
+pages print no worked numerical example of the expert.
+"""
+from .denoise import *  # noqa: F401,F403
+from .denoise import __all__  # noqa: F401

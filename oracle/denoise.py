@@ -1,0 +1,308 @@
+"""CPU oracle of the flow-matching action-expert denoise loop (numpy, fp64).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this module.  The HIP library never calls it and
+shares no code with it.
+
+What it computes (the method described in "LingBot-VLA on Thor (sm_110)",
+section 1 "Architecture / shapes": a flow-matching action expert of 36 layers
+run once per denoise step over an action chunk; section 2 names the fused
+kernels of one expert layer: AdaRMSNorm, QKV+RoPE and the SwiGLU tail; the
+"LingBot-VLA v2 Examples" page, section "Configuration / CUDA Graph", fixes
+that the per-layer prefix KV cache is built before the loop and the loop of
+fixed-shape denoise steps runs on top of it).  The pages print no equations;
+every convention below is the plainest reading, listed with its reason in the
+design notes of this repository:
+
+  x_0 = noise;  for k = 0..N-1:  x_{k+1} = x_k + (t_{k+1} - t_k) * v(x_k, t_k)
+
+  v(x, t):
+    e   = [sin(s*t*w_j), cos(s*t*w_j)],  w_j = 10000^(-j/half), s = time_scale
+    c   = SiLU(W_t2 SiLU(W_t1 e + b_t1) + b_t2)
+    h   = x W_in^T + b_in
+    per layer l, [a1, b1, g1, a2, b2, g2] = W_mod,l c + b_mod,l:
+      y = RMSNorm(h) * (1 + a1) + b1
+      q, k, v = y W_q^T, y W_k^T, y W_v^T   (heads of d_h columns)
+      q, k <- rotate-half RoPE at positions P + i
+      o_j = softmax(q_j [Kp_g; k_g]^T / sqrt(d_h)) [Vp_g; v_g],  g = j // (n_q / n_kv)
+      h = h + g1 * (o W_o^T)
+      y = RMSNorm(h) * (1 + a2) + b2
+      h = h + g2 * ((SiLU(y W_g^T) * (y W_u^T)) W_d^T)
+    [af, bf] = W_modf c + b_modf
+    v = (RMSNorm(h) * (1 + af) + bf) W_out^T + b_out
+
+Weights arrive as raw encodings (bf16 bit patterns, or OCP E4M3FN codes with
+per-output-row float32 scales); this module decodes them itself.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional
+
+import numpy as np
+
+__all__ = [
+    "ExpertDims", "decode_bf16", "decode_e4m3fn", "decode_weights",
+    "sinusoidal_embedding", "silu", "time_condition", "modulation",
+    "rms_normalize", "ada_rms_norm", "rope_rotate_half", "softmax",
+    "gqa_attention", "expert_layer", "velocity", "denoise", "cosine",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class ExpertDims:
+    """Sizes and scalar conventions of the expert (notation of the method)."""
+    n_layers: int
+    hidden: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    intermediate: int
+    action_dim: int
+    horizon: int
+    prefix_len: int
+    time_emb_dim: int = 256
+    rope_theta: float = 1.0e6
+    rms_eps: float = 1.0e-6
+    time_scale: float = 1000.0
+
+    @classmethod
+    def from_config(cls, cfg) -> "ExpertDims":
+        return cls(cfg.n_layers, cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim,
+                   cfg.intermediate, cfg.action_dim, cfg.horizon, cfg.prefix_len,
+                   cfg.time_emb_dim, cfg.rope_theta, cfg.rms_eps, cfg.time_scale)
+
+
+# ----------------------------------------------------------------------------
+# Number formats
+# ----------------------------------------------------------------------------
+
+def decode_bf16(bits: np.ndarray, dtype=np.float64) -> np.ndarray:
+    """bfloat16 bit patterns -> floats.
+
+    A bfloat16 is the upper half of an IEEE-754 binary32: shifting its 16 bits
+    into the top of a 32-bit word gives the same value as a float32.
+    """
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(dtype)
+
+
+def decode_e4m3fn(codes: np.ndarray, dtype=np.float64) -> np.ndarray:
+    """OCP 8-bit E4M3FN codes -> floats.
+
+    Format (OCP 8-bit floating point specification): 1 sign bit, 4 exponent
+    bits with bias 7, 3 mantissa bits; exponent field 0 encodes subnormals
+    m/8 * 2^-6; there are no infinities; S.1111.111 is NaN; the largest finite
+    magnitude is 1.75 * 2^8 = 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    sub = (m / 8.0) * 2.0 ** (-6)
+    val = sign * np.where(e == 0, sub, normal)
+    val = np.where((e == 15) & ((c & 7) == 7), np.nan, val)
+    return val.astype(dtype)
+
+
+def _linear(raw: dict, name: str, l: Optional[int], dtype):
+    w = raw[name] if l is None else raw[name][l]
+    if w.dtype == np.uint16:
+        return decode_bf16(w, dtype)
+    if w.dtype == np.uint8:
+        s = raw["s" + name[1]][l]
+        return (decode_e4m3fn(w, np.float64) * np.asarray(s, np.float64)[:, None]).astype(dtype)
+    raise TypeError(f"{name}: unsupported encoding {w.dtype}")
+
+
+def decode_weights(raw: dict, dtype=np.float64) -> Dict[str, object]:
+    """Decode every weight of the expert to ``dtype`` (per-layer lists kept)."""
+    out: Dict[str, object] = {}
+    for name in ("in_w", "out_w", "t1_w", "t2_w", "modf_w"):
+        out[name] = decode_bf16(raw[name], dtype)
+    for name in ("in_b", "out_b", "t1_b", "t2_b", "modf_b"):
+        out[name] = np.asarray(raw[name], dtype=np.float64).astype(dtype)
+    L = len(raw["mod_w"])
+    out["mod_w"] = [decode_bf16(raw["mod_w"][l], dtype) for l in range(L)]
+    out["mod_b"] = [np.asarray(raw["mod_b"][l], np.float64).astype(dtype) for l in range(L)]
+    for name in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"):
+        out[name] = [_linear(raw, name, l, dtype) for l in range(L)]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Time conditioning
+# ----------------------------------------------------------------------------
+
+def sinusoidal_embedding(t: float, dim: int, time_scale: float, max_period: float = 10000.0,
+                         dtype=np.float64) -> np.ndarray:
+    """Sinusoidal timestep embedding of width ``dim``: sines, then cosines.
+
+    Frequencies form a geometric ladder w_j = max_period^(-j/half),
+    j = 0..half-1, and the argument is time_scale * t * w_j.
+    """
+    half = dim // 2
+    j = np.arange(half, dtype=np.float64)
+    w = np.exp(-math.log(max_period) * j / half)
+    arg = float(time_scale) * float(t) * w
+    return np.concatenate([np.sin(arg), np.cos(arg)]).astype(dtype)
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def time_condition(t: float, W: dict, dims: ExpertDims) -> np.ndarray:
+    """Conditioning vector c (width H) of one time t: embedding -> 2-layer SiLU MLP."""
+    dtype = W["t1_w"].dtype
+    e = sinusoidal_embedding(t, dims.time_emb_dim, dims.time_scale, dtype=dtype)
+    z1 = W["t1_w"] @ e + W["t1_b"]
+    return silu(W["t2_w"] @ silu(z1) + W["t2_b"])
+
+
+def modulation(c: np.ndarray, w: np.ndarray, b: np.ndarray, n_chunks: int):
+    """Split W c + b into ``n_chunks`` H-vectors (scale/shift/gate chunks)."""
+    m = w @ c + b
+    return np.split(m, n_chunks)
+
+
+# ----------------------------------------------------------------------------
+# Normalisation, RoPE, attention
+# ----------------------------------------------------------------------------
+
+def rms_normalize(h: np.ndarray, eps: float) -> np.ndarray:
+    """Row-wise h / sqrt(mean(h^2) + eps) (no learned weight)."""
+    ms = np.mean(h * h, axis=-1, keepdims=True)
+    return h / np.sqrt(ms + eps)
+
+
+def ada_rms_norm(h: np.ndarray, scale: np.ndarray, shift: np.ndarray, eps: float) -> np.ndarray:
+    """Timestep-adaptive RMSNorm: RMSNorm(h) * (1 + scale) + shift."""
+    return rms_normalize(h, eps) * (1.0 + scale) + shift
+
+
+def rope_rotate_half(u: np.ndarray, pos: np.ndarray, theta: float) -> np.ndarray:
+    """Rotary position embedding, rotate-half pairing, on the last axis.
+
+    ``u``: [..., T, d]; ``pos``: [T].  Component m is paired with m + d/2 and the
+    pair is turned by the angle pos * theta^(-2m/d).
+    """
+    d = u.shape[-1]
+    half = d // 2
+    m = np.arange(half, dtype=np.float64)
+    inv_freq = float(theta) ** (-2.0 * m / d)
+    ang = np.asarray(pos, dtype=np.float64)[:, None] * inv_freq[None, :]
+    cos = np.cos(ang).astype(u.dtype)
+    sin = np.sin(ang).astype(u.dtype)
+    u1, u2 = u[..., :half], u[..., half:]
+    return np.concatenate([u1 * cos - u2 * sin, u2 * cos + u1 * sin], axis=-1)
+
+
+def softmax(s: np.ndarray) -> np.ndarray:
+    """Row-wise softmax along the last axis (max-shifted for range)."""
+    z = s - np.max(s, axis=-1, keepdims=True)
+    p = np.exp(z)
+    return p / np.sum(p, axis=-1, keepdims=True)
+
+
+def gqa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """Grouped-query attention with no mask.
+
+    ``q``: [n_q, T, d]; ``k``, ``v``: [n_kv, S, d].  Query head j reads KV head
+    j // (n_q / n_kv) (contiguous groups); scores are scaled by 1/sqrt(d).
+    Returns [n_q, T, d].
+    """
+    n_q, _, d = q.shape
+    n_kv = k.shape[0]
+    group = n_q // n_kv
+    out = np.empty_like(q)
+    scale = 1.0 / math.sqrt(d)
+    for j in range(n_q):
+        g = j // group
+        p = softmax((q[j] @ k[g].T) * scale)
+        out[j] = p @ v[g]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# One expert layer, the velocity field and the Euler loop
+# ----------------------------------------------------------------------------
+
+def expert_layer(h: np.ndarray, W: dict, l: int, mod, prefix_k_l: np.ndarray,
+                 prefix_v_l: np.ndarray, dims: ExpertDims) -> np.ndarray:
+    """One expert block on the chunk's hidden rows ``h`` [T, H].
+
+    ``mod`` = (a1, b1, g1, a2, b2, g2); ``prefix_k_l`` / ``prefix_v_l`` are this
+    layer's cached prefix keys/values [P, n_kv, d_h], used as given.
+    """
+    a1, b1, g1, a2, b2, g2 = mod
+    T = h.shape[0]
+    nq, nkv, dh = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    y = ada_rms_norm(h, a1, b1, dims.rms_eps)
+    q = (y @ W["wq"][l].T).reshape(T, nq, dh).transpose(1, 0, 2)
+    k = (y @ W["wk"][l].T).reshape(T, nkv, dh).transpose(1, 0, 2)
+    v = (y @ W["wv"][l].T).reshape(T, nkv, dh).transpose(1, 0, 2)
+    pos = dims.prefix_len + np.arange(T)
+    q = rope_rotate_half(q, pos, dims.rope_theta)
+    k = rope_rotate_half(k, pos, dims.rope_theta)
+    pk = prefix_k_l.astype(h.dtype).transpose(1, 0, 2)      # [n_kv, P, d_h]
+    pv = prefix_v_l.astype(h.dtype).transpose(1, 0, 2)
+    K = np.concatenate([pk, k], axis=1)
+    V = np.concatenate([pv, v], axis=1)
+    o = gqa_attention(q, K, V).transpose(1, 0, 2).reshape(T, nq * dh)
+    h = h + g1 * (o @ W["wo"][l].T)
+    y = ada_rms_norm(h, a2, b2, dims.rms_eps)
+    a = silu(y @ W["wg"][l].T) * (y @ W["wu"][l].T)
+    return h + g2 * (a @ W["wd"][l].T)
+
+
+def velocity(x: np.ndarray, t: float, W: dict, prefix_k_b: np.ndarray, prefix_v_b: np.ndarray,
+             dims: ExpertDims) -> np.ndarray:
+    """Velocity v(x, t) of one request: x [T, A] -> [T, A].
+
+    ``prefix_k_b`` / ``prefix_v_b``: this request's cache [L, P, n_kv, d_h].
+    """
+    c = time_condition(t, W, dims)
+    h = x @ W["in_w"].T + W["in_b"]
+    for l in range(dims.n_layers):
+        mod = modulation(c, W["mod_w"][l], W["mod_b"][l], 6)
+        h = expert_layer(h, W, l, mod, prefix_k_b[l], prefix_v_b[l], dims)
+    af, bf = modulation(c, W["modf_w"], W["modf_b"], 2)
+    y = ada_rms_norm(h, af, bf, dims.rms_eps)
+    return y @ W["out_w"].T + W["out_b"]
+
+
+def denoise(W: dict, dims: ExpertDims, prefix_k: np.ndarray, prefix_v: np.ndarray,
+            noise: np.ndarray, t_schedule: np.ndarray) -> np.ndarray:
+    """Explicit-Euler integration of the learned velocity field.
+
+    ``W``: decoded weights (``decode_weights``); ``prefix_k``/``prefix_v``:
+    decoded floats [B, L, P, n_kv, d_h]; ``noise``: x_0 [B, T, A];
+    ``t_schedule``: [B, N+1] times t_0..t_N per request.  Requests are
+    independent.  Each step evaluates the field at the left end point t_k and
+    advances by dt_k = t_{k+1} - t_k.  Returns x_N [B, T, A] in W's dtype.
+    """
+    dtype = W["in_w"].dtype
+    B = noise.shape[0]
+    N = t_schedule.shape[1] - 1
+    out = np.empty(noise.shape, dtype=dtype)
+    for b in range(B):
+        x = noise[b].astype(dtype)
+        ts = np.asarray(t_schedule[b], dtype=np.float64)
+        for k in range(N):
+            dt = dtype.type(ts[k + 1] - ts[k])
+            x = x + dt * velocity(x, ts[k], W, prefix_k[b], prefix_v[b], dims)
+        out[b] = x
+    return out
+
+
+def cosine(a: np.ndarray, b: np.ndarray) -> float:
+    """Cosine similarity of two flattened arrays (fp64)."""
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))

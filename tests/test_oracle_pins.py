@@ -1,0 +1,453 @@
+"""Pins of the CPU oracle: values fixed by something other than the oracle.
+
+Each test names what it pins and the plausible mistake it would catch.  The
+pages print no worked numerical example of the action expert, so the pins are
+library routines (torch, scipy), closed forms that follow from the method's
+structure, invariants and brute force on tiny inputs.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+import synth
+from oracle import ExpertDims
+
+RNG = np.random.default_rng(1234)
+
+
+def _tiny_dims(**kw):
+    base = dict(n_layers=2, hidden=32, n_q_heads=4, n_kv_heads=2, head_dim=8, intermediate=48,
+                action_dim=5, horizon=6, prefix_len=7)
+    base.update(kw)
+    return ExpertDims(**base)
+
+
+def _tiny_weights(d: ExpertDims, std=0.3, seed=0):
+    """Decoded float64 weights with larger std than the workloads, so every
+    term of the block moves the output measurably."""
+    r = np.random.default_rng(seed)
+    H, A, L, I = d.hidden, d.action_dim, d.n_layers, d.intermediate
+    qd, kvd = d.n_q_heads * d.head_dim, d.n_kv_heads * d.head_dim
+    g = lambda *s: r.standard_normal(s) * std
+    W = {"in_w": g(H, A), "in_b": g(H), "out_w": g(A, H), "out_b": g(A),
+         "t1_w": g(H, d.time_emb_dim), "t1_b": g(H), "t2_w": g(H, H), "t2_b": g(H),
+         "modf_w": g(2 * H, H), "modf_b": g(2 * H)}
+    W["mod_w"] = [g(6 * H, H) for _ in range(L)]
+    W["mod_b"] = [g(6 * H) for _ in range(L)]
+    shapes = {"wq": (qd, H), "wk": (kvd, H), "wv": (kvd, H), "wo": (H, qd), "wg": (I, H),
+              "wu": (I, H), "wd": (H, I)}
+    for n, s in shapes.items():
+        W[n] = [g(*s) for _ in range(L)]
+    return W
+
+
+def _tiny_inputs(d: ExpertDims, B=1, seed=1):
+    r = np.random.default_rng(seed)
+    pk = r.standard_normal((B, d.n_layers, d.prefix_len, d.n_kv_heads, d.head_dim))
+    pv = r.standard_normal((B, d.n_layers, d.prefix_len, d.n_kv_heads, d.head_dim))
+    x0 = r.standard_normal((B, d.horizon, d.action_dim))
+    return pk, pv, x0
+
+
+# ---------------------------------------------------------------------------
+# Number formats: pinned to torch's own conversions (library routines)
+# ---------------------------------------------------------------------------
+
+def test_bf16_decode_matches_torch_all_patterns():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.decode_bf16(bits, np.float64)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    both_nan = np.isnan(ours) & np.isnan(ref)
+    assert np.array_equal(ours[~both_nan], ref[~both_nan])
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+
+
+def test_e4m3_decode_matches_torch_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.decode_e4m3fn(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    m = ~np.isnan(ref)
+    assert np.array_equal(ours[m], ref[m])
+
+
+def test_e4m3_spec_values():
+    # OCP FP8 E4M3: max normal 448, min normal 2^-6, min subnormal 2^-9, NaN at S.1111.111
+    d = oracle.decode_e4m3fn(np.array([0x7E, 0x08, 0x01, 0x80, 0x7F, 0xFE, 0x38], np.uint8))
+    assert d[0] == 448.0 and d[1] == 2.0 ** -6 and d[2] == 2.0 ** -9
+    assert d[3] == 0.0 and np.signbit(d[3])
+    assert np.isnan(d[4]) and d[5] == -448.0 and d[6] == 1.0
+
+
+def test_generator_fp8_rows_hit_448():
+    # the per-row scale maps the largest magnitude of each row exactly onto 448
+    cfg = synth.config(1)
+    w = RNG.standard_normal((16, 64)).astype(np.float32)
+    q, s = synth.to_e4m3_rowwise(w)
+    deq = oracle.decode_e4m3fn(q) * s[:, None].astype(np.float64)
+    assert np.all(np.max(np.abs(oracle.decode_e4m3fn(q)), axis=1) == 448.0)
+    # e4m3 keeps 3 mantissa bits: relative error of round-to-nearest <= 2^-4
+    big = np.abs(w) > 2.0 ** -6 * s[:, None]
+    rel = np.abs(deq - w)[big] / np.abs(w)[big]
+    assert rel.max() <= 2.0 ** -4 + 1e-7
+    assert cfg.hidden == 256
+
+
+# ---------------------------------------------------------------------------
+# Time conditioning
+# ---------------------------------------------------------------------------
+
+def test_sinusoidal_embedding_closed_forms():
+    e0 = oracle.sinusoidal_embedding(0.0, 256, 1000.0)
+    assert np.array_equal(e0, np.r_[np.zeros(128), np.ones(128)])       # sin 0 | cos 0
+    t = 0.37
+    e = oracle.sinusoidal_embedding(t, 256, 1000.0)
+    assert np.allclose(e[:128] ** 2 + e[128:] ** 2, 1.0, atol=1e-15)
+    # first frequency is 1, frequency j = 64 is 10000^(-1/2) = 1/100
+    assert e[0] == pytest.approx(math.sin(1000.0 * t), abs=1e-13)
+    assert e[128] == pytest.approx(math.cos(1000.0 * t), abs=1e-13)
+    assert e[64] == pytest.approx(math.sin(10.0 * t), abs=1e-13)
+    assert e[127] == pytest.approx(math.sin(1000.0 * t * 10000.0 ** (-127 / 128)), abs=1e-13)
+
+
+def test_silu_matches_scipy_expit():
+    z = np.linspace(-30, 30, 1001)
+    assert np.allclose(oracle.silu(z), z * scipy.special.expit(z), rtol=1e-13, atol=1e-300)
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    assert oracle.silu(np.array([-800.0]))[0] == 0.0
+
+
+def test_time_mlp_two_silus_closed_form():
+    # W_t1 = 0, W_t2 = identity, b_t2 = 0  =>  c = SiLU(SiLU(b_t1)) elementwise.
+    d = _tiny_dims()
+    W = _tiny_weights(d)
+    W["t1_w"] = np.zeros_like(W["t1_w"])
+    W["t2_w"] = np.eye(d.hidden)
+    W["t2_b"] = np.zeros(d.hidden)
+    b1 = W["t1_b"]
+    s1 = b1 * scipy.special.expit(b1)
+    expect = s1 * scipy.special.expit(s1)
+    assert np.allclose(oracle.time_condition(0.4, W, d), expect, rtol=1e-13, atol=1e-15)
+    # W_t2 = 0  =>  c = SiLU(b_t2), whatever the first layer does
+    W2 = _tiny_weights(d)
+    W2["t2_w"] = np.zeros_like(W2["t2_w"])
+    expect2 = W2["t2_b"] * scipy.special.expit(W2["t2_b"])
+    assert np.allclose(oracle.time_condition(0.8, W2, d), expect2, rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# Normalisation
+# ---------------------------------------------------------------------------
+
+def test_rms_normalize_matches_linalg_norm():
+    h = RNG.standard_normal((5, 40))
+    ref = h / (np.linalg.norm(h, axis=1, keepdims=True) / math.sqrt(40))
+    assert np.allclose(oracle.rms_normalize(h, 0.0), ref, rtol=1e-14)
+    y = oracle.rms_normalize(h, 1e-6)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=1)), 1.0, atol=1e-6)
+
+
+def test_ada_rms_norm_scale_shift_form():
+    h = RNG.standard_normal((3, 16)) * 4.0
+    sc, sh = RNG.standard_normal(16), RNG.standard_normal(16)
+    y = oracle.ada_rms_norm(h, sc, sh, 1e-6)
+    # scale = -1 removes the normalised input entirely: output == shift
+    assert np.array_equal(oracle.ada_rms_norm(h, -np.ones(16), sh, 1e-6), np.broadcast_to(sh, h.shape))
+    # invariance to a positive rescaling of the row (up to eps)
+    assert np.allclose(oracle.ada_rms_norm(7.0 * h, sc, sh, 1e-6), y, atol=1e-7)
+    # zero modulation gives plain RMSNorm
+    assert np.array_equal(oracle.ada_rms_norm(h, np.zeros(16), np.zeros(16), 1e-6),
+                          oracle.rms_normalize(h, 1e-6))
+
+
+# ---------------------------------------------------------------------------
+# RoPE
+# ---------------------------------------------------------------------------
+
+def test_rope_invariants():
+    d, T = 16, 9
+    u = RNG.standard_normal((3, T, d))
+    pos = np.arange(T) + 5
+    r = oracle.rope_rotate_half(u, pos, 1e6)
+    assert np.allclose(np.linalg.norm(r, axis=-1), np.linalg.norm(u, axis=-1), rtol=1e-14)
+    assert np.allclose(oracle.rope_rotate_half(u, np.zeros(T), 1e6), u, atol=0)
+    # composition: turning by a then by b equals turning by a + b
+    a, b = np.arange(T) * 3, np.arange(T) + 11
+    rr = oracle.rope_rotate_half(oracle.rope_rotate_half(u, a, 1e6), b, 1e6)
+    assert np.allclose(rr, oracle.rope_rotate_half(u, a + b, 1e6), atol=1e-12)
+    # relative position: <rope(q,m), rope(k,n)> depends on n - m only
+    q, k = RNG.standard_normal(d), RNG.standard_normal(d)
+    for m, n, s in [(3, 10, 100), (0, 0, 57), (300, 2, 17)]:
+        l = oracle.rope_rotate_half(q[None, None], np.array([m]), 1e6)[0, 0] @ \
+            oracle.rope_rotate_half(k[None, None], np.array([n]), 1e6)[0, 0]
+        r2 = oracle.rope_rotate_half(q[None, None], np.array([m + s]), 1e6)[0, 0] @ \
+            oracle.rope_rotate_half(k[None, None], np.array([n + s]), 1e6)[0, 0]
+        assert l == pytest.approx(r2, rel=1e-11, abs=1e-12)
+
+
+def test_rope_pairing_and_frequency_ladder():
+    # basis vector e_m turns in the (m, m + d/2) plane by pos * theta^(-2m/d)
+    d, theta, pos = 8, 1e4, 3.0
+    for m in range(d // 2):
+        e = np.zeros((1, 1, d))
+        e[0, 0, m] = 1.0
+        r = oracle.rope_rotate_half(e, np.array([pos]), theta)[0, 0]
+        ang = math.atan2(r[m + d // 2], r[m])
+        want = math.remainder(pos * theta ** (-2.0 * m / d), 2 * math.pi)
+        assert ang == pytest.approx(want, abs=1e-12)
+        others = np.delete(r, [m, m + d // 2])
+        assert np.all(others == 0)
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+
+def _attention_brute(q, k, v):
+    n_q, T, d = q.shape
+    n_kv, S, _ = k.shape
+    out = np.zeros_like(q)
+    for j in range(n_q):
+        g = j // (n_q // n_kv)
+        for i in range(T):
+            s = [sum(q[j, i, c] * k[g, s_, c] for c in range(d)) / math.sqrt(d) for s_ in range(S)]
+            mx = max(s)
+            w = [math.exp(x - mx) for x in s]
+            z = sum(w)
+            for c in range(d):
+                out[j, i, c] = sum(w[s_] * v[g, s_, c] for s_ in range(S)) / z
+    return out
+
+
+def test_attention_brute_force():
+    q = RNG.standard_normal((4, 3, 4))
+    k = RNG.standard_normal((2, 5, 4))
+    v = RNG.standard_normal((2, 5, 4))
+    assert np.allclose(oracle.gqa_attention(q, k, v), _attention_brute(q, k, v), atol=1e-12, rtol=0)
+
+
+def test_attention_matches_torch_sdpa_gqa():
+    q = RNG.standard_normal((8, 6, 16))
+    k = RNG.standard_normal((2, 11, 16))
+    v = RNG.standard_normal((2, 11, 16))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        enable_gqa=True)[0].numpy()
+    assert np.allclose(oracle.gqa_attention(q, k, v), ref, atol=1e-12, rtol=0)
+
+
+def test_attention_special_cases():
+    v = RNG.standard_normal((2, 1, 4))
+    q = RNG.standard_normal((4, 3, 4))
+    k = RNG.standard_normal((2, 1, 4))
+    o = oracle.gqa_attention(q, k, v)                  # one key: output is that value row
+    assert np.allclose(o[0, 0], v[0, 0]) and np.allclose(o[3, 2], v[1, 0])
+    k2 = RNG.standard_normal((2, 7, 4))
+    v2 = RNG.standard_normal((2, 7, 4))
+    o0 = oracle.gqa_attention(np.zeros((4, 3, 4)), k2, v2)   # q = 0: mean of the group's values
+    assert np.allclose(o0[1, 0], v2[0].mean(axis=0)) and np.allclose(o0[2, 1], v2[1].mean(axis=0))
+
+
+def test_softmax_properties():
+    s = RNG.standard_normal((3, 9)) * 5
+    p = oracle.softmax(s)
+    assert np.allclose(p.sum(axis=-1), 1.0)
+    assert np.allclose(oracle.softmax(s + 123.0), p)
+    assert np.allclose(p, scipy.special.softmax(s, axis=-1), rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Whole block: closed forms from structured weights
+# ---------------------------------------------------------------------------
+
+def test_zeroed_blocks_are_identity():
+    d = _tiny_dims()
+    W = _tiny_weights(d)
+    for n in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"):
+        W[n] = [np.zeros_like(a) for a in W[n]]
+    pk, pv, x0 = _tiny_inputs(d)
+    t = 0.3
+    v = oracle.velocity(x0[0], t, W, pk[0], pv[0], d)
+    # independent recomputation: in-projection, final adaptive norm, out-projection
+    e = np.r_[np.sin(1000 * t * 10000.0 ** (-np.arange(128) / 128)),
+              np.cos(1000 * t * 10000.0 ** (-np.arange(128) / 128))]
+    z = W["t1_w"] @ e + W["t1_b"]
+    z = z * scipy.special.expit(z)
+    c = W["t2_w"] @ z + W["t2_b"]
+    c = c * scipy.special.expit(c)
+    mf = W["modf_w"] @ c + W["modf_b"]
+    h = x0[0] @ W["in_w"].T + W["in_b"]
+    hn = h / np.sqrt((h ** 2).mean(axis=1, keepdims=True) + d.rms_eps)
+    expect = (hn * (1 + mf[:d.hidden]) + mf[d.hidden:]) @ W["out_w"].T + W["out_b"]
+    assert np.allclose(v, expect, atol=1e-12)
+
+
+def test_closed_gate_reduces_to_plain_rmsnorm():
+    d = _tiny_dims()
+    W = _tiny_weights(d)
+    W["mod_w"] = [np.zeros_like(a) for a in W["mod_w"]]
+    W["mod_b"] = [np.zeros_like(a) for a in W["mod_b"]]
+    W["modf_w"] = np.zeros_like(W["modf_w"])
+    W["modf_b"] = np.zeros_like(W["modf_b"])
+    pk, pv, x0 = _tiny_inputs(d)
+    v = oracle.velocity(x0[0], 0.55, W, pk[0], pv[0], d)
+    h = x0[0] @ W["in_w"].T + W["in_b"]
+    hn = h / (np.linalg.norm(h, axis=1, keepdims=True) / math.sqrt(d.hidden))   # eps negligible
+    assert np.allclose(v, hn @ W["out_w"].T + W["out_b"], atol=1e-6)
+
+
+def _only_bias_chunks(d, W, chunks: dict):
+    """Modulation weights zero, bias zero except the given chunk vectors."""
+    H = d.hidden
+    W["mod_w"] = [np.zeros_like(a) for a in W["mod_w"]]
+    bs = []
+    for _ in range(d.n_layers):
+        b = np.zeros(6 * H)
+        for ci, vec in chunks.items():
+            b[ci * H:(ci + 1) * H] = vec
+        bs.append(b)
+    W["mod_b"] = bs
+
+
+def test_uniform_attention_block_closed_form():
+    # W_q = W_k = 0 => every score is 0 => each head outputs the mean of its KV
+    # group's values over prefix AND chunk keys.  Only the attention gate (chunk 2)
+    # is open; the MLP gate (chunk 5) is closed.
+    d = _tiny_dims(n_layers=1)
+    W = _tiny_weights(d)
+    W["wq"] = [np.zeros_like(W["wq"][0])]
+    W["wk"] = [np.zeros_like(W["wk"][0])]
+    g1 = RNG.standard_normal(d.hidden)
+    _only_bias_chunks(d, W, {2: g1})
+    pk, pv, x0 = _tiny_inputs(d)
+    h = RNG.standard_normal((d.horizon, d.hidden))
+    mod = oracle.modulation(np.ones(d.hidden), W["mod_w"][0], W["mod_b"][0], 6)
+    out = oracle.expert_layer(h, W, 0, mod, pk[0, 0], pv[0, 0], d)
+    y = h / np.sqrt((h ** 2).mean(axis=1, keepdims=True) + d.rms_eps)
+    vnew = (y @ W["wv"][0].T).reshape(d.horizon, d.n_kv_heads, d.head_dim)
+    allv = np.concatenate([pv[0, 0], vnew], axis=0)          # [P+T, n_kv, d_h]
+    mean_v = allv.mean(axis=0)                                # [n_kv, d_h]
+    grp = d.n_q_heads // d.n_kv_heads
+    o_row = np.concatenate([mean_v[j // grp] for j in range(d.n_q_heads)])
+    expect = h + g1 * (o_row @ W["wo"][0].T)[None, :]
+    assert np.allclose(out, expect, atol=1e-12)
+
+
+def test_mlp_block_closed_form():
+    # scale chunk 3 = -1 makes the pre-MLP norm output equal to the shift chunk 4,
+    # independent of h; gate chunk 5 opens the MLP; attention gate closed.
+    d = _tiny_dims(n_layers=1)
+    W = _tiny_weights(d)
+    beta, gam = RNG.standard_normal(d.hidden), RNG.standard_normal(d.hidden)
+    _only_bias_chunks(d, W, {3: -np.ones(d.hidden), 4: beta, 5: gam})
+    pk, pv, _ = _tiny_inputs(d)
+    h = RNG.standard_normal((d.horizon, d.hidden))
+    mod = oracle.modulation(np.ones(d.hidden), W["mod_w"][0], W["mod_b"][0], 6)
+    out = oracle.expert_layer(h, W, 0, mod, pk[0, 0], pv[0, 0], d)
+    gz = W["wg"][0] @ beta
+    a = gz * scipy.special.expit(gz) * (W["wu"][0] @ beta)
+    expect = h + (gam * (W["wd"][0] @ a))[None, :]
+    assert np.allclose(out, expect, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Euler loop
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["uniform", "warped"])
+def test_constant_velocity_closed_form(kind):
+    cfg = synth.config(1)
+    raw = synth.make_weights(cfg)
+    u = RNG.standard_normal(cfg.action_dim).astype(np.float32)
+    raw = synth.apply_variant(raw, "const_velocity", cfg, velocity_bias=u)
+    W = oracle.decode_weights(raw)
+    pk, pv = synth.make_prefix(cfg)
+    x0 = synth.make_noise(cfg)
+    ts = synth.make_schedule(cfg.n_steps, 1, kind)
+    out = oracle.denoise(W, ExpertDims.from_config(cfg), oracle.decode_bf16(pk),
+                         oracle.decode_bf16(pv), x0, ts)
+    span = float(ts[0, -1]) - float(ts[0, 0])
+    assert np.allclose(out[0], x0[0] + u.astype(np.float64) * span, atol=1e-12, rtol=0)
+
+
+def test_time_only_field_uses_left_endpoint():
+    # W_in = 0 makes v independent of x, so x_N = x_0 + sum_k dt_k v(t_k) exactly;
+    # evaluating at t_{k+1} instead gives a measurably different answer.
+    d = _tiny_dims()
+    W = _tiny_weights(d)
+    W["in_w"] = np.zeros_like(W["in_w"])
+    pk, pv, x0 = _tiny_inputs(d)
+    ts = synth.make_schedule(6, 1, "warped")
+    out = oracle.denoise(W, d, pk, pv, x0, ts)[0]
+    t = ts[0].astype(np.float64)
+    vs = [oracle.velocity(np.zeros_like(x0[0]), t[k], W, pk[0], pv[0], d) for k in range(7)]
+    left = x0[0] + sum((t[k + 1] - t[k]) * vs[k] for k in range(6))
+    right = x0[0] + sum((t[k + 1] - t[k]) * vs[k + 1] for k in range(6))
+    assert np.allclose(out, left, atol=1e-12)
+    assert not np.allclose(out, right, atol=1e-6)
+
+
+def test_schedule_splitting_is_bitwise():
+    cfg = synth.config(1)
+    W = oracle.decode_weights(synth.make_weights(cfg))
+    d = ExpertDims.from_config(cfg)
+    pk, pv = (oracle.decode_bf16(a) for a in synth.make_prefix(cfg))
+    x0 = synth.make_noise(cfg)
+    ts = synth.make_schedule(10, 1)
+    full = oracle.denoise(W, d, pk, pv, x0, ts)
+    half = oracle.denoise(W, d, pk, pv, x0, ts[:, :6])
+    rest = oracle.denoise(W, d, pk, pv, half, ts[:, 5:])
+    assert np.array_equal(full, rest)
+
+
+def test_euler_first_order_convergence():
+    # With a slowly varying field (time_scale 1) the Euler error halves with dt:
+    # (x_N - x_2N) / (x_2N - x_4N) -> 2.
+    d = _tiny_dims(time_scale=1.0)
+    W = _tiny_weights(d, std=0.1)
+    pk, pv, x0 = _tiny_inputs(d)
+    xs = {}
+    for n in (16, 32, 64):
+        ts = (np.arange(n + 1, dtype=np.float64) / n)[None]
+        xs[n] = oracle.denoise(W, d, pk, pv, x0, ts)
+    r = np.linalg.norm(xs[16] - xs[32]) / np.linalg.norm(xs[32] - xs[64])
+    assert 1.9 < r < 2.1, r
+
+
+def test_batch_independence_and_permutation():
+    cfg = synth.config(1).replace(batch=3)
+    W = oracle.decode_weights(synth.make_weights(cfg))
+    d = ExpertDims.from_config(cfg)
+    pk, pv = (oracle.decode_bf16(a) for a in synth.make_prefix(cfg))
+    x0 = synth.make_noise(cfg)
+    ts = synth.make_schedule(4, 3, "warped")
+    out = oracle.denoise(W, d, pk, pv, x0, ts)
+    for b in range(3):
+        one = oracle.denoise(W, d, pk[b:b + 1], pv[b:b + 1], x0[b:b + 1], ts[b:b + 1])
+        assert np.array_equal(one[0], out[b])
+    perm = [2, 0, 1]
+    outp = oracle.denoise(W, d, pk[perm], pv[perm], x0[perm], ts[perm])
+    assert np.array_equal(outp, out[perm])
+    # the generator's request streams: request b of a batch == batch-1 request b
+    pk1, _ = synth.make_prefix(cfg.replace(batch=1), requests=[2])
+    assert np.array_equal(oracle.decode_bf16(pk1)[0], pk[2])
+
+
+def test_fp32_twin_agrees_with_fp64():
+    cfg = synth.config(1)
+    raw = synth.make_weights(cfg)
+    d = ExpertDims.from_config(cfg)
+    pk, pv = synth.make_prefix(cfg)
+    x0 = synth.make_noise(cfg)
+    ts = synth.make_schedule(cfg.n_steps, 1)
+    o64 = oracle.denoise(oracle.decode_weights(raw, np.float64), d, oracle.decode_bf16(pk),
+                         oracle.decode_bf16(pv), x0, ts)
+    o32 = oracle.denoise(oracle.decode_weights(raw, np.float32), d,
+                         oracle.decode_bf16(pk, np.float32), oracle.decode_bf16(pv, np.float32),
+                         x0, ts)
+    assert o32.dtype == np.float32
+    assert oracle.cosine(o32, o64) >= 1 - 1e-9
