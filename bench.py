@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Throughput of the action-expert denoise loop on one MI355X.
+
+One bench "step" is one ``vla_denoise`` call: the whole hot path (prologue,
+N Euler steps of the 36-layer expert, every Euler update) over one batch of
+synthetic inputs resident in HBM. The headline workload is the LingBot-shaped
+expert (36 layers, hidden 1024, 16/2 heads of 128, SwiGLU 4096, prefix KV 256,
+chunk 50x75, 10 Euler steps, batch 1, bf16 weights and activations, fp32
+accumulation). ``value`` is denoise steps per second (Euler steps of the whole
+batch per second); chunks per second are reported beside it.
+
+Also reported:
+  * ``roofline``: the dominant kernel's algorithmic bytes (or flops) per launch
+    over its mean launch time, measured with HIP events around each launch;
+  * ``cpu_baseline``: the fp64 CPU oracle timed on a bounded sample;
+  * ``batch64``: the batched-replica workload (64 requests, GEMM M = 3200).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "denoise steps/s & chunks/s (36L bf16, chunk 50×75, b=1/64); % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def call_work(cfg):
+    """Algorithmic bytes and flops of one call (weights streamed once per Euler step)."""
+    H, L, A, T, B, P = cfg.hidden, cfg.n_layers, cfg.action_dim, cfg.horizon, cfg.batch, cfg.prefix_len
+    nq, nkv, dh, I, E, N = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.intermediate, cfg.time_emb_dim, cfg.n_steps
+    wb = 1 if cfg.weight_dtype == "fp8_e4m3" else 2
+    block_params = L * ((nq + 2 * nkv) * dh * H + H * nq * dh + 2 * I * H + H * I)
+    scales = L * ((nq + 2 * nkv) * dh + H + 2 * I + H) * 4 if wb == 1 else 0
+    inout_params = 2 * H * A
+    mod_params = (6 * L + 2) * H * H + H * E + H * H
+    prefix = B * L * P * nkv * dh * 2 * 2
+    per_step = block_params * wb + scales + prefix + inout_params * 2 + (H + A) * 4
+    once = mod_params * 2 + ((6 * L + 2) * H + 2 * H) * 4 + 2 * B * T * A * 4 + B * (N + 1) * 4
+    bytes_call = N * per_step + once
+    M = B * T
+    flops_call = (N * (2 * M * (block_params + inout_params) + 4 * B * nq * T * (P + T) * dh * L)
+                  + 2 * B * N * mod_params)
+    return bytes_call, flops_call
+
+
+def time_calls(ex, inputs, n_steps, warmup, steps):
+    import torch
+    pk, pv, x0, ts = inputs
+    out = torch.empty_like(x0)
+    ex.denoise(pk, pv, x0, ts, n_steps, out=out)         # first call captures the graph (untimed)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        ex.denoise(pk, pv, x0, ts, n_steps, out=out)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(steps):
+        ex.denoise(pk, pv, x0, ts, n_steps, out=out)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])  # ms
+    return wall, per_call, out
+
+
+def kernel_rooflines(ex, cfg, iters):
+    """Mean launch time of every kernel family of the layer (HIP events per launch)."""
+    from vla_flow_matching_denoise_amd import binding as B
+    names = {B.VLA_KERNEL_QKV: "qkv_rope_gemm", B.VLA_KERNEL_ATTN: "gqa_attention",
+             B.VLA_KERNEL_O: "o_proj_gemm", B.VLA_KERNEL_GATE_UP: "gate_up_swiglu_gemm",
+             B.VLA_KERNEL_DOWN: "down_gemm"}
+    res = {}
+    for k, name in names.items():
+        us, by, fl = B.vla_profile_kernel(ex.ctx, k, iters)
+        res[name] = {"us": us, "bytes": by, "flops": fl,
+                     "GBps": by / us / 1e3, "TFLOPs": fl / us / 1e6}
+    return res
+
+
+def dominant(res, bound):
+    # the kernel family with the largest time per Euler step (each runs once per layer)
+    name = max(res, key=lambda n: res[n]["us"])
+    r = res[name]
+    if bound == "hbm":
+        ach, peak, unit = r["GBps"], HBM_PEAK_GBS, "GB/s"
+    else:
+        ach, peak, unit = r["TFLOPs"], BF16_PEAK_TFLOPS, "TFLOP/s"
+    return name, {"bound": bound, "kernel": name, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+                  "frac": round(ach / peak, 4), "traffic": None, "us_per_launch": round(r["us"], 3),
+                  "algorithmic_bytes_per_launch": int(r["bytes"]), "algorithmic_flops_per_launch": int(r["flops"])}
+
+
+def build_inputs(cfg, seed=0):
+    import synth
+    from vla_flow_matching_denoise_amd.expert import to_device
+    pk, pv = synth.make_prefix(cfg, seed=seed)
+    x0 = synth.make_noise(cfg, seed=seed)
+    ts = synth.make_schedule(cfg.n_steps, cfg.batch)
+    return tuple(to_device(a) for a in (pk, pv, x0, ts)), (pk, pv, x0, ts)
+
+
+def cpu_baseline(cfg, raw, host_inputs, budget_s):
+    """The fp64 oracle, as it stands, on one request for as many Euler steps as fit the budget."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    pk, pv, x0, _ = host_inputs
+    W = oracle.decode_weights(raw)
+    d = oracle.ExpertDims.from_config(cfg)
+    fpk, fpv = oracle.decode_bf16(pk[:1]), oracle.decode_bf16(pv[:1])
+    one = synth.make_schedule(1, 1)
+    t0 = time.perf_counter()
+    oracle.denoise(W, d, fpk, fpv, x0[:1], one)
+    t1 = time.perf_counter() - t0
+    n = max(1, min(cfg.n_steps, int(budget_s / max(t1, 1e-3))))
+    ts = synth.make_schedule(n, 1)
+    t0 = time.perf_counter()
+    oracle.denoise(W, d, fpk, fpv, x0[:1], ts)
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 4), "unit": "denoise_steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"1 request of the {cfg.name} workload, {n} Euler step(s) (36 layers each), "
+                      f"fp64 numpy oracle, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30, help="timed denoise calls")
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--profile-iters", type=int, default=144)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-batch64", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}). Each GPU would run an independent "
+              f"replica of the loop on its own requests.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from vla_flow_matching_denoise_amd.expert import Expert, dims_from_config
+    torch.cuda.set_device(0)
+
+    cfg = synth.config(2)
+    log(f"[bench] generating weights for {cfg.name}")
+    raw = synth.make_weights(cfg, seed=0)
+    ex = Expert(raw, dims_from_config(cfg))
+    dev_in, host_in = build_inputs(cfg)
+    log(f"[bench] timing {args.steps} calls of {cfg.n_steps} Euler steps (warmup {args.warmup})")
+    wall, per_call, _ = time_calls(ex, dev_in, cfg.n_steps, args.warmup, args.steps)
+    t_call = wall / args.steps
+    bytes_call, flops_call = call_work(cfg)
+    kr = kernel_rooflines(ex, cfg, args.profile_iters)
+    _, roof = dominant(kr, "hbm")
+    ex.close()
+
+    result = {
+        "metric": METRIC,
+        "value": round(cfg.n_steps * cfg.batch / t_call, 3),
+        "unit": "denoise_steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_call * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02^2) weights, N(0,1) prefix KV and noise)",
+        "config": {"workload": "lingbot_36L_h1024_gqa16x2x128_swiglu4096_prefix256_chunk50x75_euler10_b1",
+                   "batch": cfg.batch, "euler_steps": cfg.n_steps, "chunk": [cfg.horizon, cfg.action_dim],
+                   "prefix_len": cfg.prefix_len},
+        "chunks_per_s": round(cfg.batch / t_call, 3),
+        "p50_ms": round(float(np.percentile(per_call, 50)), 4),
+        "p95_ms": round(float(np.percentile(per_call, 95)), 4),
+        "call_roofline": {"bound": "hbm", "algorithmic_bytes": int(bytes_call),
+                          "achieved_GBps": round(bytes_call / t_call / 1e9, 1),
+                          "frac": round(bytes_call / t_call / 1e9 / HBM_PEAK_GBS, 4)},
+        "roofline": roof,
+        "kernels": {k: {"us": round(v["us"], 3), "GBps": round(v["GBps"], 1), "TFLOPs": round(v["TFLOPs"], 2)}
+                    for k, v in kr.items()},
+    }
+
+    if not args.no_batch64:
+        cfg5 = synth.config(5)
+        log("[bench] batch-64 workload")
+        ex5 = Expert(raw, dims_from_config(cfg5))
+        dev5, _ = build_inputs(cfg5)
+        n5 = max(3, args.steps // 5)
+        wall5, pc5, _ = time_calls(ex5, dev5, cfg5.n_steps, 2, n5)
+        t5 = wall5 / n5
+        b5, f5 = call_work(cfg5)
+        kr5 = kernel_rooflines(ex5, cfg5, 36)
+        _, roof5 = dominant(kr5, "mfma")
+        ex5.close()
+        result["batch64"] = {
+            "workload": "lingbot_36L_h1024_chunk50x75_euler10_b64", "steps_per_s": round(cfg5.n_steps / t5, 3),
+            "chunks_per_s": round(cfg5.batch / t5, 3), "ms_per_call": round(t5 * 1e3, 3),
+            "call_mfma_frac": round(f5 / t5 / 1e12 / BF16_PEAK_TFLOPS, 4), "algorithmic_tflop": round(f5 / 1e12, 3),
+            "roofline": roof5,
+            "kernels": {k: {"us": round(v["us"], 2), "TFLOPs": round(v["TFLOPs"], 1)} for k, v in kr5.items()},
+        }
+
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(cfg, raw, host_in, args.cpu_budget)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,64 @@
+"""The C-ABI library loads and exports every entry point its header declares;
+argument validation that runs before any HIP call works without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vla_expert.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vla_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from vla_flow_matching_denoise_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from vla_flow_matching_denoise_amd import build
+        build.build()
+    return binding.lib()
+
+
+def test_header_declares_the_product_calls():
+    names = declared_functions()
+    for n in ("vla_expert_create", "vla_denoise", "vla_set_stream", "vla_expert_destroy", "vla_last_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from vla_flow_matching_denoise_amd import binding
+    names = declared_functions()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in the header but not exported"
+    assert set(names) == set(binding.EXPORTED)
+
+
+def test_host_side_argument_errors(lib):
+    from vla_flow_matching_denoise_amd import binding as B
+    assert lib.vla_denoise(None, None, None, None, None, 10, None) == B.VLA_ERR_ARG
+    assert "NULL" in B.vla_last_error()
+    assert lib.vla_set_option(None, B.VLA_OPT_USE_GRAPH, 1) == B.VLA_ERR_ARG
+    assert lib.vla_set_stream(None, None) == B.VLA_ERR_ARG
+    assert lib.vla_expert_create(None, None) is None
+    assert "weights" in B.vla_last_error()
+    lib.vla_expert_destroy(None)                      # NULL-safe
+    assert lib.vla_device_bytes(None) == 0
+
+
+@pytest.mark.parametrize("field,value", [("head_dim", 96), ("hidden", 1000), ("n_kv_heads", 3),
+                                         ("action_dim", 200), ("batch", 0), ("weight_dtype", 7),
+                                         ("time_emb_dim", 100)])
+def test_unsupported_dims_are_rejected_before_any_device_work(lib, field, value):
+    from vla_flow_matching_denoise_amd import binding as B
+    from vla_flow_matching_denoise_amd.expert import make_dims
+    d = make_dims(2, 256, 4, 2, 64, 704, 7, 16, 32, 1)
+    setattr(d, field, value)
+    w = B.VlaWeights()
+    assert lib.vla_expert_create(ctypes.byref(w), ctypes.byref(d)) is None
+    assert B.vla_last_error() != ""

@@ -1,0 +1,78 @@
+// Device-side helpers shared by the expert kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+
+#define VLA_DEV __device__ __forceinline__
+
+VLA_DEV float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Round-to-nearest-even float -> bfloat16 bits (the hardware conversion).
+VLA_DEV uint16_t f32_to_bf16(float f) {
+    __bf16 b = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+VLA_DEV uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// D += A * B on one 16x16x32 bf16 tile. Operand layout per lane l (checked on
+// gfx950): A[i][k] with i = l%16, k = 8*(l/16)+j; B[k][n] with n = l%16,
+// k = 8*(l/16)+j; D[i][n] with n = l%16, i = 4*(l/16)+r.
+VLA_DEV f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Eight OCP E4M3FN codes (two 32-bit words) -> eight bf16. Every E4M3 value is
+// a bf16 value, so taking the upper half of the exact fp32 is exact.
+VLA_DEV bf16x8 e4m3x8_to_bf16x8(u32x2 w) {
+    f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w[0], false);
+    f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w[0], true);
+    f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(w[1], false);
+    f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(w[1], true);
+    u32x4 r;
+    r[0] = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
+    r[1] = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+    r[2] = __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), 0x07060302u);
+    r[3] = __builtin_amdgcn_perm(__float_as_uint(d[1]), __float_as_uint(d[0]), 0x07060302u);
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+VLA_DEV float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Sum / max over the 16 lanes that share l/16 (one MFMA output row group).
+VLA_DEV float group16_sum(float v) {
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+VLA_DEV float group16_max(float v) {
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+VLA_DEV float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+
+// Pointers of the current call. Graph-captured kernels read them from this
+// device block, which a one-thread kernel refreshes before each replay.
+struct ArgBlock {
+    const uint16_t* prefix_k;  // [B, L, P, n_kv, d_h] bf16
+    const uint16_t* prefix_v;
+    const float* noise;        // [B, T, A]
+    const float* t_schedule;   // [B, N+1]
+    float* out;                // [B, T, A]
+};

@@ -1,0 +1,833 @@
+// Engine and C ABI of the action-expert denoise loop (see include/vla_expert.h).
+//
+// A context owns the repacked weights, every working buffer sized for its
+// batch, and one captured hipGraph per step count. A call refreshes a small
+// device argument block with its input pointers (one-thread kernel) and then
+// replays the graph; nothing is allocated or copied on the hot path.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/vla_expert.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+void set_err(const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+}
+
+#define HIPC(x)                                                                          \
+    do {                                                                                 \
+        hipError_t e_ = (x);                                                             \
+        if (e_ != hipSuccess) {                                                          \
+            set_err("%s failed: %s (%s:%d)", #x, hipGetErrorString(e_), __FILE__, __LINE__); \
+            return VLA_ERR_HIP;                                                          \
+        }                                                                                \
+    } while (0)
+
+struct GemmCfg {
+    int MT = 64, NT = 32, ksplit = 1, kchunk = 0;
+};
+
+GemmCfg choose_gemm(int M, int N, int K) {
+    GemmCfg c;
+    if (M <= 64) {
+        c.MT = 64;
+        c.NT = 32;
+    } else {
+        c.MT = 128;
+        c.NT = (N % 128 == 0) ? 128 : 64;
+    }
+    const int tiles = ((M + c.MT - 1) / c.MT) * (N / c.NT);
+    const int min_chunk = (M <= 64) ? 256 : 512;
+    int ks = 1;
+    while (tiles * ks < 256 && K / (ks * 2) >= min_chunk && K % (ks * 2 * 64) == 0) ks *= 2;
+    c.ksplit = ks;
+    c.kchunk = K / ks;
+    return c;
+}
+
+struct Linear {
+    void* w = nullptr;        // packed fragments
+    float* scale = nullptr;   // per packed row (E4M3 only)
+    int N = 0, K = 0;
+    GemmCfg cfg;
+};
+
+}  // namespace
+
+struct vla_ctx {
+    vla_dims d{};
+    int device = 0;
+    hipStream_t own_stream = nullptr;
+    hipStream_t stream = nullptr;
+    bool use_graph = true;
+    bool w8 = false;
+    int M = 0, qd = 0, kvd = 0, mod_ld = 0;
+    int64_t bytes = 0;
+    std::vector<void*> allocs;
+
+    // weights
+    uint16_t *in_w = nullptr, *out_w = nullptr, *t1_w = nullptr, *t2_w = nullptr;
+    float *in_b = nullptr, *out_b = nullptr, *t1_b = nullptr, *t2_b = nullptr;
+    Linear mod;                 // all layers' modulation + final, [(6L+2)H, H]
+    float* mod_bias = nullptr;  // [(6L+2)H]
+    std::vector<Linear> qkv, wo, gu, wd;
+    float2* rope = nullptr;
+
+    // buffers
+    float* h = nullptr;
+    uint16_t *y = nullptr, *q = nullptr, *kn = nullptr, *vn = nullptr, *o = nullptr, *act = nullptr;
+    float* ws = nullptr;
+    int* counters = nullptr;
+    ArgBlock* ab = nullptr;
+    int nb_cap = 0;             // capacity in (step, request) rows
+    float *e = nullptr, *z1 = nullptr, *modtab = nullptr;
+    uint16_t* cbf = nullptr;
+
+    std::map<int, hipGraphExec_t> graphs;
+
+    int alloc(void** p, size_t n) {
+        if (n == 0) n = 16;
+        hipError_t e = hipMalloc(p, n);
+        if (e != hipSuccess) {
+            set_err("hipMalloc(%zu) failed: %s", n, hipGetErrorString(e));
+            return VLA_ERR_OOM;
+        }
+        allocs.push_back(*p);
+        bytes += (int64_t)n;
+        return VLA_OK;
+    }
+    void release(void* p, size_t n) {
+        for (auto it = allocs.begin(); it != allocs.end(); ++it)
+            if (*it == p) {
+                allocs.erase(it);
+                (void)hipFree(p);
+                bytes -= (int64_t)n;
+                return;
+            }
+    }
+};
+
+namespace {
+
+int check_ptr(const void* p, const char* what, int align = 16) {
+    if (!p) {
+        set_err("%s is NULL", what);
+        return VLA_ERR_ARG;
+    }
+    if (((uintptr_t)p) % align) {
+        set_err("%s is not %d-byte aligned", what, align);
+        return VLA_ERR_ARG;
+    }
+    return VLA_OK;
+}
+
+int validate_dims(const vla_dims* d) {
+    if (!d) {
+        set_err("dims is NULL");
+        return VLA_ERR_ARG;
+    }
+    if (d->n_layers < 1 || d->hidden < 64 || d->hidden % 64 || d->intermediate < 64 || d->intermediate % 64) {
+        set_err("unsupported n_layers/hidden/intermediate (%d/%d/%d)", d->n_layers, d->hidden, d->intermediate);
+        return VLA_ERR_SHAPE;
+    }
+    if (d->head_dim != 64 && d->head_dim != 128) {
+        set_err("head_dim must be 64 or 128 (got %d)", d->head_dim);
+        return VLA_ERR_SHAPE;
+    }
+    if (d->n_kv_heads < 1 || d->n_q_heads < 1 || d->n_q_heads % d->n_kv_heads ||
+        (d->n_q_heads * d->head_dim) % 64) {
+        set_err("unsupported head counts (%d q / %d kv)", d->n_q_heads, d->n_kv_heads);
+        return VLA_ERR_SHAPE;
+    }
+    if (d->action_dim < 1 || d->action_dim > 128 || d->horizon < 1 || d->horizon > 256 || d->prefix_len < 0 ||
+        d->batch < 1) {
+        set_err("unsupported action_dim/horizon/prefix_len/batch (%d/%d/%d/%d)", d->action_dim, d->horizon,
+                d->prefix_len, d->batch);
+        return VLA_ERR_SHAPE;
+    }
+    if (d->time_emb_dim < 64 || d->time_emb_dim % 64) {
+        set_err("time_emb_dim must be a positive multiple of 64 (got %d)", d->time_emb_dim);
+        return VLA_ERR_SHAPE;
+    }
+    if (!(d->rms_eps > 0.f) || !(d->rope_theta > 0.f) || !std::isfinite(d->time_scale)) {
+        set_err("rms_eps and rope_theta must be positive, time_scale finite");
+        return VLA_ERR_SHAPE;
+    }
+    if (d->weight_dtype != VLA_BF16 && d->weight_dtype != VLA_FP8_E4M3) {
+        set_err("unknown weight_dtype %d", d->weight_dtype);
+        return VLA_ERR_SHAPE;
+    }
+    if ((long)d->batch * d->horizon > (1L << 24)) {
+        set_err("batch*horizon too large");
+        return VLA_ERR_SHAPE;
+    }
+    return VLA_OK;
+}
+
+int pack_linear(vla_ctx* c, Linear& lin, int N, int K, const void* const* srcs, const float* const* scales,
+                int nsrc, const int* rows, int mode, int dh) {
+    // mode 0: plain concatenation of sources; 1: rotate-half pair interleave per
+    // head within each source; 2: two sources interleaved by row (gate, up).
+    const int eb = c->w8 ? 1 : 2;
+    lin.N = N;
+    lin.K = K;
+    int rc = c->alloc(&lin.w, (size_t)N * K * eb);
+    if (rc) return rc;
+    int off = 0;
+    std::vector<float> hs(c->w8 ? N : 0);
+    for (int s = 0; s < nsrc; ++s) {
+        long total = (long)rows[s] * (K / 8);
+        int blocks = (int)((total + 255) / 256);
+        int row_mode = mode == 2 ? 2 : (mode == 1 ? 1 : 0);
+        hipLaunchKernelGGL(pack_weight_kernel, dim3(blocks), dim3(256), 0, c->stream, (const uint8_t*)srcs[s],
+                           rows[s], K, eb, (uint8_t*)lin.w, row_mode, mode == 2 ? 0 : off, dh, mode == 2 ? s : 0);
+        HIPC(hipGetLastError());
+        if (c->w8) {
+            std::vector<float> sv(rows[s]);
+            HIPC(hipMemcpy(sv.data(), scales[s], rows[s] * sizeof(float), hipMemcpyDeviceToHost));
+            for (int r = 0; r < rows[s]; ++r) {
+                int drow;
+                if (mode == 2) drow = 2 * r + s;
+                else if (mode == 1) {
+                    int head = r / dh, p = r % dh, half = dh / 2;
+                    drow = off + head * dh + (p < half ? 2 * p : 2 * (p - half) + 1);
+                } else drow = off + r;
+                hs[drow] = sv[r];
+            }
+        }
+        off += rows[s];
+    }
+    if (c->w8) {
+        rc = c->alloc((void**)&lin.scale, (size_t)N * sizeof(float));
+        if (rc) return rc;
+        HIPC(hipMemcpy(lin.scale, hs.data(), N * sizeof(float), hipMemcpyHostToDevice));
+    }
+    return VLA_OK;
+}
+
+// Plain bf16 packing of the modulation weights (never E4M3).
+int pack_mod(vla_ctx* c, const vla_weights* w) {
+    const int H = c->d.hidden, L = c->d.n_layers;
+    const int N = (6 * L + 2) * H;
+    c->mod.N = N;
+    c->mod.K = H;
+    int rc = c->alloc(&c->mod.w, (size_t)N * H * 2);
+    if (rc) return rc;
+    for (int l = 0; l <= L; ++l) {
+        const void* src = l < L ? w->mod_w[l] : w->modf_w;
+        int rows = l < L ? 6 * H : 2 * H;
+        long total = (long)rows * (H / 8);
+        hipLaunchKernelGGL(pack_weight_kernel, dim3((int)((total + 255) / 256)), dim3(256), 0, c->stream,
+                           (const uint8_t*)src, rows, H, 2, (uint8_t*)c->mod.w, 0, l * 6 * H, 64, 0);
+        HIPC(hipGetLastError());
+    }
+    rc = c->alloc((void**)&c->mod_bias, (size_t)N * sizeof(float));
+    if (rc) return rc;
+    for (int l = 0; l <= L; ++l) {
+        const float* src = l < L ? w->mod_b[l] : w->modf_b;
+        int rows = l < L ? 6 * H : 2 * H;
+        HIPC(hipMemcpyAsync(c->mod_bias + (size_t)l * 6 * H, src, rows * sizeof(float), hipMemcpyDeviceToDevice,
+                            c->stream));
+    }
+    return VLA_OK;
+}
+
+template <typename T>
+int copy_in(vla_ctx* c, T** dst, const void* src, size_t n_elems) {
+    int rc = c->alloc((void**)dst, n_elems * sizeof(T));
+    if (rc) return rc;
+    HIPC(hipMemcpyAsync(*dst, src, n_elems * sizeof(T), hipMemcpyDeviceToDevice, c->stream));
+    return VLA_OK;
+}
+
+int ensure_capacity(vla_ctx* c, int n_steps) {
+    const int nb = n_steps * c->d.batch;
+    if (nb <= c->nb_cap) return VLA_OK;
+    // graphs captured so far point at the old buffers
+    for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);
+    c->graphs.clear();
+    HIPC(hipStreamSynchronize(c->stream));
+    const int H = c->d.hidden, E = c->d.time_emb_dim;
+    if (c->e) {
+        c->release(c->e, (size_t)c->nb_cap * E * 4);
+        c->release(c->z1, (size_t)c->nb_cap * H * 4);
+        c->release(c->cbf, (size_t)c->nb_cap * H * 2);
+        c->release(c->modtab, (size_t)c->nb_cap * c->mod_ld * 4);
+    }
+    int rc;
+    if ((rc = c->alloc((void**)&c->e, (size_t)nb * E * 4))) return rc;
+    if ((rc = c->alloc((void**)&c->z1, (size_t)nb * H * 4))) return rc;
+    if ((rc = c->alloc((void**)&c->cbf, (size_t)nb * H * 2))) return rc;
+    if ((rc = c->alloc((void**)&c->modtab, (size_t)nb * c->mod_ld * 4))) return rc;
+    c->nb_cap = nb;
+    return VLA_OK;
+}
+
+// ------------------------------- launchers ---------------------------------
+
+template <int MT, int NT, bool W8>
+int launch_gemm_t(int epi, const GemmParams& p, dim3 grid, hipStream_t s) {
+    switch (epi) {
+        case EPI_BIAS_F32: hipLaunchKernelGGL((gemm_kernel<MT, NT, W8, EPI_BIAS_F32>), grid, dim3(256), 0, s, p); break;
+        case EPI_RESID: hipLaunchKernelGGL((gemm_kernel<MT, NT, W8, EPI_RESID>), grid, dim3(256), 0, s, p); break;
+        case EPI_QKV_ROPE: hipLaunchKernelGGL((gemm_kernel<MT, NT, W8, EPI_QKV_ROPE>), grid, dim3(256), 0, s, p); break;
+        case EPI_SWIGLU: hipLaunchKernelGGL((gemm_kernel<MT, NT, W8, EPI_SWIGLU>), grid, dim3(256), 0, s, p); break;
+        default: set_err("bad epilogue"); return VLA_ERR_ARG;
+    }
+    HIPC(hipGetLastError());
+    return VLA_OK;
+}
+
+int launch_gemm(vla_ctx* c, const Linear& lin, const GemmCfg& cfg, bool w8, int epi, GemmParams p) {
+    p.W = lin.w;
+    p.wscale = lin.scale;
+    p.N = lin.N;
+    p.K = lin.K;
+    p.ksplit = cfg.ksplit;
+    p.kchunk = cfg.kchunk;
+    p.ws = c->ws;
+    p.counters = c->counters;
+    dim3 grid(lin.N / cfg.NT, (p.M + cfg.MT - 1) / cfg.MT, cfg.ksplit);
+    if (cfg.MT == 64 && cfg.NT == 32) return w8 ? launch_gemm_t<64, 32, true>(epi, p, grid, c->stream)
+                                                : launch_gemm_t<64, 32, false>(epi, p, grid, c->stream);
+    if (cfg.MT == 128 && cfg.NT == 128) return w8 ? launch_gemm_t<128, 128, true>(epi, p, grid, c->stream)
+                                                  : launch_gemm_t<128, 128, false>(epi, p, grid, c->stream);
+    if (cfg.MT == 128 && cfg.NT == 64) return w8 ? launch_gemm_t<128, 64, true>(epi, p, grid, c->stream)
+                                                 : launch_gemm_t<128, 64, false>(epi, p, grid, c->stream);
+    set_err("no GEMM tile %dx%d", cfg.MT, cfg.NT);
+    return VLA_ERR_SHAPE;
+}
+
+// Prologue: time embedding, time MLP and the modulation table of n_steps.
+int enqueue_prologue(vla_ctx* c, int n_steps, const float* ts_direct) {
+    const vla_dims& d = c->d;
+    const int B = d.batch, H = d.hidden, E = d.time_emb_dim, nb = n_steps * B;
+    hipLaunchKernelGGL(time_embed_kernel, dim3((nb * E + 255) / 256), dim3(256), 0, c->stream, c->ab, ts_direct,
+                       c->e, n_steps, B, E, (double)d.time_scale);
+    HIPC(hipGetLastError());
+    long waves = (long)nb * H;
+    hipLaunchKernelGGL(small_linear_silu_kernel, dim3((int)((waves * 64 + 255) / 256)), dim3(256), 0, c->stream,
+                       c->e, c->t1_w, c->t1_b, c->z1, (uint16_t*)nullptr, nb, H, E);
+    HIPC(hipGetLastError());
+    hipLaunchKernelGGL(small_linear_silu_kernel, dim3((int)((waves * 64 + 255) / 256)), dim3(256), 0, c->stream,
+                       c->z1, c->t2_w, c->t2_b, (float*)nullptr, c->cbf, nb, H, H);
+    HIPC(hipGetLastError());
+    GemmParams p{};
+    p.A = c->cbf;
+    p.lda = H;
+    p.M = nb;
+    p.out_f32 = c->modtab;
+    p.bias = c->mod_bias;
+    GemmCfg cfg = choose_gemm(nb, c->mod.N, c->mod.K);
+    cfg.ksplit = 1;  // the modulation GEMM has plenty of column tiles
+    cfg.kchunk = c->mod.K;
+    return launch_gemm(c, c->mod, cfg, false, EPI_BIAS_F32, p);
+}
+
+int launch_attention(vla_ctx* c, int l, const uint16_t* pk, const uint16_t* pv, const uint16_t* q,
+                     const uint16_t* kn, const uint16_t* vn, uint16_t* o) {
+    const vla_dims& d = c->d;
+    AttnParams ap{};
+    ap.ab = c->ab;
+    ap.pk = pk;
+    ap.pv = pv;
+    ap.q = q;
+    ap.kn = kn;
+    ap.vn = vn;
+    ap.o = o;
+    ap.layer = l;
+    ap.L = d.n_layers;
+    ap.P = d.prefix_len;
+    ap.T = d.horizon;
+    ap.nq = d.n_q_heads;
+    ap.nkv = d.n_kv_heads;
+    ap.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
+    const int G = d.n_q_heads / d.n_kv_heads;
+    dim3 ag((G * d.horizon + 63) / 64, d.n_kv_heads, d.batch);
+    if (d.head_dim == 128) hipLaunchKernelGGL(attn_kernel<128>, ag, dim3(256), 0, c->stream, ap);
+    else hipLaunchKernelGGL(attn_kernel<64>, ag, dim3(256), 0, c->stream, ap);
+    HIPC(hipGetLastError());
+    return VLA_OK;
+}
+
+int launch_block_gemm(vla_ctx* c, int which, int step, int l) {
+    const vla_dims& d = c->d;
+    const int H = d.hidden;
+    GemmParams p{};
+    p.M = c->M;
+    p.B = d.batch;
+    p.T = d.horizon;
+    p.mod = c->modtab;
+    p.mod_ld = c->mod_ld;
+    p.step = step;
+    if (which == VLA_KERNEL_QKV) {
+        p.A = c->y;
+        p.lda = H;
+        p.q = c->q;
+        p.kn = c->kn;
+        p.vn = c->vn;
+        p.rope = c->rope;
+        p.nq = d.n_q_heads;
+        p.nkv = d.n_kv_heads;
+        p.dh = d.head_dim;
+        return launch_gemm(c, c->qkv[l], c->qkv[l].cfg, c->w8, EPI_QKV_ROPE, p);
+    }
+    if (which == VLA_KERNEL_O || which == VLA_KERNEL_DOWN) {
+        const bool o = which == VLA_KERNEL_O;
+        p.A = o ? c->o : c->act;
+        p.lda = o ? c->qd : d.intermediate;
+        p.out_f32 = c->h;
+        p.gate_off = (6 * l + (o ? 2 : 5)) * H;
+        const Linear& lin = o ? c->wo[l] : c->wd[l];
+        return launch_gemm(c, lin, lin.cfg, c->w8, EPI_RESID, p);
+    }
+    if (which == VLA_KERNEL_GATE_UP) {
+        p.A = c->y;
+        p.lda = H;
+        p.act = c->act;
+        return launch_gemm(c, c->gu[l], c->gu[l].cfg, c->w8, EPI_SWIGLU, p);
+    }
+    set_err("unknown kernel %d", which);
+    return VLA_ERR_ARG;
+}
+
+int enqueue_layer(vla_ctx* c, int step, int l, int n_steps) {
+    const vla_dims& d = c->d;
+    const int H = d.hidden, M = c->M, B = d.batch, T = d.horizon;
+    const int rows_blocks = (M + 3) / 4;
+    int rc;
+    // AdaRMSNorm (scale1, shift1)
+    hipLaunchKernelGGL(adarms_kernel, dim3(rows_blocks), dim3(256), 0, c->stream, c->h, c->y, c->modtab, M, H, T, B,
+                       step, c->mod_ld, (6 * l + 0) * H, (6 * l + 1) * H, d.rms_eps);
+    HIPC(hipGetLastError());
+    // QKV + RoPE
+    if ((rc = launch_block_gemm(c, VLA_KERNEL_QKV, step, l))) return rc;
+    // attention
+    if ((rc = launch_attention(c, l, nullptr, nullptr, c->q, c->kn, c->vn, c->o))) return rc;
+    // O projection + gated residual (gate1)
+    if ((rc = launch_block_gemm(c, VLA_KERNEL_O, step, l))) return rc;
+    // AdaRMSNorm (scale2, shift2)
+    hipLaunchKernelGGL(adarms_kernel, dim3(rows_blocks), dim3(256), 0, c->stream, c->h, c->y, c->modtab, M, H, T, B,
+                       step, c->mod_ld, (6 * l + 3) * H, (6 * l + 4) * H, d.rms_eps);
+    HIPC(hipGetLastError());
+    // gate_up + SwiGLU
+    if ((rc = launch_block_gemm(c, VLA_KERNEL_GATE_UP, step, l))) return rc;
+    // down + gated residual (gate2)
+    if ((rc = launch_block_gemm(c, VLA_KERNEL_DOWN, step, l))) return rc;
+    (void)n_steps;
+    return VLA_OK;
+}
+
+int enqueue_forward(vla_ctx* c, int n_steps) {
+    const vla_dims& d = c->d;
+    const int H = d.hidden, M = c->M;
+    int rc;
+    if ((rc = enqueue_prologue(c, n_steps, nullptr))) return rc;
+    for (int k = 0; k < n_steps; ++k) {
+        hipLaunchKernelGGL(inproj_kernel, dim3((M * H + 255) / 256), dim3(256), 0, c->stream, c->ab, k == 0 ? 1 : 0,
+                           (const float*)nullptr, c->in_w, c->in_b, c->h, M, H, d.action_dim);
+        HIPC(hipGetLastError());
+        for (int l = 0; l < d.n_layers; ++l)
+            if ((rc = enqueue_layer(c, k, l, n_steps))) return rc;
+        hipLaunchKernelGGL(final_euler_kernel, dim3((M + 3) / 4), dim3(256), 4 * H * sizeof(float), c->stream, c->ab,
+                           k == 0 ? 1 : 0, c->h, c->modtab, c->out_w, c->out_b, M, H, d.action_dim, d.horizon,
+                           d.batch, k, n_steps, c->mod_ld, 6 * d.n_layers * H, (6 * d.n_layers + 1) * H, d.rms_eps);
+        HIPC(hipGetLastError());
+    }
+    return VLA_OK;
+}
+
+int set_args(vla_ctx* c, const void* pk, const void* pv, const float* noise, const float* ts, float* out) {
+    hipLaunchKernelGGL(set_args_kernel, dim3(1), dim3(1), 0, c->stream, c->ab, (const uint16_t*)pk,
+                       (const uint16_t*)pv, noise, ts, out);
+    HIPC(hipGetLastError());
+    return VLA_OK;
+}
+
+void destroy_ctx(vla_ctx* c) {
+    if (!c) return;
+    if (c->stream) (void)hipStreamSynchronize(c->stream);
+    for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);
+    c->graphs.clear();
+    for (void* p : c->allocs) (void)hipFree(p);
+    c->allocs.clear();
+    if (c->own_stream) (void)hipStreamDestroy(c->own_stream);
+    delete c;
+}
+
+int create_impl(vla_ctx* c, const vla_weights* w) {
+    const vla_dims& d = c->d;
+    const int H = d.hidden, A = d.action_dim, E = d.time_emb_dim, L = d.n_layers, I = d.intermediate;
+    const int dh = d.head_dim;
+    c->w8 = d.weight_dtype == VLA_FP8_E4M3;
+    c->M = d.batch * d.horizon;
+    c->qd = d.n_q_heads * dh;
+    c->kvd = d.n_kv_heads * dh;
+    c->mod_ld = (6 * L + 2) * H;
+    HIPC(hipGetDevice(&c->device));
+    HIPC(hipStreamCreateWithFlags(&c->own_stream, hipStreamNonBlocking));
+    c->stream = c->own_stream;
+
+    int rc;
+    // pointer checks
+    const void* top[] = {w->in_w, w->in_b, w->out_w, w->out_b, w->t1_w, w->t1_b, w->t2_w, w->t2_b, w->modf_w, w->modf_b};
+    const char* names[] = {"in_w", "in_b", "out_w", "out_b", "t1_w", "t1_b", "t2_w", "t2_b", "modf_w", "modf_b"};
+    for (int i = 0; i < 10; ++i)
+        if ((rc = check_ptr(top[i], names[i], 4))) return rc;
+    const void* const* per[] = {(const void* const*)w->mod_w, (const void* const*)w->mod_b, w->wq, w->wk, w->wv,
+                                w->wo, w->wg, w->wu, w->wd};
+    const char* pnames[] = {"mod_w", "mod_b", "wq", "wk", "wv", "wo", "wg", "wu", "wd"};
+    for (int i = 0; i < 9; ++i) {
+        if (!per[i]) {
+            set_err("%s array is NULL", pnames[i]);
+            return VLA_ERR_ARG;
+        }
+        for (int l = 0; l < L; ++l)
+            if ((rc = check_ptr(per[i][l], pnames[i], i >= 2 ? 8 : 4))) return rc;
+    }
+    if (c->w8) {
+        const float* const* sc[] = {w->sq, w->sk, w->sv, w->so, w->sg, w->su, w->sd};
+        for (int i = 0; i < 7; ++i) {
+            if (!sc[i]) {
+                set_err("fp8 weights need all seven per-layer scale arrays");
+                return VLA_ERR_ARG;
+            }
+            for (int l = 0; l < L; ++l)
+                if ((rc = check_ptr(sc[i][l], "fp8 scale", 4))) return rc;
+        }
+    }
+
+    // small weights, copied as given
+    if ((rc = copy_in(c, &c->in_w, w->in_w, (size_t)H * A))) return rc;
+    if ((rc = copy_in(c, &c->in_b, w->in_b, H))) return rc;
+    if ((rc = copy_in(c, &c->out_w, w->out_w, (size_t)A * H))) return rc;
+    if ((rc = copy_in(c, &c->out_b, w->out_b, A))) return rc;
+    if ((rc = copy_in(c, &c->t1_w, w->t1_w, (size_t)H * E))) return rc;
+    if ((rc = copy_in(c, &c->t1_b, w->t1_b, H))) return rc;
+    if ((rc = copy_in(c, &c->t2_w, w->t2_w, (size_t)H * H))) return rc;
+    if ((rc = copy_in(c, &c->t2_b, w->t2_b, H))) return rc;
+    if ((rc = pack_mod(c, w))) return rc;
+
+    // block linears
+    c->qkv.resize(L);
+    c->wo.resize(L);
+    c->gu.resize(L);
+    c->wd.resize(L);
+    for (int l = 0; l < L; ++l) {
+        {
+            const void* srcs[3] = {w->wq[l], w->wk[l], w->wv[l]};
+            const float* scs[3] = {c->w8 ? w->sq[l] : nullptr, c->w8 ? w->sk[l] : nullptr, c->w8 ? w->sv[l] : nullptr};
+            int rows[3] = {c->qd, c->kvd, c->kvd};
+            if ((rc = pack_linear(c, c->qkv[l], c->qd + 2 * c->kvd, H, srcs, scs, 3, rows, 1, dh))) return rc;
+        }
+        {
+            const void* srcs[1] = {w->wo[l]};
+            const float* scs[1] = {c->w8 ? w->so[l] : nullptr};
+            int rows[1] = {H};
+            if ((rc = pack_linear(c, c->wo[l], H, c->qd, srcs, scs, 1, rows, 0, dh))) return rc;
+        }
+        {
+            const void* srcs[2] = {w->wg[l], w->wu[l]};
+            const float* scs[2] = {c->w8 ? w->sg[l] : nullptr, c->w8 ? w->su[l] : nullptr};
+            int rows[2] = {I, I};
+            if ((rc = pack_linear(c, c->gu[l], 2 * I, H, srcs, scs, 2, rows, 2, dh))) return rc;
+        }
+        {
+            const void* srcs[1] = {w->wd[l]};
+            const float* scs[1] = {c->w8 ? w->sd[l] : nullptr};
+            int rows[1] = {H};
+            if ((rc = pack_linear(c, c->wd[l], H, I, srcs, scs, 1, rows, 0, dh))) return rc;
+        }
+        c->qkv[l].cfg = choose_gemm(c->M, c->qkv[l].N, c->qkv[l].K);
+        c->wo[l].cfg = choose_gemm(c->M, c->wo[l].N, c->wo[l].K);
+        c->gu[l].cfg = choose_gemm(c->M, c->gu[l].N, c->gu[l].K);
+        c->wd[l].cfg = choose_gemm(c->M, c->wd[l].N, c->wd[l].K);
+    }
+
+    // rotary table
+    if ((rc = c->alloc((void**)&c->rope, (size_t)d.horizon * (dh / 2) * sizeof(float2)))) return rc;
+    hipLaunchKernelGGL(rope_table_kernel, dim3((d.horizon * (dh / 2) + 255) / 256), dim3(256), 0, c->stream, c->rope,
+                       d.horizon, d.prefix_len, dh, (double)d.rope_theta);
+    HIPC(hipGetLastError());
+
+    // working buffers
+    const size_t M = c->M;
+    if ((rc = c->alloc((void**)&c->h, M * H * 4))) return rc;
+    if ((rc = c->alloc((void**)&c->y, M * H * 2))) return rc;
+    if ((rc = c->alloc((void**)&c->q, M * c->qd * 2))) return rc;
+    if ((rc = c->alloc((void**)&c->kn, M * c->kvd * 2))) return rc;
+    if ((rc = c->alloc((void**)&c->vn, M * c->kvd * 2))) return rc;
+    if ((rc = c->alloc((void**)&c->o, M * c->qd * 2))) return rc;
+    if ((rc = c->alloc((void**)&c->act, M * I * 2))) return rc;
+    size_t ws_elems = 16;
+    size_t tiles = 16;
+    const Linear* lins[4] = {&c->qkv[0], &c->wo[0], &c->gu[0], &c->wd[0]};
+    for (const Linear* ln : lins) {
+        if (ln->cfg.ksplit > 1) ws_elems = std::max(ws_elems, (size_t)ln->cfg.ksplit * M * ln->N);
+        tiles = std::max(tiles, (size_t)((M + ln->cfg.MT - 1) / ln->cfg.MT) * (ln->N / ln->cfg.NT));
+    }
+    if ((rc = c->alloc((void**)&c->ws, ws_elems * 4))) return rc;
+    if ((rc = c->alloc((void**)&c->counters, tiles * sizeof(int)))) return rc;
+    HIPC(hipMemsetAsync(c->counters, 0, tiles * sizeof(int), c->stream));
+    if ((rc = c->alloc((void**)&c->ab, sizeof(ArgBlock)))) return rc;
+    HIPC(hipMemsetAsync(c->ab, 0, sizeof(ArgBlock), c->stream));
+    if ((rc = ensure_capacity(c, 10))) return rc;
+    HIPC(hipStreamSynchronize(c->stream));
+    return VLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+vla_ctx* vla_expert_create(const vla_weights* weights, const vla_dims* dims) {
+    g_err.clear();
+    if (!weights) {
+        set_err("weights is NULL");
+        return nullptr;
+    }
+    if (validate_dims(dims)) return nullptr;
+    vla_ctx* c = new vla_ctx();
+    c->d = *dims;
+    if (create_impl(c, weights) != VLA_OK) {
+        std::string keep = g_err;
+        destroy_ctx(c);
+        g_err = keep;
+        return nullptr;
+    }
+    return c;
+}
+
+int vla_denoise(vla_ctx* c, const void* prefix_k, const void* prefix_v, const float* noise, const float* t_schedule,
+                int n_steps, float* out_actions) {
+    g_err.clear();
+    if (!c) {
+        set_err("ctx is NULL");
+        return VLA_ERR_ARG;
+    }
+    int rc;
+    if (c->d.prefix_len > 0) {
+        if ((rc = check_ptr(prefix_k, "prefix_k"))) return rc;
+        if ((rc = check_ptr(prefix_v, "prefix_v"))) return rc;
+    }
+    if ((rc = check_ptr(noise, "noise", 4))) return rc;
+    if ((rc = check_ptr(t_schedule, "t_schedule", 4))) return rc;
+    if ((rc = check_ptr(out_actions, "out_actions", 4))) return rc;
+    if (n_steps < 1 || n_steps > 100000) {
+        set_err("n_steps must be in [1, 100000] (got %d)", n_steps);
+        return VLA_ERR_ARG;
+    }
+    HIPC(hipSetDevice(c->device));
+    if ((rc = ensure_capacity(c, n_steps))) return rc;
+    if ((rc = set_args(c, prefix_k, prefix_v, noise, t_schedule, out_actions))) return rc;
+    if (!c->use_graph) return enqueue_forward(c, n_steps);
+    auto it = c->graphs.find(n_steps);
+    if (it == c->graphs.end()) {
+        hipGraph_t g = nullptr;
+        HIPC(hipStreamBeginCapture(c->stream, hipStreamCaptureModeRelaxed));
+        rc = enqueue_forward(c, n_steps);
+        hipError_t e = hipStreamEndCapture(c->stream, &g);
+        if (rc) {
+            if (g) (void)hipGraphDestroy(g);
+            return rc;
+        }
+        if (e != hipSuccess) {
+            set_err("graph capture failed: %s", hipGetErrorString(e));
+            return VLA_ERR_HIP;
+        }
+        hipGraphExec_t ex = nullptr;
+        e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+        (void)hipGraphDestroy(g);
+        if (e != hipSuccess) {
+            set_err("graph instantiate failed: %s", hipGetErrorString(e));
+            return VLA_ERR_HIP;
+        }
+        it = c->graphs.emplace(n_steps, ex).first;
+    }
+    HIPC(hipGraphLaunch(it->second, c->stream));
+    return VLA_OK;
+}
+
+int vla_set_stream(vla_ctx* c, void* stream) {
+    g_err.clear();
+    if (!c) {
+        set_err("ctx is NULL");
+        return VLA_ERR_ARG;
+    }
+    c->stream = stream ? (hipStream_t)stream : c->own_stream;
+    return VLA_OK;
+}
+
+int vla_set_option(vla_ctx* c, int option, int value) {
+    g_err.clear();
+    if (!c) {
+        set_err("ctx is NULL");
+        return VLA_ERR_ARG;
+    }
+    if (option == VLA_OPT_USE_GRAPH) {
+        c->use_graph = value != 0;
+        return VLA_OK;
+    }
+    set_err("unknown option %d", option);
+    return VLA_ERR_ARG;
+}
+
+void vla_expert_destroy(vla_ctx* c) { destroy_ctx(c); }
+
+const char* vla_last_error(void) { return g_err.c_str(); }
+
+int64_t vla_device_bytes(const vla_ctx* c) { return c ? c->bytes : 0; }
+
+int vla_test_modulation(vla_ctx* c, const float* t_schedule, int n_steps, float* mod_out) {
+    g_err.clear();
+    if (!c) {
+        set_err("ctx is NULL");
+        return VLA_ERR_ARG;
+    }
+    int rc;
+    if ((rc = check_ptr(t_schedule, "t_schedule", 4)) || (rc = check_ptr(mod_out, "mod_out", 4))) return rc;
+    if (n_steps < 1) {
+        set_err("n_steps must be >= 1");
+        return VLA_ERR_ARG;
+    }
+    HIPC(hipSetDevice(c->device));
+    if ((rc = ensure_capacity(c, n_steps))) return rc;
+    if ((rc = enqueue_prologue(c, n_steps, t_schedule))) return rc;
+    HIPC(hipMemcpyAsync(mod_out, c->modtab, (size_t)n_steps * c->d.batch * c->mod_ld * 4, hipMemcpyDeviceToDevice,
+                        c->stream));
+    HIPC(hipStreamSynchronize(c->stream));
+    return VLA_OK;
+}
+
+int vla_test_layer(vla_ctx* c, const void* prefix_k, const void* prefix_v, const float* t_schedule, int n_steps,
+                   int step, int layer, const float* h_in, float* h_out) {
+    g_err.clear();
+    if (!c) {
+        set_err("ctx is NULL");
+        return VLA_ERR_ARG;
+    }
+    int rc;
+    if ((rc = check_ptr(t_schedule, "t_schedule", 4)) || (rc = check_ptr(h_in, "h_in", 16)) ||
+        (rc = check_ptr(h_out, "h_out", 4)))
+        return rc;
+    if (n_steps < 1 || step < 0 || step >= n_steps || layer < 0 || layer >= c->d.n_layers) {
+        set_err("bad step/layer");
+        return VLA_ERR_ARG;
+    }
+    HIPC(hipSetDevice(c->device));
+    if ((rc = ensure_capacity(c, n_steps))) return rc;
+    if ((rc = set_args(c, prefix_k, prefix_v, nullptr, t_schedule, nullptr))) return rc;
+    if ((rc = enqueue_prologue(c, n_steps, t_schedule))) return rc;
+    HIPC(hipMemcpyAsync(c->h, h_in, (size_t)c->M * c->d.hidden * 4, hipMemcpyDeviceToDevice, c->stream));
+    if ((rc = enqueue_layer(c, step, layer, n_steps))) return rc;
+    HIPC(hipMemcpyAsync(h_out, c->h, (size_t)c->M * c->d.hidden * 4, hipMemcpyDeviceToDevice, c->stream));
+    HIPC(hipStreamSynchronize(c->stream));
+    return VLA_OK;
+}
+
+int vla_test_attention(vla_ctx* c, const void* prefix_k, const void* prefix_v, int layer, const void* q,
+                       const void* k_new, const void* v_new, void* o_out) {
+    g_err.clear();
+    if (!c) {
+        set_err("ctx is NULL");
+        return VLA_ERR_ARG;
+    }
+    int rc;
+    if (c->d.prefix_len > 0 && ((rc = check_ptr(prefix_k, "prefix_k")) || (rc = check_ptr(prefix_v, "prefix_v"))))
+        return rc;
+    if ((rc = check_ptr(q, "q")) || (rc = check_ptr(k_new, "k_new")) || (rc = check_ptr(v_new, "v_new")) ||
+        (rc = check_ptr(o_out, "o_out", 2)))
+        return rc;
+    if (layer < 0 || layer >= c->d.n_layers) {
+        set_err("bad layer");
+        return VLA_ERR_ARG;
+    }
+    HIPC(hipSetDevice(c->device));
+    if ((rc = launch_attention(c, layer, (const uint16_t*)prefix_k, (const uint16_t*)prefix_v, (const uint16_t*)q,
+                               (const uint16_t*)k_new, (const uint16_t*)v_new, (uint16_t*)o_out)))
+        return rc;
+    HIPC(hipStreamSynchronize(c->stream));
+    return VLA_OK;
+}
+
+int vla_profile_kernel(vla_ctx* c, int kernel, int iters, double* us_per_launch, double* bytes_per_launch,
+                       double* flops_per_launch) {
+    g_err.clear();
+    if (!c || !us_per_launch || iters < 1) {
+        set_err("bad arguments");
+        return VLA_ERR_ARG;
+    }
+    if (kernel < VLA_KERNEL_QKV || kernel > VLA_KERNEL_DOWN) {
+        set_err("unknown kernel %d", kernel);
+        return VLA_ERR_ARG;
+    }
+    HIPC(hipSetDevice(c->device));
+    const vla_dims& d = c->d;
+    const int L = d.n_layers, M = c->M, H = d.hidden, I = d.intermediate;
+    std::vector<hipEvent_t> ev(2 * iters);
+    for (auto& e : ev) HIPC(hipEventCreate(&e));
+    int rc = VLA_OK;
+    for (int i = 0; i < iters && rc == VLA_OK; ++i) {
+        const int l = i % L;
+        HIPC(hipEventRecord(ev[2 * i], c->stream));
+        if (kernel == VLA_KERNEL_ATTN) rc = launch_attention(c, l, nullptr, nullptr, c->q, c->kn, c->vn, c->o);
+        else rc = launch_block_gemm(c, kernel, 0, l);
+        HIPC(hipEventRecord(ev[2 * i + 1], c->stream));
+    }
+    HIPC(hipStreamSynchronize(c->stream));
+    double tot = 0;
+    for (int i = 0; i < iters; ++i) {
+        float ms = 0;
+        HIPC(hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]));
+        tot += ms;
+    }
+    for (auto& e : ev) (void)hipEventDestroy(e);
+    if (rc) return rc;
+    *us_per_launch = tot * 1e3 / iters;
+    const double wb = c->w8 ? 1.0 : 2.0;
+    const double S = d.prefix_len + d.horizon;
+    double bytes = 0, flops = 0;
+    switch (kernel) {
+        case VLA_KERNEL_QKV:
+            bytes = wb * (c->qd + 2.0 * c->kvd) * H + 2.0 * M * H + 2.0 * M * (c->qd + 2.0 * c->kvd);
+            flops = 2.0 * M * (c->qd + 2.0 * c->kvd) * H;
+            break;
+        case VLA_KERNEL_ATTN:
+            bytes = 2.0 * d.batch * S * c->kvd * 2 + 2.0 * M * c->qd * 2;
+            flops = 4.0 * d.batch * d.n_q_heads * (double)d.horizon * S * d.head_dim;
+            break;
+        case VLA_KERNEL_O:
+            bytes = wb * H * (double)c->qd + 2.0 * M * c->qd + 8.0 * M * H;
+            flops = 2.0 * M * (double)H * c->qd;
+            break;
+        case VLA_KERNEL_GATE_UP:
+            bytes = wb * 2.0 * I * H + 2.0 * M * H + 2.0 * M * I;
+            flops = 4.0 * M * (double)I * H;
+            break;
+        case VLA_KERNEL_DOWN:
+            bytes = wb * (double)H * I + 2.0 * M * I + 8.0 * M * H;
+            flops = 2.0 * M * (double)H * I;
+            break;
+    }
+    if (bytes_per_launch) *bytes_per_launch = bytes;
+    if (flops_per_launch) *flops_per_launch = flops;
+    return VLA_OK;
+}
+
+}  // extern "C"
