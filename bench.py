@@ -91,8 +91,10 @@ def kernel_rooflines(ex, cfg, iters):
 
 
 def dominant(res, bound):
-    # the kernel family with the largest time per Euler step (each runs once per layer)
-    name = max(res, key=lambda n: res[n]["us"])
+    """The kernel family carrying the largest share of the path's algorithmic
+    bytes (HBM-bound) or flops (MFMA-bound); every family runs once per layer."""
+    key = "bytes" if bound == "hbm" else "flops"
+    name = max(res, key=lambda n: res[n][key])
     r = res[name]
     if bound == "hbm":
         ach, peak, unit = r["GBps"], HBM_PEAK_GBS, "GB/s"

@@ -61,7 +61,7 @@ typedef struct vla_ctx vla_ctx;
 
 /*
  * Sizes and conventions. Supported: head_dim in {64, 128}; hidden and
- * intermediate multiples of 64; n_q_heads a multiple of n_kv_heads;
+ * intermediate multiples of 64, hidden <= 2048; n_q_heads a multiple of n_kv_heads;
  * n_q_heads*head_dim a multiple of 64; 1 <= action_dim <= 128;
  * 1 <= horizon <= 256; prefix_len >= 0; batch >= 1; time_emb_dim a positive
  * multiple of 64; rms_eps > 0.
@@ -174,13 +174,15 @@ int vla_test_layer(vla_ctx* ctx, const void* prefix_k, const void* prefix_v, con
 int vla_test_attention(vla_ctx* ctx, const void* prefix_k, const void* prefix_v, int layer,
                        const void* q, const void* k_new, const void* v_new, void* o_out);
 
-/* Kernel timing for roofline figures: launches one kernel of the loop `iters`
- * times on the ctx stream (cycling through the layers, so weights stream from
- * HBM as in the loop), each launch bracketed by its own pair of HIP events,
- * and writes the mean launch duration in microseconds to *us_per_launch and
- * the algorithmic bytes and flops of one launch to *bytes_per_launch and
- * *flops_per_launch. Uses the buffers and the modulation table of the last
- * vla_denoise call (call vla_denoise first). Synchronizes. */
+/* Kernel timing for roofline figures: runs `iters` expert layers exactly as
+ * in the loop (cycling through the layers, so weights stream from HBM; step 0
+ * of the last vla_denoise call's modulation table) on the ctx stream, and
+ * times the one launch per layer of the chosen kernel family with HIP events
+ * recorded at that kernel's own start and end (hipExtLaunchKernelGGL). Writes
+ * the mean launch duration in microseconds to *us_per_launch and the
+ * algorithmic bytes and flops of one launch to *bytes_per_launch and
+ * *flops_per_launch. Overwrites the working buffers (call vla_denoise first).
+ * Synchronizes. */
 #define VLA_KERNEL_QKV 0
 #define VLA_KERNEL_ATTN 1
 #define VLA_KERNEL_O 2

@@ -67,6 +67,15 @@ VLA_DEV float group16_max(float v) {
 
 VLA_DEV float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
+// Element index of activation (row, k) of a [rows, K] bf16 matrix. Row-major
+// when frag == 0; otherwise "A-fragment" order for at most 64 rows:
+// [k/32][row/16][lane][8] with lane = row%16 + 16*((k%32)/8), i.e. each
+// 16x32 MFMA A operand is one contiguous 1 KiB run (rows >= M stay zero).
+VLA_DEV size_t act_index(int row, int k, int K, int frag) {
+    if (!frag) return (size_t)row * K + k;
+    return ((size_t)((k >> 5) * 4 + (row >> 4)) * 64 + (row & 15) + 16 * ((k & 31) >> 3)) * 8 + (k & 7);
+}
+
 // Pointers of the current call. Graph-captured kernels read them from this
 // device block, which a one-thread kernel refreshes before each replay.
 struct ArgBlock {

@@ -4,6 +4,7 @@
 // batch, and one captured hipGraph per step count. A call refreshes a small
 // device argument block with its input pointers (one-thread kernel) and then
 // replays the graph; nothing is allocated or copied on the hot path.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -20,6 +21,31 @@
 namespace {
 
 thread_local std::string g_err;
+
+// When set (kernel timing only), the GEMM and attention launches record these
+// events at the kernel's own start and end.
+thread_local hipEvent_t g_ev_start = nullptr, g_ev_stop = nullptr;
+// Kernel family (VLA_KERNEL_*) whose launches get the events above; -1: none.
+thread_local int g_prof_target = -1;
+thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+
+struct ProfScope {  // arms the timing events for one launch of the target family
+    explicit ProfScope(int which) {
+        if (which == g_prof_target) {
+            g_ev_start = g_prof_start;
+            g_ev_stop = g_prof_stop;
+        }
+    }
+    ~ProfScope() { g_ev_start = g_ev_stop = nullptr; }
+};
+
+#define VLA_LAUNCH(kernel, grid, block, shmem, stream, ...)                                                     \
+    do {                                                                                                        \
+        if (g_ev_start)                                                                                         \
+            hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, g_ev_start, g_ev_stop, 0, __VA_ARGS__);    \
+        else                                                                                                    \
+            hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                                 \
+    } while (0)
 
 void set_err(const char* fmt, ...) {
     char buf[512];
@@ -40,24 +66,43 @@ void set_err(const char* fmt, ...) {
     } while (0)
 
 struct GemmCfg {
-    int MT = 64, NT = 32, ksplit = 1, kchunk = 0;
+    bool skinny = true;  // weight-streaming kernel for M <= 64 rows
+    int MT = 0, NT = 16;
+    int ksplit = 1, kw = 0;
+    int gx = 0;          // skinny: workgroups per K split (each loops over tiles)
 };
 
-GemmCfg choose_gemm(int M, int N, int K) {
+// M <= 64: skinny kernel, one 16-column tile per workgroup; when the consumer
+// can take split-K partials (allow_split), K is split until ~320 workgroups
+// or 256-deep chunks. Larger M: tiled kernel, 128-row tiles, 128 or 64
+// columns so that a launch has >= 256 tiles when possible.
+GemmCfg choose_gemm(int M, int N, int K, bool allow_split) {
     GemmCfg c;
     if (M <= 64) {
-        c.MT = 64;
-        c.NT = 32;
-    } else {
-        c.MT = 128;
-        c.NT = (N % 128 == 0) ? 128 : 64;
+        c.skinny = true;
+        c.NT = 16;
+        const int tiles = N / 16;
+        int ks = 1;
+        if (allow_split)
+            while (tiles * ks * 2 <= 320 && K / (ks * 2) >= 256 && K % (ks * 2 * 32) == 0) ks *= 2;
+        // a workgroup's 8 waves hold at most 6 k-steps of 32 each
+        while (K / ks > SK_WAVES * SK_MAXS * 32 && allow_split && K % (ks * 2 * 32) == 0) ks *= 2;
+        if (K / ks <= SK_WAVES * SK_MAXS * 32 && (K / ks) % 32 == 0) {
+            c.ksplit = ks;
+            c.kw = K / ks;
+            c.gx = tiles < 256 ? tiles : 256;
+            return c;
+        }
+        // too deep for the skinny kernel: fall through to the tiled one
     }
-    const int tiles = ((M + c.MT - 1) / c.MT) * (N / c.NT);
-    const int min_chunk = (M <= 64) ? 256 : 512;
-    int ks = 1;
-    while (tiles * ks < 256 && K / (ks * 2) >= min_chunk && K % (ks * 2 * 64) == 0) ks *= 2;
-    c.ksplit = ks;
-    c.kchunk = K / ks;
+    {
+        c.skinny = false;
+        c.MT = 128;
+        const int mt = (M + 127) / 128;
+        c.NT = (N % 128 == 0 && mt * (N / 128) >= 256) ? 128 : 64;
+        c.ksplit = 1;
+        c.kw = K;
+    }
     return c;
 }
 
@@ -78,11 +123,12 @@ struct vla_ctx {
     bool use_graph = true;
     bool w8 = false;
     int M = 0, qd = 0, kvd = 0, mod_ld = 0;
+    int afrag = 0;      // M <= 64: activations y, o, act kept in A-fragment order (64 zero-padded rows)
     int64_t bytes = 0;
     std::vector<void*> allocs;
 
     // weights
-    uint16_t *in_w = nullptr, *out_w = nullptr, *t1_w = nullptr, *t2_w = nullptr;
+    uint16_t *in_w = nullptr, *in_wT = nullptr, *out_w = nullptr, *t1_w = nullptr, *t2_w = nullptr;
     float *in_b = nullptr, *out_b = nullptr, *t1_b = nullptr, *t2_b = nullptr;
     Linear mod;                 // all layers' modulation + final, [(6L+2)H, H]
     float* mod_bias = nullptr;  // [(6L+2)H]
@@ -91,9 +137,11 @@ struct vla_ctx {
 
     // buffers
     float* h = nullptr;
-    uint16_t *y = nullptr, *q = nullptr, *kn = nullptr, *vn = nullptr, *o = nullptr, *act = nullptr;
-    float* ws = nullptr;
-    int* counters = nullptr;
+    float* yf = nullptr;        // final AdaRMSNorm output (fp32) for the out-projection
+    uint16_t *y = nullptr, *q = nullptr, *o = nullptr, *act = nullptr;
+    float* ws = nullptr;        // split-K partials of O / down, [ksplit][M][H]
+    uint16_t *kcat = nullptr, *vcat = nullptr;  // per-layer [prefix ; chunk] K and V
+    KVLayout kv{};
     ArgBlock* ab = nullptr;
     int nb_cap = 0;             // capacity in (step, request) rows
     float *e = nullptr, *z1 = nullptr, *modtab = nullptr;
@@ -142,7 +190,7 @@ int validate_dims(const vla_dims* d) {
         set_err("dims is NULL");
         return VLA_ERR_ARG;
     }
-    if (d->n_layers < 1 || d->hidden < 64 || d->hidden % 64 || d->intermediate < 64 || d->intermediate % 64) {
+    if (d->n_layers < 1 || d->hidden < 64 || d->hidden % 64 || d->hidden > 2048 || d->intermediate < 64 || d->intermediate % 64) {
         set_err("unsupported n_layers/hidden/intermediate (%d/%d/%d)", d->n_layers, d->hidden, d->intermediate);
         return VLA_ERR_SHAPE;
     }
@@ -267,13 +315,14 @@ int ensure_capacity(vla_ctx* c, int n_steps) {
     if (c->e) {
         c->release(c->e, (size_t)c->nb_cap * E * 4);
         c->release(c->z1, (size_t)c->nb_cap * H * 4);
-        c->release(c->cbf, (size_t)c->nb_cap * H * 2);
+        c->release(c->cbf, (size_t)std::max(c->nb_cap, 64) * H * 2);
         c->release(c->modtab, (size_t)c->nb_cap * c->mod_ld * 4);
     }
     int rc;
     if ((rc = c->alloc((void**)&c->e, (size_t)nb * E * 4))) return rc;
     if ((rc = c->alloc((void**)&c->z1, (size_t)nb * H * 4))) return rc;
-    if ((rc = c->alloc((void**)&c->cbf, (size_t)nb * H * 2))) return rc;
+    if ((rc = c->alloc((void**)&c->cbf, (size_t)std::max(nb, 64) * H * 2))) return rc;
+    HIPC(hipMemsetAsync(c->cbf, 0, (size_t)std::max(nb, 64) * H * 2, c->stream));
     if ((rc = c->alloc((void**)&c->modtab, (size_t)nb * c->mod_ld * 4))) return rc;
     c->nb_cap = nb;
     return VLA_OK;
@@ -282,34 +331,57 @@ int ensure_capacity(vla_ctx* c, int n_steps) {
 // ------------------------------- launchers ---------------------------------
 
 template <int MT, int NT, bool W8>
-int launch_gemm_t(int epi, const GemmParams& p, dim3 grid, hipStream_t s) {
+int launch_tiled_t(int epi, const GemmParams& p, dim3 grid, hipStream_t s) {
     switch (epi) {
-        case EPI_BIAS_F32: hipLaunchKernelGGL((gemm_kernel<MT, NT, W8, EPI_BIAS_F32>), grid, dim3(256), 0, s, p); break;
-        case EPI_RESID: hipLaunchKernelGGL((gemm_kernel<MT, NT, W8, EPI_RESID>), grid, dim3(256), 0, s, p); break;
-        case EPI_QKV_ROPE: hipLaunchKernelGGL((gemm_kernel<MT, NT, W8, EPI_QKV_ROPE>), grid, dim3(256), 0, s, p); break;
-        case EPI_SWIGLU: hipLaunchKernelGGL((gemm_kernel<MT, NT, W8, EPI_SWIGLU>), grid, dim3(256), 0, s, p); break;
-        default: set_err("bad epilogue"); return VLA_ERR_ARG;
+        case EPI_BIAS_F32: VLA_LAUNCH((gemm_kernel<MT, NT, W8, EPI_BIAS_F32>), grid, dim3(256), 0, s, p); break;
+        case EPI_RESID: VLA_LAUNCH((gemm_kernel<MT, NT, W8, EPI_RESID>), grid, dim3(256), 0, s, p); break;
+        case EPI_QKV_ROPE: VLA_LAUNCH((gemm_kernel<MT, NT, W8, EPI_QKV_ROPE>), grid, dim3(256), 0, s, p); break;
+        case EPI_SWIGLU: VLA_LAUNCH((gemm_kernel<MT, NT, W8, EPI_SWIGLU>), grid, dim3(256), 0, s, p); break;
+        default: set_err("bad tiled epilogue %d", epi); return VLA_ERR_ARG;
     }
     HIPC(hipGetLastError());
     return VLA_OK;
 }
 
+template <bool W8>
+int launch_skinny_t(int epi, const GemmParams& p, dim3 grid, hipStream_t s) {
+    switch (epi) {
+        case EPI_BIAS_F32: VLA_LAUNCH((skinny_gemm_kernel<W8, EPI_BIAS_F32>), grid, dim3(512), 0, s, p); break;
+        case EPI_RESID: VLA_LAUNCH((skinny_gemm_kernel<W8, EPI_RESID>), grid, dim3(512), 0, s, p); break;
+        case EPI_QKV_ROPE: VLA_LAUNCH((skinny_gemm_kernel<W8, EPI_QKV_ROPE>), grid, dim3(512), 0, s, p); break;
+        case EPI_SWIGLU: VLA_LAUNCH((skinny_gemm_kernel<W8, EPI_SWIGLU>), grid, dim3(512), 0, s, p); break;
+        case EPI_PARTIAL: VLA_LAUNCH((skinny_gemm_kernel<W8, EPI_PARTIAL>), grid, dim3(512), 0, s, p); break;
+        default: set_err("bad skinny epilogue %d", epi); return VLA_ERR_ARG;
+    }
+    HIPC(hipGetLastError());
+    return VLA_OK;
+}
+
+// Launch one GEMM; a split skinny GEMM writes partials (EPI_PARTIAL) instead
+// of applying `epi`, which must then be EPI_RESID (summed by resnorm).
 int launch_gemm(vla_ctx* c, const Linear& lin, const GemmCfg& cfg, bool w8, int epi, GemmParams p) {
     p.W = lin.w;
     p.wscale = lin.scale;
     p.N = lin.N;
     p.K = lin.K;
-    p.ksplit = cfg.ksplit;
-    p.kchunk = cfg.kchunk;
+    p.kw = cfg.kw;
     p.ws = c->ws;
-    p.counters = c->counters;
-    dim3 grid(lin.N / cfg.NT, (p.M + cfg.MT - 1) / cfg.MT, cfg.ksplit);
-    if (cfg.MT == 64 && cfg.NT == 32) return w8 ? launch_gemm_t<64, 32, true>(epi, p, grid, c->stream)
-                                                : launch_gemm_t<64, 32, false>(epi, p, grid, c->stream);
-    if (cfg.MT == 128 && cfg.NT == 128) return w8 ? launch_gemm_t<128, 128, true>(epi, p, grid, c->stream)
-                                                  : launch_gemm_t<128, 128, false>(epi, p, grid, c->stream);
-    if (cfg.MT == 128 && cfg.NT == 64) return w8 ? launch_gemm_t<128, 64, true>(epi, p, grid, c->stream)
-                                                 : launch_gemm_t<128, 64, false>(epi, p, grid, c->stream);
+    if (cfg.skinny) {
+        if (cfg.ksplit > 1) {
+            if (epi != EPI_RESID) {
+                set_err("split-K only for residual epilogues");
+                return VLA_ERR_ARG;
+            }
+            epi = EPI_PARTIAL;
+        }
+        dim3 grid(cfg.gx, cfg.ksplit);
+        return w8 ? launch_skinny_t<true>(epi, p, grid, c->stream) : launch_skinny_t<false>(epi, p, grid, c->stream);
+    }
+    dim3 grid(lin.N / cfg.NT, (p.M + cfg.MT - 1) / cfg.MT);
+    if (cfg.NT == 128) return w8 ? launch_tiled_t<128, 128, true>(epi, p, grid, c->stream)
+                                 : launch_tiled_t<128, 128, false>(epi, p, grid, c->stream);
+    if (cfg.NT == 64) return w8 ? launch_tiled_t<128, 64, true>(epi, p, grid, c->stream)
+                                : launch_tiled_t<128, 64, false>(epi, p, grid, c->stream);
     set_err("no GEMM tile %dx%d", cfg.MT, cfg.NT);
     return VLA_ERR_SHAPE;
 }
@@ -323,50 +395,78 @@ int enqueue_prologue(vla_ctx* c, int n_steps, const float* ts_direct) {
     HIPC(hipGetLastError());
     long waves = (long)nb * H;
     hipLaunchKernelGGL(small_linear_silu_kernel, dim3((int)((waves * 64 + 255) / 256)), dim3(256), 0, c->stream,
-                       c->e, c->t1_w, c->t1_b, c->z1, (uint16_t*)nullptr, nb, H, E);
+                       c->e, c->t1_w, c->t1_b, c->z1, (uint16_t*)nullptr, nb, H, E, 0);
     HIPC(hipGetLastError());
     hipLaunchKernelGGL(small_linear_silu_kernel, dim3((int)((waves * 64 + 255) / 256)), dim3(256), 0, c->stream,
-                       c->z1, c->t2_w, c->t2_b, (float*)nullptr, c->cbf, nb, H, H);
+                       c->z1, c->t2_w, c->t2_b, (float*)nullptr, c->cbf, nb, H, H, nb <= 64 ? 1 : 0);
     HIPC(hipGetLastError());
     GemmParams p{};
     p.A = c->cbf;
     p.lda = H;
+    p.a_frag = nb <= 64 ? 1 : 0;
     p.M = nb;
     p.out_f32 = c->modtab;
     p.bias = c->mod_bias;
-    GemmCfg cfg = choose_gemm(nb, c->mod.N, c->mod.K);
-    cfg.ksplit = 1;  // the modulation GEMM has plenty of column tiles
-    cfg.kchunk = c->mod.K;
-    return launch_gemm(c, c->mod, cfg, false, EPI_BIAS_F32, p);
+    return launch_gemm(c, c->mod, choose_gemm(nb, c->mod.N, c->mod.K, false), false, EPI_BIAS_F32, p);
 }
 
-int launch_attention(vla_ctx* c, int l, const uint16_t* pk, const uint16_t* pv, const uint16_t* q,
-                     const uint16_t* kn, const uint16_t* vn, uint16_t* o) {
+int enqueue_prefix_repack(vla_ctx* c, const uint16_t* pk, const uint16_t* pv) {
     const vla_dims& d = c->d;
-    AttnParams ap{};
-    ap.ab = c->ab;
-    ap.pk = pk;
-    ap.pv = pv;
-    ap.q = q;
-    ap.kn = kn;
-    ap.vn = vn;
-    ap.o = o;
-    ap.layer = l;
-    ap.L = d.n_layers;
-    ap.P = d.prefix_len;
-    ap.T = d.horizon;
-    ap.nq = d.n_q_heads;
-    ap.nkv = d.n_kv_heads;
-    ap.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
-    const int G = d.n_q_heads / d.n_kv_heads;
-    dim3 ag((G * d.horizon + 63) / 64, d.n_kv_heads, d.batch);
-    if (d.head_dim == 128) hipLaunchKernelGGL(attn_kernel<128>, ag, dim3(256), 0, c->stream, ap);
-    else hipLaunchKernelGGL(attn_kernel<64>, ag, dim3(256), 0, c->stream, ap);
+    if (d.prefix_len == 0) return VLA_OK;
+    long total = (long)d.batch * d.n_layers * d.prefix_len * d.n_kv_heads * (d.head_dim / 8);
+    hipLaunchKernelGGL(prefix_repack_kernel, dim3((int)((total + 255) / 256)), dim3(256), 0, c->stream, c->ab, pk, pv,
+                       c->kcat, c->vcat, c->kv, d.batch, d.prefix_len);
     HIPC(hipGetLastError());
     return VLA_OK;
 }
 
-int launch_block_gemm(vla_ctx* c, int which, int step, int l) {
+int launch_attention(vla_ctx* c, int l, const uint16_t* q, uint16_t* o, int ofrag) {
+    ProfScope prof(VLA_KERNEL_ATTN);
+    const vla_dims& d = c->d;
+    AttnParams ap{};
+    ap.q = q;
+    ap.kcat = c->kcat;
+    ap.vcat = c->vcat;
+    ap.o = o;
+    ap.kv = c->kv;
+    ap.layer = l;
+    ap.S = d.prefix_len + d.horizon;
+    ap.T = d.horizon;
+    ap.nq = d.n_q_heads;
+    ap.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
+    ap.ofrag = ofrag;
+    const int G = d.n_q_heads / d.n_kv_heads;
+    dim3 ag((G * d.horizon + 15) / 16, d.n_kv_heads, d.batch);
+    // few workgroups (small batch): 8 waves per workgroup split the keys finer
+    const bool wide = (long)ag.x * ag.y * ag.z < 512;
+    if (d.head_dim == 128) {
+        if (wide) VLA_LAUNCH((attn_kernel<128, 8>), ag, dim3(512), 0, c->stream, ap);
+        else VLA_LAUNCH((attn_kernel<128, 4>), ag, dim3(256), 0, c->stream, ap);
+    } else {
+        if (wide) VLA_LAUNCH((attn_kernel<64, 8>), ag, dim3(512), 0, c->stream, ap);
+        else VLA_LAUNCH((attn_kernel<64, 4>), ag, dim3(256), 0, c->stream, ap);
+    }
+    HIPC(hipGetLastError());
+    return VLA_OK;
+}
+
+// Residual + AdaRMSNorm over all rows (see resnorm_kernel); skipped when it
+// would do nothing.
+int launch_resnorm(vla_ctx* c, int step, int S, int gate_off, int scale_off, int shift_off, uint16_t* y,
+                   float* yf = nullptr) {
+    if (S == 0 && !y && !yf) return VLA_OK;
+    const vla_dims& d = c->d;
+    hipLaunchKernelGGL(resnorm_kernel, dim3(c->M), dim3(256), 0, c->stream, c->h, c->ws, S, c->modtab, gate_off,
+                       scale_off, shift_off, y, yf, c->M, d.hidden, d.horizon, d.batch, step, c->mod_ld, d.rms_eps,
+                       c->afrag);
+    HIPC(hipGetLastError());
+    return VLA_OK;
+}
+
+// One block GEMM of layer l at Euler step `step`. Returns through *S the
+// number of split-K partials left in ws for resnorm (0: applied in place).
+int launch_block_gemm(vla_ctx* c, int which, int step, int l, int* S) {
+    ProfScope prof(which);
     const vla_dims& d = c->d;
     const int H = d.hidden;
     GemmParams p{};
@@ -376,12 +476,18 @@ int launch_block_gemm(vla_ctx* c, int which, int step, int l) {
     p.mod = c->modtab;
     p.mod_ld = c->mod_ld;
     p.step = step;
+    p.a_frag = c->afrag;
+    p.afrag = c->afrag;
+    if (S) *S = 0;
     if (which == VLA_KERNEL_QKV) {
         p.A = c->y;
         p.lda = H;
         p.q = c->q;
-        p.kn = c->kn;
-        p.vn = c->vn;
+        p.kcat = c->kcat;
+        p.vcat = c->vcat;
+        p.kv = c->kv;
+        p.layer = l;
+        p.P = d.prefix_len;
         p.rope = c->rope;
         p.nq = d.n_q_heads;
         p.nkv = d.n_kv_heads;
@@ -390,11 +496,12 @@ int launch_block_gemm(vla_ctx* c, int which, int step, int l) {
     }
     if (which == VLA_KERNEL_O || which == VLA_KERNEL_DOWN) {
         const bool o = which == VLA_KERNEL_O;
+        const Linear& lin = o ? c->wo[l] : c->wd[l];
         p.A = o ? c->o : c->act;
         p.lda = o ? c->qd : d.intermediate;
         p.out_f32 = c->h;
         p.gate_off = (6 * l + (o ? 2 : 5)) * H;
-        const Linear& lin = o ? c->wo[l] : c->wd[l];
+        if (S && lin.cfg.skinny && lin.cfg.ksplit > 1) *S = lin.cfg.ksplit;
         return launch_gemm(c, lin, lin.cfg, c->w8, EPI_RESID, p);
     }
     if (which == VLA_KERNEL_GATE_UP) {
@@ -407,47 +514,47 @@ int launch_block_gemm(vla_ctx* c, int which, int step, int l) {
     return VLA_ERR_ARG;
 }
 
-int enqueue_layer(vla_ctx* c, int step, int l, int n_steps) {
+// Layer l of Euler step `step`. On entry y holds the layer's first AdaRMSNorm
+// output; on exit h holds the layer output and, when norm_next, y holds the
+// next layer's first AdaRMSNorm output.
+int enqueue_layer(vla_ctx* c, int step, int l, bool norm_next, float* yf_final = nullptr) {
+    const int H = c->d.hidden, L = c->d.n_layers;
+    int rc, S = 0;
+    if ((rc = launch_block_gemm(c, VLA_KERNEL_QKV, step, l, nullptr))) return rc;
+    if ((rc = launch_attention(c, l, c->q, c->o, c->afrag))) return rc;
+    if ((rc = launch_block_gemm(c, VLA_KERNEL_O, step, l, &S))) return rc;
+    if ((rc = launch_resnorm(c, step, S, (6 * l + 2) * H, (6 * l + 3) * H, (6 * l + 4) * H, c->y))) return rc;
+    if ((rc = launch_block_gemm(c, VLA_KERNEL_GATE_UP, step, l, nullptr))) return rc;
+    if ((rc = launch_block_gemm(c, VLA_KERNEL_DOWN, step, l, &S))) return rc;
+    if (norm_next) return launch_resnorm(c, step, S, (6 * l + 5) * H, (6 * (l + 1)) * H, (6 * (l + 1) + 1) * H, c->y);
+    if (yf_final) return launch_resnorm(c, step, S, (6 * l + 5) * H, 6 * L * H, (6 * L + 1) * H, nullptr, yf_final);
+    return launch_resnorm(c, step, S, (6 * l + 5) * H, 0, 0, nullptr);
+}
+
+int enqueue_step_start(vla_ctx* c, int k, const float* x_direct) {
     const vla_dims& d = c->d;
-    const int H = d.hidden, M = c->M, B = d.batch, T = d.horizon;
-    const int rows_blocks = (M + 3) / 4;
-    int rc;
-    // AdaRMSNorm (scale1, shift1)
-    hipLaunchKernelGGL(adarms_kernel, dim3(rows_blocks), dim3(256), 0, c->stream, c->h, c->y, c->modtab, M, H, T, B,
-                       step, c->mod_ld, (6 * l + 0) * H, (6 * l + 1) * H, d.rms_eps);
+    const int H = d.hidden;
+    // in-projection + first AdaRMSNorm of layer 0
+    hipLaunchKernelGGL(inproj_norm_kernel, dim3(c->M), dim3(256), 0, c->stream, c->ab, k == 0 ? 1 : 0, x_direct,
+                       c->in_wT, c->in_b, c->h, c->y, c->modtab, 0, H, c->M, H, d.action_dim, d.horizon, d.batch, k,
+                       c->mod_ld, d.rms_eps, c->afrag);
     HIPC(hipGetLastError());
-    // QKV + RoPE
-    if ((rc = launch_block_gemm(c, VLA_KERNEL_QKV, step, l))) return rc;
-    // attention
-    if ((rc = launch_attention(c, l, nullptr, nullptr, c->q, c->kn, c->vn, c->o))) return rc;
-    // O projection + gated residual (gate1)
-    if ((rc = launch_block_gemm(c, VLA_KERNEL_O, step, l))) return rc;
-    // AdaRMSNorm (scale2, shift2)
-    hipLaunchKernelGGL(adarms_kernel, dim3(rows_blocks), dim3(256), 0, c->stream, c->h, c->y, c->modtab, M, H, T, B,
-                       step, c->mod_ld, (6 * l + 3) * H, (6 * l + 4) * H, d.rms_eps);
-    HIPC(hipGetLastError());
-    // gate_up + SwiGLU
-    if ((rc = launch_block_gemm(c, VLA_KERNEL_GATE_UP, step, l))) return rc;
-    // down + gated residual (gate2)
-    if ((rc = launch_block_gemm(c, VLA_KERNEL_DOWN, step, l))) return rc;
-    (void)n_steps;
     return VLA_OK;
 }
 
 int enqueue_forward(vla_ctx* c, int n_steps) {
     const vla_dims& d = c->d;
-    const int H = d.hidden, M = c->M;
+    const int M = c->M, L = d.n_layers;
     int rc;
+    if ((rc = enqueue_prefix_repack(c, nullptr, nullptr))) return rc;
     if ((rc = enqueue_prologue(c, n_steps, nullptr))) return rc;
     for (int k = 0; k < n_steps; ++k) {
-        hipLaunchKernelGGL(inproj_kernel, dim3((M * H + 255) / 256), dim3(256), 0, c->stream, c->ab, k == 0 ? 1 : 0,
-                           (const float*)nullptr, c->in_w, c->in_b, c->h, M, H, d.action_dim);
-        HIPC(hipGetLastError());
-        for (int l = 0; l < d.n_layers; ++l)
-            if ((rc = enqueue_layer(c, k, l, n_steps))) return rc;
-        hipLaunchKernelGGL(final_euler_kernel, dim3((M + 3) / 4), dim3(256), 4 * H * sizeof(float), c->stream, c->ab,
-                           k == 0 ? 1 : 0, c->h, c->modtab, c->out_w, c->out_b, M, H, d.action_dim, d.horizon,
-                           d.batch, k, n_steps, c->mod_ld, 6 * d.n_layers * H, (6 * d.n_layers + 1) * H, d.rms_eps);
+        if ((rc = enqueue_step_start(c, k, nullptr))) return rc;
+        for (int l = 0; l < L; ++l)
+            if ((rc = enqueue_layer(c, k, l, l + 1 < L, l + 1 < L ? nullptr : c->yf))) return rc;
+        hipLaunchKernelGGL(outproj_euler_kernel, dim3(M, (d.action_dim + 15) / 16), dim3(256), 0, c->stream,
+                           c->ab, k == 0 ? 1 : 0, c->yf, c->out_w, c->out_b, M, d.hidden, d.action_dim, d.horizon, k,
+                           n_steps);
         HIPC(hipGetLastError());
     }
     return VLA_OK;
@@ -516,6 +623,14 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
     // small weights, copied as given
     if ((rc = copy_in(c, &c->in_w, w->in_w, (size_t)H * A))) return rc;
     if ((rc = copy_in(c, &c->in_b, w->in_b, H))) return rc;
+    {
+        std::vector<uint16_t> win((size_t)H * A), wint((size_t)A * H);
+        HIPC(hipMemcpy(win.data(), w->in_w, win.size() * 2, hipMemcpyDeviceToHost));
+        for (int n = 0; n < H; ++n)
+            for (int a = 0; a < A; ++a) wint[(size_t)a * H + n] = win[(size_t)n * A + a];
+        if ((rc = c->alloc((void**)&c->in_wT, wint.size() * 2))) return rc;
+        HIPC(hipMemcpy(c->in_wT, wint.data(), wint.size() * 2, hipMemcpyHostToDevice));
+    }
     if ((rc = copy_in(c, &c->out_w, w->out_w, (size_t)A * H))) return rc;
     if ((rc = copy_in(c, &c->out_b, w->out_b, A))) return rc;
     if ((rc = copy_in(c, &c->t1_w, w->t1_w, (size_t)H * E))) return rc;
@@ -554,10 +669,10 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
             int rows[1] = {H};
             if ((rc = pack_linear(c, c->wd[l], H, I, srcs, scs, 1, rows, 0, dh))) return rc;
         }
-        c->qkv[l].cfg = choose_gemm(c->M, c->qkv[l].N, c->qkv[l].K);
-        c->wo[l].cfg = choose_gemm(c->M, c->wo[l].N, c->wo[l].K);
-        c->gu[l].cfg = choose_gemm(c->M, c->gu[l].N, c->gu[l].K);
-        c->wd[l].cfg = choose_gemm(c->M, c->wd[l].N, c->wd[l].K);
+        c->qkv[l].cfg = choose_gemm(c->M, c->qkv[l].N, c->qkv[l].K, false);
+        c->wo[l].cfg = choose_gemm(c->M, c->wo[l].N, c->wo[l].K, true);
+        c->gu[l].cfg = choose_gemm(c->M, c->gu[l].N, c->gu[l].K, false);
+        c->wd[l].cfg = choose_gemm(c->M, c->wd[l].N, c->wd[l].K, true);
     }
 
     // rotary table
@@ -569,22 +684,30 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
     // working buffers
     const size_t M = c->M;
     if ((rc = c->alloc((void**)&c->h, M * H * 4))) return rc;
-    if ((rc = c->alloc((void**)&c->y, M * H * 2))) return rc;
+    if ((rc = c->alloc((void**)&c->yf, M * H * 4))) return rc;
+    c->afrag = c->M <= 64 ? 1 : 0;
+    const size_t MR = c->afrag ? 64 : M;  // activation rows (fragment order pads to 64 zero rows)
+    if ((rc = c->alloc((void**)&c->y, MR * H * 2))) return rc;
+    HIPC(hipMemsetAsync(c->y, 0, MR * H * 2, c->stream));
     if ((rc = c->alloc((void**)&c->q, M * c->qd * 2))) return rc;
-    if ((rc = c->alloc((void**)&c->kn, M * c->kvd * 2))) return rc;
-    if ((rc = c->alloc((void**)&c->vn, M * c->kvd * 2))) return rc;
-    if ((rc = c->alloc((void**)&c->o, M * c->qd * 2))) return rc;
-    if ((rc = c->alloc((void**)&c->act, M * I * 2))) return rc;
+    if ((rc = c->alloc((void**)&c->o, MR * c->qd * 2))) return rc;
+    if ((rc = c->alloc((void**)&c->act, MR * I * 2))) return rc;
+    HIPC(hipMemsetAsync(c->o, 0, MR * c->qd * 2, c->stream));
+    HIPC(hipMemsetAsync(c->act, 0, MR * I * 2, c->stream));
+    c->kv.L = L;
+    c->kv.nkv = d.n_kv_heads;
+    c->kv.dh = dh;
+    c->kv.S_pad = (d.prefix_len + d.horizon + 31) / 32 * 32;
+    const size_t kv_elems = (size_t)d.batch * L * d.n_kv_heads * c->kv.S_pad * dh;
+    if ((rc = c->alloc((void**)&c->kcat, kv_elems * 2))) return rc;
+    if ((rc = c->alloc((void**)&c->vcat, kv_elems * 2))) return rc;
+    // padded keys past P + T stay zero (they are masked; zero values keep 0 * v finite)
+    HIPC(hipMemsetAsync(c->kcat, 0, kv_elems * 2, c->stream));
+    HIPC(hipMemsetAsync(c->vcat, 0, kv_elems * 2, c->stream));
     size_t ws_elems = 16;
-    size_t tiles = 16;
-    const Linear* lins[4] = {&c->qkv[0], &c->wo[0], &c->gu[0], &c->wd[0]};
-    for (const Linear* ln : lins) {
-        if (ln->cfg.ksplit > 1) ws_elems = std::max(ws_elems, (size_t)ln->cfg.ksplit * M * ln->N);
-        tiles = std::max(tiles, (size_t)((M + ln->cfg.MT - 1) / ln->cfg.MT) * (ln->N / ln->cfg.NT));
-    }
+    for (const Linear* ln : {&c->wo[0], &c->wd[0]})
+        if (ln->cfg.skinny && ln->cfg.ksplit > 1) ws_elems = std::max(ws_elems, (size_t)ln->cfg.ksplit * M * H);
     if ((rc = c->alloc((void**)&c->ws, ws_elems * 4))) return rc;
-    if ((rc = c->alloc((void**)&c->counters, tiles * sizeof(int)))) return rc;
-    HIPC(hipMemsetAsync(c->counters, 0, tiles * sizeof(int), c->stream));
     if ((rc = c->alloc((void**)&c->ab, sizeof(ArgBlock)))) return rc;
     HIPC(hipMemsetAsync(c->ab, 0, sizeof(ArgBlock), c->stream));
     if ((rc = ensure_capacity(c, 10))) return rc;
@@ -733,9 +856,12 @@ int vla_test_layer(vla_ctx* c, const void* prefix_k, const void* prefix_v, const
     HIPC(hipSetDevice(c->device));
     if ((rc = ensure_capacity(c, n_steps))) return rc;
     if ((rc = set_args(c, prefix_k, prefix_v, nullptr, t_schedule, nullptr))) return rc;
+    if ((rc = enqueue_prefix_repack(c, (const uint16_t*)prefix_k, (const uint16_t*)prefix_v))) return rc;
     if ((rc = enqueue_prologue(c, n_steps, t_schedule))) return rc;
     HIPC(hipMemcpyAsync(c->h, h_in, (size_t)c->M * c->d.hidden * 4, hipMemcpyDeviceToDevice, c->stream));
-    if ((rc = enqueue_layer(c, step, layer, n_steps))) return rc;
+    const int H = c->d.hidden;
+    if ((rc = launch_resnorm(c, step, 0, 0, 6 * layer * H, (6 * layer + 1) * H, c->y))) return rc;
+    if ((rc = enqueue_layer(c, step, layer, false))) return rc;
     HIPC(hipMemcpyAsync(h_out, c->h, (size_t)c->M * c->d.hidden * 4, hipMemcpyDeviceToDevice, c->stream));
     HIPC(hipStreamSynchronize(c->stream));
     return VLA_OK;
@@ -759,9 +885,14 @@ int vla_test_attention(vla_ctx* c, const void* prefix_k, const void* prefix_v, i
         return VLA_ERR_ARG;
     }
     HIPC(hipSetDevice(c->device));
-    if ((rc = launch_attention(c, layer, (const uint16_t*)prefix_k, (const uint16_t*)prefix_v, (const uint16_t*)q,
-                               (const uint16_t*)k_new, (const uint16_t*)v_new, (uint16_t*)o_out)))
-        return rc;
+    const vla_dims& d = c->d;
+    if ((rc = enqueue_prefix_repack(c, (const uint16_t*)prefix_k, (const uint16_t*)prefix_v))) return rc;
+    long n = (long)d.batch * d.n_kv_heads * d.horizon * (d.head_dim / 8);
+    hipLaunchKernelGGL(chunk_kv_store_kernel, dim3((int)((n + 255) / 256)), dim3(256), 0, c->stream,
+                       (const uint16_t*)k_new, (const uint16_t*)v_new, c->kcat, c->vcat, c->kv, layer, d.prefix_len,
+                       d.batch, d.horizon);
+    HIPC(hipGetLastError());
+    if ((rc = launch_attention(c, layer, (const uint16_t*)q, (uint16_t*)o_out, 0))) return rc;
     HIPC(hipStreamSynchronize(c->stream));
     return VLA_OK;
 }
@@ -783,13 +914,17 @@ int vla_profile_kernel(vla_ctx* c, int kernel, int iters, double* us_per_launch,
     std::vector<hipEvent_t> ev(2 * iters);
     for (auto& e : ev) HIPC(hipEventCreate(&e));
     int rc = VLA_OK;
+    // run whole layers as in the loop (step 0 of the last call's modulation
+    // table); only the target family's launches record their events
+    g_prof_target = kernel;
     for (int i = 0; i < iters && rc == VLA_OK; ++i) {
         const int l = i % L;
-        HIPC(hipEventRecord(ev[2 * i], c->stream));
-        if (kernel == VLA_KERNEL_ATTN) rc = launch_attention(c, l, nullptr, nullptr, c->q, c->kn, c->vn, c->o);
-        else rc = launch_block_gemm(c, kernel, 0, l);
-        HIPC(hipEventRecord(ev[2 * i + 1], c->stream));
+        g_prof_start = ev[2 * i];
+        g_prof_stop = ev[2 * i + 1];
+        rc = enqueue_layer(c, 0, l, l + 1 < L, l + 1 < L ? nullptr : c->yf);
     }
+    g_prof_target = -1;
+    g_prof_start = g_prof_stop = nullptr;
     HIPC(hipStreamSynchronize(c->stream));
     double tot = 0;
     for (int i = 0; i < iters; ++i) {
