@@ -56,6 +56,10 @@ extern "C" {
 
 /* Options for vla_set_option. */
 #define VLA_OPT_USE_GRAPH 1 /* 1 (default): replay a captured hipGraph per n_steps; 0: launch kernels eagerly */
+#define VLA_OPT_PERSISTENT 2 /* 1 (default): for shapes it supports (batch*horizon <= 64, 8 | n_q_heads, ...),
+                                 run the whole loop as one persistent cooperative kernel; 0: kernel-per-stage path */
+/* Query for vla_get_option: 1 when the next vla_denoise call uses the persistent kernel. */
+#define VLA_OPT_PERSISTENT_ACTIVE 3
 
 typedef struct vla_ctx vla_ctx;
 
@@ -141,6 +145,9 @@ int vla_set_stream(vla_ctx* ctx, void* stream);
 
 /* Set an option (VLA_OPT_*). Returns VLA_OK or VLA_ERR_ARG. */
 int vla_set_option(vla_ctx* ctx, int option, int value);
+
+/* Read an option (VLA_OPT_*) into *value. Returns VLA_OK or VLA_ERR_ARG. */
+int vla_get_option(const vla_ctx* ctx, int option, int* value);
 
 /* Synchronize, free everything owned by ctx. NULL-safe. */
 void vla_expert_destroy(vla_ctx* ctx);

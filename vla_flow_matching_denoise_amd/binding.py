@@ -22,10 +22,13 @@ VLA_ERR_SHAPE = -2
 VLA_ERR_OOM = -3
 VLA_ERR_HIP = -4
 VLA_OPT_USE_GRAPH = 1
+VLA_OPT_PERSISTENT = 2
+VLA_OPT_PERSISTENT_ACTIVE = 3
 
 # every symbol include/vla_expert.h declares
 EXPORTED = (
-    "vla_expert_create", "vla_denoise", "vla_set_stream", "vla_set_option", "vla_expert_destroy",
+    "vla_expert_create", "vla_denoise", "vla_set_stream", "vla_set_option", "vla_get_option",
+    "vla_expert_destroy",
     "vla_last_error", "vla_device_bytes", "vla_test_modulation", "vla_test_layer",
     "vla_test_attention", "vla_profile_kernel",
 )
@@ -73,6 +76,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vla_set_stream.argtypes = [_P, _P]
     lib.vla_set_option.restype = ctypes.c_int
     lib.vla_set_option.argtypes = [_P, ctypes.c_int, ctypes.c_int]
+    lib.vla_get_option.argtypes = [_P, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+    lib.vla_get_option.restype = ctypes.c_int
     lib.vla_expert_destroy.restype = None
     lib.vla_expert_destroy.argtypes = [_P]
     lib.vla_last_error.restype = ctypes.c_char_p
@@ -138,6 +143,12 @@ def vla_set_stream(ctx: int, stream: Optional[int]) -> int:
 
 def vla_set_option(ctx: int, option: int, value: int) -> int:
     return _check(lib().vla_set_option(ctx, option, value))
+
+
+def vla_get_option(ctx: int, option: int) -> int:
+    v = ctypes.c_int(0)
+    _check(lib().vla_get_option(ctx, option, ctypes.byref(v)))
+    return int(v.value)
 
 
 def vla_expert_destroy(ctx: Optional[int]) -> None:

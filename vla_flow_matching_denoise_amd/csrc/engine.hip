@@ -17,6 +17,7 @@
 
 #include "../../include/vla_expert.h"
 #include "kernels.h"
+#include "kernels_persist.h"
 
 namespace {
 
@@ -148,6 +149,15 @@ struct vla_ctx {
     uint16_t* cbf = nullptr;
 
     std::map<int, hipGraphExec_t> graphs;
+
+    // persistent small-batch path (one cooperative launch per call)
+    bool persist_ok = false, use_persist = true;
+    int pn_cap = 0;                // Euler steps the write-once slots hold
+    PersistParams pp{};
+    std::vector<std::pair<void*, size_t>> pbufs;
+    const uint8_t** wptrs = nullptr;  // device array: per-layer QKV, O, gate_up, down weights (4 x L)
+    unsigned *lflag = nullptr, *gflag = nullptr;
+    int* perr = nullptr;
 
     int alloc(void** p, size_t n) {
         if (n == 0) n = 16;
@@ -560,6 +570,171 @@ int enqueue_forward(vla_ctx* c, int n_steps) {
     return VLA_OK;
 }
 
+// Register-resident shape classes of the persistent kernel: column tiles per
+// workgroup and k-steps per wave of each GEMM phase, and H / 256.
+struct PersistShape {
+    int ntq, nsq, nto, nso, ntg, nsg, ntd, nsd, cpt;
+    const void* fn;
+    bool operator==(const PersistShape& o) const {
+        return ntq == o.ntq && nsq == o.nsq && nto == o.nto && nso == o.nso && ntg == o.ntg && nsg == o.nsg &&
+               ntd == o.ntd && nsd == o.nsd && cpt == o.cpt;
+    }
+};
+#define VLA_PSHAPE(a, b, c_, d_, e, f, g, h, i) \
+    PersistShape{a, b, c_, d_, e, f, g, h, i, (const void*)persist_kernel<a, b, c_, d_, e, f, g, h, i>}
+static const PersistShape kPersistShapes[] = {
+    VLA_PSHAPE(1, 4, 2, 1, 2, 4, 2, 2, 4),  // hidden 1024, 16 q heads of 128, SwiGLU 4096
+    VLA_PSHAPE(1, 2, 1, 1, 1, 2, 1, 1, 2),  // hidden 512, 8 q heads of 128, SwiGLU 1024
+};
+#undef VLA_PSHAPE
+
+static int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+PersistShape persist_shape(const vla_dims& d) {
+    const int hq = d.n_q_heads / PX, Ix = d.intermediate / PX, H = d.hidden;
+    PersistShape s{};
+    s.ntq = cdiv((hq + 2) * d.head_dim / 16, PJ);
+    s.nsq = cdiv(H / 32, PWAVES);
+    s.nto = cdiv(H / 16, PJ);
+    s.nso = cdiv(hq * d.head_dim / 32, PWAVES);
+    s.ntg = cdiv(2 * Ix / 16, PJ);
+    s.nsg = s.nsq;
+    s.ntd = s.nto;
+    s.nsd = cdiv(Ix / 32, PWAVES);
+    s.cpt = H / 256;
+    for (const PersistShape& k : kPersistShapes)
+        if (k == s) return k;
+    return s;  // fn == nullptr: no instantiation for this shape
+}
+
+bool persist_supported(const vla_ctx* c) {
+    const vla_dims& d = c->d;
+    if (c->w8 || c->M > 64 || d.head_dim != 128 || d.n_q_heads % PX) return false;
+    const int hq = d.n_q_heads / PX, G = d.n_q_heads / d.n_kv_heads;
+    if (hq < 1 || G % hq) return false;                       // an XCD's heads share one KV group
+    if (d.prefix_len % 32) return false;                      // prefix blocks never straddle the chunk
+    if (d.hidden % 256 || d.intermediate % 256) return false; // whole 32-wide k-steps per XCD slice
+    if (d.batch * ((hq * d.horizon + 15) / 16) > PJ) return false;  // attention tiles per XCD
+    return persist_shape(d).fn != nullptr;
+}
+
+// Slot strides of the persistent kernel's write-once buffers (elements), and
+// the device bytes they take for n_steps Euler steps.
+void persist_strides(const vla_ctx* c, PersistParams& p) {
+    const vla_dims& d = c->d;
+    const int H = d.hidden, B = d.batch, T = d.horizon, dh = d.head_dim, hq = d.n_q_heads / PX;
+    const int Tpad = (T + 31) / 32 * 32, Ix = d.intermediate / PX, M = c->M;
+    auto rnd = [](size_t n) { return (n + 127) / 128 * 128; };
+    p.y_sl = rnd(64 * (size_t)H);
+    p.q_sl = rnd((size_t)B * hq * T * dh);
+    p.kv_sl = rnd((size_t)B * Tpad * dh);
+    p.o_sl = rnd(64 * (size_t)hq * dh);
+    p.a_sl = rnd(64 * (size_t)Ix);
+    p.p_sl = rnd((size_t)M * H);
+    p.ss_sl = rnd(32 * 64);
+    p.yf_sl = rnd((size_t)M * H);
+    p.xs_sl = rnd((size_t)M * d.action_dim);
+}
+
+size_t persist_bytes(const vla_ctx* c, int n_steps) {
+    PersistParams p{};
+    persist_strides(c, p);
+    const size_t U = (size_t)n_steps * c->d.n_layers * PX, S8 = (size_t)n_steps * PX;
+    return U * (2 * p.y_sl * 2 + p.q_sl * 2 + 2 * p.kv_sl * 2 + p.o_sl * 2 + p.a_sl * 2 + 2 * p.p_sl * 4 +
+                2 * p.ss_sl * 4) +
+           S8 * (p.ss_sl + p.yf_sl + p.xs_sl) * 4;
+}
+
+// Calls whose write-once buffers would exceed this run on the stage path.
+constexpr size_t kPersistMaxBytes = (size_t)16 << 30;
+
+int ensure_persist(vla_ctx* c, int n_steps) {
+    if (n_steps <= c->pn_cap) return VLA_OK;
+    HIPC(hipStreamSynchronize(c->stream));
+    for (auto& b : c->pbufs) c->release(b.first, b.second);
+    c->pbufs.clear();
+    c->pn_cap = 0;
+    const size_t U = (size_t)n_steps * c->d.n_layers * PX, S8 = (size_t)n_steps * PX;
+    PersistParams& p = c->pp;
+    persist_strides(c, p);
+    int rc;
+    auto get = [&](void** ptr, size_t bytes) -> int {
+        int r = c->alloc(ptr, bytes);
+        if (r) return r;
+        c->pbufs.emplace_back(*ptr, bytes);
+        hipError_t e = hipMemsetAsync(*ptr, 0, bytes, c->stream);  // zero padding rows / keys
+        if (e != hipSuccess) {
+            set_err("hipMemsetAsync failed: %s", hipGetErrorString(e));
+            return VLA_ERR_HIP;
+        }
+        return VLA_OK;
+    };
+    if ((rc = get((void**)&p.y, U * p.y_sl * 2)) || (rc = get((void**)&p.y2, U * p.y_sl * 2)) ||
+        (rc = get((void**)&p.q, U * p.q_sl * 2)) || (rc = get((void**)&p.kc, U * p.kv_sl * 2)) ||
+        (rc = get((void**)&p.vc, U * p.kv_sl * 2)) || (rc = get((void**)&p.o, U * p.o_sl * 2)) ||
+        (rc = get((void**)&p.a, U * p.a_sl * 2)) || (rc = get((void**)&p.po, U * p.p_sl * 4)) ||
+        (rc = get((void**)&p.pd, U * p.p_sl * 4)) || (rc = get((void**)&p.ss1, U * p.ss_sl * 4)) ||
+        (rc = get((void**)&p.ss2, U * p.ss_sl * 4)) || (rc = get((void**)&p.ss0, S8 * p.ss_sl * 4)) ||
+        (rc = get((void**)&p.yf, S8 * p.yf_sl * 4)) || (rc = get((void**)&p.xs, S8 * p.xs_sl * 4)))
+        return rc;
+    HIPC(hipStreamSynchronize(c->stream));
+    c->pn_cap = n_steps;
+    return VLA_OK;
+}
+
+int enqueue_persist(vla_ctx* c, int n_steps) {
+    const vla_dims& d = c->d;
+    int rc;
+    if ((rc = enqueue_prefix_repack(c, nullptr, nullptr))) return rc;
+    if ((rc = enqueue_prologue(c, n_steps, nullptr))) return rc;
+    hipLaunchKernelGGL(persist_reset_kernel, dim3(1), dim3(256), 0, c->stream, c->lflag, c->gflag, c->perr);
+    HIPC(hipGetLastError());
+    PersistParams p = c->pp;
+    p.M = c->M;
+    p.B = d.batch;
+    p.T = d.horizon;
+    p.H = d.hidden;
+    p.L = d.n_layers;
+    p.nq = d.n_q_heads;
+    p.nkv = d.n_kv_heads;
+    p.dh = d.head_dim;
+    p.I = d.intermediate;
+    p.A = d.action_dim;
+    p.P = d.prefix_len;
+    p.hq = d.n_q_heads / PX;
+    p.G = d.n_q_heads / d.n_kv_heads;
+    p.Tpad = (d.horizon + 31) / 32 * 32;
+    p.nsteps = n_steps;
+    p.Ix = d.intermediate / PX;
+    p.mod_ld = c->mod_ld;
+    p.eps = d.rms_eps;
+    p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
+    const int L = d.n_layers;
+    p.wqkv = c->wptrs;
+    p.wo = c->wptrs + L;
+    p.wgu = c->wptrs + 2 * L;
+    p.wd = c->wptrs + 3 * L;
+    p.in_wT = c->in_wT;
+    p.in_b = c->in_b;
+    p.out_w = c->out_w;
+    p.out_b = c->out_b;
+    p.mod = c->modtab;
+    p.rope = c->rope;
+    p.kcat = c->kcat;
+    p.vcat = c->vcat;
+    p.kv = c->kv;
+    p.ab = c->ab;
+    p.lflag = c->lflag;
+    p.gflag = c->gflag;
+    p.err = c->perr;
+    void* args[] = {&p};
+    HIPC(hipLaunchCooperativeKernel(persist_shape(d).fn, dim3(PX * PJ), dim3(PWAVES * 64), args, 0, c->stream));
+    const int n = c->M * d.action_dim;
+    hipLaunchKernelGGL(persist_check_kernel, dim3(8), dim3(256), 0, c->stream, c->perr, c->ab, n);
+    HIPC(hipGetLastError());
+    return VLA_OK;
+}
+
 int set_args(vla_ctx* c, const void* pk, const void* pv, const float* noise, const float* ts, float* out) {
     hipLaunchKernelGGL(set_args_kernel, dim3(1), dim3(1), 0, c->stream, c->ab, (const uint16_t*)pk,
                        (const uint16_t*)pv, noise, ts, out);
@@ -708,6 +883,21 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
     for (const Linear* ln : {&c->wo[0], &c->wd[0]})
         if (ln->cfg.skinny && ln->cfg.ksplit > 1) ws_elems = std::max(ws_elems, (size_t)ln->cfg.ksplit * M * H);
     if ((rc = c->alloc((void**)&c->ws, ws_elems * 4))) return rc;
+    c->persist_ok = persist_supported(c);
+    if (c->persist_ok) {
+        std::vector<const uint8_t*> hp(4 * (size_t)L);
+        for (int l = 0; l < L; ++l) {
+            hp[l] = (const uint8_t*)c->qkv[l].w;
+            hp[L + l] = (const uint8_t*)c->wo[l].w;
+            hp[2 * L + l] = (const uint8_t*)c->gu[l].w;
+            hp[3 * L + l] = (const uint8_t*)c->wd[l].w;
+        }
+        if ((rc = c->alloc((void**)&c->wptrs, hp.size() * sizeof(void*)))) return rc;
+        HIPC(hipMemcpy(c->wptrs, hp.data(), hp.size() * sizeof(void*), hipMemcpyHostToDevice));
+        if ((rc = c->alloc((void**)&c->lflag, PX * PJ * sizeof(unsigned)))) return rc;
+        if ((rc = c->alloc((void**)&c->gflag, 64 * sizeof(unsigned)))) return rc;
+        if ((rc = c->alloc((void**)&c->perr, 64))) return rc;
+    }
     if ((rc = c->alloc((void**)&c->ab, sizeof(ArgBlock)))) return rc;
     HIPC(hipMemsetAsync(c->ab, 0, sizeof(ArgBlock), c->stream));
     if ((rc = ensure_capacity(c, 10))) return rc;
@@ -758,6 +948,11 @@ int vla_denoise(vla_ctx* c, const void* prefix_k, const void* prefix_v, const fl
     }
     HIPC(hipSetDevice(c->device));
     if ((rc = ensure_capacity(c, n_steps))) return rc;
+    if (c->persist_ok && c->use_persist && persist_bytes(c, n_steps) <= kPersistMaxBytes) {
+        if ((rc = ensure_persist(c, n_steps))) return rc;
+        if ((rc = set_args(c, prefix_k, prefix_v, noise, t_schedule, out_actions))) return rc;
+        return enqueue_persist(c, n_steps);
+    }
     if ((rc = set_args(c, prefix_k, prefix_v, noise, t_schedule, out_actions))) return rc;
     if (!c->use_graph) return enqueue_forward(c, n_steps);
     auto it = c->graphs.find(n_steps);
@@ -806,6 +1001,25 @@ int vla_set_option(vla_ctx* c, int option, int value) {
     if (option == VLA_OPT_USE_GRAPH) {
         c->use_graph = value != 0;
         return VLA_OK;
+    }
+    if (option == VLA_OPT_PERSISTENT) {
+        c->use_persist = value != 0;
+        return VLA_OK;
+    }
+    set_err("unknown option %d", option);
+    return VLA_ERR_ARG;
+}
+
+int vla_get_option(const vla_ctx* c, int option, int* value) {
+    g_err.clear();
+    if (!c || !value) {
+        set_err("ctx or value is NULL");
+        return VLA_ERR_ARG;
+    }
+    switch (option) {
+        case VLA_OPT_USE_GRAPH: *value = c->use_graph ? 1 : 0; return VLA_OK;
+        case VLA_OPT_PERSISTENT: *value = c->use_persist ? 1 : 0; return VLA_OK;
+        case VLA_OPT_PERSISTENT_ACTIVE: *value = (c->persist_ok && c->use_persist) ? 1 : 0; return VLA_OK;
     }
     set_err("unknown option %d", option);
     return VLA_ERR_ARG;

@@ -1,0 +1,706 @@
+// Persistent denoise loop for small batches (B*T <= 64 rows), one cooperative
+// launch per call: 256 workgroups, one per CU, 32 on each of the 8 XCDs
+// (workgroup w runs on XCD w % 8). Each layer is split tensor-parallel over
+// the XCDs:
+//   XCD x owns query heads [x*hq, (x+1)*hq) and their KV group g(x) (whose
+//   K/V it computes itself), SwiGLU columns [x*I/8, (x+1)*I/8), and the
+//   matching K-slices of the O and down projections.
+// Inside an XCD, workgroups exchange data through its L2 and synchronise with
+// flags in one 128-byte line (~1 us). Across XCDs only the O and down partial
+// sums travel, written with device-scope stores and followed by one flag per
+// XCD. Every buffer that crosses workgroups is written once per call (a slot
+// per (step, layer)), so no reader can hold a stale cache line from earlier in
+// the call; the launch itself starts from clean caches. Every wait is bounded:
+// on expiry the kernel raises an error flag and runs to its end.
+//
+// Phases of one layer (L: XCD-local sync, G: cross-XCD sync):
+//   QKV+RoPE -L- attention -L- O partial -G- reduce+residual -L- norm2 -L-
+//   gate_up+SwiGLU -L- down partial -G- reduce+residual -L- norm1(next) -L-
+// Weights of the next GEMM phase are loaded into registers right after the
+// previous GEMM's MFMAs, so they stream from HBM while the syncs wait.
+#pragma once
+
+#include "kernels_layer.h"
+
+constexpr int PX = 8;          // XCDs
+constexpr int PJ = 32;         // workgroups per XCD
+constexpr int PWAVES = 8;      // waves per workgroup
+constexpr long P_SPIN = 1l << 20;
+
+struct PersistParams {
+    int M, B, T, H, L, nq, nkv, dh, I, A, P, hq, G, Tpad, nsteps;
+    int Ix;        // I / 8, SwiGLU columns per XCD
+    int mod_ld;
+    float eps, scale_log2;
+    const uint8_t* const* wqkv;  // per-layer packed weights (device arrays of L pointers)
+    const uint8_t* const* wo;
+    const uint8_t* const* wgu;
+    const uint8_t* const* wd;
+    const uint16_t* in_wT;       // [A][H]
+    const float* in_b;
+    const uint16_t* out_w;       // [A][H]
+    const float* out_b;
+    const float* mod;
+    const float2* rope;
+    const uint16_t* kcat;        // prefix keys/values (keys < P) of every (b, layer, group)
+    const uint16_t* vcat;
+    KVLayout kv;
+    const ArgBlock* ab;
+    // write-once buffers; slot (u, x) with u = step * L + layer
+    uint16_t* y;  size_t y_sl;   // A-fragment [64][H]
+    uint16_t* y2;
+    uint16_t* q;  size_t q_sl;   // [B][hq][T][dh]
+    uint16_t* kc; uint16_t* vc; size_t kv_sl;  // [B][Tpad][dh] row-major / V-fragment order
+    uint16_t* o;  size_t o_sl;   // A-fragment [64][hq*dh]
+    uint16_t* a;  size_t a_sl;   // A-fragment [64][Ix]
+    float* po; float* pd; size_t p_sl;   // [M][H] partials (device-scope stores)
+    float* ss1; float* ss2; size_t ss_sl;  // [32][64] row sum-of-squares partials
+    // per (step, x)
+    float* ss0; float* yf; size_t yf_sl;  // yf: final norm output [M][H]
+    float* xs; size_t xs_sl;              // Euler state after the step [M][A]
+    unsigned* lflag;             // [8][32]
+    unsigned* gflag;             // [8]
+    int* err;
+};
+
+// ------------------------------- syncs -------------------------------------
+struct PSync {
+    unsigned lseq = 0, gseq = 0;
+};
+
+VLA_DEV void p_local_sync(const PersistParams& p, int x, int j, PSync& s) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are acknowledged
+    __syncthreads();
+    ++s.lseq;
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&p.lflag[x * PJ + j], s.lseq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        long budget = P_SPIN;
+        bool done = false;
+        while (!done) {
+            const unsigned v =
+                lane < PJ ? __hip_atomic_load(&p.lflag[x * PJ + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                          : s.lseq;
+            done = __all(v >= s.lseq);
+            if (!done && --budget <= 0) {
+                if (lane == 0) __hip_atomic_store(p.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            // once any wait has failed, stop waiting: the kernel only has to end
+            if (!done && (budget & 1023) == 0 &&
+                __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+                break;
+        }
+    }
+    __syncthreads();
+}
+
+// All XCDs have finished the phase whose data they wrote with device-scope stores.
+VLA_DEV void p_global_sync(const PersistParams& p, int x, int j, PSync& s) {
+    p_local_sync(p, x, j, s);
+    ++s.gseq;
+    if (j == 0 && threadIdx.x == 0)
+        __hip_atomic_store(&p.gflag[x], s.gseq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        long budget = P_SPIN;
+        bool done = false;
+        while (!done) {
+            const unsigned v =
+                lane < PX ? __hip_atomic_load(&p.gflag[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : s.gseq;
+            done = __all(v >= s.gseq);
+            if (!done && --budget <= 0) {
+                if (lane == 0) __hip_atomic_store(p.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            if (!done && (budget & 1023) == 0 &&
+                __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+                break;
+        }
+    }
+    __syncthreads();
+}
+
+// ------------------------------- GEMM phase --------------------------------
+// A wave's share of a K slice of `steps` k-steps.
+struct PSplit {
+    int beg, n;
+};
+VLA_DEV PSplit p_split(int steps, int wave) {
+    const int per = (steps + PWAVES - 1) / PWAVES;
+    const int b = min(steps, wave * per);
+    return {b, min(steps, b + per) - b};
+}
+
+// Weight fragments of NT column tiles for this wave's NS k-steps. Every load
+// is unconditional (indices clamped into range) so that the arrays are fully
+// defined on every path; fragments past a wave's share are never used.
+template <int NT, int NS, typename TileFn>
+VLA_DEV void p_load_w(bf16x8 (&w)[NT][NS], const uint8_t* W, int Kf, int kw0, int ksteps, PSplit sp,
+                      TileFn&& tile_of, int lane) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int tile = tile_of(t);
+#pragma unroll
+        for (int i = 0; i < NS; ++i) {
+            const int kk = min(sp.beg + i, ksteps - 1);
+            w[t][i] = *(const bf16x8*)(W + (((size_t)tile * Kf + kw0 + kk) * 64 + lane) * 16);
+        }
+    }
+}
+
+// D[64 rows][16 cols] per tile = A (A-fragment order) x W^T, reduced over the
+// waves; `epi(t, row, col_in_tile, v, partner)` runs on waves 0..3 (one
+// 16-row tile each) for every value of the tiles t < ntile.
+template <int NT, int NS, typename Epi>
+VLA_DEV void p_gemm(const uint16_t* A, PSplit sp, const bf16x8 (&w)[NT][NS], int ntile, float* red, int wave,
+                    int lane, Epi&& epi) {
+    bf16x8 af[NS][4];
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+            af[i][mt] = i < sp.n ? *(const bf16x8*)(A + ((size_t)((sp.beg + i) * 4 + mt) * 64 + lane) * 8)
+                                 : (bf16x8){};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        f32x4 acc[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma_16x16x32(af[i][mt], w[t][i], acc[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) *(f32x4*)(&red[((wave * 4 + mt) * 64 + lane) * 4]) = acc[mt];
+        __syncthreads();
+        if (wave < 4 && t < ntile) {
+            f32x4 sum = *(const f32x4*)(&red[((0 * 4 + wave) * 64 + lane) * 4]);
+#pragma unroll
+            for (int w2 = 1; w2 < PWAVES; ++w2) sum += *(const f32x4*)(&red[((w2 * 4 + wave) * 64 + lane) * 4]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float v = sum[r];
+                const float partner = __shfl_xor(v, 1, 64);
+                epi(t, wave * 16 + 4 * (lane >> 4) + r, lane & 15, v, partner);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// Reduce / norm phases: thread (row = tid/8, sub = tid%8) owns CPT = H/256
+// consecutive columns of every phase's row `row`, so the residual stream of
+// those columns stays in its registers for the whole call.
+
+// ------------------------------- attention ---------------------------------
+// 16 query rows (of the XCD's hq*T rows of request b) against the layer's
+// prefix blocks (kcat/vcat) and the chunk blocks (kc/vc of this slot); eight
+// waves take interleaved 32-key blocks and merge through LDS.
+VLA_DEV void p_attention(const PersistParams& p, const uint16_t* qg, int r0, const uint16_t* Kp, const uint16_t* Vp,
+                         const uint16_t* Kc, const uint16_t* Vc, uint16_t* obuf, int b, int x, uint8_t* smem,
+                         int wave, int lane) {
+    constexpr int DH = 128;
+    uint16_t(*Ps)[16][40] = (uint16_t(*)[16][40])smem;
+    float(*Om)[64][DH / 16 * 4 + 8] = (float(*)[64][DH / 16 * 4 + 8])(smem + PWAVES * 16 * 40 * 2);
+    const int rows_total = p.hq * p.T;
+    const int nbp = p.P / 32, nblk = nbp + p.Tpad / 32;
+    const int S = p.P + p.T;
+    bf16x8 qf[DH / 32];
+    {
+        const int row = r0 + (lane & 15);
+#pragma unroll
+        for (int ks = 0; ks < DH / 32; ++ks)
+            qf[ks] = row < rows_total ? *(const bf16x8*)(qg + (size_t)row * DH + ks * 32 + 8 * (lane >> 4))
+                                      : (bf16x8){};
+    }
+    float mrow[4], lrow[4];
+    f32x4 oacc[DH / 16];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { mrow[r] = -INFINITY; lrow[r] = 0.f; }
+#pragma unroll
+    for (int dn = 0; dn < DH / 16; ++dn) oacc[dn] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int kb = wave; kb < nblk; kb += PWAVES) {
+        const bool pre = kb < nbp;
+        const uint16_t* Kb = pre ? Kp + (size_t)kb * 32 * DH : Kc + (size_t)(kb - nbp) * 32 * DH;
+        const uint16_t* Vb = pre ? Vp + (size_t)kb * 32 * DH : Vc + (size_t)(kb - nbp) * 32 * DH;
+        bf16x8 kf[2][DH / 32], vf[DH / 16];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+            for (int ks = 0; ks < DH / 32; ++ks)
+                kf[sb][ks] = *(const bf16x8*)(Kb + (size_t)(sb * 16 + (lane & 15)) * DH + ks * 32 + 8 * (lane >> 4));
+#pragma unroll
+        for (int dn = 0; dn < DH / 16; ++dn) vf[dn] = *(const bf16x8*)(Vb + ((size_t)dn * 64 + lane) * 8);
+        f32x4 s[2];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            s[sb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < DH / 32; ++ks) s[sb] = mfma_16x16x32(qf[ks], kf[sb][ks], s[sb]);
+        }
+        float alpha[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float s0 = s[0][r] * p.scale_log2, s1 = s[1][r] * p.scale_log2;
+            const int key0 = kb * 32 + (lane & 15);
+            if (key0 >= S) s0 = -INFINITY;
+            if (key0 + 16 >= S) s1 = -INFINITY;
+            const float mx = group16_max(fmaxf(s0, s1));
+            const float mnew = fmaxf(mrow[r], mx);
+            alpha[r] = exp2f(mrow[r] - mnew);
+            const float p0 = exp2f(s0 - mnew), p1 = exp2f(s1 - mnew);
+            lrow[r] = lrow[r] * alpha[r] + group16_sum(p0 + p1);
+            mrow[r] = mnew;
+            Ps[wave][4 * (lane >> 4) + r][lane & 15] = f32_to_bf16(p0);
+            Ps[wave][4 * (lane >> 4) + r][16 + (lane & 15)] = f32_to_bf16(p1);
+        }
+#pragma unroll
+        for (int dn = 0; dn < DH / 16; ++dn)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) oacc[dn][r] *= alpha[r];
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        const bf16x8 pa = *(const bf16x8*)(&Ps[wave][lane & 15][8 * (lane >> 4)]);
+#pragma unroll
+        for (int dn = 0; dn < DH / 16; ++dn) oacc[dn] = mfma_16x16x32(pa, vf[dn], oacc[dn]);
+        __builtin_amdgcn_wave_barrier();
+    }
+#pragma unroll
+    for (int dn = 0; dn < DH / 16; ++dn) *(f32x4*)(&Om[wave][lane][dn * 4]) = oacc[dn];
+    *(f32x4*)(&Om[wave][lane][DH / 16 * 4]) = (f32x4){mrow[0], mrow[1], mrow[2], mrow[3]};
+    *(f32x4*)(&Om[wave][lane][DH / 16 * 4 + 4]) = (f32x4){lrow[0], lrow[1], lrow[2], lrow[3]};
+    __syncthreads();
+    float sc[PWAVES][4], inv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float mw[PWAVES], Mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < PWAVES; ++w) {
+            mw[w] = Om[w][lane][DH / 16 * 4 + r];
+            Mx = fmaxf(Mx, mw[w]);
+        }
+        float Ls = 0.f;
+#pragma unroll
+        for (int w = 0; w < PWAVES; ++w) {
+            sc[w][r] = exp2f(mw[w] - Mx);
+            Ls += sc[w][r] * Om[w][lane][DH / 16 * 4 + 4 + r];
+        }
+        inv[r] = 1.0f / Ls;
+    }
+    const int dn = wave;  // DH / 16 == PWAVES
+    f32x4 ov = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < PWAVES; ++w) {
+        const f32x4 t = *(const f32x4*)(&Om[w][lane][dn * 4]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ov[r] += sc[w][r] * t[r];
+    }
+    const int Kq = p.hq * DH;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = r0 + 4 * (lane >> 4) + r;
+        if (row < rows_total) {
+            const int hh = row / p.T, i = row % p.T;
+            obuf[act_index(b * p.T + i, hh * DH + dn * 16 + (lane & 15), Kq, 1)] = f32_to_bf16(ov[r] * inv[r]);
+        }
+    }
+    __syncthreads();
+}
+
+// ---------------------------- the persistent kernel ------------------------
+// Values the compiler must treat as unknown at every use (an empty asm).
+VLA_DEV int p_opaque_v(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+VLA_DEV int p_opaque_s(int v) {
+    asm volatile("" : "+s"(v));
+    return v;
+}
+
+// Shape class: tiles per workgroup (NT*) and k-steps per wave (NS*) of the
+// QKV, O, gate_up and down phases, and columns per thread (CPT = H/256).
+template <int NTQ, int NSQ, int NTO, int NSO, int NTG, int NSG, int NTD, int NSD, int CPT>
+__global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
+    constexpr int P_CPT = CPT;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[PWAVES * 16 * 40 * 2 + PWAVES * 64 * (128 / 16 * 4 + 8) * 4];
+    float* red = (float*)smem;  // GEMM reduction: [8 waves][4][64][4] floats = 32 KiB
+    const int H = p.H, M = p.M, L = p.L, dh = p.dh, hq = p.hq;
+    // the XCD-local exchanges rely on workgroup w running on XCD w % 8
+    if (threadIdx.x == 0 && (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xF) != (int)(blockIdx.x % PX))
+        __hip_atomic_store(p.err, 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    PSync sy;
+    bf16x8 wq[NTQ][NSQ], wo[NTO][NSO], wgu[NTG][NSG], wdn[NTD][NSD];
+    const int ks_h = H / 32, ks_o = hq * dh / 32, ks_d = p.Ix / 32;
+    const int Kf_o = p.nq * dh / 32, Kf_d = p.I / 32, Kf_h = H / 32;
+    float hreg[CPT];  // this thread's residual values, kept for the whole call
+    constexpr int cpt = CPT;  // == H / 256, checked by the host
+    const int Hc = H / PJ;
+
+    // Thread- and workgroup-derived values, re-derived at the top of every
+    // phase block from opaque copies of the ids (otherwise the compiler hoists
+    // the per-lane addresses of every phase out of the loops and spills them).
+    // Column tiles of a GEMM phase: local tile j + t*PJ, t < nt*, computed
+    // rather than stored so that no private array is indexed at run time.
+#define P_PHASE_VARS                                                                                  \
+    const int tid = p_opaque_v((int)threadIdx.x), lane = tid & 63, wave = tid >> 6;                   \
+    const int x = p_opaque_s((int)(blockIdx.x % PX)), j = p_opaque_s((int)(blockIdx.x / PX));         \
+    const int g = (x * hq) / p.G;                                                                     \
+    const int nqt = hq * dh / 16, nkt = dh / 16, n_qkv = nqt + 2 * nkt;                               \
+    const int gbase = x * (2 * p.Ix) / 16, gcount = 2 * p.Ix / 16;                                    \
+    auto ntiles = [&](int count) { return count > j ? (count - j + PJ - 1) / PJ : 0; };               \
+    const int ntq = ntiles(n_qkv), nto = ntiles(H / 16), ntg = ntiles(gcount);                        \
+    auto tq = [&](int t) {                                                                            \
+        const int lt = min(j + t * PJ, n_qkv - 1);                                                    \
+        if (lt < nqt) return (x * hq * dh) / 16 + lt;                                                 \
+        if (lt < nqt + nkt) return (p.nq * dh + g * dh) / 16 + (lt - nqt);                            \
+        return (p.nq * dh + p.nkv * dh + g * dh) / 16 + (lt - nqt - nkt);                             \
+    };                                                                                                \
+    auto to = [&](int t) { return min(j + t * PJ, H / 16 - 1); };                                     \
+    auto tg = [&](int t) { return gbase + min(j + t * PJ, gcount - 1); };                             \
+    const PSplit sp_qkv = p_split(H / 32, wave), sp_o = p_split(hq * dh / 32, wave), sp_gu = sp_qkv,  \
+                 sp_d = p_split(p.Ix / 32, wave);                                                     \
+    const int rrow = tid >> 3, sub = tid & 7, c0 = j * Hc + sub * cpt;                                \
+    const bool row_ok = rrow < M;                                                                     \
+    (void)ntq; (void)nto; (void)ntg; (void)sp_o; (void)sp_gu; (void)sp_d; (void)row_ok; (void)c0
+
+    for (int k = 0; k < p.nsteps; ++k) {
+        const float* ts = p.ab->t_schedule;
+        // ---------------- in-projection + first norm of layer 0 -------------
+        {
+            P_PHASE_VARS;
+            p_load_w(wq, p.wqkv[0], Kf_h, 0, ks_h, sp_qkv, tq, lane);
+            const float* xin = k == 0 ? p.ab->noise : p.xs + ((size_t)(k - 1) * PX + x) * p.xs_sl;
+            float* ss0 = p.ss0 + ((size_t)k * PX + x) * p.ss_sl;
+            float ssum = 0.f;
+            if (row_ok) {
+#pragma unroll
+                for (int c = 0; c < P_CPT; ++c)
+                    if (c < cpt) hreg[c] = p.in_b[c0 + c];
+                const float* xr = xin + (size_t)rrow * p.A;
+#pragma unroll 5
+                for (int a = 0; a < p.A; ++a) {
+                    const float xa = xr[a];
+                    const uint16_t* wr = p.in_wT + (size_t)a * H + c0;
+#pragma unroll
+                    for (int c = 0; c < P_CPT; c += 2)
+                        if (c < cpt) {
+                            const uint32_t w2 = *(const uint32_t*)(wr + c);
+                            hreg[c] += xa * __uint_as_float(w2 << 16);
+                            hreg[c + 1] += xa * __uint_as_float(w2 & 0xffff0000u);
+                        }
+                }
+#pragma unroll
+                for (int c = 0; c < P_CPT; ++c)
+                    if (c < cpt) ssum += hreg[c] * hreg[c];
+            }
+            ssum += __shfl_xor(ssum, 1, 64);
+            ssum += __shfl_xor(ssum, 2, 64);
+            ssum += __shfl_xor(ssum, 4, 64);
+            if (row_ok && sub == 0) ss0[j * 64 + rrow] = ssum;
+            p_local_sync(p, x, j, sy);
+            // norm1 of layer 0 -> y[slot (k, 0)]
+            float part = 0.f;
+            if (row_ok)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) part += ss0[(sub * 4 + q4) * 64 + rrow];
+            part += __shfl_xor(part, 1, 64);
+            part += __shfl_xor(part, 2, 64);
+            part += __shfl_xor(part, 4, 64);
+            const float inv = 1.0f / sqrtf(part / (float)H + p.eps);
+            uint16_t* yb = p.y + ((size_t)(k * L) * PX + x) * p.y_sl;
+            if (row_ok) {
+                const float* mr = p.mod + (size_t)(k * p.B + rrow / p.T) * p.mod_ld;
+#pragma unroll
+                for (int c = 0; c < P_CPT; c += 2)
+                    if (c < cpt) {
+                        const int cc = c0 + c;
+                        const float v0 = hreg[c] * inv * (1.f + mr[cc]) + mr[H + cc];
+                        const float v1 = hreg[c + 1] * inv * (1.f + mr[cc + 1]) + mr[H + cc + 1];
+                        *(uint32_t*)(yb + act_index(rrow, cc, H, 1)) = pack_bf16x2(v0, v1);
+                    }
+            }
+            p_local_sync(p, x, j, sy);
+        }
+
+        for (int l = 0; l < L; ++l) {
+            P_PHASE_VARS;
+            const size_t sl = (size_t)(k * L + l) * PX + x;
+            const float* mr_base = p.mod + (size_t)(k * p.B) * p.mod_ld + (size_t)(6 * l) * H;
+            // ------------------------- QKV + RoPE ---------------------------
+            {
+                const uint16_t* yb = p.y + sl * p.y_sl;
+                uint16_t* qb = p.q + sl * p.q_sl;
+                uint16_t* kcb = p.kc + sl * p.kv_sl;
+                uint16_t* vcb = p.vc + sl * p.kv_sl;
+                const int qd = p.nq * dh, kvd = p.nkv * dh;
+                p_gemm(yb, sp_qkv, wq, ntq, red, wave, lane, [&](int t, int row, int cl, float v, float partner) {
+                    if (row >= M) return;
+                    const int col = tq(t) * 16 + cl;
+                    int sec, local;
+                    if (col < qd) { sec = 0; local = col; }
+                    else if (col < qd + kvd) { sec = 1; local = col - qd; }
+                    else { sec = 2; local = col - qd - kvd; }
+                    const int head = local / dh, pp = local % dh;
+                    const int m = pp >> 1, second = pp & 1;
+                    const int b = row / p.T, i = row % p.T;
+                    float outv = v;
+                    if (sec < 2) {
+                        const float2 cs = p.rope[i * (dh / 2) + m];
+                        const float u1 = second ? partner : v;
+                        const float u2 = second ? v : partner;
+                        outv = second ? (u2 * cs.x + u1 * cs.y) : (u1 * cs.x - u2 * cs.y);
+                    }
+                    const int dim = m + second * (dh / 2);
+                    const uint16_t ob = f32_to_bf16(outv);
+                    if (sec == 0) qb[((size_t)(b * hq + (head - x * hq)) * p.T + i) * dh + dim] = ob;
+                    else if (sec == 1) kcb[((size_t)b * p.Tpad + i) * dh + dim] = ob;
+                    else {
+                        const int w = i & 31;
+                        vcb[(size_t)b * p.Tpad * dh + (size_t)(i >> 5) * 32 * dh +
+                            ((size_t)((dim >> 4) * 64 + (w >> 3) * 16 + (dim & 15)) * 8 + (w & 7))] = ob;
+                    }
+                });
+            }
+            p_load_w(wo, p.wo[l], Kf_o, x * hq * dh / 32, ks_o, sp_o, to, lane);
+            p_local_sync(p, x, j, sy);
+            // ------------------------- attention ----------------------------
+            {
+                const int tpb = (hq * p.T + 15) / 16;
+                const int b = j / tpb, tile = j % tpb;
+                if (b < p.B) {
+                    const size_t sl2 = sl;
+                    const uint16_t* qg = p.q + sl2 * p.q_sl + (size_t)(b * hq) * p.T * dh;
+                    const size_t kvb = p.kv.base(b, l, g);
+                    p_attention(p, qg, tile * 16, p.kcat + kvb, p.vcat + kvb,
+                                p.kc + sl2 * p.kv_sl + (size_t)b * p.Tpad * dh,
+                                p.vc + sl2 * p.kv_sl + (size_t)b * p.Tpad * dh, p.o + sl2 * p.o_sl, b, x, smem, wave,
+                                lane);
+                }
+            }
+            p_local_sync(p, x, j, sy);
+            // ------------------------- O partial ----------------------------
+            {
+                float* pob = p.po + sl * p.p_sl;
+                p_gemm(p.o + sl * p.o_sl, sp_o, wo, nto, red, wave, lane,
+                       [&](int t, int row, int cl, float v, float partner) {
+                           if (row >= M || (cl & 1)) return;
+                           const int col = to(t) * 16 + cl;
+                           const unsigned long long bits =
+                               (unsigned long long)__float_as_uint(v) |
+                               ((unsigned long long)__float_as_uint(partner) << 32);
+                           __hip_atomic_store((unsigned long long*)(pob + (size_t)row * H + col), bits,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                       });
+            }
+            p_load_w(wgu, p.wgu[l], Kf_h, 0, ks_h, sp_gu, tg, lane);
+            p_global_sync(p, x, j, sy);
+            // --------------- reduce O partials + gated residual -------------
+            {
+                float* ss1 = p.ss1 + sl * p.ss_sl;
+                float ssum = 0.f;
+                if (row_ok) {
+                    const float* gate = mr_base + (size_t)(rrow / p.T) * p.mod_ld + 2 * H;
+#pragma unroll
+                    for (int c = 0; c < P_CPT; ++c)
+                        if (c < cpt) {
+                            float acc = 0.f;
+#pragma unroll
+                            for (int xx = 0; xx < PX; ++xx)
+                                acc += p.po[((size_t)(k * L + l) * PX + xx) * p.p_sl + (size_t)rrow * H + c0 + c];
+                            hreg[c] += gate[c0 + c] * acc;   // residual stream stays in registers
+                            ssum += hreg[c] * hreg[c];
+                        }
+                }
+                ssum += __shfl_xor(ssum, 1, 64);
+                ssum += __shfl_xor(ssum, 2, 64);
+                ssum += __shfl_xor(ssum, 4, 64);
+                if (row_ok && sub == 0) ss1[j * 64 + rrow] = ssum;
+            }
+            p_local_sync(p, x, j, sy);
+            // ------------------------- norm 2 -------------------------------
+            {
+                const float* ss1 = p.ss1 + sl * p.ss_sl;
+                float part = 0.f;
+                if (row_ok)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) part += ss1[(sub * 4 + q4) * 64 + rrow];
+                part += __shfl_xor(part, 1, 64);
+                part += __shfl_xor(part, 2, 64);
+                part += __shfl_xor(part, 4, 64);
+                const float inv = 1.0f / sqrtf(part / (float)H + p.eps);
+                uint16_t* yb = p.y2 + sl * p.y_sl;
+                if (row_ok) {
+                    const float* mr = mr_base + (size_t)(rrow / p.T) * p.mod_ld;
+#pragma unroll
+                    for (int c = 0; c < P_CPT; c += 2)
+                        if (c < cpt) {
+                            const int cc = c0 + c;
+                            const float v0 = hreg[c] * inv * (1.f + mr[3 * H + cc]) + mr[4 * H + cc];
+                            const float v1 = hreg[c + 1] * inv * (1.f + mr[3 * H + cc + 1]) + mr[4 * H + cc + 1];
+                            *(uint32_t*)(yb + act_index(rrow, cc, H, 1)) = pack_bf16x2(v0, v1);
+                        }
+                }
+            }
+            p_local_sync(p, x, j, sy);
+            // ------------------------- gate_up + SwiGLU ---------------------
+            {
+                uint16_t* ab = p.a + sl * p.a_sl;
+                p_gemm(p.y2 + sl * p.y_sl, sp_gu, wgu, ntg, red, wave, lane,
+                       [&](int t, int row, int cl, float v, float partner) {
+                           if (row >= M || (cl & 1)) return;
+                           const int col = tg(t) * 16 + cl;
+                           const int lc = (col >> 1) - x * p.Ix;
+                           ab[act_index(row, lc, p.Ix, 1)] = f32_to_bf16(silu_f(v) * partner);
+                       });
+            }
+            p_load_w(wdn, p.wd[l], Kf_d, x * p.Ix / 32, ks_d, sp_d, to, lane);
+            p_local_sync(p, x, j, sy);
+            // ------------------------- down partial -------------------------
+            {
+                float* pdb = p.pd + sl * p.p_sl;
+                p_gemm(p.a + sl * p.a_sl, sp_d, wdn, nto, red, wave, lane,
+                       [&](int t, int row, int cl, float v, float partner) {
+                           if (row >= M || (cl & 1)) return;
+                           const int col = to(t) * 16 + cl;
+                           const unsigned long long bits =
+                               (unsigned long long)__float_as_uint(v) |
+                               ((unsigned long long)__float_as_uint(partner) << 32);
+                           __hip_atomic_store((unsigned long long*)(pdb + (size_t)row * H + col), bits,
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                       });
+            }
+            if (l + 1 < L) p_load_w(wq, p.wqkv[l + 1], Kf_h, 0, ks_h, sp_qkv, tq, lane);
+            p_global_sync(p, x, j, sy);
+            // --------------- reduce down partials + gated residual ----------
+            {
+                float* ss2 = p.ss2 + sl * p.ss_sl;
+                float ssum = 0.f;
+                if (row_ok) {
+                    const float* gate = mr_base + (size_t)(rrow / p.T) * p.mod_ld + 5 * H;
+#pragma unroll
+                    for (int c = 0; c < P_CPT; ++c)
+                        if (c < cpt) {
+                            float acc = 0.f;
+#pragma unroll
+                            for (int xx = 0; xx < PX; ++xx)
+                                acc += p.pd[((size_t)(k * L + l) * PX + xx) * p.p_sl + (size_t)rrow * H + c0 + c];
+                            hreg[c] += gate[c0 + c] * acc;
+                            ssum += hreg[c] * hreg[c];
+                        }
+                }
+                ssum += __shfl_xor(ssum, 1, 64);
+                ssum += __shfl_xor(ssum, 2, 64);
+                ssum += __shfl_xor(ssum, 4, 64);
+                if (row_ok && sub == 0) ss2[j * 64 + rrow] = ssum;
+            }
+            p_local_sync(p, x, j, sy);
+            // --------- first norm of the next layer, or the final norm ------
+            {
+                const float* ss2 = p.ss2 + sl * p.ss_sl;
+                float part = 0.f;
+                if (row_ok)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4) part += ss2[(sub * 4 + q4) * 64 + rrow];
+                part += __shfl_xor(part, 1, 64);
+                part += __shfl_xor(part, 2, 64);
+                part += __shfl_xor(part, 4, 64);
+                const float inv = 1.0f / sqrtf(part / (float)H + p.eps);
+                if (row_ok) {
+                    const float* mrow = p.mod + (size_t)(k * p.B + rrow / p.T) * p.mod_ld;
+                    if (l + 1 < L) {
+                        uint16_t* yb = p.y + ((size_t)(k * L + l + 1) * PX + x) * p.y_sl;
+                        const float* sc = mrow + (size_t)(6 * (l + 1)) * H;
+#pragma unroll
+                        for (int c = 0; c < P_CPT; c += 2)
+                            if (c < cpt) {
+                                const int cc = c0 + c;
+                                const float v0 = hreg[c] * inv * (1.f + sc[cc]) + sc[H + cc];
+                                const float v1 = hreg[c + 1] * inv * (1.f + sc[cc + 1]) + sc[H + cc + 1];
+                                *(uint32_t*)(yb + act_index(rrow, cc, H, 1)) = pack_bf16x2(v0, v1);
+                            }
+                    } else {
+                        float* yf = p.yf + ((size_t)k * PX + x) * p.yf_sl;
+                        const float* sc = mrow + (size_t)(6 * L) * H;
+#pragma unroll
+                        for (int c = 0; c < P_CPT; ++c)
+                            if (c < cpt) {
+                                const int cc = c0 + c;
+                                yf[rrow * H + cc] = hreg[c] * inv * (1.f + sc[cc]) + sc[H + cc];
+                            }
+                    }
+                }
+            }
+            p_local_sync(p, x, j, sy);
+        }
+
+        // ------------------ out-projection + Euler update -------------------
+        // every XCD computes the full update into its own copy of the state;
+        // a wave owns one row and 16 outputs, loading the weights of 8 at a time
+        {
+            P_PHASE_VARS;
+            const float* yf = p.yf + ((size_t)k * PX + x) * p.yf_sl;
+            const float* xin = k == 0 ? p.ab->noise : p.xs + ((size_t)(k - 1) * PX + x) * p.xs_sl;
+            float* xo = p.xs + ((size_t)k * PX + x) * p.xs_sl;
+            const bool last = k + 1 == p.nsteps;
+            const int chunks = (p.A + 15) / 16;
+            for (int it = j * PWAVES + wave; it < M * chunks; it += PJ * PWAVES) {
+                const int r = it / chunks, a0 = (it % chunks) * 16;
+                float mine = 0.f;
+                float4 yrow[CPT];
+#pragma unroll
+                for (int i = 0; i < CPT; ++i) yrow[i] = *(const float4*)(yf + (size_t)r * H + lane * 4 + 256 * i);
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    uint2 wv[8][CPT];
+#pragma unroll
+                    for (int o = 0; o < 8; ++o) {
+                        const int aa = min(a0 + half * 8 + o, p.A - 1);
+#pragma unroll
+                        for (int i = 0; i < CPT; ++i)
+                            wv[o][i] = *(const uint2*)(p.out_w + (size_t)aa * H + lane * 4 + 256 * i);
+                    }
+#pragma unroll
+                    for (int o = 0; o < 8; ++o) {
+                        float s = 0.f;
+#pragma unroll
+                        for (int i = 0; i < CPT; ++i)
+                            s += yrow[i].x * __uint_as_float(wv[o][i].x << 16) +
+                                 yrow[i].y * __uint_as_float(wv[o][i].x & 0xffff0000u) +
+                                 yrow[i].z * __uint_as_float(wv[o][i].y << 16) +
+                                 yrow[i].w * __uint_as_float(wv[o][i].y & 0xffff0000u);
+                        s = wave_sum(s);
+                        if (lane == half * 8 + o) mine = s;
+                    }
+                }
+                if (lane < 16 && a0 + lane < p.A) {
+                    const int a = a0 + lane, b = r / p.T;
+                    const float dt = ts[b * (p.nsteps + 1) + k + 1] - ts[b * (p.nsteps + 1) + k];
+                    const float xv = xin[r * p.A + a] + dt * (mine + p.out_b[a]);
+                    xo[r * p.A + a] = xv;
+                    if (last && x == 0) p.ab->out[r * p.A + a] = xv;
+                }
+            }
+            p_local_sync(p, x, j, sy);
+        }
+    }
+#undef P_PHASE_VARS
+}
+
+// Flags start at zero for every call (a kernel, so that a captured graph
+// could hold it too).
+__global__ void persist_reset_kernel(unsigned* lflag, unsigned* gflag, int* err) {
+    const int t = threadIdx.x;
+    if (t < PX * PJ) lflag[t] = 0u;
+    if (t < PX) gflag[t] = 0u;
+    if (t == 0) *err = 0;
+}
+
+// After the persistent kernel: if any wait expired, poison the output so the
+// caller cannot mistake it for a result.
+__global__ void persist_check_kernel(const int* err, const ArgBlock* ab, int n) {
+    if (*err == 0) return;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) ab->out[i] = NAN;
+}

@@ -75,6 +75,14 @@ class Expert:
     def set_option(self, option: int, value: int) -> None:
         B.vla_set_option(self.ctx, option, value)
 
+    def get_option(self, option: int) -> int:
+        return B.vla_get_option(self.ctx, option)
+
+    @property
+    def persistent_active(self) -> bool:
+        """True when calls run as one persistent cooperative kernel."""
+        return B.vla_get_option(self.ctx, B.VLA_OPT_PERSISTENT_ACTIVE) == 1
+
     def denoise(self, prefix_k, prefix_v, noise, t_schedule, n_steps: int, out=None):
         """All arguments torch device tensors (prefix as int16/bf16 bits); returns ``out``."""
         import torch
