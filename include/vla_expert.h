@@ -56,8 +56,8 @@ extern "C" {
 
 /* Options for vla_set_option. */
 #define VLA_OPT_USE_GRAPH 1 /* 1 (default): replay a captured hipGraph per n_steps; 0: launch kernels eagerly */
-#define VLA_OPT_PERSISTENT 2 /* 1 (default): for shapes it supports (batch*horizon <= 64, 8 | n_q_heads, ...),
-                                 run the whole loop as one persistent cooperative kernel; 0: kernel-per-stage path */
+#define VLA_OPT_PERSISTENT 2 /* 1: for shapes it supports (batch*horizon <= 64, 8 | n_q_heads, ...),
+                                 run the whole loop as one persistent cooperative kernel; 0 (default): kernel-per-stage path */
 /* Query for vla_get_option: 1 when the next vla_denoise call uses the persistent kernel. */
 #define VLA_OPT_PERSISTENT_ACTIVE 3
 

@@ -2,9 +2,9 @@
 CPU oracle, against the kernel-per-stage path, and across repeated calls.
 
 The persistent kernel runs the whole loop in one cooperative launch with the
-layer split over the eight XCDs; it is chosen by default for the shapes it
-supports. Gates are those of the other bf16 parity tests: cosine >= 0.9995 and
-max|gpu - oracle| <= 2e-2 * RMS(oracle).
+layer split over the eight XCDs; it runs for the shapes it supports when
+switched on (VLA_OPT_PERSISTENT). Gates are those of the other bf16 parity
+tests: cosine >= 0.9995 and max|gpu - oracle| <= 2e-2 * RMS(oracle).
 """
 import numpy as np
 import pytest
@@ -35,6 +35,14 @@ def _gate(out, ref, tag):
     assert m["maxabs_over_rms"] <= BF16_MAXABS, m
 
 
+def _case(cfg, raw, *ins):
+    """A GpuCase with the persistent path switched on."""
+    from vla_flow_matching_denoise_amd import binding as B
+    case = GpuCase(cfg, raw, *ins)
+    case.expert.set_option(B.VLA_OPT_PERSISTENT, 1)
+    return case
+
+
 def _small_raw():
     return synth.make_weights(SMALL, seed=0)
 
@@ -46,7 +54,7 @@ def test_persistent_small_end_to_end_and_vs_stage_path():
     pk, pv, x0, ts = _inputs(cfg)
     ref = run_oracle(cfg, __import__("oracle").decode_weights(raw), pk, pv, x0, ts)
     say("[persist small] 2 layers, h512, 8x1x128 heads, chunk 16x7, 4 steps")
-    case = GpuCase(cfg, raw, pk, pv, x0, ts)
+    case = _case(cfg, raw, pk, pv, x0, ts)
     try:
         assert case.expert.persistent_active
         out_p = case.run()
@@ -71,7 +79,7 @@ def test_persistent_repeat_bitwise_and_input_switch():
     ins_a = _inputs(cfg, seed=0)
     ins_b = _inputs(cfg, seed=5, schedule="warped")
     say("[persist small] A, B, A calls with different prefix / noise / schedule")
-    case = GpuCase(cfg, raw, *ins_a)
+    case = _case(cfg, raw, *ins_a)
     try:
         a1 = case.run()
         dev_b = [to_device(t) for t in ins_b]
@@ -98,7 +106,7 @@ def test_persistent_step_counts():
             pk, pv, x0, ts = _inputs(cfg, n_steps=n)
             say(f"[persist small] n_steps={n}")
             if case is None:
-                case = GpuCase(cfg, raw, pk, pv, x0, ts)
+                case = _case(cfg, raw, pk, pv, x0, ts)
             else:
                 from vla_flow_matching_denoise_amd.expert import to_device
                 case.ts = to_device(ts)
@@ -116,7 +124,7 @@ def test_persistent_ragged_batches(batch, horizon, action_dim, prefix_len):
     raw = synth.make_weights(cfg, seed=1)
     pk, pv, x0, ts = _inputs(cfg, seed=2, schedule="warped")
     say(f"[persist ragged] batch={batch} horizon={horizon} action_dim={action_dim} prefix={prefix_len}")
-    case = GpuCase(cfg, raw, pk, pv, x0, ts)
+    case = _case(cfg, raw, pk, pv, x0, ts)
     try:
         assert case.expert.persistent_active
         out = case.run()
@@ -131,7 +139,7 @@ def test_persistent_lingbot_b1_vs_stage_path():
     cfg = synth.config(2).replace(n_steps=3)
     pk, pv, x0, ts = _inputs(cfg)
     say("[persist cfg2] 36 layers, h1024, chunk 50x75, 3 steps")
-    case = GpuCase(cfg, weights(2), pk, pv, x0, ts)
+    case = _case(cfg, weights(2), pk, pv, x0, ts)
     try:
         assert case.expert.persistent_active
         out_p = case.run()

@@ -151,7 +151,7 @@ struct vla_ctx {
     std::map<int, hipGraphExec_t> graphs;
 
     // persistent small-batch path (one cooperative launch per call)
-    bool persist_ok = false, use_persist = true;
+    bool persist_ok = false, use_persist = false;
     int pn_cap = 0;                // Euler steps the write-once slots hold
     PersistParams pp{};
     std::vector<std::pair<void*, size_t>> pbufs;
