@@ -152,7 +152,7 @@ struct vla_ctx {
 
     // persistent small-batch path (one cooperative launch per call)
     bool persist_ok = false, use_persist = false;
-    int pn_cap = 0;                // Euler steps the write-once slots hold
+    int pn_cap = 0;                // 1 once the exchange buffers exist
     PersistParams pp{};
     std::vector<std::pair<void*, size_t>> pbufs;
     const uint8_t** wptrs = nullptr;  // device array: per-layer QKV, O, gate_up, down weights (4 x L)
@@ -613,7 +613,9 @@ bool persist_supported(const vla_ctx* c) {
     const int hq = d.n_q_heads / PX, G = d.n_q_heads / d.n_kv_heads;
     if (hq < 1 || G % hq) return false;                       // an XCD's heads share one KV group
     if (d.prefix_len % 32) return false;                      // prefix blocks never straddle the chunk
-    if (d.hidden % 256 || d.intermediate % 256) return false; // whole 32-wide k-steps per XCD slice
+    if (d.intermediate % 256) return false;                   // whole 32-wide k-steps per XCD slice
+    if (d.hidden != 512 && d.hidden != 1024 && d.hidden != 2048) return false;  // H/256 even, divides 16
+    if (d.batch > P_BMAX) return false;                       // staged modulation vectors
     if (d.batch * ((hq * d.horizon + 15) / 16) > PJ) return false;  // attention tiles per XCD
     return persist_shape(d).fn != nullptr;
 }
@@ -636,33 +638,19 @@ void persist_strides(const vla_ctx* c, PersistParams& p) {
     p.xs_sl = rnd((size_t)M * d.action_dim);
 }
 
-size_t persist_bytes(const vla_ctx* c, int n_steps) {
-    PersistParams p{};
-    persist_strides(c, p);
-    const size_t U = (size_t)n_steps * c->d.n_layers * PX, S8 = (size_t)n_steps * PX;
-    return U * (2 * p.y_sl * 2 + p.q_sl * 2 + 2 * p.kv_sl * 2 + p.o_sl * 2 + p.a_sl * 2 + 2 * p.p_sl * 4 +
-                2 * p.ss_sl * 4) +
-           S8 * (p.ss_sl + p.yf_sl + p.xs_sl) * 4;
-}
-
-// Calls whose write-once buffers would exceed this run on the stage path.
-constexpr size_t kPersistMaxBytes = (size_t)16 << 30;
-
-int ensure_persist(vla_ctx* c, int n_steps) {
-    if (n_steps <= c->pn_cap) return VLA_OK;
-    HIPC(hipStreamSynchronize(c->stream));
-    for (auto& b : c->pbufs) c->release(b.first, b.second);
-    c->pbufs.clear();
-    c->pn_cap = 0;
-    const size_t U = (size_t)n_steps * c->d.n_layers * PX, S8 = (size_t)n_steps * PX;
+// Exchange buffers of the persistent kernel: one slot per XCD (two for the
+// Euler state), the same for every step count.
+int ensure_persist(vla_ctx* c) {
+    if (c->pn_cap) return VLA_OK;
     PersistParams& p = c->pp;
     persist_strides(c, p);
+    const size_t U = PX;
     int rc;
     auto get = [&](void** ptr, size_t bytes) -> int {
         int r = c->alloc(ptr, bytes);
         if (r) return r;
         c->pbufs.emplace_back(*ptr, bytes);
-        hipError_t e = hipMemsetAsync(*ptr, 0, bytes, c->stream);  // zero padding rows / keys
+        hipError_t e = hipMemsetAsync(*ptr, 0, bytes, c->stream);  // padding rows / keys stay zero
         if (e != hipSuccess) {
             set_err("hipMemsetAsync failed: %s", hipGetErrorString(e));
             return VLA_ERR_HIP;
@@ -674,11 +662,11 @@ int ensure_persist(vla_ctx* c, int n_steps) {
         (rc = get((void**)&p.vc, U * p.kv_sl * 2)) || (rc = get((void**)&p.o, U * p.o_sl * 2)) ||
         (rc = get((void**)&p.a, U * p.a_sl * 2)) || (rc = get((void**)&p.po, U * p.p_sl * 4)) ||
         (rc = get((void**)&p.pd, U * p.p_sl * 4)) || (rc = get((void**)&p.ss1, U * p.ss_sl * 4)) ||
-        (rc = get((void**)&p.ss2, U * p.ss_sl * 4)) || (rc = get((void**)&p.ss0, S8 * p.ss_sl * 4)) ||
-        (rc = get((void**)&p.yf, S8 * p.yf_sl * 4)) || (rc = get((void**)&p.xs, S8 * p.xs_sl * 4)))
+        (rc = get((void**)&p.ss2, U * p.ss_sl * 4)) || (rc = get((void**)&p.ss0, U * p.ss_sl * 4)) ||
+        (rc = get((void**)&p.yf, U * p.yf_sl * 4)) || (rc = get((void**)&p.xs, 2 * U * p.xs_sl * 4)))
         return rc;
     HIPC(hipStreamSynchronize(c->stream));
-    c->pn_cap = n_steps;
+    c->pn_cap = 1;
     return VLA_OK;
 }
 
@@ -726,6 +714,7 @@ int enqueue_persist(vla_ctx* c, int n_steps) {
     p.ab = c->ab;
     p.lflag = c->lflag;
     p.gflag = c->gflag;
+    p.sink = c->gflag + 384;
     p.err = c->perr;
     void* args[] = {&p};
     HIPC(hipLaunchCooperativeKernel(persist_shape(d).fn, dim3(PX * PJ), dim3(PWAVES * 64), args, 0, c->stream));
@@ -895,7 +884,8 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
         if ((rc = c->alloc((void**)&c->wptrs, hp.size() * sizeof(void*)))) return rc;
         HIPC(hipMemcpy(c->wptrs, hp.data(), hp.size() * sizeof(void*), hipMemcpyHostToDevice));
         if ((rc = c->alloc((void**)&c->lflag, PX * PJ * sizeof(unsigned)))) return rc;
-        if ((rc = c->alloc((void**)&c->gflag, 64 * sizeof(unsigned)))) return rc;
+        // 256 pair flags, then (from word 384, its own lines) the warm-up sink
+        if ((rc = c->alloc((void**)&c->gflag, 512 * sizeof(unsigned)))) return rc;
         if ((rc = c->alloc((void**)&c->perr, 64))) return rc;
     }
     if ((rc = c->alloc((void**)&c->ab, sizeof(ArgBlock)))) return rc;
@@ -948,8 +938,8 @@ int vla_denoise(vla_ctx* c, const void* prefix_k, const void* prefix_v, const fl
     }
     HIPC(hipSetDevice(c->device));
     if ((rc = ensure_capacity(c, n_steps))) return rc;
-    if (c->persist_ok && c->use_persist && persist_bytes(c, n_steps) <= kPersistMaxBytes) {
-        if ((rc = ensure_persist(c, n_steps))) return rc;
+    if (c->persist_ok && c->use_persist) {
+        if ((rc = ensure_persist(c))) return rc;
         if ((rc = set_args(c, prefix_k, prefix_v, noise, t_schedule, out_actions))) return rc;
         return enqueue_persist(c, n_steps);
     }

@@ -7,17 +7,23 @@
 //   matching K-slices of the O and down projections.
 // Inside an XCD, workgroups exchange data through its L2 and synchronise with
 // flags in one 128-byte line (~1 us). Across XCDs only the O and down partial
-// sums travel, written with device-scope stores and followed by one flag per
-// XCD. Every buffer that crosses workgroups is written once per call (a slot
-// per (step, layer)), so no reader can hold a stale cache line from earlier in
-// the call; the launch itself starts from clean caches. Every wait is bounded:
-// on expiry the kernel raises an error flag and runs to its end.
+// sums travel, written with device-scope stores. Workgroup j of every XCD
+// computes the same output column tiles of O and down and later reduces
+// exactly those columns, so the cross-XCD exchange is point to point: it waits
+// for the flags of the eight workgroups j only. The exchange buffers are
+// reused by every layer and step (small, so their pages stay in the TLBs):
+// each sync ends with an L1 invalidate, and the partial sums from other XCDs
+// are read with device-scope loads, so no reader sees a stale line. Every wait
+// is bounded: on expiry the kernel raises an error flag and runs to its end.
 //
-// Phases of one layer (L: XCD-local sync, G: cross-XCD sync):
+// Phases of one layer (L: XCD-local sync, G: exchange between the eight
+// workgroups j):
 //   QKV+RoPE -L- attention -L- O partial -G- reduce+residual -L- norm2 -L-
 //   gate_up+SwiGLU -L- down partial -G- reduce+residual -L- norm1(next) -L-
 // Weights of the next GEMM phase are loaded into registers right after the
-// previous GEMM's MFMAs, so they stream from HBM while the syncs wait.
+// previous GEMM's MFMAs, so they stream from HBM while the syncs wait; the
+// layer's modulation vectors are staged into LDS during the QKV phase and the
+// RoPE factors once per call, so the reduce/norm phases read no HBM.
 #pragma once
 
 #include "kernels_layer.h"
@@ -25,6 +31,9 @@
 constexpr int PX = 8;          // XCDs
 constexpr int PJ = 32;         // workgroups per XCD
 constexpr int PWAVES = 8;      // waves per workgroup
+constexpr int P_BMAX = 4;      // requests per call on this path
+constexpr int P_COLS = 64;     // max output columns per workgroup of O / down (H <= 2048)
+constexpr int P_MODPT = 3;     // staged modulation values per thread (6 * P_BMAX * P_COLS / 512)
 constexpr long P_SPIN = 1l << 20;
 
 struct PersistParams {
@@ -46,24 +55,30 @@ struct PersistParams {
     const uint16_t* vcat;
     KVLayout kv;
     const ArgBlock* ab;
-    // write-once buffers; slot (u, x) with u = step * L + layer
+    // exchange buffers: one slot per XCD (xs: two per XCD, by step parity)
     uint16_t* y;  size_t y_sl;   // A-fragment [64][H]
     uint16_t* y2;
     uint16_t* q;  size_t q_sl;   // [B][hq][T][dh]
     uint16_t* kc; uint16_t* vc; size_t kv_sl;  // [B][Tpad][dh] row-major / V-fragment order
     uint16_t* o;  size_t o_sl;   // A-fragment [64][hq*dh]
     uint16_t* a;  size_t a_sl;   // A-fragment [64][Ix]
-    float* po; float* pd; size_t p_sl;   // [M][H] partials (device-scope stores)
+    float* po; float* pd; size_t p_sl;   // [M][H] partials of each XCD (device-scope stores)
     float* ss1; float* ss2; size_t ss_sl;  // [32][64] row sum-of-squares partials
-    // per (step, x)
     float* ss0; float* yf; size_t yf_sl;  // yf: final norm output [M][H]
     float* xs; size_t xs_sl;              // Euler state after the step [M][A]
     unsigned* lflag;             // [8][32]
-    unsigned* gflag;             // [8]
+    unsigned* gflag;             // [32][8]: flag of workgroup j on XCD x at j * 8 + x
+    unsigned* sink;              // never-taken store target of the L2 warm-up loads
     int* err;
 };
 
 // ------------------------------- syncs -------------------------------------
+// Buffers are reused by every layer, so after each sync a wave drops the
+// lines its CU's L1 may still hold from earlier writes by other CUs (the XCD's
+// L2 is coherent for its CUs; data from other XCDs is read with device-scope
+// loads). Not a load: nothing is returned to registers.
+VLA_DEV void p_l1_invalidate() { asm volatile("buffer_inv sc0\n\ts_waitcnt vmcnt(0)" ::: "memory"); }
+
 struct PSync {
     unsigned lseq = 0, gseq = 0;
 };
@@ -94,21 +109,25 @@ VLA_DEV void p_local_sync(const PersistParams& p, int x, int j, PSync& s) {
         }
     }
     __syncthreads();
+    p_l1_invalidate();
 }
 
-// All XCDs have finished the phase whose data they wrote with device-scope stores.
-VLA_DEV void p_global_sync(const PersistParams& p, int x, int j, PSync& s) {
-    p_local_sync(p, x, j, s);
+// Workgroup j of every XCD has finished the phase whose data it wrote with
+// device-scope stores (the O / down partial sums of its column tiles).
+VLA_DEV void p_pair_sync(const PersistParams& p, int x, int j, PSync& s) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
     ++s.gseq;
-    if (j == 0 && threadIdx.x == 0)
-        __hip_atomic_store(&p.gflag[x], s.gseq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0)
+        __hip_atomic_store(&p.gflag[j * PX + x], s.gseq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
         long budget = P_SPIN;
         bool done = false;
         while (!done) {
             const unsigned v =
-                lane < PX ? __hip_atomic_load(&p.gflag[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : s.gseq;
+                lane < PX ? __hip_atomic_load(&p.gflag[j * PX + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                          : s.gseq;
             done = __all(v >= s.gseq);
             if (!done && --budget <= 0) {
                 if (lane == 0) __hip_atomic_store(p.err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -120,6 +139,7 @@ VLA_DEV void p_global_sync(const PersistParams& p, int x, int j, PSync& s) {
         }
     }
     __syncthreads();
+    p_l1_invalidate();
 }
 
 // ------------------------------- GEMM phase --------------------------------
@@ -145,17 +165,23 @@ VLA_DEV void p_load_w(bf16x8 (&w)[NT][NS], const uint8_t* W, int Kf, int kw0, in
 #pragma unroll
         for (int i = 0; i < NS; ++i) {
             const int kk = min(sp.beg + i, ksteps - 1);
-            w[t][i] = *(const bf16x8*)(W + (((size_t)tile * Kf + kw0 + kk) * 64 + lane) * 16);
+            // streamed once per step: keep them from evicting the L2-resident data
+            w[t][i] = __builtin_nontemporal_load((const bf16x8*)(W + (((size_t)tile * Kf + kw0 + kk) * 64 + lane) * 16));
         }
     }
 }
 
-// D[64 rows][16 cols] per tile = A (A-fragment order) x W^T, reduced over the
-// waves; `epi(t, row, col_in_tile, v, partner)` runs on waves 0..3 (one
-// 16-row tile each) for every value of the tiles t < ntile.
-template <int NT, int NS, typename Epi>
+// D[64 rows][16 cols] per tile = A (A-fragment order) x W^T. The eight waves
+// split K; their partial tiles meet in LDS (NT * 32 KiB at `red`) in one round,
+// and each (tile, 16-row block) is summed by one wave, which runs
+// `epi(t, row, col_in_tile, v, partner)` on its values (partner = the value of
+// the neighbouring column, col ^ 1). `prefetch()` runs right after the A loads
+// are issued: loads it issues return after them (vector memory returns in
+// issue order), so they overlap this GEMM instead of delaying it. The caller
+// synchronises the workgroup before `red` is used again.
+template <int NT, int NS, typename Pre, typename Epi>
 VLA_DEV void p_gemm(const uint16_t* A, PSplit sp, const bf16x8 (&w)[NT][NS], int ntile, float* red, int wave,
-                    int lane, Epi&& epi) {
+                    int lane, Pre&& prefetch, Epi&& epi) {
     bf16x8 af[NS][4];
 #pragma unroll
     for (int i = 0; i < NS; ++i)
@@ -163,35 +189,42 @@ VLA_DEV void p_gemm(const uint16_t* A, PSplit sp, const bf16x8 (&w)[NT][NS], int
         for (int mt = 0; mt < 4; ++mt)
             af[i][mt] = i < sp.n ? *(const bf16x8*)(A + ((size_t)((sp.beg + i) * 4 + mt) * 64 + lane) * 8)
                                  : (bf16x8){};
+    prefetch();
+    f32x4 acc[NT][4];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-        f32x4 acc[4];
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < 4; ++mt) acc[t][mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < NS; ++i)
+    for (int i = 0; i < NS; ++i)
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma_16x16x32(af[i][mt], w[t][i], acc[mt]);
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) *(f32x4*)(&red[((wave * 4 + mt) * 64 + lane) * 4]) = acc[mt];
-        __syncthreads();
-        if (wave < 4 && t < ntile) {
-            f32x4 sum = *(const f32x4*)(&red[((0 * 4 + wave) * 64 + lane) * 4]);
+            for (int mt = 0; mt < 4; ++mt) acc[t][mt] = mfma_16x16x32(af[i][mt], w[t][i], acc[t][mt]);
 #pragma unroll
-            for (int w2 = 1; w2 < PWAVES; ++w2) sum += *(const f32x4*)(&red[((w2 * 4 + wave) * 64 + lane) * 4]);
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float v = sum[r];
-                const float partner = __shfl_xor(v, 1, 64);
-                epi(t, wave * 16 + 4 * (lane >> 4) + r, lane & 15, v, partner);
-            }
+        for (int mt = 0; mt < 4; ++mt)
+            *(f32x4*)(&red[(((t * PWAVES + wave) * 4 + mt) * 64 + lane) * 4]) = acc[t][mt];
+    __syncthreads();
+    for (int item = wave; item < NT * 4; item += PWAVES) {
+        const int t = item >> 2, mt = item & 3;
+        if (t >= ntile) continue;
+        f32x4 sum = *(const f32x4*)(&red[(((t * PWAVES + 0) * 4 + mt) * 64 + lane) * 4]);
+#pragma unroll
+        for (int w2 = 1; w2 < PWAVES; ++w2) sum += *(const f32x4*)(&red[(((t * PWAVES + w2) * 4 + mt) * 64 + lane) * 4]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float v = sum[r];
+            const float partner = __shfl_xor(v, 1, 64);
+            epi(t, mt * 16 + 4 * (lane >> 4) + r, lane & 15, v, partner);
         }
-        __syncthreads();
     }
 }
 
-// Reduce / norm phases: thread (row = tid/8, sub = tid%8) owns CPT = H/256
-// consecutive columns of every phase's row `row`, so the residual stream of
+// Reduce / norm phases: workgroup j owns the columns of its O / down tiles
+// (tiles j, j+32, ...: 16*nt columns); thread (row = tid/8, sub = tid%8) owns
+// CPT = H/256 consecutive ones of them in row `row`, so the residual stream of
 // those columns stays in its registers for the whole call.
 
 // ------------------------------- attention ---------------------------------
@@ -306,7 +339,6 @@ VLA_DEV void p_attention(const PersistParams& p, const uint16_t* qg, int r0, con
             obuf[act_index(b * p.T + i, hh * DH + dn * 16 + (lane & 15), Kq, 1)] = f32_to_bf16(ov[r] * inv[r]);
         }
     }
-    __syncthreads();
 }
 
 // ---------------------------- the persistent kernel ------------------------
@@ -315,18 +347,24 @@ VLA_DEV int p_opaque_v(int v) {
     asm volatile("" : "+v"(v));
     return v;
 }
-VLA_DEV int p_opaque_s(int v) {
-    asm volatile("" : "+s"(v));
-    return v;
-}
+VLA_DEV int p_opaque_s(int v) { return __builtin_amdgcn_readfirstlane(p_opaque_v(v)); }
+
+// LDS of the persistent kernel: a union region (GEMM reduction, or attention's
+// probability tiles and merge buffers), then the staged modulation vectors and
+// RoPE factors.
+constexpr int P_ATT_BYTES = PWAVES * 16 * 40 * 2 + PWAVES * 64 * (128 / 16 * 4 + 8) * 4;
+constexpr int p_union_bytes(int nt) { return nt * 32768 > P_ATT_BYTES ? nt * 32768 : P_ATT_BYTES; }
 
 // Shape class: tiles per workgroup (NT*) and k-steps per wave (NS*) of the
 // QKV, O, gate_up and down phases, and columns per thread (CPT = H/256).
 template <int NTQ, int NSQ, int NTO, int NSO, int NTG, int NSG, int NTD, int NSD, int CPT>
 __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
-    constexpr int P_CPT = CPT;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[PWAVES * 16 * 40 * 2 + PWAVES * 64 * (128 / 16 * 4 + 8) * 4];
-    float* red = (float*)smem;  // GEMM reduction: [8 waves][4][64][4] floats = 32 KiB
+    constexpr int NTMAX = NTQ > NTO ? (NTQ > NTG ? NTQ : NTG) : (NTO > NTG ? NTO : NTG);
+    constexpr int UNION = p_union_bytes(NTMAX > NTD ? NTMAX : NTD);
+    __shared__ __attribute__((aligned(16))) uint8_t smem[UNION];
+    __shared__ float modl[6 * P_BMAX * P_COLS];     // [q][b][f]: gate1, scale2, shift2, gate2, scale1', shift1'
+    __shared__ float2 ropel[NTQ * 64 * 8];          // [t][position][pair]
+    float* red = (float*)smem;
     const int H = p.H, M = p.M, L = p.L, dh = p.dh, hq = p.hq;
     // the XCD-local exchanges rely on workgroup w running on XCD w % 8
     if (threadIdx.x == 0 && (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xF) != (int)(blockIdx.x % PX))
@@ -336,14 +374,15 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
     const int ks_h = H / 32, ks_o = hq * dh / 32, ks_d = p.Ix / 32;
     const int Kf_o = p.nq * dh / 32, Kf_d = p.I / 32, Kf_h = H / 32;
     float hreg[CPT];  // this thread's residual values, kept for the whole call
-    constexpr int cpt = CPT;  // == H / 256, checked by the host
-    const int Hc = H / PJ;
+    constexpr int cpt = CPT;  // == H / 256, checked by the host (and divides 16)
 
     // Thread- and workgroup-derived values, re-derived at the top of every
     // phase block from opaque copies of the ids (otherwise the compiler hoists
     // the per-lane addresses of every phase out of the loops and spills them).
     // Column tiles of a GEMM phase: local tile j + t*PJ, t < nt*, computed
     // rather than stored so that no private array is indexed at run time.
+    // Reduce / norm columns: f = sub*cpt + c of the workgroup's 16*nto O / down
+    // columns, i.e. global column pcol(f).
 #define P_PHASE_VARS                                                                                  \
     const int tid = p_opaque_v((int)threadIdx.x), lane = tid & 63, wave = tid >> 6;                   \
     const int x = p_opaque_s((int)(blockIdx.x % PX)), j = p_opaque_s((int)(blockIdx.x / PX));         \
@@ -360,11 +399,31 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
     };                                                                                                \
     auto to = [&](int t) { return min(j + t * PJ, H / 16 - 1); };                                     \
     auto tg = [&](int t) { return gbase + min(j + t * PJ, gcount - 1); };                             \
+    auto pcol = [&](int f) { return (j + (f >> 4) * PJ) * 16 + (f & 15); };                           \
     const PSplit sp_qkv = p_split(H / 32, wave), sp_o = p_split(hq * dh / 32, wave), sp_gu = sp_qkv,  \
                  sp_d = p_split(p.Ix / 32, wave);                                                     \
-    const int rrow = tid >> 3, sub = tid & 7, c0 = j * Hc + sub * cpt;                                \
+    const int rrow = tid >> 3, sub = tid & 7, f0 = sub * cpt, c0 = pcol(f0);                          \
     const bool row_ok = rrow < M;                                                                     \
-    (void)ntq; (void)nto; (void)ntg; (void)sp_o; (void)sp_gu; (void)sp_d; (void)row_ok; (void)c0
+    const int rb = row_ok ? rrow / p.T : 0;                                                           \
+    (void)ntq; (void)nto; (void)ntg; (void)sp_o; (void)sp_gu; (void)sp_d; (void)row_ok; (void)c0;     \
+    (void)rb; (void)f0
+
+    // RoPE factors of this workgroup's QKV tiles (positions < T, 8 pairs per tile)
+    {
+        P_PHASE_VARS;
+        for (int e = tid; e < NTQ * 64 * 8; e += PWAVES * 64) {
+            const int t = e >> 9, i = (e >> 3) & 63, mm = e & 7;
+            float2 cs = make_float2(1.f, 0.f);
+            if (t < ntq && i < p.T) {
+                const int col = tq(t) * 16, qd = p.nq * dh, kvd = p.nkv * dh;
+                if (col < qd + kvd) {
+                    const int local = col < qd ? col : col - qd;
+                    cs = p.rope[i * (dh / 2) + ((local % dh) >> 1) + mm];
+                }
+            }
+            ropel[e] = cs;
+        }
+    }
 
     for (int k = 0; k < p.nsteps; ++k) {
         const float* ts = p.ab->t_schedule;
@@ -372,36 +431,33 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
         {
             P_PHASE_VARS;
             p_load_w(wq, p.wqkv[0], Kf_h, 0, ks_h, sp_qkv, tq, lane);
-            const float* xin = k == 0 ? p.ab->noise : p.xs + ((size_t)(k - 1) * PX + x) * p.xs_sl;
-            float* ss0 = p.ss0 + ((size_t)k * PX + x) * p.ss_sl;
+            const float* xin = k == 0 ? p.ab->noise : p.xs + ((size_t)((k - 1) & 1) * PX + x) * p.xs_sl;
+            float* ss0 = p.ss0 + (size_t)x * p.ss_sl;
             float ssum = 0.f;
             if (row_ok) {
 #pragma unroll
-                for (int c = 0; c < P_CPT; ++c)
-                    if (c < cpt) hreg[c] = p.in_b[c0 + c];
+                for (int c = 0; c < CPT; ++c) hreg[c] = p.in_b[c0 + c];
                 const float* xr = xin + (size_t)rrow * p.A;
 #pragma unroll 5
                 for (int a = 0; a < p.A; ++a) {
                     const float xa = xr[a];
                     const uint16_t* wr = p.in_wT + (size_t)a * H + c0;
 #pragma unroll
-                    for (int c = 0; c < P_CPT; c += 2)
-                        if (c < cpt) {
-                            const uint32_t w2 = *(const uint32_t*)(wr + c);
-                            hreg[c] += xa * __uint_as_float(w2 << 16);
-                            hreg[c + 1] += xa * __uint_as_float(w2 & 0xffff0000u);
-                        }
+                    for (int c = 0; c < CPT; c += 2) {
+                        const uint32_t w2 = *(const uint32_t*)(wr + c);
+                        hreg[c] += xa * __uint_as_float(w2 << 16);
+                        hreg[c + 1] += xa * __uint_as_float(w2 & 0xffff0000u);
+                    }
                 }
 #pragma unroll
-                for (int c = 0; c < P_CPT; ++c)
-                    if (c < cpt) ssum += hreg[c] * hreg[c];
+                for (int c = 0; c < CPT; ++c) ssum += hreg[c] * hreg[c];
             }
             ssum += __shfl_xor(ssum, 1, 64);
             ssum += __shfl_xor(ssum, 2, 64);
             ssum += __shfl_xor(ssum, 4, 64);
             if (row_ok && sub == 0) ss0[j * 64 + rrow] = ssum;
             p_local_sync(p, x, j, sy);
-            // norm1 of layer 0 -> y[slot (k, 0)]
+            // norm1 of layer 0 -> y
             float part = 0.f;
             if (row_ok)
 #pragma unroll
@@ -410,25 +466,38 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
             part += __shfl_xor(part, 2, 64);
             part += __shfl_xor(part, 4, 64);
             const float inv = 1.0f / sqrtf(part / (float)H + p.eps);
-            uint16_t* yb = p.y + ((size_t)(k * L) * PX + x) * p.y_sl;
+            uint16_t* yb = p.y + (size_t)x * p.y_sl;
             if (row_ok) {
-                const float* mr = p.mod + (size_t)(k * p.B + rrow / p.T) * p.mod_ld;
+                const float* mr = p.mod + (size_t)(k * p.B + rb) * p.mod_ld;
 #pragma unroll
-                for (int c = 0; c < P_CPT; c += 2)
-                    if (c < cpt) {
-                        const int cc = c0 + c;
-                        const float v0 = hreg[c] * inv * (1.f + mr[cc]) + mr[H + cc];
-                        const float v1 = hreg[c + 1] * inv * (1.f + mr[cc + 1]) + mr[H + cc + 1];
-                        *(uint32_t*)(yb + act_index(rrow, cc, H, 1)) = pack_bf16x2(v0, v1);
-                    }
+                for (int c = 0; c < CPT; c += 2) {
+                    const int cc = c0 + c;
+                    const float v0 = hreg[c] * inv * (1.f + mr[cc]) + mr[H + cc];
+                    const float v1 = hreg[c + 1] * inv * (1.f + mr[cc + 1]) + mr[H + cc + 1];
+                    *(uint32_t*)(yb + act_index(rrow, cc, H, 1)) = pack_bf16x2(v0, v1);
+                }
             }
             p_local_sync(p, x, j, sy);
         }
 
         for (int l = 0; l < L; ++l) {
             P_PHASE_VARS;
-            const size_t sl = (size_t)(k * L + l) * PX + x;
-            const float* mr_base = p.mod + (size_t)(k * p.B) * p.mod_ld + (size_t)(6 * l) * H;
+            const size_t sl = x;  // per-XCD buffers, reused by every layer and step
+            // this layer's modulation vectors of the workgroup's columns: loaded
+            // during the QKV GEMM, written to LDS after it
+            float modv[P_MODPT];
+            const int nmod = 6 * p.B * 16 * nto;
+            auto load_mod = [&]() {
+#pragma unroll
+                for (int u = 0; u < P_MODPT; ++u) {
+                    const int e = tid + u * PWAVES * 64;
+                    modv[u] = 0.f;
+                    if (e < nmod) {
+                        const int f = e % (16 * nto), qb = e / (16 * nto), b = qb % p.B, q = qb / p.B;
+                        modv[u] = p.mod[(size_t)(k * p.B + b) * p.mod_ld + (size_t)(6 * l + 2 + q) * H + pcol(f)];
+                    }
+                }
+            };
             // ------------------------- QKV + RoPE ---------------------------
             {
                 const uint16_t* yb = p.y + sl * p.y_sl;
@@ -436,7 +505,11 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
                 uint16_t* kcb = p.kc + sl * p.kv_sl;
                 uint16_t* vcb = p.vc + sl * p.kv_sl;
                 const int qd = p.nq * dh, kvd = p.nkv * dh;
-                p_gemm(yb, sp_qkv, wq, ntq, red, wave, lane, [&](int t, int row, int cl, float v, float partner) {
+                auto pre = [&]() {
+                    load_mod();
+                    p_load_w(wo, p.wo[l], Kf_o, x * hq * dh / 32, ks_o, sp_o, to, lane);
+                };
+                p_gemm(yb, sp_qkv, wq, ntq, red, wave, lane, pre, [&](int t, int row, int cl, float v, float partner) {
                     if (row >= M) return;
                     const int col = tq(t) * 16 + cl;
                     int sec, local;
@@ -448,7 +521,7 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
                     const int b = row / p.T, i = row % p.T;
                     float outv = v;
                     if (sec < 2) {
-                        const float2 cs = p.rope[i * (dh / 2) + m];
+                        const float2 cs = ropel[(t * 64 + i) * 8 + (cl >> 1)];
                         const float u1 = second ? partner : v;
                         const float u2 = second ? v : partner;
                         outv = second ? (u2 * cs.x + u1 * cs.y) : (u1 * cs.x - u2 * cs.y);
@@ -464,27 +537,47 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
                     }
                 });
             }
-            p_load_w(wo, p.wo[l], Kf_o, x * hq * dh / 32, ks_o, sp_o, to, lane);
+#pragma unroll
+            for (int u = 0; u < P_MODPT; ++u) {
+                const int e = tid + u * PWAVES * 64;
+                if (e < nmod) {
+                    const int f = e % (16 * nto), qb = e / (16 * nto), b = qb % p.B, q = qb / p.B;
+                    modl[(q * P_BMAX + b) * P_COLS + f] = modv[u];
+                }
+            }
             p_local_sync(p, x, j, sy);
             // ------------------------- attention ----------------------------
             {
-                const int tpb = (hq * p.T + 15) / 16;
-                const int b = j / tpb, tile = j % tpb;
-                if (b < p.B) {
-                    const size_t sl2 = sl;
-                    const uint16_t* qg = p.q + sl2 * p.q_sl + (size_t)(b * hq) * p.T * dh;
+                const int tpb = (hq * p.T + 15) / 16, natt = p.B * tpb;
+                if (j < natt) {
+                    const int b = j / tpb, tile = j % tpb;
+                    const uint16_t* qg = p.q + sl * p.q_sl + (size_t)(b * hq) * p.T * dh;
                     const size_t kvb = p.kv.base(b, l, g);
                     p_attention(p, qg, tile * 16, p.kcat + kvb, p.vcat + kvb,
-                                p.kc + sl2 * p.kv_sl + (size_t)b * p.Tpad * dh,
-                                p.vc + sl2 * p.kv_sl + (size_t)b * p.Tpad * dh, p.o + sl2 * p.o_sl, b, x, smem, wave,
+                                p.kc + sl * p.kv_sl + (size_t)b * p.Tpad * dh,
+                                p.vc + sl * p.kv_sl + (size_t)b * p.Tpad * dh, p.o + sl * p.o_sl, b, x, smem, wave,
                                 lane);
+                } else if (l + 1 < L) {
+                    // idle workgroups pull the next layer's prefix K/V of this
+                    // XCD's group into its L2 (one load per 128-byte line)
+                    const int lines = 2 * p.P * dh * 2 / 128;  // K and V lines of one request
+                    unsigned acc = 0u;
+                    for (int e = (j - natt) * PWAVES * 64 + tid; e < p.B * lines; e += (PJ - natt) * PWAVES * 64) {
+                        const int b = e / lines, ln = e % lines;
+                        const size_t base = p.kv.base(b, l + 1, g);
+                        const uint16_t* src = ln < lines / 2 ? p.kcat + base + (size_t)ln * 64
+                                                             : p.vcat + base + (size_t)(ln - lines / 2) * 64;
+                        acc ^= *(const unsigned*)src;
+                    }
+                    if (acc == 0x9E3779B9u) p.sink[tid & 63] = acc;  // keeps the loads; harmless if taken
                 }
             }
             p_local_sync(p, x, j, sy);
             // ------------------------- O partial ----------------------------
             {
                 float* pob = p.po + sl * p.p_sl;
-                p_gemm(p.o + sl * p.o_sl, sp_o, wo, nto, red, wave, lane,
+                auto pre = [&]() { p_load_w(wgu, p.wgu[l], Kf_h, 0, ks_h, sp_gu, tg, lane); };
+                p_gemm(p.o + sl * p.o_sl, sp_o, wo, nto, red, wave, lane, pre,
                        [&](int t, int row, int cl, float v, float partner) {
                            if (row >= M || (cl & 1)) return;
                            const int col = to(t) * 16 + cl;
@@ -495,24 +588,33 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                        });
             }
-            p_load_w(wgu, p.wgu[l], Kf_h, 0, ks_h, sp_gu, tg, lane);
-            p_global_sync(p, x, j, sy);
+            p_pair_sync(p, x, j, sy);
             // --------------- reduce O partials + gated residual -------------
             {
                 float* ss1 = p.ss1 + sl * p.ss_sl;
                 float ssum = 0.f;
                 if (row_ok) {
-                    const float* gate = mr_base + (size_t)(rrow / p.T) * p.mod_ld + 2 * H;
+                    const float* gate = &modl[(0 * P_BMAX + rb) * P_COLS + f0];
+                    float acc[CPT];
 #pragma unroll
-                    for (int c = 0; c < P_CPT; ++c)
-                        if (c < cpt) {
-                            float acc = 0.f;
+                    for (int c = 0; c < CPT; ++c) acc[c] = 0.f;
 #pragma unroll
-                            for (int xx = 0; xx < PX; ++xx)
-                                acc += p.po[((size_t)(k * L + l) * PX + xx) * p.p_sl + (size_t)rrow * H + c0 + c];
-                            hreg[c] += gate[c0 + c] * acc;   // residual stream stays in registers
-                            ssum += hreg[c] * hreg[c];
+                    for (int xx = 0; xx < PX; ++xx) {
+                        const float* src = p.po + (size_t)xx * p.p_sl + (size_t)rrow * H + c0;
+#pragma unroll
+                        for (int c = 0; c < CPT; c += 2) {
+                            // written by other XCDs: read past this XCD's L2
+                            const unsigned long long v2 = __hip_atomic_load(
+                                (unsigned long long*)(src + c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            acc[c] += __uint_as_float((unsigned)v2);
+                            acc[c + 1] += __uint_as_float((unsigned)(v2 >> 32));
                         }
+                    }
+#pragma unroll
+                    for (int c = 0; c < CPT; ++c) {
+                        hreg[c] += gate[c] * acc[c];  // residual stream stays in registers
+                        ssum += hreg[c] * hreg[c];
+                    }
                 }
                 ssum += __shfl_xor(ssum, 1, 64);
                 ssum += __shfl_xor(ssum, 2, 64);
@@ -533,22 +635,22 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
                 const float inv = 1.0f / sqrtf(part / (float)H + p.eps);
                 uint16_t* yb = p.y2 + sl * p.y_sl;
                 if (row_ok) {
-                    const float* mr = mr_base + (size_t)(rrow / p.T) * p.mod_ld;
+                    const float* sc = &modl[(1 * P_BMAX + rb) * P_COLS + f0];
+                    const float* sh = &modl[(2 * P_BMAX + rb) * P_COLS + f0];
 #pragma unroll
-                    for (int c = 0; c < P_CPT; c += 2)
-                        if (c < cpt) {
-                            const int cc = c0 + c;
-                            const float v0 = hreg[c] * inv * (1.f + mr[3 * H + cc]) + mr[4 * H + cc];
-                            const float v1 = hreg[c + 1] * inv * (1.f + mr[3 * H + cc + 1]) + mr[4 * H + cc + 1];
-                            *(uint32_t*)(yb + act_index(rrow, cc, H, 1)) = pack_bf16x2(v0, v1);
-                        }
+                    for (int c = 0; c < CPT; c += 2) {
+                        const float v0 = hreg[c] * inv * (1.f + sc[c]) + sh[c];
+                        const float v1 = hreg[c + 1] * inv * (1.f + sc[c + 1]) + sh[c + 1];
+                        *(uint32_t*)(yb + act_index(rrow, c0 + c, H, 1)) = pack_bf16x2(v0, v1);
+                    }
                 }
             }
             p_local_sync(p, x, j, sy);
             // ------------------------- gate_up + SwiGLU ---------------------
             {
                 uint16_t* ab = p.a + sl * p.a_sl;
-                p_gemm(p.y2 + sl * p.y_sl, sp_gu, wgu, ntg, red, wave, lane,
+                auto pre = [&]() { p_load_w(wdn, p.wd[l], Kf_d, x * p.Ix / 32, ks_d, sp_d, to, lane); };
+                p_gemm(p.y2 + sl * p.y_sl, sp_gu, wgu, ntg, red, wave, lane, pre,
                        [&](int t, int row, int cl, float v, float partner) {
                            if (row >= M || (cl & 1)) return;
                            const int col = tg(t) * 16 + cl;
@@ -556,12 +658,14 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
                            ab[act_index(row, lc, p.Ix, 1)] = f32_to_bf16(silu_f(v) * partner);
                        });
             }
-            p_load_w(wdn, p.wd[l], Kf_d, x * p.Ix / 32, ks_d, sp_d, to, lane);
             p_local_sync(p, x, j, sy);
             // ------------------------- down partial -------------------------
             {
                 float* pdb = p.pd + sl * p.p_sl;
-                p_gemm(p.a + sl * p.a_sl, sp_d, wdn, nto, red, wave, lane,
+                auto pre = [&]() {
+                    if (l + 1 < L) p_load_w(wq, p.wqkv[l + 1], Kf_h, 0, ks_h, sp_qkv, tq, lane);
+                };
+                p_gemm(p.a + sl * p.a_sl, sp_d, wdn, nto, red, wave, lane, pre,
                        [&](int t, int row, int cl, float v, float partner) {
                            if (row >= M || (cl & 1)) return;
                            const int col = to(t) * 16 + cl;
@@ -572,24 +676,33 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                        });
             }
-            if (l + 1 < L) p_load_w(wq, p.wqkv[l + 1], Kf_h, 0, ks_h, sp_qkv, tq, lane);
-            p_global_sync(p, x, j, sy);
+            p_pair_sync(p, x, j, sy);
             // --------------- reduce down partials + gated residual ----------
             {
                 float* ss2 = p.ss2 + sl * p.ss_sl;
                 float ssum = 0.f;
                 if (row_ok) {
-                    const float* gate = mr_base + (size_t)(rrow / p.T) * p.mod_ld + 5 * H;
+                    const float* gate = &modl[(3 * P_BMAX + rb) * P_COLS + f0];
+                    float acc[CPT];
 #pragma unroll
-                    for (int c = 0; c < P_CPT; ++c)
-                        if (c < cpt) {
-                            float acc = 0.f;
+                    for (int c = 0; c < CPT; ++c) acc[c] = 0.f;
 #pragma unroll
-                            for (int xx = 0; xx < PX; ++xx)
-                                acc += p.pd[((size_t)(k * L + l) * PX + xx) * p.p_sl + (size_t)rrow * H + c0 + c];
-                            hreg[c] += gate[c0 + c] * acc;
-                            ssum += hreg[c] * hreg[c];
+                    for (int xx = 0; xx < PX; ++xx) {
+                        const float* src = p.pd + (size_t)xx * p.p_sl + (size_t)rrow * H + c0;
+#pragma unroll
+                        for (int c = 0; c < CPT; c += 2) {
+                            // written by other XCDs: read past this XCD's L2
+                            const unsigned long long v2 = __hip_atomic_load(
+                                (unsigned long long*)(src + c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            acc[c] += __uint_as_float((unsigned)v2);
+                            acc[c + 1] += __uint_as_float((unsigned)(v2 >> 32));
                         }
+                    }
+#pragma unroll
+                    for (int c = 0; c < CPT; ++c) {
+                        hreg[c] += gate[c] * acc[c];
+                        ssum += hreg[c] * hreg[c];
+                    }
                 }
                 ssum += __shfl_xor(ssum, 1, 64);
                 ssum += __shfl_xor(ssum, 2, 64);
@@ -609,27 +722,21 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
                 part += __shfl_xor(part, 4, 64);
                 const float inv = 1.0f / sqrtf(part / (float)H + p.eps);
                 if (row_ok) {
-                    const float* mrow = p.mod + (size_t)(k * p.B + rrow / p.T) * p.mod_ld;
+                    // layer l+1's scale1/shift1, or the final ones after the last layer
+                    const float* sc = &modl[(4 * P_BMAX + rb) * P_COLS + f0];
+                    const float* sh = &modl[(5 * P_BMAX + rb) * P_COLS + f0];
                     if (l + 1 < L) {
-                        uint16_t* yb = p.y + ((size_t)(k * L + l + 1) * PX + x) * p.y_sl;
-                        const float* sc = mrow + (size_t)(6 * (l + 1)) * H;
+                        uint16_t* yb = p.y + (size_t)x * p.y_sl;
 #pragma unroll
-                        for (int c = 0; c < P_CPT; c += 2)
-                            if (c < cpt) {
-                                const int cc = c0 + c;
-                                const float v0 = hreg[c] * inv * (1.f + sc[cc]) + sc[H + cc];
-                                const float v1 = hreg[c + 1] * inv * (1.f + sc[cc + 1]) + sc[H + cc + 1];
-                                *(uint32_t*)(yb + act_index(rrow, cc, H, 1)) = pack_bf16x2(v0, v1);
-                            }
+                        for (int c = 0; c < CPT; c += 2) {
+                            const float v0 = hreg[c] * inv * (1.f + sc[c]) + sh[c];
+                            const float v1 = hreg[c + 1] * inv * (1.f + sc[c + 1]) + sh[c + 1];
+                            *(uint32_t*)(yb + act_index(rrow, c0 + c, H, 1)) = pack_bf16x2(v0, v1);
+                        }
                     } else {
-                        float* yf = p.yf + ((size_t)k * PX + x) * p.yf_sl;
-                        const float* sc = mrow + (size_t)(6 * L) * H;
+                        float* yf = p.yf + (size_t)x * p.yf_sl;
 #pragma unroll
-                        for (int c = 0; c < P_CPT; ++c)
-                            if (c < cpt) {
-                                const int cc = c0 + c;
-                                yf[rrow * H + cc] = hreg[c] * inv * (1.f + sc[cc]) + sc[H + cc];
-                            }
+                        for (int c = 0; c < CPT; ++c) yf[rrow * H + c0 + c] = hreg[c] * inv * (1.f + sc[c]) + sh[c];
                     }
                 }
             }
@@ -641,9 +748,9 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
         // a wave owns one row and 16 outputs, loading the weights of 8 at a time
         {
             P_PHASE_VARS;
-            const float* yf = p.yf + ((size_t)k * PX + x) * p.yf_sl;
-            const float* xin = k == 0 ? p.ab->noise : p.xs + ((size_t)(k - 1) * PX + x) * p.xs_sl;
-            float* xo = p.xs + ((size_t)k * PX + x) * p.xs_sl;
+            const float* yf = p.yf + (size_t)x * p.yf_sl;
+            const float* xin = k == 0 ? p.ab->noise : p.xs + ((size_t)((k - 1) & 1) * PX + x) * p.xs_sl;
+            float* xo = p.xs + ((size_t)(k & 1) * PX + x) * p.xs_sl;
             const bool last = k + 1 == p.nsteps;
             const int chunks = (p.A + 15) / 16;
             for (int it = j * PWAVES + wave; it < M * chunks; it += PJ * PWAVES) {
@@ -694,7 +801,7 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
 __global__ void persist_reset_kernel(unsigned* lflag, unsigned* gflag, int* err) {
     const int t = threadIdx.x;
     if (t < PX * PJ) lflag[t] = 0u;
-    if (t < PX) gflag[t] = 0u;
+    if (t < PX * PJ) gflag[t] = 0u;
     if (t == 0) *err = 0;
 }
 
