@@ -16,6 +16,9 @@ Also reported:
   * ``batch64``: the batched-replica workload (64 requests, GEMM M = 3200).
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -29,6 +32,16 @@ sys.path.insert(0, ROOT)
 METRIC = "denoise steps/s & chunks/s (36L bf16, chunk 50×75, b=1/64); % HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+
+# HBM traffic of the dominant batch-1 kernel (the gate_up + SwiGLU skinny GEMM,
+# skinny_gemm_kernel<false, 3>) from rocprofv3 FETCH_SIZE / WRITE_SIZE counter
+# runs, scaled by what the counters read for a plain copy of known size. The
+# summary records a hash of the kernel sources; once they change, the figure
+# no longer describes the kernel and `traffic` is reported as null.
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gate_up_swiglu_gemm_lingbot_b1_counters.txt")
+TRAFFIC_KERNEL = "skinny_gemm_kernel<false, 3>"
+KERNEL_SOURCES = ("vla_flow_matching_denoise_amd/csrc/common.h", "vla_flow_matching_denoise_amd/csrc/kernels_layer.h")
+COPY_BYTES = 256 << 20
 
 
 def log(*a):
@@ -105,6 +118,112 @@ def dominant(res, bound):
                   "algorithmic_bytes_per_launch": int(r["bytes"]), "algorithmic_flops_per_launch": int(r["flops"])}
 
 
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """Bytes per launch from the committed counter summary, or None when absent
+    or taken on kernel sources other than the current ones."""
+    if not os.path.exists(TRAFFIC_SUMMARY):
+        return None
+    fields = {}
+    with open(TRAFFIC_SUMMARY) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def counter_run(iters):
+    """Workload of the counter runs: a plain copy of COPY_BYTES (calibration),
+    then whole layers of the batch-1 workload with the gate_up GEMM inside."""
+    import torch
+    import synth
+    from vla_flow_matching_denoise_amd import binding as B
+    from vla_flow_matching_denoise_amd.expert import Expert, dims_from_config
+    torch.cuda.set_device(0)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    cfg = synth.config(2)
+    ex = Expert(synth.make_weights(cfg, seed=0), dims_from_config(cfg))
+    dev_in, _ = build_inputs(cfg)
+    ex.denoise(*dev_in, cfg.n_steps)             # fills the modulation table
+    torch.cuda.synchronize()
+    B.vla_profile_kernel(ex.ctx, B.VLA_KERNEL_GATE_UP, iters)
+    torch.cuda.synchronize()
+    ex.close()
+    log(f"[bench] counter run done: copy of {COPY_BYTES} B x3, {iters} layers")
+
+
+def _counter_rows(d):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    with open(files[0]) as fh:
+        return list(csv.DictReader(fh))
+
+
+def _per_dispatch(rows, counter, match):
+    vals = {}
+    for r in rows:
+        if r.get("Counter_Name") == counter and match(r.get("Kernel_Name", "")):
+            vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return list(vals.values())
+
+
+def traffic_from(fetch_dir, write_dir, cmd_fetch, cmd_write):
+    """Writes the counter summary from two rocprofv3 --pmc output folders."""
+    out = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d)
+        copy = _per_dispatch(rows, name, lambda k: "copy" in k.lower())
+        gemm = _per_dispatch(rows, name, lambda k: TRAFFIC_KERNEL in k)
+        if not copy or not gemm:
+            raise SystemExit(f"{name}: copy dispatches {len(copy)}, gate_up dispatches {len(gemm)}")
+        kib_copy = max(copy)
+        scale = (COPY_BYTES / 1024.0) / kib_copy      # bytes of KiB reported, per counted KiB
+        out[name] = {"copy_kib": kib_copy, "scale": scale, "gemm_kib_mean": float(np.mean(gemm)),
+                     "gemm_bytes": float(np.mean(gemm)) * scale * 1024.0, "n": len(gemm)}
+    total = out["FETCH_SIZE"]["gemm_bytes"] + out["WRITE_SIZE"]["gemm_bytes"]
+    lines = [
+        "# HBM traffic of the gate_up + SwiGLU skinny GEMM (skinny_gemm_kernel<false, 3>),",
+        "# LingBot-shaped batch-1 workload (M = 50 rows, N = 8192, K = 1024, bf16 weights).",
+        "# Two rocprofv3 counter runs of `python bench.py --counter-run`, each scaled by the",
+        "# counter's reading for a plain device copy of 256 MiB (read 256 MiB, write 256 MiB).",
+        f"# fetch command: {cmd_fetch}",
+        f"# write command: {cmd_write}",
+        f"# summary: python bench.py --traffic-from <fetch dir> <write dir>",
+        f"copy_fetch_kib: {out['FETCH_SIZE']['copy_kib']:.1f}",
+        f"copy_write_kib: {out['WRITE_SIZE']['copy_kib']:.1f}",
+        f"fetch_scale: {out['FETCH_SIZE']['scale']:.4f}",
+        f"write_scale: {out['WRITE_SIZE']['scale']:.4f}",
+        f"gate_up_dispatches: {out['FETCH_SIZE']['n']}",
+        f"gate_up_fetch_kib_mean: {out['FETCH_SIZE']['gemm_kib_mean']:.1f}",
+        f"gate_up_write_kib_mean: {out['WRITE_SIZE']['gemm_kib_mean']:.1f}",
+        f"fetch_bytes_per_launch: {out['FETCH_SIZE']['gemm_bytes']:.0f}",
+        f"write_bytes_per_launch: {out['WRITE_SIZE']['gemm_bytes']:.0f}",
+        f"traffic_bytes_per_launch: {total:.0f}",
+        f"source_sha256_16: {kernel_source_hash()}",
+    ]
+    with open(TRAFFIC_SUMMARY, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def build_inputs(cfg, seed=0):
     import synth
     from vla_flow_matching_denoise_amd.expert import to_device
@@ -150,7 +269,15 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch64", action="store_true")
+    ap.add_argument("--counter-run", action="store_true",
+                    help="run only the workload of the rocprofv3 counter runs (copy calibration + layers)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write the traffic summary from two rocprofv3 --pmc output folders")
+    ap.add_argument("--traffic-cmds", nargs=2, metavar=("FETCH_CMD", "WRITE_CMD"), default=("?", "?"))
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from, *args.traffic_cmds)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -158,8 +285,13 @@ def main():
               f"replica of the loop on its own requests.", file=sys.stderr)
         sys.exit(2)
 
+    if args.counter_run:
+        counter_run(72)
+        return
+
     import torch
     import synth
+    from vla_flow_matching_denoise_amd import binding as B
     from vla_flow_matching_denoise_amd.expert import Expert, dims_from_config
     torch.cuda.set_device(0)
 
@@ -174,6 +306,16 @@ def main():
     bytes_call, flops_call = call_work(cfg)
     kr = kernel_rooflines(ex, cfg, args.profile_iters)
     _, roof = dominant(kr, "hbm")
+    roof["traffic"] = recorded_traffic()
+    # the opt-in persistent single-launch path on the same workload
+    ex.set_option(B.VLA_OPT_PERSISTENT, 1)
+    persistent = None
+    if ex.persistent_active:
+        wall_p, pc_p, _ = time_calls(ex, dev_in, cfg.n_steps, args.warmup, args.steps)
+        tp = wall_p / args.steps
+        persistent = {"ms_per_call": round(tp * 1e3, 4), "steps_per_s": round(cfg.n_steps * cfg.batch / tp, 3),
+                      "p50_ms": round(float(np.percentile(pc_p, 50)), 4)}
+    ex.set_option(B.VLA_OPT_PERSISTENT, 0)
     ex.close()
 
     result = {
@@ -201,6 +343,7 @@ def main():
         "roofline": roof,
         "kernels": {k: {"us": round(v["us"], 3), "GBps": round(v["GBps"], 1), "TFLOPs": round(v["TFLOPs"], 2)}
                     for k, v in kr.items()},
+        "persistent_b1": persistent,
     }
 
     if not args.no_batch64:

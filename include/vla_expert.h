@@ -57,7 +57,8 @@ extern "C" {
 /* Options for vla_set_option. */
 #define VLA_OPT_USE_GRAPH 1 /* 1 (default): replay a captured hipGraph per n_steps; 0: launch kernels eagerly */
 #define VLA_OPT_PERSISTENT 2 /* 1: for shapes it supports (batch*horizon <= 64, 8 | n_q_heads, ...),
-                                 run the whole loop as one persistent cooperative kernel; 0 (default): kernel-per-stage path */
+                                 run the whole loop as one persistent kernel (needs every CU: other work on the GPU
+                                 makes its bounded waits expire and the output NaN); 0 (default): kernel-per-stage path */
 /* Query for vla_get_option: 1 when the next vla_denoise call uses the persistent kernel. */
 #define VLA_OPT_PERSISTENT_ACTIVE 3
 
@@ -139,8 +140,11 @@ vla_ctx* vla_expert_create(const vla_weights* weights, const vla_dims* dims);
 int vla_denoise(vla_ctx* ctx, const void* prefix_k, const void* prefix_v, const float* noise,
                 const float* t_schedule, int n_steps, float* out_actions);
 
-/* Use `stream` (a hipStream_t) for every later call on ctx; NULL selects the
- * library-created stream. Returns VLA_OK or VLA_ERR_ARG. */
+/* Use `stream` (a hipStream_t) for every later call on ctx. NULL (also the
+ * state after vla_expert_create) orders each call with the legacy default
+ * stream: the work runs on a library-created stream that first waits for the
+ * default stream's earlier work, and the default stream's later work waits for
+ * the call. Returns VLA_OK or VLA_ERR_ARG. */
 int vla_set_stream(vla_ctx* ctx, void* stream);
 
 /* Set an option (VLA_OPT_*). Returns VLA_OK or VLA_ERR_ARG. */

@@ -1,7 +1,7 @@
 """GPU parity of the persistent single-launch path (small batches) against the
 CPU oracle, against the kernel-per-stage path, and across repeated calls.
 
-The persistent kernel runs the whole loop in one cooperative launch with the
+The persistent kernel runs the whole loop in one resident launch with the
 layer split over the eight XCDs; it runs for the shapes it supports when
 switched on (VLA_OPT_PERSISTENT). Gates are those of the other bf16 parity
 tests: cosine >= 0.9995 and max|gpu - oracle| <= 2e-2 * RMS(oracle).
@@ -150,3 +150,35 @@ def test_persistent_lingbot_b1_vs_stage_path():
     ref = run_oracle(cfg, decoded(2), pk, pv, x0, ts)
     _gate(out_p, ref, "persist cfg2")
     _gate(out_s, ref, "stage path cfg2")
+
+
+@pytest.mark.parametrize("persistent", [0, 1])
+def test_default_stream_ordering(persistent):
+    """With no stream set, a call is ordered with torch's default stream: an
+    input written by a torch kernel just before the call is seen, and the
+    output is complete for a plain .cpu() read, with no device-wide sync."""
+    import torch
+    from vla_flow_matching_denoise_amd import binding as B
+    from vla_flow_matching_denoise_amd.expert import to_device
+    cfg = SMALL
+    raw = _small_raw()
+    pk, pv, x0, ts = _inputs(cfg)
+    case = GpuCase(cfg, raw, pk, pv, x0, ts)
+    try:
+        case.expert.set_option(B.VLA_OPT_PERSISTENT, persistent)
+        ref = case.run()                                   # fully synchronised
+        for _ in range(3):
+            big = torch.randn(1 << 22, device="cuda")      # keep the default stream busy
+            for _ in range(4):
+                big = big * 1.0001
+            noise = (to_device(x0) + big[0] * 0.0) * 1.0   # written by a kernel on the default stream
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            out = case.expert.denoise(case.pk, case.pv, noise, case.ts, cfg.n_steps)
+            ev1.record()
+            got = out.cpu().numpy()                       # ordered after the call, no global sync
+            assert np.array_equal(got, ref)
+            ev1.synchronize()
+            assert ev0.elapsed_time(ev1) > 0.02            # the events bracket the call's GPU work
+    finally:
+        case.close()

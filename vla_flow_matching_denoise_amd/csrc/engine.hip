@@ -121,6 +121,9 @@ struct vla_ctx {
     int device = 0;
     hipStream_t own_stream = nullptr;
     hipStream_t stream = nullptr;
+    // no stream set: every call is ordered with the legacy default stream
+    bool join_null = true;
+    hipEvent_t join_in = nullptr, join_out = nullptr;
     bool use_graph = true;
     bool w8 = false;
     int M = 0, qd = 0, kvd = 0, mod_ld = 0;
@@ -150,7 +153,7 @@ struct vla_ctx {
 
     std::map<int, hipGraphExec_t> graphs;
 
-    // persistent small-batch path (one cooperative launch per call)
+    // persistent small-batch path (one resident launch per call)
     bool persist_ok = false, use_persist = false;
     int pn_cap = 0;                // 1 once the exchange buffers exist
     PersistParams pp{};
@@ -716,11 +719,33 @@ int enqueue_persist(vla_ctx* c, int n_steps) {
     p.gflag = c->gflag;
     p.sink = c->gflag + 384;
     p.err = c->perr;
+    // A plain launch (stream order and events behave as for any kernel): with
+    // one 512-thread, 100 KiB-LDS workgroup per CU, the 256 workgroups are
+    // resident together on an otherwise idle GPU. If other work holds CUs,
+    // the bounded waits expire and the output is poisoned instead of hanging.
     void* args[] = {&p};
-    HIPC(hipLaunchCooperativeKernel(persist_shape(d).fn, dim3(PX * PJ), dim3(PWAVES * 64), args, 0, c->stream));
+    HIPC(hipLaunchKernel(persist_shape(d).fn, dim3(PX * PJ), dim3(PWAVES * 64), args, 0, c->stream));
     const int n = c->M * d.action_dim;
     hipLaunchKernelGGL(persist_check_kernel, dim3(8), dim3(256), 0, c->stream, c->perr, c->ab, n);
     HIPC(hipGetLastError());
+    return VLA_OK;
+}
+
+// With no stream set, a call runs on the library's own stream (a graph cannot
+// be captured on the legacy default stream) and is joined to the default
+// stream: it waits for the default stream's earlier work, and the default
+// stream's later work waits for it.
+int stream_enter(vla_ctx* c) {
+    if (!c->join_null) return VLA_OK;
+    HIPC(hipEventRecord(c->join_in, nullptr));
+    HIPC(hipStreamWaitEvent(c->stream, c->join_in, 0));
+    return VLA_OK;
+}
+
+int stream_exit(vla_ctx* c) {
+    if (!c->join_null) return VLA_OK;
+    HIPC(hipEventRecord(c->join_out, c->stream));
+    HIPC(hipStreamWaitEvent(nullptr, c->join_out, 0));
     return VLA_OK;
 }
 
@@ -739,6 +764,8 @@ void destroy_ctx(vla_ctx* c) {
     for (void* p : c->allocs) (void)hipFree(p);
     c->allocs.clear();
     if (c->own_stream) (void)hipStreamDestroy(c->own_stream);
+    if (c->join_in) (void)hipEventDestroy(c->join_in);
+    if (c->join_out) (void)hipEventDestroy(c->join_out);
     delete c;
 }
 
@@ -754,6 +781,8 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
     HIPC(hipGetDevice(&c->device));
     HIPC(hipStreamCreateWithFlags(&c->own_stream, hipStreamNonBlocking));
     c->stream = c->own_stream;
+    HIPC(hipEventCreateWithFlags(&c->join_in, hipEventDisableTiming));
+    HIPC(hipEventCreateWithFlags(&c->join_out, hipEventDisableTiming));
 
     int rc;
     // pointer checks
@@ -897,6 +926,44 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
 
 }  // namespace
 
+static int denoise_enqueue(vla_ctx* c, const void* prefix_k, const void* prefix_v, const float* noise,
+                           const float* t_schedule, int n_steps, float* out_actions) {
+    int rc;
+    if ((rc = ensure_capacity(c, n_steps))) return rc;
+    if (c->persist_ok && c->use_persist) {
+        if ((rc = ensure_persist(c))) return rc;
+        if ((rc = set_args(c, prefix_k, prefix_v, noise, t_schedule, out_actions))) return rc;
+        return enqueue_persist(c, n_steps);
+    }
+    if ((rc = set_args(c, prefix_k, prefix_v, noise, t_schedule, out_actions))) return rc;
+    if (!c->use_graph) return enqueue_forward(c, n_steps);
+    auto it = c->graphs.find(n_steps);
+    if (it == c->graphs.end()) {
+        hipGraph_t g = nullptr;
+        HIPC(hipStreamBeginCapture(c->stream, hipStreamCaptureModeRelaxed));
+        rc = enqueue_forward(c, n_steps);
+        hipError_t e = hipStreamEndCapture(c->stream, &g);
+        if (rc) {
+            if (g) (void)hipGraphDestroy(g);
+            return rc;
+        }
+        if (e != hipSuccess) {
+            set_err("graph capture failed: %s", hipGetErrorString(e));
+            return VLA_ERR_HIP;
+        }
+        hipGraphExec_t ex = nullptr;
+        e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+        (void)hipGraphDestroy(g);
+        if (e != hipSuccess) {
+            set_err("graph instantiate failed: %s", hipGetErrorString(e));
+            return VLA_ERR_HIP;
+        }
+        it = c->graphs.emplace(n_steps, ex).first;
+    }
+    HIPC(hipGraphLaunch(it->second, c->stream));
+    return VLA_OK;
+}
+
 extern "C" {
 
 vla_ctx* vla_expert_create(const vla_weights* weights, const vla_dims* dims) {
@@ -937,39 +1004,10 @@ int vla_denoise(vla_ctx* c, const void* prefix_k, const void* prefix_v, const fl
         return VLA_ERR_ARG;
     }
     HIPC(hipSetDevice(c->device));
-    if ((rc = ensure_capacity(c, n_steps))) return rc;
-    if (c->persist_ok && c->use_persist) {
-        if ((rc = ensure_persist(c))) return rc;
-        if ((rc = set_args(c, prefix_k, prefix_v, noise, t_schedule, out_actions))) return rc;
-        return enqueue_persist(c, n_steps);
-    }
-    if ((rc = set_args(c, prefix_k, prefix_v, noise, t_schedule, out_actions))) return rc;
-    if (!c->use_graph) return enqueue_forward(c, n_steps);
-    auto it = c->graphs.find(n_steps);
-    if (it == c->graphs.end()) {
-        hipGraph_t g = nullptr;
-        HIPC(hipStreamBeginCapture(c->stream, hipStreamCaptureModeRelaxed));
-        rc = enqueue_forward(c, n_steps);
-        hipError_t e = hipStreamEndCapture(c->stream, &g);
-        if (rc) {
-            if (g) (void)hipGraphDestroy(g);
-            return rc;
-        }
-        if (e != hipSuccess) {
-            set_err("graph capture failed: %s", hipGetErrorString(e));
-            return VLA_ERR_HIP;
-        }
-        hipGraphExec_t ex = nullptr;
-        e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
-        (void)hipGraphDestroy(g);
-        if (e != hipSuccess) {
-            set_err("graph instantiate failed: %s", hipGetErrorString(e));
-            return VLA_ERR_HIP;
-        }
-        it = c->graphs.emplace(n_steps, ex).first;
-    }
-    HIPC(hipGraphLaunch(it->second, c->stream));
-    return VLA_OK;
+    if ((rc = stream_enter(c))) return rc;
+    rc = denoise_enqueue(c, prefix_k, prefix_v, noise, t_schedule, n_steps, out_actions);
+    const int rc2 = stream_exit(c);
+    return rc ? rc : rc2;
 }
 
 int vla_set_stream(vla_ctx* c, void* stream) {
@@ -979,6 +1017,7 @@ int vla_set_stream(vla_ctx* c, void* stream) {
         return VLA_ERR_ARG;
     }
     c->stream = stream ? (hipStream_t)stream : c->own_stream;
+    c->join_null = stream == nullptr;
     return VLA_OK;
 }
 
@@ -1034,6 +1073,10 @@ int vla_test_modulation(vla_ctx* c, const float* t_schedule, int n_steps, float*
         return VLA_ERR_ARG;
     }
     HIPC(hipSetDevice(c->device));
+    {
+        const int rj = stream_enter(c);  // inputs written on the default stream
+        if (rj) return rj;
+    }
     if ((rc = ensure_capacity(c, n_steps))) return rc;
     if ((rc = enqueue_prologue(c, n_steps, t_schedule))) return rc;
     HIPC(hipMemcpyAsync(mod_out, c->modtab, (size_t)n_steps * c->d.batch * c->mod_ld * 4, hipMemcpyDeviceToDevice,
@@ -1058,6 +1101,10 @@ int vla_test_layer(vla_ctx* c, const void* prefix_k, const void* prefix_v, const
         return VLA_ERR_ARG;
     }
     HIPC(hipSetDevice(c->device));
+    {
+        const int rj = stream_enter(c);  // inputs written on the default stream
+        if (rj) return rj;
+    }
     if ((rc = ensure_capacity(c, n_steps))) return rc;
     if ((rc = set_args(c, prefix_k, prefix_v, nullptr, t_schedule, nullptr))) return rc;
     if ((rc = enqueue_prefix_repack(c, (const uint16_t*)prefix_k, (const uint16_t*)prefix_v))) return rc;
@@ -1089,6 +1136,10 @@ int vla_test_attention(vla_ctx* c, const void* prefix_k, const void* prefix_v, i
         return VLA_ERR_ARG;
     }
     HIPC(hipSetDevice(c->device));
+    {
+        const int rj = stream_enter(c);  // inputs written on the default stream
+        if (rj) return rj;
+    }
     const vla_dims& d = c->d;
     if ((rc = enqueue_prefix_repack(c, (const uint16_t*)prefix_k, (const uint16_t*)prefix_v))) return rc;
     long n = (long)d.batch * d.n_kv_heads * d.horizon * (d.head_dim / 8);
@@ -1113,6 +1164,10 @@ int vla_profile_kernel(vla_ctx* c, int kernel, int iters, double* us_per_launch,
         return VLA_ERR_ARG;
     }
     HIPC(hipSetDevice(c->device));
+    {
+        const int rj = stream_enter(c);  // inputs written on the default stream
+        if (rj) return rj;
+    }
     const vla_dims& d = c->d;
     const int L = d.n_layers, M = c->M, H = d.hidden, I = d.intermediate;
     std::vector<hipEvent_t> ev(2 * iters);

@@ -1,4 +1,4 @@
-// Persistent denoise loop for small batches (B*T <= 64 rows), one cooperative
+// Persistent denoise loop for small batches (B*T <= 64 rows), one resident
 // launch per call: 256 workgroups, one per CU, 32 on each of the 8 XCDs
 // (workgroup w runs on XCD w % 8). Each layer is split tensor-parallel over
 // the XCDs:
