@@ -61,6 +61,10 @@ extern "C" {
                                  makes its bounded waits expire and the output NaN); 0 (default): kernel-per-stage path */
 /* Query for vla_get_option: 1 when the next vla_denoise call uses the persistent kernel. */
 #define VLA_OPT_PERSISTENT_ACTIVE 3
+/* Query for vla_get_option: waits for the ctx stream, then gives the outcome of the last persistent
+ * call: 0 completed, 1 an XCD-local wait expired, 2 a cross-XCD wait expired, 3 the workgroups were
+ * not spread 32 per XCD. After 1-3 the call's output holds NaN. */
+#define VLA_OPT_PERSISTENT_STATUS 4
 
 typedef struct vla_ctx vla_ctx;
 
@@ -141,10 +145,9 @@ int vla_denoise(vla_ctx* ctx, const void* prefix_k, const void* prefix_v, const 
                 const float* t_schedule, int n_steps, float* out_actions);
 
 /* Use `stream` (a hipStream_t) for every later call on ctx. NULL (also the
- * state after vla_expert_create) orders each call with the legacy default
- * stream: the work runs on a library-created stream that first waits for the
- * default stream's earlier work, and the default stream's later work waits for
- * the call. Returns VLA_OK or VLA_ERR_ARG. */
+ * state after vla_expert_create) selects the legacy default stream. Graphs
+ * are captured once on a library-created stream and replayed on this one.
+ * Returns VLA_OK or VLA_ERR_ARG. */
 int vla_set_stream(vla_ctx* ctx, void* stream);
 
 /* Set an option (VLA_OPT_*). Returns VLA_OK or VLA_ERR_ARG. */

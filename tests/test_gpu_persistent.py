@@ -43,6 +43,12 @@ def _case(cfg, raw, *ins):
     return case
 
 
+def _status_ok(case):
+    from vla_flow_matching_denoise_amd import binding as B
+    st = case.expert.get_option(B.VLA_OPT_PERSISTENT_STATUS)
+    assert st == 0, f"persistent kernel reported status {st}"
+
+
 def _small_raw():
     return synth.make_weights(SMALL, seed=0)
 
@@ -58,6 +64,7 @@ def test_persistent_small_end_to_end_and_vs_stage_path():
     try:
         assert case.expert.persistent_active
         out_p = case.run()
+        _status_ok(case)
         _gate(out_p, ref, "persist small")
         case.expert.set_option(B.VLA_OPT_PERSISTENT, 0)
         assert not case.expert.persistent_active
@@ -128,6 +135,7 @@ def test_persistent_ragged_batches(batch, horizon, action_dim, prefix_len):
     try:
         assert case.expert.persistent_active
         out = case.run()
+        _status_ok(case)
     finally:
         case.close()
     _gate(out, run_oracle(cfg, oracle.decode_weights(raw), pk, pv, x0, ts), "persist ragged")
@@ -143,6 +151,7 @@ def test_persistent_lingbot_b1_vs_stage_path():
     try:
         assert case.expert.persistent_active
         out_p = case.run()
+        _status_ok(case)
         case.expert.set_option(B.VLA_OPT_PERSISTENT, 0)
         out_s = case.run()
     finally:

@@ -24,6 +24,7 @@ VLA_ERR_HIP = -4
 VLA_OPT_USE_GRAPH = 1
 VLA_OPT_PERSISTENT = 2
 VLA_OPT_PERSISTENT_ACTIVE = 3
+VLA_OPT_PERSISTENT_STATUS = 4
 
 # every symbol include/vla_expert.h declares
 EXPORTED = (

@@ -121,9 +121,6 @@ struct vla_ctx {
     int device = 0;
     hipStream_t own_stream = nullptr;
     hipStream_t stream = nullptr;
-    // no stream set: every call is ordered with the legacy default stream
-    bool join_null = true;
-    hipEvent_t join_in = nullptr, join_out = nullptr;
     bool use_graph = true;
     bool w8 = false;
     int M = 0, qd = 0, kvd = 0, mod_ld = 0;
@@ -678,7 +675,8 @@ int enqueue_persist(vla_ctx* c, int n_steps) {
     int rc;
     if ((rc = enqueue_prefix_repack(c, nullptr, nullptr))) return rc;
     if ((rc = enqueue_prologue(c, n_steps, nullptr))) return rc;
-    hipLaunchKernelGGL(persist_reset_kernel, dim3(1), dim3(256), 0, c->stream, c->lflag, c->gflag, c->perr);
+    hipLaunchKernelGGL(persist_reset_kernel, dim3(1), dim3(256), 0, c->stream, c->lflag, c->gflag, c->gflag + 320,
+                       c->perr);
     HIPC(hipGetLastError());
     PersistParams p = c->pp;
     p.M = c->M;
@@ -718,6 +716,7 @@ int enqueue_persist(vla_ctx* c, int n_steps) {
     p.lflag = c->lflag;
     p.gflag = c->gflag;
     p.sink = c->gflag + 384;
+    p.ticket = c->gflag + 320;
     p.err = c->perr;
     // A plain launch (stream order and events behave as for any kernel): with
     // one 512-thread, 100 KiB-LDS workgroup per CU, the 256 workgroups are
@@ -731,24 +730,6 @@ int enqueue_persist(vla_ctx* c, int n_steps) {
     return VLA_OK;
 }
 
-// With no stream set, a call runs on the library's own stream (a graph cannot
-// be captured on the legacy default stream) and is joined to the default
-// stream: it waits for the default stream's earlier work, and the default
-// stream's later work waits for it.
-int stream_enter(vla_ctx* c) {
-    if (!c->join_null) return VLA_OK;
-    HIPC(hipEventRecord(c->join_in, nullptr));
-    HIPC(hipStreamWaitEvent(c->stream, c->join_in, 0));
-    return VLA_OK;
-}
-
-int stream_exit(vla_ctx* c) {
-    if (!c->join_null) return VLA_OK;
-    HIPC(hipEventRecord(c->join_out, c->stream));
-    HIPC(hipStreamWaitEvent(nullptr, c->join_out, 0));
-    return VLA_OK;
-}
-
 int set_args(vla_ctx* c, const void* pk, const void* pv, const float* noise, const float* ts, float* out) {
     hipLaunchKernelGGL(set_args_kernel, dim3(1), dim3(1), 0, c->stream, c->ab, (const uint16_t*)pk,
                        (const uint16_t*)pv, noise, ts, out);
@@ -758,14 +739,13 @@ int set_args(vla_ctx* c, const void* pk, const void* pv, const float* noise, con
 
 void destroy_ctx(vla_ctx* c) {
     if (!c) return;
-    if (c->stream) (void)hipStreamSynchronize(c->stream);
+    (void)hipStreamSynchronize(c->stream);  // the caller's stream, or the legacy default stream
+    if (c->own_stream) (void)hipStreamSynchronize(c->own_stream);
     for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);
     c->graphs.clear();
     for (void* p : c->allocs) (void)hipFree(p);
     c->allocs.clear();
     if (c->own_stream) (void)hipStreamDestroy(c->own_stream);
-    if (c->join_in) (void)hipEventDestroy(c->join_in);
-    if (c->join_out) (void)hipEventDestroy(c->join_out);
     delete c;
 }
 
@@ -779,10 +759,10 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
     c->kvd = d.n_kv_heads * dh;
     c->mod_ld = (6 * L + 2) * H;
     HIPC(hipGetDevice(&c->device));
+    // graphs are captured on this stream; work runs on `stream`, the legacy
+    // default stream until vla_set_stream names another
     HIPC(hipStreamCreateWithFlags(&c->own_stream, hipStreamNonBlocking));
-    c->stream = c->own_stream;
-    HIPC(hipEventCreateWithFlags(&c->join_in, hipEventDisableTiming));
-    HIPC(hipEventCreateWithFlags(&c->join_out, hipEventDisableTiming));
+    c->stream = nullptr;
 
     int rc;
     // pointer checks
@@ -913,7 +893,7 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
         if ((rc = c->alloc((void**)&c->wptrs, hp.size() * sizeof(void*)))) return rc;
         HIPC(hipMemcpy(c->wptrs, hp.data(), hp.size() * sizeof(void*), hipMemcpyHostToDevice));
         if ((rc = c->alloc((void**)&c->lflag, PX * PJ * sizeof(unsigned)))) return rc;
-        // 256 pair flags, then (from word 384, its own lines) the warm-up sink
+        // 256 pair flags, the 8 XCD tickets at word 320, the warm-up sink at 384
         if ((rc = c->alloc((void**)&c->gflag, 512 * sizeof(unsigned)))) return rc;
         if ((rc = c->alloc((void**)&c->perr, 64))) return rc;
     }
@@ -939,10 +919,20 @@ static int denoise_enqueue(vla_ctx* c, const void* prefix_k, const void* prefix_
     if (!c->use_graph) return enqueue_forward(c, n_steps);
     auto it = c->graphs.find(n_steps);
     if (it == c->graphs.end()) {
+        // a graph cannot be captured on the legacy default stream: capture on
+        // the library's stream, replay on the caller's
+        const hipStream_t run = c->stream;
+        c->stream = run ? run : c->own_stream;
         hipGraph_t g = nullptr;
-        HIPC(hipStreamBeginCapture(c->stream, hipStreamCaptureModeRelaxed));
+        hipError_t e = hipStreamBeginCapture(c->stream, hipStreamCaptureModeRelaxed);
+        if (e != hipSuccess) {
+            c->stream = run;
+            set_err("graph capture failed to start: %s", hipGetErrorString(e));
+            return VLA_ERR_HIP;
+        }
         rc = enqueue_forward(c, n_steps);
-        hipError_t e = hipStreamEndCapture(c->stream, &g);
+        e = hipStreamEndCapture(c->stream, &g);
+        c->stream = run;
         if (rc) {
             if (g) (void)hipGraphDestroy(g);
             return rc;
@@ -1004,10 +994,7 @@ int vla_denoise(vla_ctx* c, const void* prefix_k, const void* prefix_v, const fl
         return VLA_ERR_ARG;
     }
     HIPC(hipSetDevice(c->device));
-    if ((rc = stream_enter(c))) return rc;
-    rc = denoise_enqueue(c, prefix_k, prefix_v, noise, t_schedule, n_steps, out_actions);
-    const int rc2 = stream_exit(c);
-    return rc ? rc : rc2;
+    return denoise_enqueue(c, prefix_k, prefix_v, noise, t_schedule, n_steps, out_actions);
 }
 
 int vla_set_stream(vla_ctx* c, void* stream) {
@@ -1016,8 +1003,7 @@ int vla_set_stream(vla_ctx* c, void* stream) {
         set_err("ctx is NULL");
         return VLA_ERR_ARG;
     }
-    c->stream = stream ? (hipStream_t)stream : c->own_stream;
-    c->join_null = stream == nullptr;
+    c->stream = (hipStream_t)stream;
     return VLA_OK;
 }
 
@@ -1049,6 +1035,15 @@ int vla_get_option(const vla_ctx* c, int option, int* value) {
         case VLA_OPT_USE_GRAPH: *value = c->use_graph ? 1 : 0; return VLA_OK;
         case VLA_OPT_PERSISTENT: *value = c->use_persist ? 1 : 0; return VLA_OK;
         case VLA_OPT_PERSISTENT_ACTIVE: *value = (c->persist_ok && c->use_persist) ? 1 : 0; return VLA_OK;
+        case VLA_OPT_PERSISTENT_STATUS: {
+            int e = 0;
+            if (c->perr) {
+                HIPC(hipStreamSynchronize(c->stream));
+                HIPC(hipMemcpy(&e, c->perr, sizeof(int), hipMemcpyDeviceToHost));
+            }
+            *value = e;
+            return VLA_OK;
+        }
     }
     set_err("unknown option %d", option);
     return VLA_ERR_ARG;
@@ -1073,10 +1068,6 @@ int vla_test_modulation(vla_ctx* c, const float* t_schedule, int n_steps, float*
         return VLA_ERR_ARG;
     }
     HIPC(hipSetDevice(c->device));
-    {
-        const int rj = stream_enter(c);  // inputs written on the default stream
-        if (rj) return rj;
-    }
     if ((rc = ensure_capacity(c, n_steps))) return rc;
     if ((rc = enqueue_prologue(c, n_steps, t_schedule))) return rc;
     HIPC(hipMemcpyAsync(mod_out, c->modtab, (size_t)n_steps * c->d.batch * c->mod_ld * 4, hipMemcpyDeviceToDevice,
@@ -1101,10 +1092,6 @@ int vla_test_layer(vla_ctx* c, const void* prefix_k, const void* prefix_v, const
         return VLA_ERR_ARG;
     }
     HIPC(hipSetDevice(c->device));
-    {
-        const int rj = stream_enter(c);  // inputs written on the default stream
-        if (rj) return rj;
-    }
     if ((rc = ensure_capacity(c, n_steps))) return rc;
     if ((rc = set_args(c, prefix_k, prefix_v, nullptr, t_schedule, nullptr))) return rc;
     if ((rc = enqueue_prefix_repack(c, (const uint16_t*)prefix_k, (const uint16_t*)prefix_v))) return rc;
@@ -1136,10 +1123,6 @@ int vla_test_attention(vla_ctx* c, const void* prefix_k, const void* prefix_v, i
         return VLA_ERR_ARG;
     }
     HIPC(hipSetDevice(c->device));
-    {
-        const int rj = stream_enter(c);  // inputs written on the default stream
-        if (rj) return rj;
-    }
     const vla_dims& d = c->d;
     if ((rc = enqueue_prefix_repack(c, (const uint16_t*)prefix_k, (const uint16_t*)prefix_v))) return rc;
     long n = (long)d.batch * d.n_kv_heads * d.horizon * (d.head_dim / 8);
@@ -1164,10 +1147,6 @@ int vla_profile_kernel(vla_ctx* c, int kernel, int iters, double* us_per_launch,
         return VLA_ERR_ARG;
     }
     HIPC(hipSetDevice(c->device));
-    {
-        const int rj = stream_enter(c);  // inputs written on the default stream
-        if (rj) return rj;
-    }
     const vla_dims& d = c->d;
     const int L = d.n_layers, M = c->M, H = d.hidden, I = d.intermediate;
     std::vector<hipEvent_t> ev(2 * iters);

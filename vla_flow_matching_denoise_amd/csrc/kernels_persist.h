@@ -1,6 +1,7 @@
 // Persistent denoise loop for small batches (B*T <= 64 rows), one resident
 // launch per call: 256 workgroups, one per CU, 32 on each of the 8 XCDs
-// (workgroup w runs on XCD w % 8). Each layer is split tensor-parallel over
+// (each workgroup learns its XCD from the hardware and takes an index on
+// it). Each layer is split tensor-parallel over
 // the XCDs:
 //   XCD x owns query heads [x*hq, (x+1)*hq) and their KV group g(x) (whose
 //   K/V it computes itself), SwiGLU columns [x*I/8, (x+1)*I/8), and the
@@ -69,6 +70,7 @@ struct PersistParams {
     unsigned* lflag;             // [8][32]
     unsigned* gflag;             // [32][8]: flag of workgroup j on XCD x at j * 8 + x
     unsigned* sink;              // never-taken store target of the L2 warm-up loads
+    unsigned* ticket;            // [8]: workgroups that have taken an index on each XCD
     int* err;
 };
 
@@ -366,9 +368,24 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
     __shared__ float2 ropel[NTQ * 64 * 8];          // [t][position][pair]
     float* red = (float*)smem;
     const int H = p.H, M = p.M, L = p.L, dh = p.dh, hq = p.hq;
-    // the XCD-local exchanges rely on workgroup w running on XCD w % 8
-    if (threadIdx.x == 0 && (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xF) != (int)(blockIdx.x % PX))
-        __hip_atomic_store(p.err, 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Identity: x = the XCD this workgroup runs on (hardware XCC_ID), j = its
+    // ticket among the workgroups on that XCD, so nothing depends on how the
+    // dispatcher spreads workgroups over XCDs. With 256 workgroups, one per
+    // CU, every XCD holds exactly 32; anything else is reported (error 3) and
+    // the other workgroups' bounded waits end the call.
+    __shared__ int s_id[2];
+    if (threadIdx.x == 0) {
+        const int xcc = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 0xF);
+        const int t = xcc < PX ? (int)__hip_atomic_fetch_add(&p.ticket[xcc], 1u, __ATOMIC_RELAXED,
+                                                               __HIP_MEMORY_SCOPE_AGENT)
+                               : PJ;
+        s_id[0] = xcc;
+        s_id[1] = t;
+        if (t >= PJ) __hip_atomic_store(p.err, 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    const int x_id = s_id[0], j_id = s_id[1];
+    if (j_id >= PJ) return;
     PSync sy;
     bf16x8 wq[NTQ][NSQ], wo[NTO][NSO], wgu[NTG][NSG], wdn[NTD][NSD];
     const int ks_h = H / 32, ks_o = hq * dh / 32, ks_d = p.Ix / 32;
@@ -385,7 +402,7 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
     // columns, i.e. global column pcol(f).
 #define P_PHASE_VARS                                                                                  \
     const int tid = p_opaque_v((int)threadIdx.x), lane = tid & 63, wave = tid >> 6;                   \
-    const int x = p_opaque_s((int)(blockIdx.x % PX)), j = p_opaque_s((int)(blockIdx.x / PX));         \
+    const int x = p_opaque_s(x_id), j = p_opaque_s(j_id);                                             \
     const int g = (x * hq) / p.G;                                                                     \
     const int nqt = hq * dh / 16, nkt = dh / 16, n_qkv = nqt + 2 * nkt;                               \
     const int gbase = x * (2 * p.Ix) / 16, gcount = 2 * p.Ix / 16;                                    \
@@ -798,10 +815,11 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
 
 // Flags start at zero for every call (a kernel, so that a captured graph
 // could hold it too).
-__global__ void persist_reset_kernel(unsigned* lflag, unsigned* gflag, int* err) {
+__global__ void persist_reset_kernel(unsigned* lflag, unsigned* gflag, unsigned* ticket, int* err) {
     const int t = threadIdx.x;
     if (t < PX * PJ) lflag[t] = 0u;
     if (t < PX * PJ) gflag[t] = 0u;
+    if (t < PX) ticket[t] = 0u;
     if (t == 0) *err = 0;
 }
 
