@@ -387,7 +387,7 @@ int launch_gemm(vla_ctx* c, const Linear& lin, const GemmCfg& cfg, bool w8, int 
         dim3 grid(cfg.gx, cfg.ksplit);
         return w8 ? launch_skinny_t<true>(epi, p, grid, c->stream) : launch_skinny_t<false>(epi, p, grid, c->stream);
     }
-    dim3 grid(lin.N / cfg.NT, (p.M + cfg.MT - 1) / cfg.MT);
+    dim3 grid((lin.N / cfg.NT) * ((p.M + cfg.MT - 1) / cfg.MT));  // tile from the linear id
     if (cfg.NT == 128) return w8 ? launch_tiled_t<128, 128, true>(epi, p, grid, c->stream)
                                  : launch_tiled_t<128, 128, false>(epi, p, grid, c->stream);
     if (cfg.NT == 64) return w8 ? launch_tiled_t<128, 64, true>(epi, p, grid, c->stream)
@@ -449,12 +449,14 @@ int launch_attention(vla_ctx* c, int l, const uint16_t* q, uint16_t* o, int ofra
     dim3 ag((G * d.horizon + 15) / 16, d.n_kv_heads, d.batch);
     // few workgroups (small batch): 8 waves per workgroup split the keys finer
     const bool wide = (long)ag.x * ag.y * ag.z < 512;
-    if (d.head_dim == 128) {
-        if (wide) VLA_LAUNCH((attn_kernel<128, 8>), ag, dim3(512), 0, c->stream, ap);
-        else VLA_LAUNCH((attn_kernel<128, 4>), ag, dim3(256), 0, c->stream, ap);
+    if (wide) {
+        if (d.head_dim == 128) VLA_LAUNCH((attn_kernel<128, 8>), ag, dim3(512), 0, c->stream, ap);
+        else VLA_LAUNCH((attn_kernel<64, 8>), ag, dim3(512), 0, c->stream, ap);
     } else {
-        if (wide) VLA_LAUNCH((attn_kernel<64, 8>), ag, dim3(512), 0, c->stream, ap);
-        else VLA_LAUNCH((attn_kernel<64, 4>), ag, dim3(256), 0, c->stream, ap);
+        // many rows: 64 query rows per workgroup, K/V staged once through LDS
+        const dim3 rg((G * d.horizon + 63) / 64, d.n_kv_heads, d.batch);
+        if (d.head_dim == 128) VLA_LAUNCH((attn_rows_kernel<128>), rg, dim3(256), 0, c->stream, ap);
+        else VLA_LAUNCH((attn_rows_kernel<64>), rg, dim3(256), 0, c->stream, ap);
     }
     HIPC(hipGetLastError());
     return VLA_OK;
@@ -483,6 +485,7 @@ int launch_block_gemm(vla_ctx* c, int which, int step, int l, int* S) {
     p.M = c->M;
     p.B = d.batch;
     p.T = d.horizon;
+    p.inv_T = 1.0f / (float)d.horizon;
     p.mod = c->modtab;
     p.mod_ld = c->mod_ld;
     p.step = step;
@@ -502,6 +505,7 @@ int launch_block_gemm(vla_ctx* c, int which, int step, int l, int* S) {
         p.nq = d.n_q_heads;
         p.nkv = d.n_kv_heads;
         p.dh = d.head_dim;
+        p.dh_shift = d.head_dim == 128 ? 7 : 6;
         return launch_gemm(c, c->qkv[l], c->qkv[l].cfg, c->w8, EPI_QKV_ROPE, p);
     }
     if (which == VLA_KERNEL_O || which == VLA_KERNEL_DOWN) {

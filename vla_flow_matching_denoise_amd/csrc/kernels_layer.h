@@ -182,8 +182,19 @@ struct GemmParams {
     int layer, P;
     const float2* rope;  // [T][dh/2]
     int nq, nkv, dh;
+    int dh_shift;        // log2(dh)
+    float inv_T;         // 1/T, for the row -> request split without a divide
     uint16_t* act;       // EPI_SWIGLU output [M][N/2]
 };
+
+// row / T for row >= 0: a float estimate corrected to the exact quotient
+// (epilogues run this per element, where an integer divide costs ~40 ops).
+VLA_DEV int div_T(int row, const GemmParams& p) {
+    int b = (int)((float)row * p.inv_T);
+    if (b * p.T > row) --b;
+    else if ((b + 1) * p.T <= row) ++b;
+    return b;
+}
 
 // v: this lane's value of (row, col); partner: the value of (row, col ^ 1).
 template <int EPI>
@@ -194,7 +205,7 @@ VLA_DEV void epilogue_store(const GemmParams& p, int row, int col, float v, floa
     } else if constexpr (EPI == EPI_BIAS_F32) {
         p.out_f32[(size_t)row * p.N + col] = v + p.bias[col];
     } else if constexpr (EPI == EPI_RESID) {
-        const int b = row / p.T;
+        const int b = div_T(row, p);
         const float g = p.mod[(size_t)(p.step * p.B + b) * p.mod_ld + p.gate_off + col];
         float* hp = p.out_f32 + (size_t)row * p.N + col;
         *hp = *hp + g * v;
@@ -206,9 +217,9 @@ VLA_DEV void epilogue_store(const GemmParams& p, int row, int col, float v, floa
         if (col < qd) { sec = 0; local = col; }
         else if (col < qd + kvd) { sec = 1; local = col - qd; }
         else { sec = 2; local = col - qd - kvd; }
-        const int head = local / p.dh, pp = local % p.dh;
+        const int head = local >> p.dh_shift, pp = local & (p.dh - 1);
         const int m = pp >> 1, second = pp & 1;
-        const int b = row / p.T, i = row % p.T;
+        const int b = div_T(row, p), i = row - b * p.T;
         float outv = v;
         if (sec < 2) {
             const float2 cs = p.rope[i * (p.dh / 2) + m];
@@ -325,7 +336,9 @@ __global__ __launch_bounds__(512) void skinny_gemm_kernel(GemmParams p) {
 // ---------------------------------------------------------------------------
 template <int MT, int NT, bool W8, int EPI>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
-    constexpr int KT = 64;
+    // k-tile per LDS stage: 128x128 tiles take 32 (36 KiB of LDS, four
+    // workgroups per CU hide the load latency); narrower tiles take 64
+    constexpr int KT = NT == 128 ? 32 : 64;
     constexpr int WM = MT / 2, WN = NT / 2;
     constexpr int FM = WM / 16, FN = WN / 16;
     constexpr int APAD = KT + 8;
@@ -341,7 +354,21 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int m0 = blockIdx.y * MT, n0 = blockIdx.x * NT;
+    // Tile of this workgroup. Consecutive workgroups run on consecutive XCDs,
+    // so when the N-tiles split evenly over the 8 XCDs, workgroup w takes an
+    // N-tile of XCD group w % 8 for every M-tile: each XCD's L2 then holds one
+    // eighth of the weights and reuses each A tile across its N-tiles.
+    const int ntn = p.N / NT, ntm = (p.M + MT - 1) / MT;
+    int mt_i, nt_i;
+    if (ntn % 8 == 0) {
+        const int w = blockIdx.x, per = ntn / 8, s = w >> 3;
+        mt_i = s / per;
+        nt_i = (w & 7) * per + s % per;
+    } else {
+        mt_i = blockIdx.x / ntn;
+        nt_i = blockIdx.x % ntn;
+    }
+    const int m0 = mt_i * MT, n0 = nt_i * NT;
     const int nk = p.K / KT;
     const int Kf = p.K / 32;
 
@@ -351,40 +378,50 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    u32x4 ra[A_CH], rb[B_CH];
-    auto load_tile = [&](int kt) {
+    u32x4 ra[1][A_CH], rb[1][B_CH];
+    // Branch-free loads (rows past M read row M-1 and are zeroed by a select;
+    // the A layout is a uniform choice), so the compiler can count the
+    // loads in flight instead of draining them at divergent joins.
+    auto load_tile = [&](int kt, u32x4 (&sa)[A_CH], u32x4 (&sb)[B_CH]) {
         const int k0 = kt * KT;
+        if (p.a_frag) {
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            int c = tid + i * 256;
-            int row = c / (KT / 8), c8 = c % (KT / 8);
-            int grow = m0 + row;
-            ra[i] = grow < p.M ? *(const u32x4*)(p.A + act_index(grow, k0 + c8 * 8, p.lda, p.a_frag))
-                               : (u32x4){0u, 0u, 0u, 0u};
+            for (int i = 0; i < A_CH; ++i) {
+                const int c = tid + i * 256, row = c / (KT / 8), c8 = c % (KT / 8), grow = m0 + row;
+                const u32x4 v = *(const u32x4*)(p.A + act_index(min(grow, p.M - 1), k0 + c8 * 8, p.lda, 1));
+                sa[i] = grow < p.M ? v : (u32x4){0u, 0u, 0u, 0u};
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < A_CH; ++i) {
+                const int c = tid + i * 256, row = c / (KT / 8), c8 = c % (KT / 8), grow = m0 + row;
+                const u32x4 v = *(const u32x4*)(p.A + (size_t)min(grow, p.M - 1) * p.lda + k0 + c8 * 8);
+                sa[i] = grow < p.M ? v : (u32x4){0u, 0u, 0u, 0u};
+            }
         }
 #pragma unroll
         for (int i = 0; i < B_CH; ++i) {
-            int c = tid + i * 256;
-            if (c < B_THREADS) {
-                int byte = c * 16;
-                int frag = byte / WFRAG_BYTES, within = byte % WFRAG_BYTES;
-                int fn = frag / (KT / 32), fk = frag % (KT / 32);
-                size_t g = ((size_t)(n0 / 16 + fn) * Kf + (k0 / 32 + fk)) * WFRAG_BYTES + within;
-                rb[i] = *(const u32x4*)((const uint8_t*)p.W + g);
+            const int c = tid + i * 256;
+            if (B_THREADS % 256 == 0 || c < B_THREADS) {
+                const int byte = c * 16;
+                const int frag = byte / WFRAG_BYTES, within = byte % WFRAG_BYTES;
+                const int fn = frag / (KT / 32), fk = frag % (KT / 32);
+                const size_t g = ((size_t)(n0 / 16 + fn) * Kf + (k0 / 32 + fk)) * WFRAG_BYTES + within;
+                sb[i] = *(const u32x4*)((const uint8_t*)p.W + g);
             }
         }
     };
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](int buf, const u32x4 (&sa)[A_CH], const u32x4 (&sb)[B_CH]) {
 #pragma unroll
         for (int i = 0; i < A_CH; ++i) {
             int c = tid + i * 256;
             int row = c / (KT / 8), c8 = c % (KT / 8);
-            *(u32x4*)(&As[buf][row][c8 * 8]) = ra[i];
+            *(u32x4*)(&As[buf][row][c8 * 8]) = sa[i];
         }
 #pragma unroll
         for (int i = 0; i < B_CH; ++i) {
-            int c = tid + i * 256;
-            if (c < B_THREADS) *(u32x4*)(&Bs[buf][c * 16]) = rb[i];
+            const int c = tid + i * 256;
+            if (B_THREADS % 256 == 0 || c < B_THREADS) *(u32x4*)(&Bs[buf][c * 16]) = sb[i];
         }
     };
     auto compute = [&](int buf) {
@@ -413,13 +450,15 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmParams p) {
         }
     };
 
-    load_tile(0);
-    store_tile(0);
+    // k-tile kt+1 is loaded into registers while k-tile kt is multiplied
+    // from LDS, then written to the other LDS buffer.
+    load_tile(0, ra[0], rb[0]);
+    store_tile(0, ra[0], rb[0]);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) load_tile(kt + 1);
+        if (kt + 1 < nk) load_tile(kt + 1, ra[0], rb[0]);
         compute(kt & 1);
-        if (kt + 1 < nk) store_tile((kt + 1) & 1);
+        if (kt + 1 < nk) store_tile((kt + 1) & 1, ra[0], rb[0]);
         __syncthreads();
     }
 
@@ -592,6 +631,138 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
                 p.o[act_index(b * p.T + i, (g * G + hh) * DH + dn * 16 + (lane & 15), p.nq * DH, p.ofrag)] =
                     f32_to_bf16(o[r] * inv[r]);
             }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The same attention for many query rows (large batches): a workgroup of four
+// waves takes 64 query rows of one (request, KV group), each wave owning 16 of
+// them over the whole key range, and every 32-key K/V block is staged once
+// per workgroup through LDS (double-buffered). K/V is then read from L2 once
+// per 64 query rows instead of once per 16, and the waves never merge.
+// LDS: K rows padded by 16 bytes so the 16 lanes that read one fragment hit
+// distinct banks; V kept in PV-operand order.
+// ---------------------------------------------------------------------------
+template <int DH>
+__global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
+    constexpr int KROW = DH * 2 + 16;            // padded K row in LDS, bytes
+    constexpr int KCH = DH * 2 / 16;             // 16-byte chunks per key row
+    constexpr int BLK = 32 * DH * 2;             // one 32-key block of K (or V), bytes
+    constexpr int CH = BLK / 16 / 256;           // chunks of a block per thread
+    static_assert(CH >= 1, "head too small");
+    __shared__ __attribute__((aligned(16))) uint8_t Ks[2][32 * KROW];
+    __shared__ __attribute__((aligned(16))) uint8_t Vs[2][BLK];
+    __shared__ __attribute__((aligned(16))) uint16_t Ps[4][16][40];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int G = p.nq / p.kv.nkv;
+    const int rows_total = G * p.T;
+    const int g = blockIdx.y, b = blockIdx.z;
+    const int r0 = blockIdx.x * 64 + wave * 16;
+    const int nblk = p.kv.S_pad / 32;
+    const size_t base = p.kv.base(b, p.layer, g);
+    const uint8_t* K = (const uint8_t*)(p.kcat + base);
+    const uint8_t* V = (const uint8_t*)(p.vcat + base);
+
+    bf16x8 qf[DH / 32];
+    {
+        const uint16_t* qg = p.q + (size_t)(b * p.nq + g * G) * p.T * DH;
+        const int row = r0 + (lane & 15);
+        const int rowc = min(row, rows_total - 1);
+#pragma unroll
+        for (int ks = 0; ks < DH / 32; ++ks) {
+            const bf16x8 v = *(const bf16x8*)(qg + (size_t)rowc * DH + ks * 32 + 8 * (lane >> 4));
+            qf[ks] = row < rows_total ? v : (bf16x8){};
+        }
+    }
+
+    float mrow[4], lrow[4];
+    f32x4 oacc[DH / 16];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) { mrow[r] = -INFINITY; lrow[r] = 0.f; }
+#pragma unroll
+    for (int dn = 0; dn < DH / 16; ++dn) oacc[dn] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    u32x4 rk[CH], rv[CH];
+    auto gload = [&](int kb) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int c = tid + i * 256;
+            rk[i] = *(const u32x4*)(K + (size_t)kb * BLK + (size_t)c * 16);
+            rv[i] = *(const u32x4*)(V + (size_t)kb * BLK + (size_t)c * 16);
+        }
+    };
+    auto sstore = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int c = tid + i * 256;
+            *(u32x4*)(&Ks[buf][(c / KCH) * KROW + (c % KCH) * 16]) = rk[i];
+            *(u32x4*)(&Vs[buf][c * 16]) = rv[i];
+        }
+    };
+
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kb = 0; kb < nblk; ++kb) {
+        const int buf = kb & 1;
+        if (kb + 1 < nblk) gload(kb + 1);   // next block in flight during this one
+        f32x4 s[2];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            s[sb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < DH / 32; ++ks) {
+                const bf16x8 kf =
+                    *(const bf16x8*)(&Ks[buf][(sb * 16 + (lane & 15)) * KROW + ks * 64 + 16 * (lane >> 4)]);
+                s[sb] = mfma_16x16x32(qf[ks], kf, s[sb]);
+            }
+        }
+        float alpha[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float s0 = s[0][r] * p.scale_log2, s1 = s[1][r] * p.scale_log2;
+            const int key0 = kb * 32 + (lane & 15);
+            if (key0 >= p.S) s0 = -INFINITY;
+            if (key0 + 16 >= p.S) s1 = -INFINITY;
+            const float mx = group16_max(fmaxf(s0, s1));
+            const float mnew = fmaxf(mrow[r], mx);
+            alpha[r] = exp2f(mrow[r] - mnew);
+            const float p0 = exp2f(s0 - mnew), p1 = exp2f(s1 - mnew);
+            lrow[r] = lrow[r] * alpha[r] + group16_sum(p0 + p1);
+            mrow[r] = mnew;
+            Ps[wave][4 * (lane >> 4) + r][lane & 15] = f32_to_bf16(p0);
+            Ps[wave][4 * (lane >> 4) + r][16 + (lane & 15)] = f32_to_bf16(p1);
+        }
+#pragma unroll
+        for (int dn = 0; dn < DH / 16; ++dn)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) oacc[dn][r] *= alpha[r];
+        // the P tile is private to this wave: LDS ops of one wave complete in order
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        const bf16x8 pa = *(const bf16x8*)(&Ps[wave][lane & 15][8 * (lane >> 4)]);
+#pragma unroll
+        for (int dn = 0; dn < DH / 16; ++dn) {
+            const bf16x8 vf = *(const bf16x8*)(&Vs[buf][(dn * 64 + lane) * 16]);
+            oacc[dn] = mfma_16x16x32(pa, vf, oacc[dn]);
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (kb + 1 < nblk) sstore(buf ^ 1);  // that buffer was last read before the previous barrier
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = r0 + 4 * (lane >> 4) + r;
+        if (row < rows_total) {
+            const float inv = 1.0f / lrow[r];
+            const int hh = row / p.T, i = row % p.T;
+#pragma unroll
+            for (int dn = 0; dn < DH / 16; ++dn)
+                p.o[act_index(b * p.T + i, (g * G + hh) * DH + dn * 16 + (lane & 15), p.nq * DH, p.ofrag)] =
+                    f32_to_bf16(oacc[dn][r] * inv);
         }
     }
 }
