@@ -699,6 +699,7 @@ int enqueue_persist(vla_ctx* c, int n_steps) {
     p.Tpad = (d.horizon + 31) / 32 * 32;
     p.nsteps = n_steps;
     p.Ix = d.intermediate / PX;
+    p.inv_T = 1.0f / (float)d.horizon;
     p.mod_ld = c->mod_ld;
     p.eps = d.rms_eps;
     p.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));

@@ -40,6 +40,7 @@ constexpr long P_SPIN = 1l << 20;
 struct PersistParams {
     int M, B, T, H, L, nq, nkv, dh, I, A, P, hq, G, Tpad, nsteps;
     int Ix;        // I / 8, SwiGLU columns per XCD
+    float inv_T;   // 1 / T
     int mod_ld;
     float eps, scale_log2;
     const uint8_t* const* wqkv;  // per-layer packed weights (device arrays of L pointers)
@@ -73,6 +74,15 @@ struct PersistParams {
     unsigned* ticket;            // [8]: workgroups that have taken an index on each XCD
     int* err;
 };
+
+// row / T without an integer divide: a float estimate corrected to the exact
+// quotient (inv_T = 1/T).
+VLA_DEV int p_div_T(int row, int T, float inv_T) {
+    int b = (int)((float)row * inv_T);
+    if (b * T > row) --b;
+    else if ((b + 1) * T <= row) ++b;
+    return b;
+}
 
 // ------------------------------- syncs -------------------------------------
 // Buffers are reused by every layer, so after each sync a wave drops the
@@ -337,7 +347,7 @@ VLA_DEV void p_attention(const PersistParams& p, const uint16_t* qg, int r0, con
     for (int r = 0; r < 4; ++r) {
         const int row = r0 + 4 * (lane >> 4) + r;
         if (row < rows_total) {
-            const int hh = row / p.T, i = row % p.T;
+            const int hh = p_div_T(row, p.T, p.inv_T), i = row - hh * p.T;
             obuf[act_index(b * p.T + i, hh * DH + dn * 16 + (lane & 15), Kq, 1)] = f32_to_bf16(ov[r] * inv[r]);
         }
     }
@@ -367,7 +377,8 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
     __shared__ float modl[6 * P_BMAX * P_COLS];     // [q][b][f]: gate1, scale2, shift2, gate2, scale1', shift1'
     __shared__ float2 ropel[NTQ * 64 * 8];          // [t][position][pair]
     float* red = (float*)smem;
-    const int H = p.H, M = p.M, L = p.L, dh = p.dh, hq = p.hq;
+    const int H = p.H, M = p.M, L = p.L, hq = p.hq;
+    constexpr int dh = 128;  // the host admits head_dim 128 only
     // Identity: x = the XCD this workgroup runs on (hardware XCC_ID), j = its
     // ticket among the workgroups on that XCD, so nothing depends on how the
     // dispatcher spreads workgroups over XCDs. With 256 workgroups, one per
@@ -421,7 +432,7 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
                  sp_d = p_split(p.Ix / 32, wave);                                                     \
     const int rrow = tid >> 3, sub = tid & 7, f0 = sub * cpt, c0 = pcol(f0);                          \
     const bool row_ok = rrow < M;                                                                     \
-    const int rb = row_ok ? rrow / p.T : 0;                                                           \
+    const int rb = row_ok ? p_div_T(rrow, p.T, p.inv_T) : 0;                                          \
     (void)ntq; (void)nto; (void)ntg; (void)sp_o; (void)sp_gu; (void)sp_d; (void)row_ok; (void)c0;     \
     (void)rb; (void)f0
 
@@ -533,9 +544,9 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
                     if (col < qd) { sec = 0; local = col; }
                     else if (col < qd + kvd) { sec = 1; local = col - qd; }
                     else { sec = 2; local = col - qd - kvd; }
-                    const int head = local / dh, pp = local % dh;
+                    const int head = local >> 7, pp = local & 127;  // head_dim 128 on this path
                     const int m = pp >> 1, second = pp & 1;
-                    const int b = row / p.T, i = row % p.T;
+                    const int b = p_div_T(row, p.T, p.inv_T), i = row - b * p.T;
                     float outv = v;
                     if (sec < 2) {
                         const float2 cs = ropel[(t * 64 + i) * 8 + (cl >> 1)];
@@ -800,7 +811,7 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
                     }
                 }
                 if (lane < 16 && a0 + lane < p.A) {
-                    const int a = a0 + lane, b = r / p.T;
+                    const int a = a0 + lane, b = p_div_T(r, p.T, p.inv_T);
                     const float dt = ts[b * (p.nsteps + 1) + k + 1] - ts[b * (p.nsteps + 1) + k];
                     const float xv = xin[r * p.A + a] + dt * (mine + p.out_b[a]);
                     xo[r * p.A + a] = xv;
