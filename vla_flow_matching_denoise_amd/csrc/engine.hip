@@ -342,11 +342,12 @@ int ensure_capacity(vla_ctx* c, int n_steps) {
 
 template <int MT, int NT, bool W8>
 int launch_tiled_t(int epi, const GemmParams& p, dim3 grid, hipStream_t s) {
+    const dim3 blk(64 * gemm_waves(MT, NT));
     switch (epi) {
-        case EPI_BIAS_F32: VLA_LAUNCH((gemm_kernel<MT, NT, W8, EPI_BIAS_F32>), grid, dim3(256), 0, s, p); break;
-        case EPI_RESID: VLA_LAUNCH((gemm_kernel<MT, NT, W8, EPI_RESID>), grid, dim3(256), 0, s, p); break;
-        case EPI_QKV_ROPE: VLA_LAUNCH((gemm_kernel<MT, NT, W8, EPI_QKV_ROPE>), grid, dim3(256), 0, s, p); break;
-        case EPI_SWIGLU: VLA_LAUNCH((gemm_kernel<MT, NT, W8, EPI_SWIGLU>), grid, dim3(256), 0, s, p); break;
+        case EPI_BIAS_F32: VLA_LAUNCH((gemm_kernel<MT, NT, W8, EPI_BIAS_F32>), grid, blk, 0, s, p); break;
+        case EPI_RESID: VLA_LAUNCH((gemm_kernel<MT, NT, W8, EPI_RESID>), grid, blk, 0, s, p); break;
+        case EPI_QKV_ROPE: VLA_LAUNCH((gemm_kernel<MT, NT, W8, EPI_QKV_ROPE>), grid, blk, 0, s, p); break;
+        case EPI_SWIGLU: VLA_LAUNCH((gemm_kernel<MT, NT, W8, EPI_SWIGLU>), grid, blk, 0, s, p); break;
         default: set_err("bad tiled epilogue %d", epi); return VLA_ERR_ARG;
     }
     HIPC(hipGetLastError());
