@@ -144,6 +144,20 @@ vla_ctx* vla_expert_create(const vla_weights* weights, const vla_dims* dims);
 int vla_denoise(vla_ctx* ctx, const void* prefix_k, const void* prefix_v, const float* noise,
                 const float* t_schedule, int n_steps, float* out_actions);
 
+/* vla_denoise with a prefix length per request, for prefixes padded to a fixed
+ * P (FlashRT flash_rt/api.py page: fixed-shape mode with a device-side valid
+ * length; LingBot-VLA v2 Examples: language padded to a fixed length).
+ * prefix_valid: device pointer to int32 [B], 4-byte aligned. Request b uses
+ * prefix tokens [0, prefix_valid[b]) of its P-token prefix (values are
+ * clamped to [0, P]); tokens past that are padding no query attends to, and
+ * the chunk's RoPE positions are prefix_valid[b] .. prefix_valid[b] + T - 1.
+ * So request b's result equals vla_denoise on a prefix of exactly
+ * prefix_valid[b] tokens. The values are read when the call runs on the GPU:
+ * one captured graph serves calls with different values. NULL: every request
+ * uses all P tokens (vla_denoise). Same ownership and errors as vla_denoise. */
+int vla_denoise_varlen(vla_ctx* ctx, const void* prefix_k, const void* prefix_v, const int32_t* prefix_valid,
+                       const float* noise, const float* t_schedule, int n_steps, float* out_actions);
+
 /* Use `stream` (a hipStream_t) for every later call on ctx. NULL (also the
  * state after vla_expert_create) selects the legacy default stream. Graphs
  * are captured once on a library-created stream and replayed on this one.

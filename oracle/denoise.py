@@ -46,7 +46,7 @@ __all__ = [
     "ExpertDims", "decode_bf16", "decode_e4m3fn", "decode_weights",
     "sinusoidal_embedding", "silu", "time_condition", "modulation",
     "rms_normalize", "ada_rms_norm", "rope_rotate_half", "softmax",
-    "gqa_attention", "expert_layer", "velocity", "denoise", "cosine",
+    "gqa_attention", "expert_layer", "velocity", "denoise", "denoise_varlen", "cosine",
 ]
 
 
@@ -298,6 +298,27 @@ def denoise(W: dict, dims: ExpertDims, prefix_k: np.ndarray, prefix_v: np.ndarra
             dt = dtype.type(ts[k + 1] - ts[k])
             x = x + dt * velocity(x, ts[k], W, prefix_k[b], prefix_v[b], dims)
         out[b] = x
+    return out
+
+
+def denoise_varlen(W: dict, dims: ExpertDims, prefix_k: np.ndarray, prefix_v: np.ndarray,
+                   noise: np.ndarray, t_schedule: np.ndarray, prefix_valid) -> np.ndarray:
+    """The loop over prefixes padded to a common length P, request b using only
+    its first ``prefix_valid[b]`` tokens (the fixed-shape mode with a
+    device-side valid length on the FlashRT ``flash_rt/api.py`` page; the
+    language part is padded to a fixed length on the "LingBot-VLA v2
+    Examples" page).  Reading taken: the padded tokens do not exist for the
+    request, so its result is the plain loop on the prefix truncated to those
+    tokens, and its chunk tokens sit at positions ``prefix_valid[b] + i``.
+    Lengths outside [0, P] are clamped.
+    """
+    out = np.empty(noise.shape, dtype=W["in_w"].dtype)
+    P = prefix_k.shape[2]
+    for b in range(noise.shape[0]):
+        n = min(max(int(prefix_valid[b]), 0), P)
+        d = dataclasses.replace(dims, prefix_len=n)
+        out[b] = denoise(W, d, prefix_k[b:b + 1, :, :n], prefix_v[b:b + 1, :, :n], noise[b:b + 1],
+                         t_schedule[b:b + 1])[0]
     return out
 
 

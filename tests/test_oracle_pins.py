@@ -451,3 +451,55 @@ def test_fp32_twin_agrees_with_fp64():
                          x0, ts)
     assert o32.dtype == np.float32
     assert oracle.cosine(o32, o64) >= 1 - 1e-9
+
+
+# ---------------------------------------------------------------------------
+# Prefixes padded to a common length (per-request valid length)
+# ---------------------------------------------------------------------------
+def test_padded_prefix_keys_are_masked_keys():
+    """Attention over a prefix truncated to n tokens equals attention over all
+    P tokens with the padded keys' scores set to -inf (written out here with
+    numpy, not through the oracle's attention)."""
+    r = np.random.default_rng(5)
+    T, P, nq, nkv, dh, n = 6, 9, 4, 2, 8, 4
+    q = r.standard_normal((nq, T, dh))
+    kp, vp = r.standard_normal((nkv, P, dh)), r.standard_normal((nkv, P, dh))
+    kc, vc = r.standard_normal((nkv, T, dh)), r.standard_normal((nkv, T, dh))
+    K = np.concatenate([kp, kc], axis=1)
+    V = np.concatenate([vp, vc], axis=1)
+    want = np.empty((nq, T, dh))
+    for j in range(nq):
+        g = j // (nq // nkv)
+        s = q[j] @ K[g].T / math.sqrt(dh)
+        s[:, n:P] = -np.inf
+        e = np.exp(s - s.max(axis=1, keepdims=True))
+        want[j] = (e / e.sum(axis=1, keepdims=True)) @ V[g]
+    got = oracle.gqa_attention(q, np.concatenate([kp[:, :n], kc], axis=1), np.concatenate([vp[:, :n], vc], axis=1))
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_varlen_full_lengths_and_padding_invariance():
+    d = _tiny_dims()
+    W = _tiny_weights(d)
+    pk, pv, x0 = _tiny_inputs(d, B=3)
+    ts = np.tile(np.linspace(0.0, 1.0, 4), (3, 1))
+    full = oracle.denoise(W, d, pk, pv, x0, ts)
+    # every request at the full length (and lengths past P, clamped) is the plain loop, bitwise
+    assert np.array_equal(oracle.denoise_varlen(W, d, pk, pv, x0, ts, [d.prefix_len] * 3), full)
+    assert np.array_equal(oracle.denoise_varlen(W, d, pk, pv, x0, ts, [99, d.prefix_len, 1000]), full)
+    valid = [d.prefix_len, 3, 0]
+    a = oracle.denoise_varlen(W, d, pk, pv, x0, ts, valid)
+    assert np.array_equal(a[0], full[0])
+    assert not np.allclose(a[1], full[1]) and not np.allclose(a[2], full[2])
+    # what sits in the padded tokens never matters
+    pk2, pv2 = pk.copy(), pv.copy()
+    pk2[1, :, 3:] = 1e3
+    pv2[1, :, 3:] = -1e3
+    pk2[2], pv2[2] = 7.0, -7.0
+    assert np.array_equal(oracle.denoise_varlen(W, d, pk2, pv2, x0, ts, valid), a)
+    # a length of 0 is the loop without a prefix; negative lengths clamp to 0
+    d0 = ExpertDims(**{**d.__dict__, "prefix_len": 0})
+    none = oracle.denoise(W, d0, pk[2:3, :, :0], pv[2:3, :, :0], x0[2:3], ts[2:3])
+    assert np.array_equal(a[2], none[0])
+    assert np.array_equal(oracle.denoise_varlen(W, d, pk, pv, x0, ts, [d.prefix_len, 3, -5]), a)
+

@@ -28,7 +28,7 @@ VLA_OPT_PERSISTENT_STATUS = 4
 
 # every symbol include/vla_expert.h declares
 EXPORTED = (
-    "vla_expert_create", "vla_denoise", "vla_set_stream", "vla_set_option", "vla_get_option",
+    "vla_expert_create", "vla_denoise", "vla_denoise_varlen", "vla_set_stream", "vla_set_option", "vla_get_option",
     "vla_expert_destroy",
     "vla_last_error", "vla_device_bytes", "vla_test_modulation", "vla_test_layer",
     "vla_test_attention", "vla_profile_kernel",
@@ -73,6 +73,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vla_expert_create.argtypes = [ctypes.POINTER(VlaWeights), ctypes.POINTER(VlaDims)]
     lib.vla_denoise.restype = ctypes.c_int
     lib.vla_denoise.argtypes = [_P, _P, _P, _P, _P, ctypes.c_int, _P]
+    lib.vla_denoise_varlen.restype = ctypes.c_int
+    lib.vla_denoise_varlen.argtypes = [_P, _P, _P, _P, _P, _P, ctypes.c_int, _P]
     lib.vla_set_stream.restype = ctypes.c_int
     lib.vla_set_stream.argtypes = [_P, _P]
     lib.vla_set_option.restype = ctypes.c_int
@@ -135,6 +137,13 @@ def vla_expert_create(weights: VlaWeights, dims: VlaDims) -> int:
 def vla_denoise(ctx: int, prefix_k: int, prefix_v: int, noise: int, t_schedule: int, n_steps: int,
                 out_actions: int, check: bool = True) -> int:
     rc = lib().vla_denoise(ctx, prefix_k, prefix_v, noise, t_schedule, int(n_steps), out_actions)
+    return _check(rc) if check else rc
+
+
+def vla_denoise_varlen(ctx: int, prefix_k: int, prefix_v: int, prefix_valid: Optional[int], noise: int,
+                       t_schedule: int, n_steps: int, out_actions: int, check: bool = True) -> int:
+    rc = lib().vla_denoise_varlen(ctx, prefix_k, prefix_v, prefix_valid, noise, t_schedule, int(n_steps),
+                                  out_actions)
     return _check(rc) if check else rc
 
 

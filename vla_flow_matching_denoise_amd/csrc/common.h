@@ -84,4 +84,12 @@ struct ArgBlock {
     const float* noise;        // [B, T, A]
     const float* t_schedule;   // [B, N+1]
     float* out;                // [B, T, A]
+    const int* prefix_valid;   // [B] valid prefix tokens per request, or null (all P)
 };
+
+// Valid prefix tokens of request b (clamped to [0, P]): keys [valid, P) are
+// padding, and the chunk's RoPE positions start at `valid`.
+VLA_DEV int prefix_valid(const ArgBlock* ab, int b, int P) {
+    const int* v = ab->prefix_valid;
+    return v ? min(max(v[b], 0), P) : P;
+}

@@ -443,6 +443,8 @@ int launch_attention(vla_ctx* c, int l, const uint16_t* q, uint16_t* o, int ofra
     ap.layer = l;
     ap.S = d.prefix_len + d.horizon;
     ap.T = d.horizon;
+    ap.P = d.prefix_len;
+    ap.ab = c->ab;
     ap.nq = d.n_q_heads;
     ap.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
     ap.ofrag = ofrag;
@@ -503,6 +505,7 @@ int launch_block_gemm(vla_ctx* c, int which, int step, int l, int* S) {
         p.layer = l;
         p.P = d.prefix_len;
         p.rope = c->rope;
+        p.ab = c->ab;
         p.nq = d.n_q_heads;
         p.nkv = d.n_kv_heads;
         p.dh = d.head_dim;
@@ -736,9 +739,10 @@ int enqueue_persist(vla_ctx* c, int n_steps) {
     return VLA_OK;
 }
 
-int set_args(vla_ctx* c, const void* pk, const void* pv, const float* noise, const float* ts, float* out) {
+int set_args(vla_ctx* c, const void* pk, const void* pv, const float* noise, const float* ts, float* out,
+             const int* pvalid = nullptr) {
     hipLaunchKernelGGL(set_args_kernel, dim3(1), dim3(1), 0, c->stream, c->ab, (const uint16_t*)pk,
-                       (const uint16_t*)pv, noise, ts, out);
+                       (const uint16_t*)pv, noise, ts, out, pvalid);
     HIPC(hipGetLastError());
     return VLA_OK;
 }
@@ -854,10 +858,11 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
         c->wd[l].cfg = choose_gemm(c->M, c->wd[l].N, c->wd[l].K, true);
     }
 
-    // rotary table
-    if ((rc = c->alloc((void**)&c->rope, (size_t)d.horizon * (dh / 2) * sizeof(float2)))) return rc;
-    hipLaunchKernelGGL(rope_table_kernel, dim3((d.horizon * (dh / 2) + 255) / 256), dim3(256), 0, c->stream, c->rope,
-                       d.horizon, d.prefix_len, dh, (double)d.rope_theta);
+    // rotary table over every absolute position a chunk token can take
+    const int npos = d.prefix_len + d.horizon;
+    if ((rc = c->alloc((void**)&c->rope, (size_t)npos * (dh / 2) * sizeof(float2)))) return rc;
+    hipLaunchKernelGGL(rope_table_kernel, dim3((npos * (dh / 2) + 255) / 256), dim3(256), 0, c->stream, c->rope,
+                       npos, dh, (double)d.rope_theta);
     HIPC(hipGetLastError());
 
     // working buffers
@@ -912,16 +917,16 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
 
 }  // namespace
 
-static int denoise_enqueue(vla_ctx* c, const void* prefix_k, const void* prefix_v, const float* noise,
-                           const float* t_schedule, int n_steps, float* out_actions) {
+static int denoise_enqueue(vla_ctx* c, const void* prefix_k, const void* prefix_v, const int* prefix_valid,
+                           const float* noise, const float* t_schedule, int n_steps, float* out_actions) {
     int rc;
     if ((rc = ensure_capacity(c, n_steps))) return rc;
     if (c->persist_ok && c->use_persist) {
         if ((rc = ensure_persist(c))) return rc;
-        if ((rc = set_args(c, prefix_k, prefix_v, noise, t_schedule, out_actions))) return rc;
+        if ((rc = set_args(c, prefix_k, prefix_v, noise, t_schedule, out_actions, prefix_valid))) return rc;
         return enqueue_persist(c, n_steps);
     }
-    if ((rc = set_args(c, prefix_k, prefix_v, noise, t_schedule, out_actions))) return rc;
+    if ((rc = set_args(c, prefix_k, prefix_v, noise, t_schedule, out_actions, prefix_valid))) return rc;
     if (!c->use_graph) return enqueue_forward(c, n_steps);
     auto it = c->graphs.find(n_steps);
     if (it == c->graphs.end()) {
@@ -980,8 +985,8 @@ vla_ctx* vla_expert_create(const vla_weights* weights, const vla_dims* dims) {
     return c;
 }
 
-int vla_denoise(vla_ctx* c, const void* prefix_k, const void* prefix_v, const float* noise, const float* t_schedule,
-                int n_steps, float* out_actions) {
+int vla_denoise_varlen(vla_ctx* c, const void* prefix_k, const void* prefix_v, const int32_t* prefix_valid,
+                       const float* noise, const float* t_schedule, int n_steps, float* out_actions) {
     g_err.clear();
     if (!c) {
         set_err("ctx is NULL");
@@ -1000,7 +1005,13 @@ int vla_denoise(vla_ctx* c, const void* prefix_k, const void* prefix_v, const fl
         return VLA_ERR_ARG;
     }
     HIPC(hipSetDevice(c->device));
-    return denoise_enqueue(c, prefix_k, prefix_v, noise, t_schedule, n_steps, out_actions);
+    if (prefix_valid && (rc = check_ptr(prefix_valid, "prefix_valid", 4))) return rc;
+    return denoise_enqueue(c, prefix_k, prefix_v, prefix_valid, noise, t_schedule, n_steps, out_actions);
+}
+
+int vla_denoise(vla_ctx* c, const void* prefix_k, const void* prefix_v, const float* noise, const float* t_schedule,
+                int n_steps, float* out_actions) {
+    return vla_denoise_varlen(c, prefix_k, prefix_v, nullptr, noise, t_schedule, n_steps, out_actions);
 }
 
 int vla_set_stream(vla_ctx* c, void* stream) {

@@ -18,12 +18,13 @@
 // Call-argument refresh (one thread, launched before each graph replay)
 // ---------------------------------------------------------------------------
 __global__ void set_args_kernel(ArgBlock* ab, const uint16_t* pk, const uint16_t* pv,
-                                const float* noise, const float* ts, float* out) {
+                                const float* noise, const float* ts, float* out, const int* pvalid) {
     ab->prefix_k = pk;
     ab->prefix_v = pv;
     ab->noise = noise;
     ab->t_schedule = ts;
     ab->out = out;
+    ab->prefix_valid = pvalid;
 }
 
 // ---------------------------------------------------------------------------
@@ -68,12 +69,14 @@ __global__ void pack_weight_kernel(const uint8_t* __restrict__ src, int R, int K
 
 // cos/sin of the rotary angle (P + i) * theta^(-2m/d_h), i < T, m < d_h/2,
 // evaluated in double precision once at create time.
-__global__ void rope_table_kernel(float2* tab, int T, int P, int dh, double theta) {
+// cos/sin of every absolute position 0..npos-1 (the chunk of request b sits
+// at positions valid_b .. valid_b + T - 1): tab[pos][m], m < dh/2.
+__global__ void rope_table_kernel(float2* tab, int npos, int dh, double theta) {
     int idx = blockIdx.x * blockDim.x + threadIdx.x;
     int half = dh / 2;
-    if (idx >= T * half) return;
-    int i = idx / half, m = idx % half;
-    double ang = (double)(P + i) * pow(theta, -2.0 * m / dh);
+    if (idx >= npos * half) return;
+    int pos = idx / half, m = idx % half;
+    double ang = (double)pos * pow(theta, -2.0 * m / dh);
     tab[idx] = make_float2((float)cos(ang), (float)sin(ang));
 }
 

@@ -180,7 +180,8 @@ struct GemmParams {
     uint16_t* vcat;
     KVLayout kv;
     int layer, P;
-    const float2* rope;  // [T][dh/2]
+    const float2* rope;  // [P + T][dh/2], by absolute position
+    const ArgBlock* ab;  // per-request valid prefix lengths (RoPE positions of the chunk)
     int nq, nkv, dh;
     int dh_shift;        // log2(dh)
     float inv_T;         // 1/T, for the row -> request split without a divide
@@ -222,7 +223,7 @@ VLA_DEV void epilogue_store(const GemmParams& p, int row, int col, float v, floa
         const int b = div_T(row, p), i = row - b * p.T;
         float outv = v;
         if (sec < 2) {
-            const float2 cs = p.rope[i * (p.dh / 2) + m];
+            const float2 cs = p.rope[(prefix_valid(p.ab, b, p.P) + i) * (p.dh / 2) + m];
             const float u1 = second ? partner : v;
             const float u2 = second ? v : partner;
             outv = second ? (u2 * cs.x + u1 * cs.y) : (u1 * cs.x - u2 * cs.y);
@@ -503,6 +504,8 @@ struct AttnParams {
     int layer, S, T, nq;
     int ofrag;
     float scale_log2;       // log2(e)/sqrt(dh)
+    int P;                  // prefix keys per request (the first valid_b of them count)
+    const ArgBlock* ab;     // per-request valid prefix lengths
 };
 
 template <int DH, int AT_WAVES>
@@ -519,6 +522,7 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
     const size_t base = p.kv.base(b, p.layer, g);
     const uint16_t* K = p.kcat + base;
     const uint16_t* V = p.vcat + base;
+    const int pvb = prefix_valid(p.ab, b, p.P);  // prefix keys past this are padding
 
     bf16x8 qf[DH / 32];
     {
@@ -563,13 +567,16 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float s0 = s[0][r] * p.scale_log2, s1 = s[1][r] * p.scale_log2;
-            const int key0 = kb * 32 + (lane & 15);
-            if (key0 >= p.S) s0 = -INFINITY;
-            if (key0 + 16 >= p.S) s1 = -INFINITY;
+            const int key0 = kb * 32 + (lane & 15), key1 = key0 + 16;
+            if (key0 >= p.S || (key0 < p.P && key0 >= pvb)) s0 = -INFINITY;
+            if (key1 >= p.S || (key1 < p.P && key1 >= pvb)) s1 = -INFINITY;
             const float mx = group16_max(fmaxf(s0, s1));
             const float mnew = fmaxf(mrow[r], mx);
-            alpha[r] = exp2f(mrow[r] - mnew);
-            const float p0 = exp2f(s0 - mnew), p1 = exp2f(s1 - mnew);
+            // while every key so far is masked (a padded prefix block) the row
+            // keeps m = -inf; its exponents then use 0, giving 0, not NaN
+            const float mref = mnew == -INFINITY ? 0.f : mnew;
+            alpha[r] = exp2f(mrow[r] - mref);
+            const float p0 = exp2f(s0 - mref), p1 = exp2f(s1 - mref);
             lrow[r] = lrow[r] * alpha[r] + group16_sum(p0 + p1);
             mrow[r] = mnew;
             Ps[wave][4 * (lane >> 4) + r][lane & 15] = f32_to_bf16(p0);
@@ -672,6 +679,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
     const size_t base = p.kv.base(b, p.layer, g);
     const uint8_t* K = (const uint8_t*)(p.kcat + base);
     const uint8_t* V = (const uint8_t*)(p.vcat + base);
+    const int pvb = prefix_valid(p.ab, b, p.P);  // prefix keys past this are padding
 
     bf16x8 qf[DH / 32];
     {
@@ -731,13 +739,16 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float s0 = s[0][r] * p.scale_log2, s1 = s[1][r] * p.scale_log2;
-            const int key0 = kb * 32 + (lane & 15);
-            if (key0 >= p.S) s0 = -INFINITY;
-            if (key0 + 16 >= p.S) s1 = -INFINITY;
+            const int key0 = kb * 32 + (lane & 15), key1 = key0 + 16;
+            if (key0 >= p.S || (key0 < p.P && key0 >= pvb)) s0 = -INFINITY;
+            if (key1 >= p.S || (key1 < p.P && key1 >= pvb)) s1 = -INFINITY;
             const float mx = group16_max(fmaxf(s0, s1));
             const float mnew = fmaxf(mrow[r], mx);
-            alpha[r] = exp2f(mrow[r] - mnew);
-            const float p0 = exp2f(s0 - mnew), p1 = exp2f(s1 - mnew);
+            // while every key so far is masked (a padded prefix block) the row
+            // keeps m = -inf; its exponents then use 0, giving 0, not NaN
+            const float mref = mnew == -INFINITY ? 0.f : mnew;
+            alpha[r] = exp2f(mrow[r] - mref);
+            const float p0 = exp2f(s0 - mref), p1 = exp2f(s1 - mref);
             lrow[r] = lrow[r] * alpha[r] + group16_sum(p0 + p1);
             mrow[r] = mnew;
             Ps[wave][4 * (lane >> 4) + r][lane & 15] = f32_to_bf16(p0);

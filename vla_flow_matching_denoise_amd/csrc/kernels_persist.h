@@ -252,6 +252,7 @@ VLA_DEV void p_attention(const PersistParams& p, const uint16_t* qg, int r0, con
     const int rows_total = p.hq * p.T;
     const int nbp = p.P / 32, nblk = nbp + p.Tpad / 32;
     const int S = p.P + p.T;
+    const int pvb = prefix_valid(p.ab, b, p.P);  // prefix keys past this are padding
     bf16x8 qf[DH / 32];
     {
         const int row = r0 + (lane & 15);
@@ -289,13 +290,16 @@ VLA_DEV void p_attention(const PersistParams& p, const uint16_t* qg, int r0, con
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float s0 = s[0][r] * p.scale_log2, s1 = s[1][r] * p.scale_log2;
-            const int key0 = kb * 32 + (lane & 15);
-            if (key0 >= S) s0 = -INFINITY;
-            if (key0 + 16 >= S) s1 = -INFINITY;
+            const int key0 = kb * 32 + (lane & 15), key1 = key0 + 16;
+            if (key0 >= S || (key0 < p.P && key0 >= pvb)) s0 = -INFINITY;
+            if (key1 >= S || (key1 < p.P && key1 >= pvb)) s1 = -INFINITY;
             const float mx = group16_max(fmaxf(s0, s1));
             const float mnew = fmaxf(mrow[r], mx);
-            alpha[r] = exp2f(mrow[r] - mnew);
-            const float p0 = exp2f(s0 - mnew), p1 = exp2f(s1 - mnew);
+            // while every key so far is masked (a padded prefix block) the row
+            // keeps m = -inf; its exponents then use 0, giving 0, not NaN
+            const float mref = mnew == -INFINITY ? 0.f : mnew;
+            alpha[r] = exp2f(mrow[r] - mref);
+            const float p0 = exp2f(s0 - mref), p1 = exp2f(s1 - mref);
             lrow[r] = lrow[r] * alpha[r] + group16_sum(p0 + p1);
             mrow[r] = mnew;
             Ps[wave][4 * (lane >> 4) + r][lane & 15] = f32_to_bf16(p0);
@@ -375,7 +379,7 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
     constexpr int UNION = p_union_bytes(NTMAX > NTD ? NTMAX : NTD);
     __shared__ __attribute__((aligned(16))) uint8_t smem[UNION];
     __shared__ float modl[6 * P_BMAX * P_COLS];     // [q][b][f]: gate1, scale2, shift2, gate2, scale1', shift1'
-    __shared__ float2 ropel[NTQ * 64 * 8];          // [t][position][pair]
+    __shared__ float2 ropel[NTQ * 64 * 8];          // [t][row][pair]
     float* red = (float*)smem;
     const int H = p.H, M = p.M, L = p.L, hq = p.hq;
     constexpr int dh = 128;  // the host admits head_dim 128 only
@@ -436,17 +440,20 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
     (void)ntq; (void)nto; (void)ntg; (void)sp_o; (void)sp_gu; (void)sp_d; (void)row_ok; (void)c0;     \
     (void)rb; (void)f0
 
-    // RoPE factors of this workgroup's QKV tiles (positions < T, 8 pairs per tile)
+    // RoPE factors of this workgroup's QKV tiles for every row (row b*T + i
+    // sits at position valid_b + i), 8 pairs per tile
     {
         P_PHASE_VARS;
         for (int e = tid; e < NTQ * 64 * 8; e += PWAVES * 64) {
-            const int t = e >> 9, i = (e >> 3) & 63, mm = e & 7;
+            const int t = e >> 9, row = (e >> 3) & 63, mm = e & 7;
             float2 cs = make_float2(1.f, 0.f);
-            if (t < ntq && i < p.T) {
+            if (t < ntq && row < M) {
                 const int col = tq(t) * 16, qd = p.nq * dh, kvd = p.nkv * dh;
                 if (col < qd + kvd) {
                     const int local = col < qd ? col : col - qd;
-                    cs = p.rope[i * (dh / 2) + ((local % dh) >> 1) + mm];
+                    const int b = p_div_T(row, p.T, p.inv_T), i = row - b * p.T;
+                    const int pos = prefix_valid(p.ab, b, p.P) + i;
+                    cs = p.rope[pos * (dh / 2) + ((local % dh) >> 1) + mm];
                 }
             }
             ropel[e] = cs;
@@ -549,7 +556,7 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
                     const int b = p_div_T(row, p.T, p.inv_T), i = row - b * p.T;
                     float outv = v;
                     if (sec < 2) {
-                        const float2 cs = ropel[(t * 64 + i) * 8 + (cl >> 1)];
+                        const float2 cs = ropel[(t * 64 + row) * 8 + (cl >> 1)];
                         const float u1 = second ? partner : v;
                         const float u2 = second ? v : partner;
                         outv = second ? (u2 * cs.x + u1 * cs.y) : (u1 * cs.x - u2 * cs.y);

@@ -83,14 +83,21 @@ class Expert:
         """True when calls run as one persistent cooperative kernel."""
         return B.vla_get_option(self.ctx, B.VLA_OPT_PERSISTENT_ACTIVE) == 1
 
-    def denoise(self, prefix_k, prefix_v, noise, t_schedule, n_steps: int, out=None):
-        """All arguments torch device tensors (prefix as int16/bf16 bits); returns ``out``."""
+    def denoise(self, prefix_k, prefix_v, noise, t_schedule, n_steps: int, out=None, prefix_valid=None):
+        """All arguments torch device tensors (prefix as int16/bf16 bits); returns ``out``.
+        ``prefix_valid``: optional int32 device tensor [B] of valid prefix tokens per request."""
         import torch
         if out is None:
             out = torch.empty_like(noise)
         B.vla_set_stream(self.ctx, torch.cuda.current_stream().cuda_stream)
-        B.vla_denoise(self.ctx, prefix_k.data_ptr(), prefix_v.data_ptr(), noise.data_ptr(),
-                      t_schedule.data_ptr(), n_steps, out.data_ptr())
+        if prefix_valid is None:
+            B.vla_denoise(self.ctx, prefix_k.data_ptr(), prefix_v.data_ptr(), noise.data_ptr(),
+                          t_schedule.data_ptr(), n_steps, out.data_ptr())
+        else:
+            if prefix_valid.dtype != torch.int32 or not prefix_valid.is_cuda:
+                raise ValueError("prefix_valid must be an int32 CUDA tensor")
+            B.vla_denoise_varlen(self.ctx, prefix_k.data_ptr(), prefix_v.data_ptr(), prefix_valid.data_ptr(),
+                                 noise.data_ptr(), t_schedule.data_ptr(), n_steps, out.data_ptr())
         return out
 
     def device_bytes(self) -> int:
