@@ -67,6 +67,11 @@ VLA_DEV float group16_max(float v) {
 
 VLA_DEV float silu_f(float z) { return z / (1.0f + __expf(-z)); }
 
+// 2^x for softmax weights: the hardware v_exp_f32 alone. The library exp2f adds
+// range scaling for results below 2^-126 (six more instructions); softmax
+// weights that small are negligible against the row maximum's weight of 1.
+VLA_DEV float attn_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Element index of activation (row, k) of a [rows, K] bf16 matrix. Row-major
 // when frag == 0; otherwise "A-fragment" order for at most 64 rows:
 // [k/32][row/16][lane][8] with lane = row%16 + 16*((k%32)/8), i.e. each

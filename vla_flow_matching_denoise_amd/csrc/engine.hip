@@ -134,7 +134,8 @@ struct vla_ctx {
     Linear mod;                 // all layers' modulation + final, [(6L+2)H, H]
     float* mod_bias = nullptr;  // [(6L+2)H]
     std::vector<Linear> qkv, wo, gu, wd;
-    float2* rope = nullptr;
+    float2* rope = nullptr;        // [P + T][dh/2] by absolute position
+    int* pv_eff = nullptr;         // [B] this call's valid prefix lengths
 
     // buffers
     float* h = nullptr;
@@ -444,7 +445,7 @@ int launch_attention(vla_ctx* c, int l, const uint16_t* q, uint16_t* o, int ofra
     ap.S = d.prefix_len + d.horizon;
     ap.T = d.horizon;
     ap.P = d.prefix_len;
-    ap.ab = c->ab;
+    ap.pvalid = c->pv_eff;
     ap.nq = d.n_q_heads;
     ap.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.head_dim));
     ap.ofrag = ofrag;
@@ -505,7 +506,7 @@ int launch_block_gemm(vla_ctx* c, int which, int step, int l, int* S) {
         p.layer = l;
         p.P = d.prefix_len;
         p.rope = c->rope;
-        p.ab = c->ab;
+        p.pvalid = c->pv_eff;
         p.nq = d.n_q_heads;
         p.nkv = d.n_kv_heads;
         p.dh = d.head_dim;
@@ -560,10 +561,21 @@ int enqueue_step_start(vla_ctx* c, int k, const float* x_direct) {
     return VLA_OK;
 }
 
+// This call's valid prefix lengths (from the argument block, so a captured
+// graph picks up each call's lengths).
+int enqueue_varlen_setup(vla_ctx* c) {
+    const vla_dims& d = c->d;
+    hipLaunchKernelGGL(varlen_setup_kernel, dim3((d.batch + 255) / 256), dim3(256), 0, c->stream, c->ab, c->pv_eff,
+                       d.batch, d.prefix_len);
+    HIPC(hipGetLastError());
+    return VLA_OK;
+}
+
 int enqueue_forward(vla_ctx* c, int n_steps) {
     const vla_dims& d = c->d;
     const int M = c->M, L = d.n_layers;
     int rc;
+    if ((rc = enqueue_varlen_setup(c))) return rc;
     if ((rc = enqueue_prefix_repack(c, nullptr, nullptr))) return rc;
     if ((rc = enqueue_prologue(c, n_steps, nullptr))) return rc;
     for (int k = 0; k < n_steps; ++k) {
@@ -681,6 +693,7 @@ int ensure_persist(vla_ctx* c) {
 int enqueue_persist(vla_ctx* c, int n_steps) {
     const vla_dims& d = c->d;
     int rc;
+    if ((rc = enqueue_varlen_setup(c))) return rc;
     if ((rc = enqueue_prefix_repack(c, nullptr, nullptr))) return rc;
     if ((rc = enqueue_prologue(c, n_steps, nullptr))) return rc;
     hipLaunchKernelGGL(persist_reset_kernel, dim3(1), dim3(256), 0, c->stream, c->lflag, c->gflag, c->gflag + 320,
@@ -718,6 +731,7 @@ int enqueue_persist(vla_ctx* c, int n_steps) {
     p.out_b = c->out_b;
     p.mod = c->modtab;
     p.rope = c->rope;
+    p.pvalid = c->pv_eff;
     p.kcat = c->kcat;
     p.vcat = c->vcat;
     p.kv = c->kv;
@@ -863,6 +877,7 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
     if ((rc = c->alloc((void**)&c->rope, (size_t)npos * (dh / 2) * sizeof(float2)))) return rc;
     hipLaunchKernelGGL(rope_table_kernel, dim3((npos * (dh / 2) + 255) / 256), dim3(256), 0, c->stream, c->rope,
                        npos, dh, (double)d.rope_theta);
+    if ((rc = c->alloc((void**)&c->pv_eff, (size_t)d.batch * sizeof(int)))) return rc;
     HIPC(hipGetLastError());
 
     // working buffers
@@ -1111,6 +1126,7 @@ int vla_test_layer(vla_ctx* c, const void* prefix_k, const void* prefix_v, const
     HIPC(hipSetDevice(c->device));
     if ((rc = ensure_capacity(c, n_steps))) return rc;
     if ((rc = set_args(c, prefix_k, prefix_v, nullptr, t_schedule, nullptr))) return rc;
+    if ((rc = enqueue_varlen_setup(c))) return rc;
     if ((rc = enqueue_prefix_repack(c, (const uint16_t*)prefix_k, (const uint16_t*)prefix_v))) return rc;
     if ((rc = enqueue_prologue(c, n_steps, t_schedule))) return rc;
     HIPC(hipMemcpyAsync(c->h, h_in, (size_t)c->M * c->d.hidden * 4, hipMemcpyDeviceToDevice, c->stream));
@@ -1141,6 +1157,8 @@ int vla_test_attention(vla_ctx* c, const void* prefix_k, const void* prefix_v, i
     }
     HIPC(hipSetDevice(c->device));
     const vla_dims& d = c->d;
+    if ((rc = set_args(c, prefix_k, prefix_v, nullptr, nullptr, nullptr))) return rc;  // full prefixes
+    if ((rc = enqueue_varlen_setup(c))) return rc;
     if ((rc = enqueue_prefix_repack(c, (const uint16_t*)prefix_k, (const uint16_t*)prefix_v))) return rc;
     long n = (long)d.batch * d.n_kv_heads * d.horizon * (d.head_dim / 8);
     hipLaunchKernelGGL(chunk_kv_store_kernel, dim3((int)((n + 255) / 256)), dim3(256), 0, c->stream,

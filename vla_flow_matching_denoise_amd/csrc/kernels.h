@@ -80,6 +80,13 @@ __global__ void rope_table_kernel(float2* tab, int npos, int dh, double theta) {
     tab[idx] = make_float2((float)cos(ang), (float)sin(ang));
 }
 
+// Per call: each request's valid prefix length, clamped to [0, P], read by
+// the QKV epilogues (RoPE position pvalid[b] + i) and the attention masks.
+__global__ void varlen_setup_kernel(const ArgBlock* ab, int* pv_eff, int B, int P) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < B) pv_eff[b] = prefix_valid(ab, b, P);
+}
+
 // ---------------------------------------------------------------------------
 // Prologue: time embedding and time MLP for every (step, request)
 // ---------------------------------------------------------------------------

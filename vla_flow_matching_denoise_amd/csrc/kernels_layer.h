@@ -180,8 +180,8 @@ struct GemmParams {
     uint16_t* vcat;
     KVLayout kv;
     int layer, P;
-    const float2* rope;  // [P + T][dh/2], by absolute position
-    const ArgBlock* ab;  // per-request valid prefix lengths (RoPE positions of the chunk)
+    const float2* rope;  // [P + T][dh/2] by absolute position
+    const int* pvalid;   // [B] this call's valid prefix lengths: row b*T+i sits at pvalid[b] + i
     int nq, nkv, dh;
     int dh_shift;        // log2(dh)
     float inv_T;         // 1/T, for the row -> request split without a divide
@@ -198,8 +198,15 @@ VLA_DEV int div_T(int row, const GemmParams& p) {
 }
 
 // v: this lane's value of (row, col); partner: the value of (row, col ^ 1).
+// RoPE position of chunk row r = b*T + i: pvalid[b] + i (QKV epilogue only).
+VLA_DEV int qkv_row_pos(const GemmParams& p, int row) {
+    const int b = div_T(row, p);
+    return p.pvalid[b] + row - b * p.T;
+}
+
+// rpos: qkv_row_pos(p, row) for EPI_QKV_ROPE (callers hoist it per row).
 template <int EPI>
-VLA_DEV void epilogue_store(const GemmParams& p, int row, int col, float v, float partner, int kz) {
+VLA_DEV void epilogue_store(const GemmParams& p, int row, int col, float v, float partner, int kz, int rpos) {
     if (row >= p.M) return;
     if constexpr (EPI == EPI_PARTIAL) {
         p.ws[((size_t)kz * p.M + row) * p.N + col] = v;
@@ -223,7 +230,7 @@ VLA_DEV void epilogue_store(const GemmParams& p, int row, int col, float v, floa
         const int b = div_T(row, p), i = row - b * p.T;
         float outv = v;
         if (sec < 2) {
-            const float2 cs = p.rope[(prefix_valid(p.ab, b, p.P) + i) * (p.dh / 2) + m];
+            const float2 cs = p.rope[rpos * (p.dh / 2) + m];
             const float u1 = second ? partner : v;
             const float u2 = second ? v : partner;
             outv = second ? (u2 * cs.x + u1 * cs.y) : (u1 * cs.x - u2 * cs.y);
@@ -322,7 +329,8 @@ __global__ __launch_bounds__(512) void skinny_gemm_kernel(GemmParams p) {
                 const int row = wave * 16 + 4 * (lane >> 4) + r;
                 const float v = sum[r] * wsc;
                 const float partner = __shfl_xor(v, 1, 64);
-                epilogue_store<EPI>(p, row, col, v, partner, kz);
+                epilogue_store<EPI>(p, row, col, v, partner, kz,
+                                    EPI == EPI_QKV_ROPE && row < p.M ? qkv_row_pos(p, row) : 0);
             }
         }
         buf ^= 1;
@@ -471,18 +479,22 @@ __global__ __launch_bounds__(64 * gemm_waves(MT, NT)) void gemm_kernel(GemmParam
         __syncthreads();
     }
 
+    float wsc[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) wsc[fn] = W8 ? p.wscale[n0 + wn * WN + fn * 16 + (lane & 15)] : 1.0f;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            const int col = n0 + wn * WN + fn * 16 + (lane & 15);
-            const float wsc = W8 ? p.wscale[col] : 1.0f;
+        for (int r = 0; r < 4; ++r) {
+            const int row = m0 + wm * WM + fm * 16 + 4 * (lane >> 4) + r;
+            // per-row work (the RoPE position) once, not per column
+            const int rpos = EPI == EPI_QKV_ROPE && row < p.M ? qkv_row_pos(p, row) : 0;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = m0 + wm * WM + fm * 16 + 4 * (lane >> 4) + r;
-                float v = acc[fm][fn][r] * wsc;
+            for (int fn = 0; fn < FN; ++fn) {
+                const int col = n0 + wn * WN + fn * 16 + (lane & 15);
+                float v = acc[fm][fn][r] * wsc[fn];
                 float partner = __shfl_xor(v, 1, 64);
-                epilogue_store<EPI>(p, row, col, v, partner, 0);
+                epilogue_store<EPI>(p, row, col, v, partner, 0, rpos);
             }
         }
 }
@@ -504,8 +516,8 @@ struct AttnParams {
     int layer, S, T, nq;
     int ofrag;
     float scale_log2;       // log2(e)/sqrt(dh)
-    int P;                  // prefix keys per request (the first valid_b of them count)
-    const ArgBlock* ab;     // per-request valid prefix lengths
+    int P;                  // prefix keys per request (the first valid[b] of them count)
+    const int* pvalid;      // [B] valid prefix lengths of this call
 };
 
 template <int DH, int AT_WAVES>
@@ -522,7 +534,7 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
     const size_t base = p.kv.base(b, p.layer, g);
     const uint16_t* K = p.kcat + base;
     const uint16_t* V = p.vcat + base;
-    const int pvb = prefix_valid(p.ab, b, p.P);  // prefix keys past this are padding
+    const int pvb = p.pvalid[b];  // prefix keys past this are padding
 
     bf16x8 qf[DH / 32];
     {
@@ -537,7 +549,10 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
     float mrow[4], lrow[4];
     f32x4 oacc[DH / 16];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) { mrow[r] = -INFINITY; lrow[r] = 0.f; }
+    // running max starts finite: a block whose keys are all masked (padding)
+    // then leaves m finite and adds weight 0, where -inf would give
+    // exp2(-inf - -inf) = NaN
+    for (int r = 0; r < 4; ++r) { mrow[r] = -1e30f; lrow[r] = 0.f; }
 #pragma unroll
     for (int dn = 0; dn < DH / 16; ++dn) oacc[dn] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
@@ -563,20 +578,21 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
 #pragma unroll
             for (int ks = 0; ks < DH / 32; ++ks) s[sb] = mfma_16x16x32(qf[ks], kf[sb][ks], s[sb]);
         }
+        // every key of the block real (a uniform test): no per-key mask
+        const bool whole = (kb * 32 + 32 <= pvb) || (kb * 32 >= p.P && kb * 32 + 32 <= p.S);
         float alpha[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float s0 = s[0][r] * p.scale_log2, s1 = s[1][r] * p.scale_log2;
-            const int key0 = kb * 32 + (lane & 15), key1 = key0 + 16;
-            if (key0 >= p.S || (key0 < p.P && key0 >= pvb)) s0 = -INFINITY;
-            if (key1 >= p.S || (key1 < p.P && key1 >= pvb)) s1 = -INFINITY;
+            if (!whole) {  // a block with padded prefix keys or keys past P + T
+                const int key0 = kb * 32 + (lane & 15), key1 = key0 + 16;
+                if (key0 >= p.S || (key0 < p.P && key0 >= pvb)) s0 = -INFINITY;
+                if (key1 >= p.S || (key1 < p.P && key1 >= pvb)) s1 = -INFINITY;
+            }
             const float mx = group16_max(fmaxf(s0, s1));
             const float mnew = fmaxf(mrow[r], mx);
-            // while every key so far is masked (a padded prefix block) the row
-            // keeps m = -inf; its exponents then use 0, giving 0, not NaN
-            const float mref = mnew == -INFINITY ? 0.f : mnew;
-            alpha[r] = exp2f(mrow[r] - mref);
-            const float p0 = exp2f(s0 - mref), p1 = exp2f(s1 - mref);
+            alpha[r] = attn_exp2(mrow[r] - mnew);
+            const float p0 = attn_exp2(s0 - mnew), p1 = attn_exp2(s1 - mnew);
             lrow[r] = lrow[r] * alpha[r] + group16_sum(p0 + p1);
             mrow[r] = mnew;
             Ps[wave][4 * (lane >> 4) + r][lane & 15] = f32_to_bf16(p0);
@@ -625,7 +641,7 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
         float L = 0.f;
 #pragma unroll
         for (int w = 0; w < AT_WAVES; ++w) {
-            scale[w][r] = exp2f(mw[w][r] - M);
+            scale[w][r] = attn_exp2(mw[w][r] - M);
             L += scale[w][r] * lw[w][r];
         }
         inv[r] = 1.0f / L;
@@ -679,7 +695,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
     const size_t base = p.kv.base(b, p.layer, g);
     const uint8_t* K = (const uint8_t*)(p.kcat + base);
     const uint8_t* V = (const uint8_t*)(p.vcat + base);
-    const int pvb = prefix_valid(p.ab, b, p.P);  // prefix keys past this are padding
+    const int pvb = p.pvalid[b];  // prefix keys past this are padding
 
     bf16x8 qf[DH / 32];
     {
@@ -696,7 +712,10 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
     float mrow[4], lrow[4];
     f32x4 oacc[DH / 16];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) { mrow[r] = -INFINITY; lrow[r] = 0.f; }
+    // running max starts finite: a block whose keys are all masked (padding)
+    // then leaves m finite and adds weight 0, where -inf would give
+    // exp2(-inf - -inf) = NaN
+    for (int r = 0; r < 4; ++r) { mrow[r] = -1e30f; lrow[r] = 0.f; }
 #pragma unroll
     for (int dn = 0; dn < DH / 16; ++dn) oacc[dn] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
@@ -735,20 +754,21 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
                 s[sb] = mfma_16x16x32(qf[ks], kf, s[sb]);
             }
         }
+        // every key of the block real (a uniform test): no per-key mask
+        const bool whole = (kb * 32 + 32 <= pvb) || (kb * 32 >= p.P && kb * 32 + 32 <= p.S);
         float alpha[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float s0 = s[0][r] * p.scale_log2, s1 = s[1][r] * p.scale_log2;
-            const int key0 = kb * 32 + (lane & 15), key1 = key0 + 16;
-            if (key0 >= p.S || (key0 < p.P && key0 >= pvb)) s0 = -INFINITY;
-            if (key1 >= p.S || (key1 < p.P && key1 >= pvb)) s1 = -INFINITY;
+            if (!whole) {  // a block with padded prefix keys or keys past P + T
+                const int key0 = kb * 32 + (lane & 15), key1 = key0 + 16;
+                if (key0 >= p.S || (key0 < p.P && key0 >= pvb)) s0 = -INFINITY;
+                if (key1 >= p.S || (key1 < p.P && key1 >= pvb)) s1 = -INFINITY;
+            }
             const float mx = group16_max(fmaxf(s0, s1));
             const float mnew = fmaxf(mrow[r], mx);
-            // while every key so far is masked (a padded prefix block) the row
-            // keeps m = -inf; its exponents then use 0, giving 0, not NaN
-            const float mref = mnew == -INFINITY ? 0.f : mnew;
-            alpha[r] = exp2f(mrow[r] - mref);
-            const float p0 = exp2f(s0 - mref), p1 = exp2f(s1 - mref);
+            alpha[r] = attn_exp2(mrow[r] - mnew);
+            const float p0 = attn_exp2(s0 - mnew), p1 = attn_exp2(s1 - mnew);
             lrow[r] = lrow[r] * alpha[r] + group16_sum(p0 + p1);
             mrow[r] = mnew;
             Ps[wave][4 * (lane >> 4) + r][lane & 15] = f32_to_bf16(p0);

@@ -52,7 +52,8 @@ struct PersistParams {
     const uint16_t* out_w;       // [A][H]
     const float* out_b;
     const float* mod;
-    const float2* rope;
+    const float2* rope;          // [P + T][dh/2] by absolute position
+    const int* pvalid;           // [B] valid prefix lengths of this call (row b*T+i at pvalid[b] + i)
     const uint16_t* kcat;        // prefix keys/values (keys < P) of every (b, layer, group)
     const uint16_t* vcat;
     KVLayout kv;
@@ -252,7 +253,7 @@ VLA_DEV void p_attention(const PersistParams& p, const uint16_t* qg, int r0, con
     const int rows_total = p.hq * p.T;
     const int nbp = p.P / 32, nblk = nbp + p.Tpad / 32;
     const int S = p.P + p.T;
-    const int pvb = prefix_valid(p.ab, b, p.P);  // prefix keys past this are padding
+    const int pvb = p.pvalid[b];  // prefix keys past this are padding
     bf16x8 qf[DH / 32];
     {
         const int row = r0 + (lane & 15);
@@ -264,7 +265,10 @@ VLA_DEV void p_attention(const PersistParams& p, const uint16_t* qg, int r0, con
     float mrow[4], lrow[4];
     f32x4 oacc[DH / 16];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) { mrow[r] = -INFINITY; lrow[r] = 0.f; }
+    // running max starts finite: a block whose keys are all masked (padding)
+    // then leaves m finite and adds weight 0, where -inf would give
+    // exp2(-inf - -inf) = NaN
+    for (int r = 0; r < 4; ++r) { mrow[r] = -1e30f; lrow[r] = 0.f; }
 #pragma unroll
     for (int dn = 0; dn < DH / 16; ++dn) oacc[dn] = (f32x4){0.f, 0.f, 0.f, 0.f};
     for (int kb = wave; kb < nblk; kb += PWAVES) {
@@ -286,20 +290,21 @@ VLA_DEV void p_attention(const PersistParams& p, const uint16_t* qg, int r0, con
 #pragma unroll
             for (int ks = 0; ks < DH / 32; ++ks) s[sb] = mfma_16x16x32(qf[ks], kf[sb][ks], s[sb]);
         }
+        // every key of the block real (a uniform test): no per-key mask
+        const bool whole = (kb * 32 + 32 <= pvb) || (kb * 32 >= p.P && kb * 32 + 32 <= S);
         float alpha[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float s0 = s[0][r] * p.scale_log2, s1 = s[1][r] * p.scale_log2;
-            const int key0 = kb * 32 + (lane & 15), key1 = key0 + 16;
-            if (key0 >= S || (key0 < p.P && key0 >= pvb)) s0 = -INFINITY;
-            if (key1 >= S || (key1 < p.P && key1 >= pvb)) s1 = -INFINITY;
+            if (!whole) {  // a block with padded prefix keys or keys past P + T
+                const int key0 = kb * 32 + (lane & 15), key1 = key0 + 16;
+                if (key0 >= S || (key0 < p.P && key0 >= pvb)) s0 = -INFINITY;
+                if (key1 >= S || (key1 < p.P && key1 >= pvb)) s1 = -INFINITY;
+            }
             const float mx = group16_max(fmaxf(s0, s1));
             const float mnew = fmaxf(mrow[r], mx);
-            // while every key so far is masked (a padded prefix block) the row
-            // keeps m = -inf; its exponents then use 0, giving 0, not NaN
-            const float mref = mnew == -INFINITY ? 0.f : mnew;
-            alpha[r] = exp2f(mrow[r] - mref);
-            const float p0 = exp2f(s0 - mref), p1 = exp2f(s1 - mref);
+            alpha[r] = attn_exp2(mrow[r] - mnew);
+            const float p0 = attn_exp2(s0 - mnew), p1 = attn_exp2(s1 - mnew);
             lrow[r] = lrow[r] * alpha[r] + group16_sum(p0 + p1);
             mrow[r] = mnew;
             Ps[wave][4 * (lane >> 4) + r][lane & 15] = f32_to_bf16(p0);
@@ -333,7 +338,7 @@ VLA_DEV void p_attention(const PersistParams& p, const uint16_t* qg, int r0, con
         float Ls = 0.f;
 #pragma unroll
         for (int w = 0; w < PWAVES; ++w) {
-            sc[w][r] = exp2f(mw[w] - Mx);
+            sc[w][r] = attn_exp2(mw[w] - Mx);
             Ls += sc[w][r] * Om[w][lane][DH / 16 * 4 + 4 + r];
         }
         inv[r] = 1.0f / Ls;
@@ -452,8 +457,7 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
                 if (col < qd + kvd) {
                     const int local = col < qd ? col : col - qd;
                     const int b = p_div_T(row, p.T, p.inv_T), i = row - b * p.T;
-                    const int pos = prefix_valid(p.ab, b, p.P) + i;
-                    cs = p.rope[pos * (dh / 2) + ((local % dh) >> 1) + mm];
+                    cs = p.rope[(p.pvalid[b] + i) * (dh / 2) + ((local % dh) >> 1) + mm];
                 }
             }
             ropel[e] = cs;
