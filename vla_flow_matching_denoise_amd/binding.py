@@ -25,6 +25,7 @@ VLA_OPT_USE_GRAPH = 1
 VLA_OPT_PERSISTENT = 2
 VLA_OPT_PERSISTENT_ACTIVE = 3
 VLA_OPT_PERSISTENT_STATUS = 4
+VLA_OPT_GEMM_TILE = 5
 
 # every symbol include/vla_expert.h declares
 EXPORTED = (

@@ -75,11 +75,13 @@ struct GemmCfg {
 
 // M <= 64: skinny kernel, one 16-column tile per workgroup; when the consumer
 // can take split-K partials (allow_split), K is split until ~320 workgroups
-// or 256-deep chunks. Larger M: tiled kernel, 128-row tiles, 128 or 64
-// columns so that a launch has >= 256 tiles when possible.
-GemmCfg choose_gemm(int M, int N, int K, bool allow_split) {
+// or 256-deep chunks. Larger M: tiled kernel (one workgroup per CU), with
+// the tile shape of least modelled time: rounds of `ncu` tiles times the
+// time of one tile relative to a 128x128 tile (measured at K = 1024: a
+// 256x256 tile takes 2.75 times as long, a 128x64 tile about 0.65).
+GemmCfg choose_gemm(int M, int N, int K, bool allow_split, int ncu, int force_tile = 0) {
     GemmCfg c;
-    if (M <= 64) {
+    if (M <= 64 && force_tile == 0) {
         c.skinny = true;
         c.NT = 16;
         const int tiles = N / 16;
@@ -96,13 +98,24 @@ GemmCfg choose_gemm(int M, int N, int K, bool allow_split) {
         }
         // too deep for the skinny kernel: fall through to the tiled one
     }
-    {
-        c.skinny = false;
-        c.MT = 128;
-        const int mt = (M + 127) / 128;
-        c.NT = (N % 128 == 0 && mt * (N / 128) >= 256) ? 128 : 64;
-        c.ksplit = 1;
-        c.kw = K;
+    c.skinny = false;
+    c.ksplit = 1;
+    c.kw = K;
+    struct Cand { int MT, NT; double rel; };
+    const Cand cands[3] = {{256, 256, 2.75}, {128, 128, 1.0}, {128, 64, 0.65}};
+    double best = 0.0;
+    // force_tile 1..3 picks cands[force_tile - 1] where it divides N
+    const bool forced = force_tile >= 1 && force_tile <= 3 && N % cands[force_tile - 1].NT == 0;
+    for (int i = 0; i < 3; ++i) {
+        const Cand& t = cands[i];
+        if (forced ? i != force_tile - 1 : (N % t.NT != 0 || (t.MT == 256 && M <= 128))) continue;
+        const long tiles = (long)((M + t.MT - 1) / t.MT) * (N / t.NT);
+        const double cost = (double)((tiles + ncu - 1) / ncu) * t.rel;
+        if (c.MT == 0 || cost < best) {
+            best = cost;
+            c.MT = t.MT;
+            c.NT = t.NT;
+        }
     }
     return c;
 }
@@ -119,6 +132,8 @@ struct Linear {
 struct vla_ctx {
     vla_dims d{};
     int device = 0;
+    int ncu = 256;      // compute units of the device (tile rounds of the tiled GEMM)
+    int gemm_tile = 0;  // VLA_OPT_GEMM_TILE
     hipStream_t own_stream = nullptr;
     hipStream_t stream = nullptr;
     bool use_graph = true;
@@ -343,7 +358,7 @@ int ensure_capacity(vla_ctx* c, int n_steps) {
 
 template <int MT, int NT, bool W8>
 int launch_tiled_t(int epi, const GemmParams& p, dim3 grid, hipStream_t s) {
-    const dim3 blk(64 * gemm_waves(MT, NT));
+    const dim3 blk(64 * GEMM_WAVES);
     switch (epi) {
         case EPI_BIAS_F32: VLA_LAUNCH((gemm_kernel<MT, NT, W8, EPI_BIAS_F32>), grid, blk, 0, s, p); break;
         case EPI_RESID: VLA_LAUNCH((gemm_kernel<MT, NT, W8, EPI_RESID>), grid, blk, 0, s, p); break;
@@ -389,11 +404,17 @@ int launch_gemm(vla_ctx* c, const Linear& lin, const GemmCfg& cfg, bool w8, int 
         dim3 grid(cfg.gx, cfg.ksplit);
         return w8 ? launch_skinny_t<true>(epi, p, grid, c->stream) : launch_skinny_t<false>(epi, p, grid, c->stream);
     }
+    if (lin.K % GEMM_KT != 0) {
+        set_err("tiled GEMM needs K %% %d == 0 (K = %d)", GEMM_KT, lin.K);
+        return VLA_ERR_SHAPE;
+    }
     dim3 grid((lin.N / cfg.NT) * ((p.M + cfg.MT - 1) / cfg.MT));  // tile from the linear id
-    if (cfg.NT == 128) return w8 ? launch_tiled_t<128, 128, true>(epi, p, grid, c->stream)
-                                 : launch_tiled_t<128, 128, false>(epi, p, grid, c->stream);
-    if (cfg.NT == 64) return w8 ? launch_tiled_t<128, 64, true>(epi, p, grid, c->stream)
-                                : launch_tiled_t<128, 64, false>(epi, p, grid, c->stream);
+    if (cfg.MT == 256 && cfg.NT == 256) return w8 ? launch_tiled_t<256, 256, true>(epi, p, grid, c->stream)
+                                                  : launch_tiled_t<256, 256, false>(epi, p, grid, c->stream);
+    if (cfg.MT == 128 && cfg.NT == 128) return w8 ? launch_tiled_t<128, 128, true>(epi, p, grid, c->stream)
+                                                  : launch_tiled_t<128, 128, false>(epi, p, grid, c->stream);
+    if (cfg.MT == 128 && cfg.NT == 64) return w8 ? launch_tiled_t<128, 64, true>(epi, p, grid, c->stream)
+                                                 : launch_tiled_t<128, 64, false>(epi, p, grid, c->stream);
     set_err("no GEMM tile %dx%d", cfg.MT, cfg.NT);
     return VLA_ERR_SHAPE;
 }
@@ -419,7 +440,7 @@ int enqueue_prologue(vla_ctx* c, int n_steps, const float* ts_direct) {
     p.M = nb;
     p.out_f32 = c->modtab;
     p.bias = c->mod_bias;
-    return launch_gemm(c, c->mod, choose_gemm(nb, c->mod.N, c->mod.K, false), false, EPI_BIAS_F32, p);
+    return launch_gemm(c, c->mod, choose_gemm(nb, c->mod.N, c->mod.K, false, c->ncu, c->gemm_tile), false, EPI_BIAS_F32, p);
 }
 
 int enqueue_prefix_repack(vla_ctx* c, const uint16_t* pk, const uint16_t* pv) {
@@ -783,6 +804,7 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
     c->kvd = d.n_kv_heads * dh;
     c->mod_ld = (6 * L + 2) * H;
     HIPC(hipGetDevice(&c->device));
+    HIPC(hipDeviceGetAttribute(&c->ncu, hipDeviceAttributeMultiprocessorCount, c->device));
     // graphs are captured on this stream; work runs on `stream`, the legacy
     // default stream until vla_set_stream names another
     HIPC(hipStreamCreateWithFlags(&c->own_stream, hipStreamNonBlocking));
@@ -866,10 +888,10 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
             int rows[1] = {H};
             if ((rc = pack_linear(c, c->wd[l], H, I, srcs, scs, 1, rows, 0, dh))) return rc;
         }
-        c->qkv[l].cfg = choose_gemm(c->M, c->qkv[l].N, c->qkv[l].K, false);
-        c->wo[l].cfg = choose_gemm(c->M, c->wo[l].N, c->wo[l].K, true);
-        c->gu[l].cfg = choose_gemm(c->M, c->gu[l].N, c->gu[l].K, false);
-        c->wd[l].cfg = choose_gemm(c->M, c->wd[l].N, c->wd[l].K, true);
+        c->qkv[l].cfg = choose_gemm(c->M, c->qkv[l].N, c->qkv[l].K, false, c->ncu, c->gemm_tile);
+        c->wo[l].cfg = choose_gemm(c->M, c->wo[l].N, c->wo[l].K, true, c->ncu, c->gemm_tile);
+        c->gu[l].cfg = choose_gemm(c->M, c->gu[l].N, c->gu[l].K, false, c->ncu, c->gemm_tile);
+        c->wd[l].cfg = choose_gemm(c->M, c->wd[l].N, c->wd[l].K, true, c->ncu, c->gemm_tile);
     }
 
     // rotary table over every absolute position a chunk token can take
@@ -1053,6 +1075,25 @@ int vla_set_option(vla_ctx* c, int option, int value) {
         c->use_persist = value != 0;
         return VLA_OK;
     }
+    if (option == VLA_OPT_GEMM_TILE) {
+        if (value < 0 || value > 3) {
+            set_err("VLA_OPT_GEMM_TILE takes 0..3, not %d", value);
+            return VLA_ERR_ARG;
+        }
+        HIPC(hipSetDevice(c->device));
+        HIPC(hipStreamSynchronize(c->stream));
+        c->gemm_tile = value;
+        for (int l = 0; l < c->d.n_layers; ++l) {
+            c->qkv[l].cfg = choose_gemm(c->M, c->qkv[l].N, c->qkv[l].K, false, c->ncu, value);
+            c->wo[l].cfg = choose_gemm(c->M, c->wo[l].N, c->wo[l].K, true, c->ncu, value);
+            c->gu[l].cfg = choose_gemm(c->M, c->gu[l].N, c->gu[l].K, false, c->ncu, value);
+            c->wd[l].cfg = choose_gemm(c->M, c->wd[l].N, c->wd[l].K, true, c->ncu, value);
+        }
+        // captured graphs hold the old launches
+        for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);
+        c->graphs.clear();
+        return VLA_OK;
+    }
     set_err("unknown option %d", option);
     return VLA_ERR_ARG;
 }
@@ -1066,6 +1107,7 @@ int vla_get_option(const vla_ctx* c, int option, int* value) {
     switch (option) {
         case VLA_OPT_USE_GRAPH: *value = c->use_graph ? 1 : 0; return VLA_OK;
         case VLA_OPT_PERSISTENT: *value = c->use_persist ? 1 : 0; return VLA_OK;
+        case VLA_OPT_GEMM_TILE: *value = c->gemm_tile; return VLA_OK;
         case VLA_OPT_PERSISTENT_ACTIVE: *value = (c->persist_ok && c->use_persist) ? 1 : 0; return VLA_OK;
         case VLA_OPT_PERSISTENT_STATUS: {
             int e = 0;

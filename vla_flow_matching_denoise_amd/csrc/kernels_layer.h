@@ -246,6 +246,80 @@ VLA_DEV void epilogue_store(const GemmParams& p, int row, int col, float v, floa
     }
 }
 
+// The epilogue of 16 consecutive columns col0..col0+15 of one row (col0 a
+// multiple of 16) for the tiled kernel: the same results as epilogue_store
+// column by column, with 16-byte global accesses.
+template <int EPI>
+VLA_DEV void epilogue16(const GemmParams& p, int row, int col0, const float (&v)[16]) {
+    if constexpr (EPI == EPI_BIAS_F32) {
+        float* o = p.out_f32 + (size_t)row * p.N + col0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 bq = *(const f32x4*)(p.bias + col0 + 4 * q);
+            *(f32x4*)(o + 4 * q) = (f32x4){v[4 * q] + bq[0], v[4 * q + 1] + bq[1], v[4 * q + 2] + bq[2],
+                                           v[4 * q + 3] + bq[3]};
+        }
+    } else if constexpr (EPI == EPI_RESID) {
+        const int b = div_T(row, p);
+        const float* g = p.mod + (size_t)(p.step * p.B + b) * p.mod_ld + p.gate_off + col0;
+        float* hp = p.out_f32 + (size_t)row * p.N + col0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 gq = *(const f32x4*)(g + 4 * q);
+            const f32x4 hq = *(const f32x4*)(hp + 4 * q);
+            *(f32x4*)(hp + 4 * q) = (f32x4){hq[0] + gq[0] * v[4 * q], hq[1] + gq[1] * v[4 * q + 1],
+                                            hq[2] + gq[2] * v[4 * q + 2], hq[3] + gq[3] * v[4 * q + 3]};
+        }
+    } else if constexpr (EPI == EPI_SWIGLU) {
+        // columns alternate gate (even) and up (odd) of outputs col0/2 .. col0/2 + 7
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            o[j] = pack_bf16x2(silu_f(v[4 * j]) * v[4 * j + 1], silu_f(v[4 * j + 2]) * v[4 * j + 3]);
+        *(u32x4*)(p.act + act_index(row, col0 >> 1, p.N / 2, p.afrag)) = o;
+    } else if constexpr (EPI == EPI_QKV_ROPE) {
+        // the 16 columns are 8 rotate-half pairs (m, m + d_h/2), m = m0 .. m0+7, of one head
+        const int qd = p.nq * p.dh, kvd = p.nkv * p.dh;
+        int sec, local;
+        if (col0 < qd) { sec = 0; local = col0; }
+        else if (col0 < qd + kvd) { sec = 1; local = col0 - qd; }
+        else { sec = 2; local = col0 - qd - kvd; }
+        const int head = local >> p.dh_shift, m0 = (local & (p.dh - 1)) >> 1;
+        const int b = div_T(row, p), i = row - b * p.T;
+        float lo[8], hi[8];
+        if (sec < 2) {
+            const float2* cs = p.rope + (size_t)(p.pvalid[b] + i) * (p.dh / 2) + m0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float2 c = cs[j];
+                lo[j] = v[2 * j] * c.x - v[2 * j + 1] * c.y;
+                hi[j] = v[2 * j + 1] * c.x + v[2 * j] * c.y;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) { lo[j] = v[2 * j]; hi[j] = v[2 * j + 1]; }
+        }
+        if (sec < 2) {
+            uint16_t* dst = sec == 0 ? p.q + ((size_t)(b * p.nq + head) * p.T + i) * p.dh
+                                     : p.kcat + p.kv.k_at(b, p.layer, head, p.P + i, 0);
+            u32x4 a, c;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                a[j] = pack_bf16x2(lo[2 * j], lo[2 * j + 1]);
+                c[j] = pack_bf16x2(hi[2 * j], hi[2 * j + 1]);
+            }
+            *(u32x4*)(dst + m0) = a;
+            *(u32x4*)(dst + m0 + p.dh / 2) = c;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                p.vcat[p.kv.v_at(b, p.layer, head, p.P + i, m0 + j)] = f32_to_bf16(lo[j]);
+                p.vcat[p.kv.v_at(b, p.layer, head, p.P + i, m0 + j + p.dh / 2)] = f32_to_bf16(hi[j]);
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Skinny GEMM for M <= 64 rows (weight streaming). A workgroup of 8 waves
 // owns one K split and a strided set of 16-column tiles (tile = blockIdx.x +
@@ -340,42 +414,61 @@ __global__ __launch_bounds__(512) void skinny_gemm_kernel(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Tiled GEMM for larger M: tile MT x NT per workgroup (4 waves as 2x2), K
-// staged through LDS 64 at a time with register double buffering.
+// Tiled GEMM for larger M: an MT x NT tile per workgroup of 8 waves (2 along
+// M, 4 along N). K advances in 64-deep stages through a ring of GEMM_STAGES
+// LDS buffers that global->LDS DMA loads fill directly (no register staging):
+// stage kt+S is requested as soon as every wave is done with stage kt, so S-1
+// stages are in flight while one is multiplied. Both operands sit in LDS as
+// 1 KiB MFMA fragments (lane i's 16 bytes at offset 16 i), so the DMA writes
+// and the fragment reads are free of bank conflicts.
 // ---------------------------------------------------------------------------
-// Workgroup shape of a tile: 256x256 tiles would run 8 waves (2 x 4, each
-// 128x64); the tiles in use (128 x 128 / 64) run 4 waves (2 x 2). Measured at
-// M = 3200: 256x256 tiles (one 8-wave workgroup per CU, 1.6 rounds of tiles)
-// ran gate_up in 92 us against 85 us for 128x128.
-constexpr int gemm_waves(int MT, int NT) { return MT >= 256 && NT >= 256 ? 8 : 4; }
+constexpr int GEMM_WAVES = 8, GEMM_KT = 64, GEMM_KS = GEMM_KT / 32;
+
+// 16 bytes per lane from global memory into LDS: the 64 lanes fill the
+// 1 KiB at byte offset `lds` (lane i at lds + 16 i). No register receives
+// data; the kernel waits for these loads itself (gemm_vm_wait) before the
+// barrier that publishes a stage, and before it exits.
+VLA_DEV void gemm_dma16(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+template <int N>
+VLA_DEV void gemm_vm_wait() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// LDS stages per tile shape: as many 64-deep stages as fit in 144 KiB, at
+// most 3 (one workgroup per CU).
+template <int MT, int NT, bool W8>
+struct GemmShape {
+    static constexpr int AF = MT / 16 * GEMM_KS;                 // A fragments per stage (1 KiB each)
+    static constexpr int BBYTES = NT / 16 * GEMM_KS * (W8 ? 512 : 1024);
+    static constexpr int BCH = BBYTES / 1024;                    // 1 KiB DMA chunks of B per stage
+    static constexpr int STAGE = AF * 1024 + BBYTES;
+    static constexpr int S = 147456 / STAGE >= 3 ? 3 : 147456 / STAGE;
+    static constexpr int LA = (AF + GEMM_WAVES - 1) / GEMM_WAVES;   // DMA loads per wave and stage
+    static constexpr int LB = (BCH + GEMM_WAVES - 1) / GEMM_WAVES;
+    static constexpr int LPW = LA + LB;
+    static_assert(S >= 2, "tile too large for two LDS stages");
+};
 
 template <int MT, int NT, bool W8, int EPI>
-__global__ __launch_bounds__(64 * gemm_waves(MT, NT)) void gemm_kernel(GemmParams p) {
-    // k-tile per LDS stage: 128x128 tiles take 32 (36 KiB of LDS: four
-    // workgroups per CU hide the load latency); narrower tiles take 64
-    constexpr int KT = NT >= 128 ? 32 : 64;
-    constexpr int NWAVES = gemm_waves(MT, NT), NTHR = 64 * NWAVES;
-    constexpr int WGN = NWAVES / 2;  // waves along N (2 along M)
-    constexpr int WM = MT / 2, WN = NT / WGN;
-    constexpr int FM = WM / 16, FN = WN / 16;
-    constexpr int APAD = KT + 8;
-    constexpr int A_CH = MT * KT / 8 / NTHR;
-    constexpr int WFRAG_BYTES = W8 ? 512 : 1024;
-    constexpr int B_BYTES = (NT / 16) * (KT / 32) * WFRAG_BYTES;
-    constexpr int B_CH = B_BYTES / 16 / NTHR > 0 ? B_BYTES / 16 / NTHR : 1;
-    constexpr int B_THREADS = B_BYTES / 16;
-    static_assert(A_CH >= 1 && MT * KT / 8 == A_CH * NTHR, "A tile does not split over the threads");
+__global__ __launch_bounds__(64 * GEMM_WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_kernel(GemmParams p) {
+    using G = GemmShape<MT, NT, W8>;
+    constexpr int S = G::S, AF = G::AF, BCH = G::BCH, LA = G::LA, LB = G::LB, LPW = G::LPW, STAGE = G::STAGE;
+    constexpr int KS = GEMM_KS, WGN = 4;
+    constexpr int WM = MT / 2, WN = NT / WGN, FM = WM / 16, FN = WN / 16;
+    static_assert(FM >= 1 && FN >= 1, "tile smaller than the wave grid");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[S * STAGE];
 
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][MT][APAD];
-    __shared__ __attribute__((aligned(16))) uint8_t Bs[2][B_BYTES];
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
     // Tile of this workgroup. Consecutive workgroups run on consecutive XCDs,
     // so when the N-tiles split evenly over the 8 XCDs, workgroup w takes an
     // N-tile of XCD group w % 8 for every M-tile: each XCD's L2 then holds one
     // eighth of the weights and reuses each A tile across its N-tiles.
-    const int ntn = p.N / NT, ntm = (p.M + MT - 1) / MT;
+    const int ntn = p.N / NT;
     int mt_i, nt_i;
     if (ntn % 8 == 0) {
         const int w = blockIdx.x, per = ntn / 8, s = w >> 3;
@@ -386,117 +479,149 @@ __global__ __launch_bounds__(64 * gemm_waves(MT, NT)) void gemm_kernel(GemmParam
         nt_i = blockIdx.x % ntn;
     }
     const int m0 = mt_i * MT, n0 = nt_i * NT;
-    const int nk = p.K / KT;
-    const int Kf = p.K / 32;
+    const int nk = p.K / GEMM_KT, Kf = p.K / 32;
+    const uint32_t lbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+
+    // Per-lane source of each DMA load of this wave (stage 0) and the stride
+    // per stage. Fragment f = (row block, k-step) of A, chunk c of B. Waves
+    // with fewer fragments than loads repeat one (same bytes, same place).
+    const uint16_t* asrc[LA];
+    uint32_t adst[LA];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+        const int f = (wave * LA + i) % AF, rb = f / KS, ks = f % KS;
+        if (p.a_frag) {
+            // A-fragment order of <= 64 rows: fragment (k-step, row block) is 1 KiB
+            const int rbc = min(rb + m0 / 16, 3);
+            asrc[i] = p.A + ((size_t)(ks * 4 + rbc) * 64 + lane) * 8;
+        } else {
+            // rows past M read row M-1; their results are never stored
+            const int row = min(m0 + rb * 16 + (lane & 15), p.M - 1);
+            asrc[i] = p.A + (size_t)row * p.lda + ks * 32 + 8 * (lane >> 4);
+        }
+        adst[i] = (uint32_t)f * 1024;
+    }
+    const size_t astride = p.a_frag ? (size_t)KS * 4 * 512 : (size_t)GEMM_KT;
+    const uint8_t* bsrc[LB];
+    uint32_t bdst[LB];
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+        const int c = (wave * LB + i) % BCH;
+        if constexpr (W8) {
+            // one chunk = the 2 k-steps (512 bytes each) of one 16-column tile
+            bsrc[i] = (const uint8_t*)p.W + ((size_t)(n0 / 16 + c) * Kf) * 512 + lane * 16;
+        } else {
+            const int fn = c / KS, ks = c % KS;
+            bsrc[i] = (const uint8_t*)p.W + ((size_t)(n0 / 16 + fn) * Kf + ks) * 1024 + lane * 16;
+        }
+        bdst[i] = (uint32_t)(AF * 1024 + c * 1024);
+    }
+    constexpr size_t bstride = (size_t)KS * (W8 ? 512 : 1024);
+    // Stage kt into ring slot kt % S. Past the last stage the loads repeat it
+    // (into a slot no later stage uses), so every wave always has the same
+    // number of loads in flight and the waits are constants.
+    auto issue = [&](int kt_raw) {
+        const uint32_t sb = lbase + (uint32_t)((kt_raw % S) * STAGE);
+        const int kt = min(kt_raw, nk - 1);
+#pragma unroll
+        for (int i = 0; i < LA; ++i) gemm_dma16(asrc[i] + kt * astride, sb + adst[i]);
+#pragma unroll
+        for (int i = 0; i < LB; ++i) gemm_dma16(bsrc[i] + kt * bstride, sb + bdst[i]);
+    };
 
     f32x4 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-    u32x4 ra[1][A_CH], rb[1][B_CH];
-    // Branch-free loads (rows past M read row M-1 and are zeroed by a select;
-    // the A layout is a uniform choice), so the compiler can count the
-    // loads in flight instead of draining them at divergent joins.
-    auto load_tile = [&](int kt, u32x4 (&sa)[A_CH], u32x4 (&sb)[B_CH]) {
-        const int k0 = kt * KT;
-        if (p.a_frag) {
+    // fragments of k-step ks + 1 are read while k-step ks is multiplied
+    bf16x8 fa[2][FM], fb[2][FN];
+    auto read_frags = [&](int buf, const uint8_t* st, int ks) {
 #pragma unroll
-            for (int i = 0; i < A_CH; ++i) {
-                const int c = tid + i * NTHR, row = c / (KT / 8), c8 = c % (KT / 8), grow = m0 + row;
-                const u32x4 v = *(const u32x4*)(p.A + act_index(min(grow, p.M - 1), k0 + c8 * 8, p.lda, 1));
-                sa[i] = grow < p.M ? v : (u32x4){0u, 0u, 0u, 0u};
-            }
-        } else {
+        for (int fm = 0; fm < FM; ++fm)
+            fa[buf][fm] = *(const bf16x8*)(st + ((wm * FM + fm) * KS + ks) * 1024 + lane * 16);
 #pragma unroll
-            for (int i = 0; i < A_CH; ++i) {
-                const int c = tid + i * NTHR, row = c / (KT / 8), c8 = c % (KT / 8), grow = m0 + row;
-                const u32x4 v = *(const u32x4*)(p.A + (size_t)min(grow, p.M - 1) * p.lda + k0 + c8 * 8);
-                sa[i] = grow < p.M ? v : (u32x4){0u, 0u, 0u, 0u};
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-            const int c = tid + i * NTHR;
-            if (B_THREADS % NTHR == 0 || c < B_THREADS) {
-                const int byte = c * 16;
-                const int frag = byte / WFRAG_BYTES, within = byte % WFRAG_BYTES;
-                const int fn = frag / (KT / 32), fk = frag % (KT / 32);
-                const size_t g = ((size_t)(n0 / 16 + fn) * Kf + (k0 / 32 + fk)) * WFRAG_BYTES + within;
-                sb[i] = *(const u32x4*)((const uint8_t*)p.W + g);
-            }
+        for (int fn = 0; fn < FN; ++fn) {
+            const int frag = (wn * FN + fn) * KS + ks;
+            if constexpr (W8) fb[buf][fn] = e4m3x8_to_bf16x8(*(const u32x2*)(st + AF * 1024 + frag * 512 + lane * 8));
+            else fb[buf][fn] = *(const bf16x8*)(st + AF * 1024 + frag * 1024 + lane * 16);
         }
     };
-    auto store_tile = [&](int buf, const u32x4 (&sa)[A_CH], const u32x4 (&sb)[B_CH]) {
+    auto multiply = [&](int buf) {
 #pragma unroll
-        for (int i = 0; i < A_CH; ++i) {
-            int c = tid + i * NTHR;
-            int row = c / (KT / 8), c8 = c % (KT / 8);
-            *(u32x4*)(&As[buf][row][c8 * 8]) = sa[i];
-        }
+        for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-        for (int i = 0; i < B_CH; ++i) {
-            const int c = tid + i * NTHR;
-            if (B_THREADS % NTHR == 0 || c < B_THREADS) *(u32x4*)(&Bs[buf][c * 16]) = sb[i];
-        }
-    };
-    auto compute = [&](int buf) {
-#pragma unroll
-        for (int ks = 0; ks < KT / 32; ++ks) {
-            bf16x8 af[FM], bfr[FN];
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                int row = wm * WM + fm * 16 + (lane & 15);
-                af[fm] = *(const bf16x8*)(&As[buf][row][ks * 32 + 8 * (lane >> 4)]);
-            }
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                int frag = (wn * FN + fn) * (KT / 32) + ks;
-                if constexpr (W8) {
-                    u32x2 w = *(const u32x2*)(&Bs[buf][frag * 512 + lane * 8]);
-                    bfr[fn] = e4m3x8_to_bf16x8(w);
-                } else {
-                    bfr[fn] = *(const bf16x8*)(&Bs[buf][frag * 1024 + lane * 16]);
-                }
-            }
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_16x16x32(af[fm], bfr[fn], acc[fm][fn]);
-        }
+            for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_16x16x32(fa[buf][fm], fb[buf][fn], acc[fm][fn]);
     };
 
-    // k-tile kt+1 is loaded into registers while k-tile kt is multiplied
-    // from LDS, then written to the other LDS buffer.
-    load_tile(0, ra[0], rb[0]);
-    store_tile(0, ra[0], rb[0]);
+#pragma unroll
+    for (int s = 0; s < S; ++s) issue(s);
+    gemm_vm_wait<(S - 1) * LPW>();
     __syncthreads();
+    read_frags(0, lds, 0);
     for (int kt = 0; kt < nk; ++kt) {
-        if (kt + 1 < nk) load_tile(kt + 1, ra[0], rb[0]);
-        compute(kt & 1);
-        if (kt + 1 < nk) store_tile((kt + 1) & 1, ra[0], rb[0]);
-        __syncthreads();
+        const uint8_t* st = lds + (kt % S) * STAGE;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) {
+                read_frags((ks + 1) & 1, st, ks + 1);
+            } else {
+                // stage kt+1 landed (this wave's loads), then every wave's
+                // loads landed and every wave is done reading stage kt
+                gemm_vm_wait<(S - 2) * LPW>();
+                __syncthreads();
+                issue(kt + S);
+                read_frags(0, lds + ((kt + 1) % S) * STAGE, 0);
+            }
+            // keep the fragment reads ahead of the multiplies they overlap
+            __builtin_amdgcn_sched_barrier(0);
+            multiply(ks & 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
+    gemm_vm_wait<0>();  // the repeated tail loads land before the LDS is reused
+    __syncthreads();    // every wave is done with the ring
 
+    // Epilogue through LDS, 64 tile rows per pass: the waves holding those
+    // rows write their accumulators (times the E4M3 row scales) as fp32 rows,
+    // then all threads apply the epilogue to 16 consecutive columns each, so
+    // that global reads and writes are 16-byte vectors.
+    constexpr int CLD = NT + 16;   // row pitch in floats: 4-row groups of a fragment land on distinct banks
+    constexpr int PPW = FM / 4;    // passes per wave row
+    constexpr int UPR = NT / 16;   // 16-column units per row
+    static_assert(FM % 4 == 0 && 64 * CLD * 4 <= S * STAGE, "epilogue pass does not fit the ring");
+    float* ct = (float*)lds;
     float wsc[FN];
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) wsc[fn] = W8 ? p.wscale[n0 + wn * WN + fn * 16 + (lane & 15)] : 1.0f;
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int pass = 0; pass < MT / 64; ++pass) {
+        if (wm == pass / PPW) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = m0 + wm * WM + fm * 16 + 4 * (lane >> 4) + r;
-            // per-row work (the RoPE position) once, not per column
-            const int rpos = EPI == EPI_QKV_ROPE && row < p.M ? qkv_row_pos(p, row) : 0;
+            for (int f = 0; f < 4; ++f)
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                const int col = n0 + wn * WN + fn * 16 + (lane & 15);
-                float v = acc[fm][fn][r] * wsc[fn];
-                float partner = __shfl_xor(v, 1, 64);
-                epilogue_store<EPI>(p, row, col, v, partner, 0, rpos);
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        ct[(f * 16 + 4 * (lane >> 4) + r) * CLD + wn * WN + fn * 16 + (lane & 15)] =
+                            acc[(pass % PPW) * 4 + f][fn][r] * wsc[fn];
+        }
+        __syncthreads();
+        for (int u = tid; u < 64 * UPR; u += 64 * GEMM_WAVES) {
+            const int lr = u / UPR, uc = u % UPR;
+            const int row = m0 + pass * 64 + lr;
+            if (row < p.M) {
+                float v[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 t = *(const f32x4*)(ct + lr * CLD + uc * 16 + 4 * q);
+                    v[4 * q] = t[0]; v[4 * q + 1] = t[1]; v[4 * q + 2] = t[2]; v[4 * q + 3] = t[3];
+                }
+                epilogue16<EPI>(p, row, n0 + uc * 16, v);
             }
         }
+        __syncthreads();
+    }
 }
 
 // ---------------------------------------------------------------------------
