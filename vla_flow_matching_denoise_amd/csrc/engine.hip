@@ -408,7 +408,12 @@ int launch_gemm(vla_ctx* c, const Linear& lin, const GemmCfg& cfg, bool w8, int 
         set_err("tiled GEMM needs K %% %d == 0 (K = %d)", GEMM_KT, lin.K);
         return VLA_ERR_SHAPE;
     }
-    dim3 grid((lin.N / cfg.NT) * ((p.M + cfg.MT - 1) / cfg.MT));  // tile from the linear id
+    // row tiles over the XCDs when A is the larger operand and the padded
+    // grid is one round of tiles (see gemm_kernel; more rounds would leave
+    // the XCD with an extra row tile behind)
+    const int ntm = (p.M + cfg.MT - 1) / cfg.MT;
+    p.tile_map = p.M > lin.N && ntm >= 8 && (ntm + 7) / 8 * 8 * (lin.N / cfg.NT) <= c->ncu ? 1 : 0;
+    dim3 grid((lin.N / cfg.NT) * (p.tile_map ? (ntm + 7) / 8 * 8 : ntm));  // tile from the linear id
     if (cfg.MT == 256 && cfg.NT == 256) return w8 ? launch_tiled_t<256, 256, true>(epi, p, grid, c->stream)
                                                   : launch_tiled_t<256, 256, false>(epi, p, grid, c->stream);
     if (cfg.MT == 128 && cfg.NT == 128) return w8 ? launch_tiled_t<128, 128, true>(epi, p, grid, c->stream)

@@ -166,6 +166,7 @@ struct GemmParams {
     int lda;
     int a_frag;          // A given in A-fragment order (required by the skinny kernel)
     int afrag;           // act (SwiGLU output) written in A-fragment order
+    int tile_map;        // tiled kernel: 1 = row tiles split over the XCDs (grid padded to 8 row-tile groups)
     const void* W;       // packed fragments
     const float* wscale; // per packed row (E4M3), else null
     int M, N, K;
@@ -414,13 +415,16 @@ __global__ __launch_bounds__(512) void skinny_gemm_kernel(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Tiled GEMM for larger M: an MT x NT tile per workgroup of 8 waves (2 along
-// M, 4 along N). K advances in 64-deep stages through a ring of GEMM_STAGES
-// LDS buffers that global->LDS DMA loads fill directly (no register staging):
-// stage kt+S is requested as soon as every wave is done with stage kt, so S-1
-// stages are in flight while one is multiplied. Both operands sit in LDS as
-// 1 KiB MFMA fragments (lane i's 16 bytes at offset 16 i), so the DMA writes
-// and the fragment reads are free of bank conflicts.
+// Tiled GEMM for larger M: an MT x NT tile per workgroup of 8 waves. K
+// advances in 64-deep stages through a ring of LDS buffers that global->LDS
+// DMA loads fill directly (no register staging): stage kt+S is requested as
+// soon as every wave is done with stage kt, so S-1 stages are in flight
+// while one is multiplied. Both operands sit in LDS as 1 KiB MFMA fragments
+// (lane i's 16 bytes at offset 16 i), so the DMA writes and the fragment
+// reads are free of bank conflicts. The 8 waves form a 2 x 4 grid of
+// MT/2 x NT/4 wave tiles. (Two k-groups of 2 x 2 waves with 64 x 64 wave
+// tiles, for half the LDS bytes per MFMA on 128-row tiles, measured no
+// faster: the 128-row tiles are not bound by LDS bandwidth.)
 // ---------------------------------------------------------------------------
 constexpr int GEMM_WAVES = 8, GEMM_KT = 64, GEMM_KS = GEMM_KT / 32;
 
@@ -464,13 +468,20 @@ void gemm_kernel(GemmParams p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WGN, wn = wave % WGN;
-    // Tile of this workgroup. Consecutive workgroups run on consecutive XCDs,
-    // so when the N-tiles split evenly over the 8 XCDs, workgroup w takes an
-    // N-tile of XCD group w % 8 for every M-tile: each XCD's L2 then holds one
-    // eighth of the weights and reuses each A tile across its N-tiles.
+    // Tile of this workgroup. Consecutive workgroups run on consecutive XCDs
+    // (workgroup w on XCD w % 8), and each XCD has its own L2, so the larger
+    // operand is split over the XCDs: with tile_map 1, XCD x takes the row
+    // tiles x, x + 8, ... (every column tile of each), so each XCD reads one
+    // eighth of A; otherwise, when the column tiles split evenly over the
+    // XCDs, XCD x takes one eighth of them (and of W) for every row tile.
     const int ntn = p.N / NT;
     int mt_i, nt_i;
-    if (ntn % 8 == 0) {
+    if (p.tile_map == 1) {
+        const int w = blockIdx.x, s = w >> 3;
+        mt_i = (w & 7) + 8 * (s / ntn);
+        nt_i = s % ntn;
+        if (mt_i * MT >= p.M) return;  // padding of the last group of 8 row tiles
+    } else if (ntn % 8 == 0) {
         const int w = blockIdx.x, per = ntn / 8, s = w >> 3;
         mt_i = s / per;
         nt_i = (w & 7) * per + s % per;
@@ -586,7 +597,7 @@ void gemm_kernel(GemmParams p) {
     // rows write their accumulators (times the E4M3 row scales) as fp32 rows,
     // then all threads apply the epilogue to 16 consecutive columns each, so
     // that global reads and writes are 16-byte vectors.
-    constexpr int CLD = NT + 16;   // row pitch in floats: 4-row groups of a fragment land on distinct banks
+    constexpr int CLD = NT + 4;    // row pitch in floats: a fragment writes rows r, r+4, r+8, r+12 (16 lanes each), 16 banks apart
     constexpr int PPW = FM / 4;    // passes per wave row
     constexpr int UPR = NT / 16;   // 16-column units per row
     static_assert(FM % 4 == 0 && 64 * CLD * 4 <= S * STAGE, "epilogue pass does not fit the ring");
