@@ -53,15 +53,28 @@ VLA_DEV float wave_sum(float v) {
     return v;
 }
 
-// Sum / max over the 16 lanes that share l/16 (one MFMA output row group).
+// v of another lane of the same 16-lane row, by a DPP lane permutation (a
+// VALU operand modifier; all 64 lanes must be active, as around an MFMA).
+template <int CTRL>
+VLA_DEV float row_dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sum / max over the 16 lanes that share l/16 (one MFMA output row group),
+// as a butterfly: lane ^ 1 and lane ^ 2 (quad permutations), then lane i
+// with 7 - i within each 8 (half-row mirror), then i with 15 - i (row
+// mirror). Every lane ends with the reduction of all 16.
 VLA_DEV float group16_sum(float v) {
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    v += row_dpp<0xB1>(v);
+    v += row_dpp<0x4E>(v);
+    v += row_dpp<0x141>(v);
+    v += row_dpp<0x140>(v);
     return v;
 }
 VLA_DEV float group16_max(float v) {
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    v = fmaxf(v, row_dpp<0xB1>(v));
+    v = fmaxf(v, row_dpp<0x4E>(v));
+    v = fmaxf(v, row_dpp<0x141>(v));
+    v = fmaxf(v, row_dpp<0x140>(v));
     return v;
 }
 
