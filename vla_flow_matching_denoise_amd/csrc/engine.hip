@@ -483,10 +483,18 @@ int launch_attention(vla_ctx* c, int l, const uint16_t* q, uint16_t* o, int ofra
         if (d.head_dim == 128) VLA_LAUNCH((attn_kernel<128, 8>), ag, dim3(512), 0, c->stream, ap);
         else VLA_LAUNCH((attn_kernel<64, 8>), ag, dim3(512), 0, c->stream, ap);
     } else {
-        // many rows: 64 query rows per workgroup, K/V staged once through LDS
-        const dim3 rg((G * d.horizon + 63) / 64, d.n_kv_heads, d.batch);
-        if (d.head_dim == 128) VLA_LAUNCH((attn_rows_kernel<128>), rg, dim3(256), 0, c->stream, ap);
-        else VLA_LAUNCH((attn_rows_kernel<64>), rg, dim3(256), 0, c->stream, ap);
+        // many rows: 64 or 128 query rows per workgroup (128 when a KV group
+        // has more than 64 rows), K/V staged once through LDS
+        const int rows = G * d.horizon;
+        if (rows > 64) {
+            const dim3 rg((rows + 127) / 128, d.n_kv_heads, d.batch);
+            if (d.head_dim == 128) VLA_LAUNCH((attn_rows_kernel<128, 2>), rg, dim3(256), 0, c->stream, ap);
+            else VLA_LAUNCH((attn_rows_kernel<64, 2>), rg, dim3(256), 0, c->stream, ap);
+        } else {
+            const dim3 rg((rows + 63) / 64, d.n_kv_heads, d.batch);
+            if (d.head_dim == 128) VLA_LAUNCH((attn_rows_kernel<128, 1>), rg, dim3(256), 0, c->stream, ap);
+            else VLA_LAUNCH((attn_rows_kernel<64, 1>), rg, dim3(256), 0, c->stream, ap);
+        }
     }
     HIPC(hipGetLastError());
     return VLA_OK;

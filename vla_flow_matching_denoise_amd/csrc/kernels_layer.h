@@ -430,13 +430,13 @@ constexpr int GEMM_WAVES = 8, GEMM_KT = 64, GEMM_KS = GEMM_KT / 32;
 
 // 16 bytes per lane from global memory into LDS: the 64 lanes fill the
 // 1 KiB at byte offset `lds` (lane i at lds + 16 i). No register receives
-// data; the kernel waits for these loads itself (gemm_vm_wait) before the
+// data; the kernel waits for these loads itself (vm_wait) before the
 // barrier that publishes a stage, and before it exits.
-VLA_DEV void gemm_dma16(const void* g, uint32_t lds) {
+VLA_DEV void lds_dma16(const void* g, uint32_t lds) {
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
 template <int N>
-VLA_DEV void gemm_vm_wait() {
+VLA_DEV void vm_wait() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
@@ -535,9 +535,9 @@ void gemm_kernel(GemmParams p) {
         const uint32_t sb = lbase + (uint32_t)((kt_raw % S) * STAGE);
         const int kt = min(kt_raw, nk - 1);
 #pragma unroll
-        for (int i = 0; i < LA; ++i) gemm_dma16(asrc[i] + kt * astride, sb + adst[i]);
+        for (int i = 0; i < LA; ++i) lds_dma16(asrc[i] + kt * astride, sb + adst[i]);
 #pragma unroll
-        for (int i = 0; i < LB; ++i) gemm_dma16(bsrc[i] + kt * bstride, sb + bdst[i]);
+        for (int i = 0; i < LB; ++i) lds_dma16(bsrc[i] + kt * bstride, sb + bdst[i]);
     };
 
     f32x4 acc[FM][FN];
@@ -567,7 +567,7 @@ void gemm_kernel(GemmParams p) {
 
 #pragma unroll
     for (int s = 0; s < S; ++s) issue(s);
-    gemm_vm_wait<(S - 1) * LPW>();
+    vm_wait<(S - 1) * LPW>();
     __syncthreads();
     read_frags(0, lds, 0);
     for (int kt = 0; kt < nk; ++kt) {
@@ -579,7 +579,7 @@ void gemm_kernel(GemmParams p) {
             } else {
                 // stage kt+1 landed (this wave's loads), then every wave's
                 // loads landed and every wave is done reading stage kt
-                gemm_vm_wait<(S - 2) * LPW>();
+                vm_wait<(S - 2) * LPW>();
                 __syncthreads();
                 issue(kt + S);
                 read_frags(0, lds + ((kt + 1) % S) * STAGE, 0);
@@ -590,7 +590,7 @@ void gemm_kernel(GemmParams p) {
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    gemm_vm_wait<0>();  // the repeated tail loads land before the LDS is reused
+    vm_wait<0>();  // the repeated tail loads land before the LDS is reused
     __syncthreads();    // every wave is done with the ring
 
     // Epilogue through LDS, 64 tile rows per pass: the waves holding those
@@ -804,14 +804,21 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
 
 // ---------------------------------------------------------------------------
 // The same attention for many query rows (large batches): a workgroup of four
-// waves takes 64 query rows of one (request, KV group), each wave owning 16 of
-// them over the whole key range, and every 32-key K/V block is staged once
-// per workgroup through LDS (double-buffered). K/V is then read from L2 once
-// per 64 query rows instead of once per 16, and the waves never merge.
+// waves takes 64 * RT query rows of one (request, KV group), each wave owning
+// RT 16-row tiles over the whole key range, and every 32-key K/V block is
+// staged once per workgroup through LDS (double-buffered). K/V is then read
+// from L2 once per 64 * RT query rows, each K or V fragment read from LDS
+// serves RT tiles, and the waves never merge.
+// The running maximum moves only when a block's maximum exceeds it by more
+// than ATT_SLACK (log2 units), so most blocks skip the rescale of the
+// accumulators and its exponentials; the unnormalised weights stay below
+// 2^ATT_SLACK, well inside bf16 and fp32 range.
 // LDS: K rows padded by 16 bytes so the 16 lanes that read one fragment hit
 // distinct banks; V kept in PV-operand order.
 // ---------------------------------------------------------------------------
-template <int DH>
+constexpr float ATT_SLACK = 8.0f;
+
+template <int DH, int RT>
 __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
     constexpr int KROW = DH * 2 + 16;            // padded K row in LDS, bytes
     constexpr int KCH = DH * 2 / 16;             // 16-byte chunks per key row
@@ -820,40 +827,46 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
     static_assert(CH >= 1, "head too small");
     __shared__ __attribute__((aligned(16))) uint8_t Ks[2][32 * KROW];
     __shared__ __attribute__((aligned(16))) uint8_t Vs[2][BLK];
-    __shared__ __attribute__((aligned(16))) uint16_t Ps[4][16][40];
+    __shared__ __attribute__((aligned(16))) uint16_t Ps[4][RT * 16][40];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int G = p.nq / p.kv.nkv;
     const int rows_total = G * p.T;
     const int g = blockIdx.y, b = blockIdx.z;
-    const int r0 = blockIdx.x * 64 + wave * 16;
+    const int r0 = blockIdx.x * 64 * RT + wave * 16 * RT;
     const int nblk = p.kv.S_pad / 32;
     const size_t base = p.kv.base(b, p.layer, g);
     const uint8_t* K = (const uint8_t*)(p.kcat + base);
     const uint8_t* V = (const uint8_t*)(p.vcat + base);
     const int pvb = p.pvalid[b];  // prefix keys past this are padding
 
-    bf16x8 qf[DH / 32];
+    bf16x8 qf[RT][DH / 32];
     {
         const uint16_t* qg = p.q + (size_t)(b * p.nq + g * G) * p.T * DH;
-        const int row = r0 + (lane & 15);
-        const int rowc = min(row, rows_total - 1);
 #pragma unroll
-        for (int ks = 0; ks < DH / 32; ++ks) {
-            const bf16x8 v = *(const bf16x8*)(qg + (size_t)rowc * DH + ks * 32 + 8 * (lane >> 4));
-            qf[ks] = row < rows_total ? v : (bf16x8){};
+        for (int t = 0; t < RT; ++t) {
+            const int row = r0 + t * 16 + (lane & 15);
+            const int rowc = min(row, rows_total - 1);
+#pragma unroll
+            for (int ks = 0; ks < DH / 32; ++ks) {
+                const bf16x8 v = *(const bf16x8*)(qg + (size_t)rowc * DH + ks * 32 + 8 * (lane >> 4));
+                qf[t][ks] = row < rows_total ? v : (bf16x8){};
+            }
         }
     }
 
-    float mrow[4], lrow[4];
-    f32x4 oacc[DH / 16];
-#pragma unroll
+    float mrow[RT][4], lrow[RT][4];
+    f32x4 oacc[RT][DH / 16];
     // running max starts finite: a block whose keys are all masked (padding)
     // then leaves m finite and adds weight 0, where -inf would give
     // exp2(-inf - -inf) = NaN
-    for (int r = 0; r < 4; ++r) { mrow[r] = -1e30f; lrow[r] = 0.f; }
 #pragma unroll
-    for (int dn = 0; dn < DH / 16; ++dn) oacc[dn] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < RT; ++t) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { mrow[t][r] = -1e30f; lrow[t][r] = 0.f; }
+#pragma unroll
+        for (int dn = 0; dn < DH / 16; ++dn) oacc[t][dn] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
 
     u32x4 rk[CH], rv[CH];
     auto gload = [&](int kb) {
@@ -879,49 +892,70 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
     for (int kb = 0; kb < nblk; ++kb) {
         const int buf = kb & 1;
         if (kb + 1 < nblk) gload(kb + 1);   // next block in flight during this one
-        f32x4 s[2];
+        f32x4 s[RT][2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
-            s[sb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < RT; ++t) s[t][sb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < DH / 32; ++ks) {
                 const bf16x8 kf =
                     *(const bf16x8*)(&Ks[buf][(sb * 16 + (lane & 15)) * KROW + ks * 64 + 16 * (lane >> 4)]);
-                s[sb] = mfma_16x16x32(qf[ks], kf, s[sb]);
+#pragma unroll
+                for (int t = 0; t < RT; ++t) s[t][sb] = mfma_16x16x32(qf[t][ks], kf, s[t][sb]);
             }
         }
         // every key of the block real (a uniform test): no per-key mask
         const bool whole = (kb * 32 + 32 <= pvb) || (kb * 32 >= p.P && kb * 32 + 32 <= p.S);
-        float alpha[4];
+        float s0[RT][4], s1[RT][4], mx[RT][4];
+        bool grow = false;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float s0 = s[0][r] * p.scale_log2, s1 = s[1][r] * p.scale_log2;
-            if (!whole) {  // a block with padded prefix keys or keys past P + T
-                const int key0 = kb * 32 + (lane & 15), key1 = key0 + 16;
-                if (key0 >= p.S || (key0 < p.P && key0 >= pvb)) s0 = -INFINITY;
-                if (key1 >= p.S || (key1 < p.P && key1 >= pvb)) s1 = -INFINITY;
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                s0[t][r] = s[t][0][r] * p.scale_log2;
+                s1[t][r] = s[t][1][r] * p.scale_log2;
+                if (!whole) {  // a block with padded prefix keys or keys past P + T
+                    const int key0 = kb * 32 + (lane & 15), key1 = key0 + 16;
+                    if (key0 >= p.S || (key0 < p.P && key0 >= pvb)) s0[t][r] = -INFINITY;
+                    if (key1 >= p.S || (key1 < p.P && key1 >= pvb)) s1[t][r] = -INFINITY;
+                }
+                mx[t][r] = group16_max(fmaxf(s0[t][r], s1[t][r]));
+                grow |= mx[t][r] > mrow[t][r] + ATT_SLACK;
             }
-            const float mx = group16_max(fmaxf(s0, s1));
-            const float mnew = fmaxf(mrow[r], mx);
-            alpha[r] = attn_exp2(mrow[r] - mnew);
-            const float p0 = attn_exp2(s0 - mnew), p1 = attn_exp2(s1 - mnew);
-            lrow[r] = lrow[r] * alpha[r] + group16_sum(p0 + p1);
-            mrow[r] = mnew;
-            Ps[wave][4 * (lane >> 4) + r][lane & 15] = f32_to_bf16(p0);
-            Ps[wave][4 * (lane >> 4) + r][16 + (lane & 15)] = f32_to_bf16(p1);
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // uniform: move the maxima, rescale
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float mnew = fmaxf(mrow[t][r], mx[t][r]);
+                    const float alpha = attn_exp2(mrow[t][r] - mnew);
+                    lrow[t][r] *= alpha;
+                    mrow[t][r] = mnew;
+#pragma unroll
+                    for (int dn = 0; dn < DH / 16; ++dn) oacc[t][dn][r] *= alpha;
+                }
         }
 #pragma unroll
-        for (int dn = 0; dn < DH / 16; ++dn)
+        for (int t = 0; t < RT; ++t)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) oacc[dn][r] *= alpha[r];
-        // the P tile is private to this wave: LDS ops of one wave complete in order
+            for (int r = 0; r < 4; ++r) {
+                const float p0 = attn_exp2(s0[t][r] - mrow[t][r]), p1 = attn_exp2(s1[t][r] - mrow[t][r]);
+                lrow[t][r] += group16_sum(p0 + p1);
+                Ps[wave][t * 16 + 4 * (lane >> 4) + r][lane & 15] = f32_to_bf16(p0);
+                Ps[wave][t * 16 + 4 * (lane >> 4) + r][16 + (lane & 15)] = f32_to_bf16(p1);
+            }
+        // the P tiles are private to this wave: LDS ops of one wave complete in order
         __builtin_amdgcn_s_waitcnt(0xc07f);
         __builtin_amdgcn_wave_barrier();
-        const bf16x8 pa = *(const bf16x8*)(&Ps[wave][lane & 15][8 * (lane >> 4)]);
+        bf16x8 pa[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t) pa[t] = *(const bf16x8*)(&Ps[wave][t * 16 + (lane & 15)][8 * (lane >> 4)]);
 #pragma unroll
         for (int dn = 0; dn < DH / 16; ++dn) {
             const bf16x8 vf = *(const bf16x8*)(&Vs[buf][(dn * 64 + lane) * 16]);
-            oacc[dn] = mfma_16x16x32(pa, vf, oacc[dn]);
+#pragma unroll
+            for (int t = 0; t < RT; ++t) oacc[t][dn] = mfma_16x16x32(pa[t], vf, oacc[t][dn]);
         }
         __builtin_amdgcn_wave_barrier();
         if (kb + 1 < nblk) sstore(buf ^ 1);  // that buffer was last read before the previous barrier
@@ -929,15 +963,17 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
     }
 
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int row = r0 + 4 * (lane >> 4) + r;
-        if (row < rows_total) {
-            const float inv = 1.0f / lrow[r];
-            const int hh = row / p.T, i = row % p.T;
+    for (int t = 0; t < RT; ++t)
 #pragma unroll
-            for (int dn = 0; dn < DH / 16; ++dn)
-                p.o[act_index(b * p.T + i, (g * G + hh) * DH + dn * 16 + (lane & 15), p.nq * DH, p.ofrag)] =
-                    f32_to_bf16(oacc[dn][r] * inv);
+        for (int r = 0; r < 4; ++r) {
+            const int row = r0 + t * 16 + 4 * (lane >> 4) + r;
+            if (row < rows_total) {
+                const float inv = 1.0f / lrow[t][r];
+                const int hh = row / p.T, i = row % p.T;
+#pragma unroll
+                for (int dn = 0; dn < DH / 16; ++dn)
+                    p.o[act_index(b * p.T + i, (g * G + hh) * DH + dn * 16 + (lane & 15), p.nq * DH, p.ofrag)] =
+                        f32_to_bf16(oacc[t][dn][r] * inv);
+            }
         }
-    }
 }
