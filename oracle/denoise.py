@@ -47,6 +47,7 @@ __all__ = [
     "sinusoidal_embedding", "silu", "time_condition", "modulation",
     "rms_normalize", "ada_rms_norm", "rope_rotate_half", "softmax",
     "gqa_attention", "expert_layer", "velocity", "denoise", "denoise_varlen", "cosine",
+    "quantize_e4m3fn", "quantize_per_token_e4m3",
 ]
 
 
@@ -106,6 +107,44 @@ def decode_e4m3fn(codes: np.ndarray, dtype=np.float64) -> np.ndarray:
     val = sign * np.where(e == 0, sub, normal)
     val = np.where((e == 15) & ((c & 7) == 7), np.nan, val)
     return val.astype(dtype)
+
+
+def _e4m3fn_table() -> np.ndarray:
+    """The 127 finite non-negative E4M3FN values, indexed by code 0x00..0x7E
+    (increasing with the code)."""
+    return decode_e4m3fn(np.arange(0x7F, dtype=np.uint8))
+
+
+def quantize_e4m3fn(x: np.ndarray) -> np.ndarray:
+    """Nearest E4M3FN value of each element (the format of ``decode_e4m3fn``),
+    as floats.  Ties go to the code with an even mantissa; magnitudes above
+    448 saturate to 448 (no infinities in the format); NaN stays NaN.  Written
+    as a search over the decoded value table, i.e. straight from the format's
+    definition.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    tab = _e4m3fn_table()
+    mag = np.minimum(np.abs(x), tab[-1])
+    hi = np.clip(np.searchsorted(tab, mag, side="left"), 0, tab.size - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = mag - tab[lo], tab[hi] - mag
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    q = np.where(pick_hi, tab[hi], tab[lo])
+    return np.where(np.isnan(x), np.nan, np.copysign(q, x))
+
+
+def quantize_per_token_e4m3(a: np.ndarray) -> np.ndarray:
+    """Per-token FP8 activations ("LingBot-VLA v2 Examples", section
+    "Configuration / Online Quantization": the tf-kernel-fp8 profile
+    quantizes activations per token and weights per output channel).  The
+    page gives no formula; the reading taken: each row r of a GEMM input
+    [rows, K] gets the scale s_r = max_k |a[r, k]| / 448 (1 for an all-zero
+    row) and the GEMM sees q(a[r, k] / s_r) * s_r, q = ``quantize_e4m3fn``.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    amax = np.max(np.abs(a), axis=-1, keepdims=True)
+    s = np.where(amax > 0, amax / 448.0, 1.0)
+    return quantize_e4m3fn(a / s) * s
 
 
 def _linear(raw: dict, name: str, l: Optional[int], dtype):
@@ -234,16 +273,20 @@ def gqa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 def expert_layer(h: np.ndarray, W: dict, l: int, mod, prefix_k_l: np.ndarray,
-                 prefix_v_l: np.ndarray, dims: ExpertDims) -> np.ndarray:
+                 prefix_v_l: np.ndarray, dims: ExpertDims, act_quant: bool = False) -> np.ndarray:
     """One expert block on the chunk's hidden rows ``h`` [T, H].
 
     ``mod`` = (a1, b1, g1, a2, b2, g2); ``prefix_k_l`` / ``prefix_v_l`` are this
-    layer's cached prefix keys/values [P, n_kv, d_h], used as given.
+    layer's cached prefix keys/values [P, n_kv, d_h], used as given.  With
+    ``act_quant`` the input of each block linear (y before QKV, o before O,
+    y before gate_up, the SwiGLU output before down) is replaced by its
+    per-token FP8 version (``quantize_per_token_e4m3``).
     """
+    aq = quantize_per_token_e4m3 if act_quant else (lambda z: z)
     a1, b1, g1, a2, b2, g2 = mod
     T = h.shape[0]
     nq, nkv, dh = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
-    y = ada_rms_norm(h, a1, b1, dims.rms_eps)
+    y = aq(ada_rms_norm(h, a1, b1, dims.rms_eps))
     q = (y @ W["wq"][l].T).reshape(T, nq, dh).transpose(1, 0, 2)
     k = (y @ W["wk"][l].T).reshape(T, nkv, dh).transpose(1, 0, 2)
     v = (y @ W["wv"][l].T).reshape(T, nkv, dh).transpose(1, 0, 2)
@@ -254,15 +297,15 @@ def expert_layer(h: np.ndarray, W: dict, l: int, mod, prefix_k_l: np.ndarray,
     pv = prefix_v_l.astype(h.dtype).transpose(1, 0, 2)
     K = np.concatenate([pk, k], axis=1)
     V = np.concatenate([pv, v], axis=1)
-    o = gqa_attention(q, K, V).transpose(1, 0, 2).reshape(T, nq * dh)
+    o = aq(gqa_attention(q, K, V).transpose(1, 0, 2).reshape(T, nq * dh))
     h = h + g1 * (o @ W["wo"][l].T)
-    y = ada_rms_norm(h, a2, b2, dims.rms_eps)
-    a = silu(y @ W["wg"][l].T) * (y @ W["wu"][l].T)
+    y = aq(ada_rms_norm(h, a2, b2, dims.rms_eps))
+    a = aq(silu(y @ W["wg"][l].T) * (y @ W["wu"][l].T))
     return h + g2 * (a @ W["wd"][l].T)
 
 
 def velocity(x: np.ndarray, t: float, W: dict, prefix_k_b: np.ndarray, prefix_v_b: np.ndarray,
-             dims: ExpertDims) -> np.ndarray:
+             dims: ExpertDims, act_quant: bool = False) -> np.ndarray:
     """Velocity v(x, t) of one request: x [T, A] -> [T, A].
 
     ``prefix_k_b`` / ``prefix_v_b``: this request's cache [L, P, n_kv, d_h].
@@ -271,14 +314,14 @@ def velocity(x: np.ndarray, t: float, W: dict, prefix_k_b: np.ndarray, prefix_v_
     h = x @ W["in_w"].T + W["in_b"]
     for l in range(dims.n_layers):
         mod = modulation(c, W["mod_w"][l], W["mod_b"][l], 6)
-        h = expert_layer(h, W, l, mod, prefix_k_b[l], prefix_v_b[l], dims)
+        h = expert_layer(h, W, l, mod, prefix_k_b[l], prefix_v_b[l], dims, act_quant)
     af, bf = modulation(c, W["modf_w"], W["modf_b"], 2)
     y = ada_rms_norm(h, af, bf, dims.rms_eps)
     return y @ W["out_w"].T + W["out_b"]
 
 
 def denoise(W: dict, dims: ExpertDims, prefix_k: np.ndarray, prefix_v: np.ndarray,
-            noise: np.ndarray, t_schedule: np.ndarray) -> np.ndarray:
+            noise: np.ndarray, t_schedule: np.ndarray, act_quant: bool = False) -> np.ndarray:
     """Explicit-Euler integration of the learned velocity field.
 
     ``W``: decoded weights (``decode_weights``); ``prefix_k``/``prefix_v``:
@@ -286,6 +329,7 @@ def denoise(W: dict, dims: ExpertDims, prefix_k: np.ndarray, prefix_v: np.ndarra
     ``t_schedule``: [B, N+1] times t_0..t_N per request.  Requests are
     independent.  Each step evaluates the field at the left end point t_k and
     advances by dt_k = t_{k+1} - t_k.  Returns x_N [B, T, A] in W's dtype.
+    ``act_quant``: per-token FP8 inputs of the block linears (``expert_layer``).
     """
     dtype = W["in_w"].dtype
     B = noise.shape[0]
@@ -296,7 +340,7 @@ def denoise(W: dict, dims: ExpertDims, prefix_k: np.ndarray, prefix_v: np.ndarra
         ts = np.asarray(t_schedule[b], dtype=np.float64)
         for k in range(N):
             dt = dtype.type(ts[k + 1] - ts[k])
-            x = x + dt * velocity(x, ts[k], W, prefix_k[b], prefix_v[b], dims)
+            x = x + dt * velocity(x, ts[k], W, prefix_k[b], prefix_v[b], dims, act_quant)
         out[b] = x
     return out
 

@@ -503,3 +503,83 @@ def test_varlen_full_lengths_and_padding_invariance():
     assert np.array_equal(a[2], none[0])
     assert np.array_equal(oracle.denoise_varlen(W, d, pk, pv, x0, ts, [d.prefix_len, 3, -5]), a)
 
+
+
+# ---------------------------------------------------------------------------
+# Per-token FP8 activations (the batched E4M3 tier)
+# ---------------------------------------------------------------------------
+
+def _e4m3_values():
+    return oracle.decode_e4m3fn(np.arange(0x7F, dtype=np.uint8))
+
+
+def test_e4m3_encoder_matches_torch_cast():
+    """The E4M3FN encoder against torch's float8_e4m3fn cast (round to nearest
+    even) on random in-range values and on every midpoint between adjacent
+    representable values. Catches a wrong tie rule, exponent bias or
+    subnormal step."""
+    tab = _e4m3_values()
+    mids = (tab[:-1] + tab[1:]) / 2
+    mags = np.exp2(RNG.uniform(-12, np.log2(448.0), 4000))
+    x = np.concatenate([mids, -mids, mags * RNG.choice([-1.0, 1.0], mags.size), [0.0, -0.0]])
+    want = torch.tensor(x, dtype=torch.float64).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.quantize_e4m3fn(x), want)
+
+
+def test_e4m3_encoder_fixed_points_and_saturation():
+    tab = _e4m3_values()
+    np.testing.assert_array_equal(oracle.quantize_e4m3fn(tab), tab)
+    np.testing.assert_array_equal(oracle.quantize_e4m3fn(-tab), -tab)
+    np.testing.assert_array_equal(oracle.quantize_e4m3fn(np.array([1000.0, -500.0, 448.0, 464.0])),
+                                  [448.0, -448.0, 448.0, 448.0])
+    assert np.isnan(oracle.quantize_e4m3fn(np.array([np.nan]))[0])
+
+
+def test_per_token_quantization_properties():
+    """Scale = row max / 448: rows are independent, a power-of-two row scaling
+    commutes exactly, zero rows stay zero, each row's largest element is kept,
+    and the relative error of normal-range elements is at most half an ulp
+    (2^-4) of a 3-bit mantissa."""
+    a = RNG.standard_normal((7, 96)) * np.exp2(RNG.integers(-8, 8, (7, 1)))
+    a[3] = 0.0
+    q = oracle.quantize_per_token_e4m3(a)
+    np.testing.assert_array_equal(q, np.vstack([oracle.quantize_per_token_e4m3(r[None]) for r in a]))
+    np.testing.assert_array_equal(oracle.quantize_per_token_e4m3(a * 2.0 ** 5), q * 2.0 ** 5)
+    assert np.all(q[3] == 0.0)
+    for r in (0, 1, 2, 4, 5, 6):
+        j = np.argmax(np.abs(a[r]))
+        assert abs(q[r, j] - a[r, j]) <= 1e-12 * abs(a[r, j])
+        s = np.max(np.abs(a[r])) / 448.0
+        normal = np.abs(a[r]) >= s * 2.0 ** -6
+        assert np.all(np.abs(q[r] - a[r])[normal] <= 2.0 ** -4 * np.abs(a[r])[normal] * (1 + 1e-12))
+
+
+def test_act_quant_wiring_in_the_layer(monkeypatch):
+    """With act_quant the four block-linear inputs, and only they, go through
+    the per-token quantizer: y [T, H] before QKV, o [T, n_q d_h] before O,
+    y [T, H] before gate_up, the SwiGLU output [T, I] before down. Off by
+    default (the layer is then unchanged, bitwise)."""
+    d = _tiny_dims()
+    W = _tiny_weights(d)
+    T, H = d.horizon, d.hidden
+    h = RNG.standard_normal((T, H))
+    mod = [RNG.standard_normal(H) * 0.2 for _ in range(6)]
+    pk = RNG.standard_normal((d.prefix_len, d.n_kv_heads, d.head_dim))
+    pv = RNG.standard_normal((d.prefix_len, d.n_kv_heads, d.head_dim))
+    base = oracle.expert_layer(h, W, 0, mod, pk, pv, d)
+    shapes = []
+    real = oracle.quantize_per_token_e4m3
+
+    def counting(z):
+        shapes.append(z.shape)
+        return real(z)
+
+    import sys
+    od = sys.modules["oracle.denoise"]   # the module (the package re-exports its function `denoise`)
+    monkeypatch.setattr(od, "quantize_per_token_e4m3", counting)
+    np.testing.assert_array_equal(od.expert_layer(h, W, 0, mod, pk, pv, d), base)
+    assert shapes == []
+    out = od.expert_layer(h, W, 0, mod, pk, pv, d, act_quant=True)
+    assert shapes == [(T, H), (T, d.n_q_heads * d.head_dim), (T, H), (T, d.intermediate)]
+    rel = np.linalg.norm(out - base) / np.linalg.norm(base - h)
+    assert 1e-4 < rel < 0.2, rel
