@@ -1,0 +1,123 @@
+"""GPU parity of the batched E4M3 tier (more than 64 rows with E4M3 weights):
+per-token E4M3 activations and the 16x16x128 FP8 MFMA in every block linear.
+
+Reading under test (LingBot-VLA v2 Examples, Configuration / Online
+Quantization: FP8 with per-token activation and per-output-channel weight
+scales): each input row of a block linear is scaled by max|row| / 448 and
+rounded to E4M3; the oracle models this with ``act_quant=True``.
+
+Gates. Against the oracle that models the same quantization (dequantized
+weights, per-token E4M3 inputs): cosine >= 0.999 and max-abs <= 0.3 * RMS.
+These are looser than the bf16 gates because the GPU quantizes its own
+rounded intermediates (bf16 attention and SwiGLU outputs, fp32 norms): about
+one input in thirty lands on the other side of a rounding boundary (bf16's
+2^-9 against E4M3's 2^-4 half-step) and takes the neighbouring code, one
+E4M3 step (up to 2^-3 of its value) away, so single outputs fed by a large
+flipped input move by a sizeable fraction of the RMS while the cosine stays
+high. Against the bf16-weight oracle without any quantization: the FP8 gate
+of the pages, cosine >= 0.995.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import FP8_COS, metrics, say
+
+pytestmark = pytest.mark.gpu
+
+TILES = {0: "auto", 1: "256x256", 2: "128x128", 3: "128x64"}
+Q_COS, Q_MAXABS = 0.999, 0.3
+
+
+def _gate_q(m, tag):
+    say(f"[{tag}] vs quantization-modelling oracle: cos={m['cos']:.6f} min_req_cos={m['min_req_cos']:.6f} "
+        f"maxabs/rms={m['maxabs_over_rms']:.3e}")
+    assert m["min_req_cos"] >= Q_COS and m["maxabs_over_rms"] <= Q_MAXABS, (tag, m)
+
+
+def test_fp8_batched_layer_every_tile_shape():
+    """One layer at batch 8 (400 rows), LingBot widths, every tile shape."""
+    import torch
+    from vla_flow_matching_denoise_amd import binding as B
+    from vla_flow_matching_denoise_amd.expert import Expert, dims_from_config, to_device
+    cfg = synth.config(4).replace(n_layers=2, batch=8)
+    raw = synth.apply_variant(synth.make_weights(cfg, seed=0), "gate_open", cfg)
+    pk, pv = synth.make_prefix(cfg)
+    ts = synth.make_schedule(cfg.n_steps, cfg.batch, "warped")
+    h_in = np.random.default_rng(7).standard_normal((cfg.m_rows, cfg.hidden)).astype(np.float32)
+    layer, step, T = 1, 3, cfg.horizon
+    Wd = oracle.decode_weights(raw)
+    d = oracle.ExpertDims.from_config(cfg)
+    fpk, fpv = oracle.decode_bf16(pk), oracle.decode_bf16(pv)
+    want_q = np.empty((cfg.batch, T, cfg.hidden))
+    want = np.empty_like(want_q)
+    for b in range(cfg.batch):
+        c = oracle.time_condition(float(ts[b, step]), Wd, d)
+        mod = oracle.modulation(c, Wd["mod_w"][layer], Wd["mod_b"][layer], 6)
+        hb = h_in[b * T:(b + 1) * T].astype(np.float64)
+        want_q[b] = oracle.expert_layer(hb, Wd, layer, mod, fpk[b, layer], fpv[b, layer], d, act_quant=True) - hb
+        want[b] = oracle.expert_layer(hb, Wd, layer, mod, fpk[b, layer], fpv[b, layer], d) - hb
+    ex = Expert(raw, dims_from_config(cfg))
+    try:
+        dpk, dpv, dts, hi = (to_device(a) for a in (pk, pv, ts, h_in))
+        for tile in (0, 1, 2, 3):
+            ex.set_option(B.VLA_OPT_GEMM_TILE, tile)
+            ho = torch.empty_like(hi)
+            B.vla_test_layer(ex.ctx, dpk.data_ptr(), dpv.data_ptr(), dts.data_ptr(), cfg.n_steps, step, layer,
+                             hi.data_ptr(), ho.data_ptr())
+            got = (ho.cpu().numpy() - h_in).reshape(cfg.batch, T, -1)
+            assert np.all(np.isfinite(got))
+            _gate_q(metrics(got, want_q), f"fp8 layer b8 {TILES[tile]}")
+            m = metrics(got, want)
+            say(f"  vs unquantized-activation oracle: cos={m['cos']:.6f}")
+            assert m["cos"] >= FP8_COS, m
+    finally:
+        ex.close()
+
+
+def test_fp8_batched_end_to_end():
+    """Four-layer LingBot-width expert, 8 requests, 3 warped Euler steps."""
+    from tests.gpu_util import GpuCase
+    cfg = synth.config(4).replace(n_layers=4, batch=8, n_steps=3)
+    raw = synth.make_weights(cfg, seed=1)
+    raw_bf16 = synth.make_weights(cfg, seed=1, weight_dtype="bf16")
+    pk, pv = synth.make_prefix(cfg, seed=2)
+    x0 = synth.make_noise(cfg, seed=2)
+    ts = synth.make_schedule(cfg.n_steps, cfg.batch, "warped")
+    case = GpuCase(cfg, raw, pk, pv, x0, ts)
+    try:
+        out = case.run()
+    finally:
+        case.close()
+    d = oracle.ExpertDims.from_config(cfg)
+    fpk, fpv = oracle.decode_bf16(pk), oracle.decode_bf16(pv)
+    ref_q = oracle.denoise(oracle.decode_weights(raw), d, fpk, fpv, x0, ts, act_quant=True)
+    _gate_q(metrics(out, ref_q), "fp8 e2e b8")
+    ref = oracle.denoise(oracle.decode_weights(raw_bf16), d, fpk, fpv, x0, ts)
+    m = metrics(out, ref)
+    say(f"[fp8 e2e b8] vs bf16-weight oracle: cos={m['cos']:.6f} min_req_cos={m['min_req_cos']:.6f}")
+    assert m["cos"] >= FP8_COS, m
+
+
+def test_fp8_batch64_sampled_requests():
+    """LingBot-shaped E4M3 expert at batch 64 (M = 3200), 2 steps; three
+    requests checked against the oracle."""
+    from tests.gpu_util import GpuCase
+    cfg = synth.config(4).replace(batch=64, n_steps=2)
+    raw = synth.make_weights(cfg, seed=0)
+    pk, pv = synth.make_prefix(cfg)
+    x0 = synth.make_noise(cfg)
+    ts = synth.make_schedule(cfg.n_steps, cfg.batch, "warped")
+    say("[fp8 b64] 36 layers, batch 64, 2 steps")
+    case = GpuCase(cfg, raw, pk, pv, x0, ts)
+    try:
+        out = case.run()
+    finally:
+        case.close()
+    d = oracle.ExpertDims.from_config(cfg)
+    W = oracle.decode_weights(raw)
+    for b in (0, 41):
+        ref_q = oracle.denoise(W, d, oracle.decode_bf16(pk[b:b + 1]), oracle.decode_bf16(pv[b:b + 1]),
+                               x0[b:b + 1], ts[b:b + 1], act_quant=True)
+        _gate_q(metrics(out[b:b + 1], ref_q), f"fp8 b64 request {b}")

@@ -36,12 +36,17 @@ def test_layer_every_tile_shape(cfg_id, batch):
     d = oracle.ExpertDims.from_config(cfg)
     fpk, fpv = oracle.decode_bf16(pk), oracle.decode_bf16(pv)
     T = cfg.horizon
+    # E4M3 weights with more than 64 rows run the batched E4M3 tier (per-token
+    # E4M3 activations): compare with the oracle that models it, at that
+    # tier's gates (tests/test_gpu_fp8_batched.py)
+    aq = cfg.weight_dtype == "fp8_e4m3" and cfg.m_rows > 64
+    gate_cos, gate_maxabs = (0.999, 0.3) if aq else (0.9995, 2e-2)
     want = np.empty_like(h_in, dtype=np.float64)
     for b in range(batch):
         c = oracle.time_condition(float(ts[b, step]), Wd, d)
         mod = oracle.modulation(c, Wd["mod_w"][layer], Wd["mod_b"][layer], 6)
         want[b * T:(b + 1) * T] = oracle.expert_layer(h_in[b * T:(b + 1) * T].astype(np.float64), Wd, layer, mod,
-                                                     fpk[b, layer], fpv[b, layer], d)
+                                                     fpk[b, layer], fpv[b, layer], d, act_quant=aq)
     ex = Expert(raw, dims_from_config(cfg))
     try:
         dpk, dpv, dts, hi = (to_device(a) for a in (pk, pv, ts, h_in))
@@ -58,7 +63,7 @@ def test_layer_every_tile_shape(cfg_id, batch):
             dw = (want - h_in).reshape(batch, T, -1)
             m = metrics(dg, dw)
             say(f"  cos={m['cos']:.7f} min_req_cos={m['min_req_cos']:.7f} maxabs/rms={m['maxabs_over_rms']:.3e}")
-            assert m["min_req_cos"] >= 0.9995 and m["maxabs_over_rms"] <= 2e-2, (TILES[tile], m)
+            assert m["min_req_cos"] >= gate_cos and m["maxabs_over_rms"] <= gate_maxabs, (TILES[tile], m)
     finally:
         ex.close()
 

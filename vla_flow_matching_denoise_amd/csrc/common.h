@@ -10,6 +10,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
 
 #define VLA_DEV __device__ __forceinline__
 
@@ -45,6 +46,14 @@ VLA_DEV bf16x8 e4m3x8_to_bf16x8(u32x2 w) {
     r[2] = __builtin_amdgcn_perm(__float_as_uint(c[1]), __float_as_uint(c[0]), 0x07060302u);
     r[3] = __builtin_amdgcn_perm(__float_as_uint(d[1]), __float_as_uint(d[0]), 0x07060302u);
     return __builtin_bit_cast(bf16x8, r);
+}
+
+// Four floats -> four OCP E4M3FN codes (v_cvt_pk_fp8_f32: round to nearest
+// even), first value in the lowest byte.
+VLA_DEV uint32_t f32x4_to_e4m3x4(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
 }
 
 VLA_DEV float wave_sum(float v) {

@@ -156,6 +156,11 @@ struct vla_ctx {
     float* h = nullptr;
     float* yf = nullptr;        // final AdaRMSNorm output (fp32) for the out-projection
     uint16_t *y = nullptr, *q = nullptr, *o = nullptr, *act = nullptr;
+    // E4M3 weights with more than 64 rows: per-token E4M3 copies of the
+    // block linears' inputs (row-major) and their row scales
+    bool a8 = false;
+    uint8_t *y8 = nullptr, *o8 = nullptr, *act8 = nullptr;
+    float *y8s = nullptr, *o8s = nullptr, *act8s = nullptr;
     float* ws = nullptr;        // split-K partials of O / down, [ksplit][M][H]
     uint16_t *kcat = nullptr, *vcat = nullptr;  // per-layer [prefix ; chunk] K and V
     KVLayout kv{};
@@ -270,7 +275,8 @@ int pack_linear(vla_ctx* c, Linear& lin, int N, int K, const void* const* srcs, 
         int blocks = (int)((total + 255) / 256);
         int row_mode = mode == 2 ? 2 : (mode == 1 ? 1 : 0);
         hipLaunchKernelGGL(pack_weight_kernel, dim3(blocks), dim3(256), 0, c->stream, (const uint8_t*)srcs[s],
-                           rows[s], K, eb, (uint8_t*)lin.w, row_mode, mode == 2 ? 0 : off, dh, mode == 2 ? s : 0);
+                           rows[s], K, eb, (uint8_t*)lin.w, row_mode, mode == 2 ? 0 : off, dh, mode == 2 ? s : 0,
+                           c->a8 ? 1 : 0);
         HIPC(hipGetLastError());
         if (c->w8) {
             std::vector<float> sv(rows[s]);
@@ -308,7 +314,7 @@ int pack_mod(vla_ctx* c, const vla_weights* w) {
         int rows = l < L ? 6 * H : 2 * H;
         long total = (long)rows * (H / 8);
         hipLaunchKernelGGL(pack_weight_kernel, dim3((int)((total + 255) / 256)), dim3(256), 0, c->stream,
-                           (const uint8_t*)src, rows, H, 2, (uint8_t*)c->mod.w, 0, l * 6 * H, 64, 0);
+                           (const uint8_t*)src, rows, H, 2, (uint8_t*)c->mod.w, 0, l * 6 * H, 64, 0, 0);
         HIPC(hipGetLastError());
     }
     rc = c->alloc((void**)&c->mod_bias, (size_t)N * sizeof(float));
@@ -370,6 +376,19 @@ int launch_tiled_t(int epi, const GemmParams& p, dim3 grid, hipStream_t s) {
     return VLA_OK;
 }
 
+template <int MT, int NT>
+int launch_tiled8_t(int epi, const GemmParams& p, dim3 grid, hipStream_t s) {
+    const dim3 blk(64 * GEMM_WAVES);
+    switch (epi) {
+        case EPI_RESID: VLA_LAUNCH((gemm8_kernel<MT, NT, EPI_RESID>), grid, blk, 0, s, p); break;
+        case EPI_QKV_ROPE: VLA_LAUNCH((gemm8_kernel<MT, NT, EPI_QKV_ROPE>), grid, blk, 0, s, p); break;
+        case EPI_SWIGLU: VLA_LAUNCH((gemm8_kernel<MT, NT, EPI_SWIGLU>), grid, blk, 0, s, p); break;
+        default: set_err("bad FP8 tiled epilogue %d", epi); return VLA_ERR_ARG;
+    }
+    HIPC(hipGetLastError());
+    return VLA_OK;
+}
+
 template <bool W8>
 int launch_skinny_t(int epi, const GemmParams& p, dim3 grid, hipStream_t s) {
     switch (epi) {
@@ -414,6 +433,17 @@ int launch_gemm(vla_ctx* c, const Linear& lin, const GemmCfg& cfg, bool w8, int 
     const int ntm = (p.M + cfg.MT - 1) / cfg.MT;
     p.tile_map = p.M > lin.N && ntm >= 8 && (ntm + 7) / 8 * 8 * (lin.N / cfg.NT) <= c->ncu ? 1 : 0;
     dim3 grid((lin.N / cfg.NT) * (p.tile_map ? (ntm + 7) / 8 * 8 : ntm));  // tile from the linear id
+    if (w8 && c->a8) {
+        if (lin.K % GEMM8_KT != 0) {
+            set_err("FP8 GEMM needs K %% %d == 0 (K = %d)", GEMM8_KT, lin.K);
+            return VLA_ERR_SHAPE;
+        }
+        if (cfg.MT == 256 && cfg.NT == 256) return launch_tiled8_t<256, 256>(epi, p, grid, c->stream);
+        if (cfg.MT == 128 && cfg.NT == 128) return launch_tiled8_t<128, 128>(epi, p, grid, c->stream);
+        if (cfg.MT == 128 && cfg.NT == 64) return launch_tiled8_t<128, 64>(epi, p, grid, c->stream);
+        set_err("no FP8 GEMM tile %dx%d", cfg.MT, cfg.NT);
+        return VLA_ERR_SHAPE;
+    }
     if (cfg.MT == 256 && cfg.NT == 256) return w8 ? launch_tiled_t<256, 256, true>(epi, p, grid, c->stream)
                                                   : launch_tiled_t<256, 256, false>(epi, p, grid, c->stream);
     if (cfg.MT == 128 && cfg.NT == 128) return w8 ? launch_tiled_t<128, 128, true>(epi, p, grid, c->stream)
@@ -506,9 +536,11 @@ int launch_resnorm(vla_ctx* c, int step, int S, int gate_off, int scale_off, int
                    float* yf = nullptr) {
     if (S == 0 && !y && !yf) return VLA_OK;
     const vla_dims& d = c->d;
+    // the batched E4M3 tier takes y as per-token E4M3 codes instead of bf16
+    uint8_t* y8 = c->a8 && y ? c->y8 : nullptr;
     hipLaunchKernelGGL(resnorm_kernel, dim3(c->M), dim3(256), 0, c->stream, c->h, c->ws, S, c->modtab, gate_off,
-                       scale_off, shift_off, y, yf, c->M, d.hidden, d.horizon, d.batch, step, c->mod_ld, d.rms_eps,
-                       c->afrag);
+                       scale_off, shift_off, y8 ? nullptr : y, yf, c->M, d.hidden, d.horizon, d.batch, step, c->mod_ld,
+                       d.rms_eps, c->afrag, y8, c->y8s);
     HIPC(hipGetLastError());
     return VLA_OK;
 }
@@ -531,7 +563,8 @@ int launch_block_gemm(vla_ctx* c, int which, int step, int l, int* S) {
     p.afrag = c->afrag;
     if (S) *S = 0;
     if (which == VLA_KERNEL_QKV) {
-        p.A = c->y;
+        p.A = c->a8 ? (const uint16_t*)c->y8 : c->y;
+        p.ascale = c->y8s;
         p.lda = H;
         p.q = c->q;
         p.kcat = c->kcat;
@@ -551,6 +584,10 @@ int launch_block_gemm(vla_ctx* c, int which, int step, int l, int* S) {
         const bool o = which == VLA_KERNEL_O;
         const Linear& lin = o ? c->wo[l] : c->wd[l];
         p.A = o ? c->o : c->act;
+        if (c->a8) {
+            p.A = (const uint16_t*)(o ? c->o8 : c->act8);
+            p.ascale = o ? c->o8s : c->act8s;
+        }
         p.lda = o ? c->qd : d.intermediate;
         p.out_f32 = c->h;
         p.gate_off = (6 * l + (o ? 2 : 5)) * H;
@@ -558,7 +595,8 @@ int launch_block_gemm(vla_ctx* c, int which, int step, int l, int* S) {
         return launch_gemm(c, lin, lin.cfg, c->w8, EPI_RESID, p);
     }
     if (which == VLA_KERNEL_GATE_UP) {
-        p.A = c->y;
+        p.A = c->a8 ? (const uint16_t*)c->y8 : c->y;
+        p.ascale = c->y8s;
         p.lda = H;
         p.act = c->act;
         return launch_gemm(c, c->gu[l], c->gu[l].cfg, c->w8, EPI_SWIGLU, p);
@@ -570,14 +608,23 @@ int launch_block_gemm(vla_ctx* c, int which, int step, int l, int* S) {
 // Layer l of Euler step `step`. On entry y holds the layer's first AdaRMSNorm
 // output; on exit h holds the layer output and, when norm_next, y holds the
 // next layer's first AdaRMSNorm output.
+// Per-token E4M3 copy of a bf16 [M][K] activation (batched E4M3 tier).
+int launch_quant(vla_ctx* c, const uint16_t* src, int K, uint8_t* dst, float* scale) {
+    hipLaunchKernelGGL(quant_rows_kernel, dim3(c->M), dim3(256), 0, c->stream, src, K, dst, scale);
+    HIPC(hipGetLastError());
+    return VLA_OK;
+}
+
 int enqueue_layer(vla_ctx* c, int step, int l, bool norm_next, float* yf_final = nullptr) {
     const int H = c->d.hidden, L = c->d.n_layers;
     int rc, S = 0;
     if ((rc = launch_block_gemm(c, VLA_KERNEL_QKV, step, l, nullptr))) return rc;
     if ((rc = launch_attention(c, l, c->q, c->o, c->afrag))) return rc;
+    if (c->a8 && (rc = launch_quant(c, c->o, c->qd, c->o8, c->o8s))) return rc;
     if ((rc = launch_block_gemm(c, VLA_KERNEL_O, step, l, &S))) return rc;
     if ((rc = launch_resnorm(c, step, S, (6 * l + 2) * H, (6 * l + 3) * H, (6 * l + 4) * H, c->y))) return rc;
     if ((rc = launch_block_gemm(c, VLA_KERNEL_GATE_UP, step, l, nullptr))) return rc;
+    if (c->a8 && (rc = launch_quant(c, c->act, c->d.intermediate, c->act8, c->act8s))) return rc;
     if ((rc = launch_block_gemm(c, VLA_KERNEL_DOWN, step, l, &S))) return rc;
     if (norm_next) return launch_resnorm(c, step, S, (6 * l + 5) * H, (6 * (l + 1)) * H, (6 * (l + 1) + 1) * H, c->y);
     if (yf_final) return launch_resnorm(c, step, S, (6 * l + 5) * H, 6 * L * H, (6 * L + 1) * H, nullptr, yf_final);
@@ -592,6 +639,7 @@ int enqueue_step_start(vla_ctx* c, int k, const float* x_direct) {
                        c->in_wT, c->in_b, c->h, c->y, c->modtab, 0, H, c->M, H, d.action_dim, d.horizon, d.batch, k,
                        c->mod_ld, d.rms_eps, c->afrag);
     HIPC(hipGetLastError());
+    if (c->a8) return launch_quant(c, c->y, H, c->y8, c->y8s);
     return VLA_OK;
 }
 
@@ -816,6 +864,9 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
     c->qd = d.n_q_heads * dh;
     c->kvd = d.n_kv_heads * dh;
     c->mod_ld = (6 * L + 2) * H;
+    // batched E4M3 tier: per-token E4M3 activations and the FP8 MFMA (inputs
+    // of every block linear a multiple of 128)
+    c->a8 = c->w8 && c->M > 64 && H % 128 == 0 && c->qd % 128 == 0 && I % 128 == 0;
     HIPC(hipGetDevice(&c->device));
     HIPC(hipDeviceGetAttribute(&c->ncu, hipDeviceAttributeMultiprocessorCount, c->device));
     // graphs are captured on this stream; work runs on `stream`, the legacy
@@ -928,6 +979,14 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
     if ((rc = c->alloc((void**)&c->act, MR * I * 2))) return rc;
     HIPC(hipMemsetAsync(c->o, 0, MR * c->qd * 2, c->stream));
     HIPC(hipMemsetAsync(c->act, 0, MR * I * 2, c->stream));
+    if (c->a8) {
+        if ((rc = c->alloc((void**)&c->y8, M * H))) return rc;
+        if ((rc = c->alloc((void**)&c->o8, M * c->qd))) return rc;
+        if ((rc = c->alloc((void**)&c->act8, M * I))) return rc;
+        if ((rc = c->alloc((void**)&c->y8s, M * 4))) return rc;
+        if ((rc = c->alloc((void**)&c->o8s, M * 4))) return rc;
+        if ((rc = c->alloc((void**)&c->act8s, M * 4))) return rc;
+    }
     c->kv.L = L;
     c->kv.nkv = d.n_kv_heads;
     c->kv.dh = dh;

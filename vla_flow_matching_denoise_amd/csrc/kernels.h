@@ -38,7 +38,7 @@ __global__ void set_args_kernel(ArgBlock* ab, const uint16_t* pk, const uint16_t
 // row_mode 2: dst row = 2*src row + parity (gate/up interleave)
 __global__ void pack_weight_kernel(const uint8_t* __restrict__ src, int R, int K, int elem_bytes,
                                    uint8_t* __restrict__ dst, int row_mode, int dst_off, int dh,
-                                   int parity) {
+                                   int parity, int layout) {
     const int chunks_per_row = K / 8;  // 8 inputs per chunk
     long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (long)R * chunks_per_row) return;
@@ -55,15 +55,69 @@ __global__ void pack_weight_kernel(const uint8_t* __restrict__ src, int R, int K
         drow = dst_off + r;
     }
     int k = kc * 8;
-    int Kf = K / 32;
-    int nt = drow / 16, lane = (drow % 16) + 16 * ((k % 32) / 8), kt = k / 32;
-    size_t frag = (size_t)nt * Kf + kt;
-    size_t dst_off_b = (frag * 64 + lane) * 8 * elem_bytes;
+    size_t dst_off_b;
+    if (layout == 1) {
+        // E4M3 fragments of the 16x16x128 FP8 MFMA: 16 rows x 128 inputs, two
+        // 1 KiB halves; lane l = row%16 + 16*(w/32) holds inputs w%32 of the
+        // 128 (w = k%128), bytes 0-15 in half 0 and 16-31 in half 1
+        const int Kq = K / 128, w = k % 128, lane = (drow % 16) + 16 * (w / 32), b = w % 32;
+        const size_t frag = (size_t)(drow / 16) * Kq + k / 128;
+        dst_off_b = ((frag * 2 + b / 16) * 64 + lane) * 16 + (b % 16);
+    } else {
+        int Kf = K / 32;
+        int nt = drow / 16, lane = (drow % 16) + 16 * ((k % 32) / 8), kt = k / 32;
+        size_t frag = (size_t)nt * Kf + kt;
+        dst_off_b = (frag * 64 + lane) * 8 * elem_bytes;
+    }
     size_t src_off_b = ((size_t)r * K + k) * elem_bytes;
     if (elem_bytes == 2) {
         *(u32x4*)(dst + dst_off_b) = *(const u32x4*)(src + src_off_b);
     } else {
         *(u32x2*)(dst + dst_off_b) = *(const u32x2*)(src + src_off_b);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-token E4M3 activations: row r of a bf16 [M][K] matrix (K <= 8192, a
+// multiple of 8) becomes codes q = RNE(x * 448 / max|x_r|) with the row
+// scale max|x_r| / 448 (1 for an all-zero row), so x ~ q * scale.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ src, int K,
+                                                         uint8_t* __restrict__ dst, float* __restrict__ scale) {
+    __shared__ float red[4];
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const uint16_t* sr = src + (size_t)row * K;
+    float v[4][8];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = (tid + 256 * i) * 8;
+        if (c < K) {
+            const u32x4 w = *(const u32x4*)(sr + c);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[i][2 * j] = __uint_as_float(w[j] << 16);
+                v[i][2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+                amax = fmaxf(amax, fmaxf(fabsf(v[i][2 * j]), fabsf(v[i][2 * j + 1])));
+            }
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    if ((tid & 63) == 0) red[tid >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
+    if (tid == 0) scale[row] = amax > 0.f ? amax / 448.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = (tid + 256 * i) * 8;
+        if (c < K) {
+            u32x2 q;
+            q[0] = f32x4_to_e4m3x4(v[i][0] * inv, v[i][1] * inv, v[i][2] * inv, v[i][3] * inv);
+            q[1] = f32x4_to_e4m3x4(v[i][4] * inv, v[i][5] * inv, v[i][6] * inv, v[i][7] * inv);
+            *(u32x2*)(dst + (size_t)row * K + c) = q;
+        }
     }
 }
 

@@ -19,14 +19,14 @@ __global__ __launch_bounds__(256) void resnorm_kernel(float* __restrict__ h, con
                                                       const float* __restrict__ mod, int gate_off, int scale_off,
                                                       int shift_off, uint16_t* __restrict__ y, float* __restrict__ yf,
                                                       int M, int H, int T, int B, int step, int mod_ld, float eps,
-                                                      int afrag) {
-    __shared__ float red[4];
+                                                      int afrag, uint8_t* __restrict__ y8, float* __restrict__ y8s) {
+    __shared__ float red[4], red8[4];
     const int row = blockIdx.x, tid = threadIdx.x;
     const int b = row / T;
     float* hr = h + (size_t)row * H;
     const float* mr = mod + (size_t)(step * B + b) * mod_ld;
     float4 v[2], part[2][RN_MAXS], g[2], sc[2], sh[2];
-    const bool norm = y || yf;
+    const bool norm = y || yf || y8;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int c = (tid + 256 * j) * 4;
@@ -65,15 +65,18 @@ __global__ __launch_bounds__(256) void resnorm_kernel(float* __restrict__ h, con
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
     const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
+    float4 ov[2];
+    float amax = 0.f;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int c = (tid + 256 * j) * 4;
         if (c < H) {
-            float4 o;
+            float4& o = ov[j];
             o.x = v[j].x * inv * (1.f + sc[j].x) + sh[j].x;
             o.y = v[j].y * inv * (1.f + sc[j].y) + sh[j].y;
             o.z = v[j].z * inv * (1.f + sc[j].z) + sh[j].z;
             o.w = v[j].w * inv * (1.f + sc[j].w) + sh[j].w;
+            amax = fmaxf(amax, fmaxf(fmaxf(fabsf(o.x), fabsf(o.y)), fmaxf(fabsf(o.z), fabsf(o.w))));
             if (y) {
                 uint2 ob;
                 ob.x = pack_bf16x2(o.x, o.y);
@@ -81,6 +84,24 @@ __global__ __launch_bounds__(256) void resnorm_kernel(float* __restrict__ h, con
                 *(uint2*)(y + act_index(row, c, H, afrag)) = ob;
             }
             if (yf) *(float4*)(yf + (size_t)row * H + c) = o;
+        }
+    }
+    if (y8) {
+        // per-token E4M3 copy of y (row-major, for the FP8 GEMMs): codes
+        // RNE(y * 448 / max|y|), row scale max|y| / 448 (1 for a zero row)
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        if ((tid & 63) == 0) red8[tid >> 6] = amax;
+        __syncthreads();
+        amax = fmaxf(fmaxf(red8[0], red8[1]), fmaxf(red8[2], red8[3]));
+        const float qs = amax > 0.f ? 448.0f / amax : 1.0f;
+        if (tid == 0) y8s[row] = amax > 0.f ? amax / 448.0f : 1.0f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int c = (tid + 256 * j) * 4;
+            if (c < H)
+                *(uint32_t*)(y8 + (size_t)row * H + c) =
+                    f32x4_to_e4m3x4(ov[j].x * qs, ov[j].y * qs, ov[j].z * qs, ov[j].w * qs);
         }
     }
 }
@@ -167,6 +188,7 @@ struct GemmParams {
     int a_frag;          // A given in A-fragment order (required by the skinny kernel)
     int afrag;           // act (SwiGLU output) written in A-fragment order
     int tile_map;        // tiled kernel: 1 = row tiles split over the XCDs (grid padded to 8 row-tile groups)
+    const float* ascale; // FP8 tiled kernel: per-row scales of the E4M3 A operand
     const void* W;       // packed fragments
     const float* wscale; // per packed row (E4M3), else null
     int M, N, K;
@@ -627,6 +649,181 @@ void gemm_kernel(GemmParams p) {
                 for (int q = 0; q < 4; ++q) {
                     const f32x4 t = *(const f32x4*)(ct + lr * CLD + uc * 16 + 4 * q);
                     v[4 * q] = t[0]; v[4 * q + 1] = t[1]; v[4 * q + 2] = t[2]; v[4 * q + 3] = t[3];
+                }
+                epilogue16<EPI>(p, row, n0 + uc * 16, v);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// FP8 tiled GEMM for larger M (E4M3 weights with per-output-channel scales,
+// per-token E4M3 activations): the structure of gemm_kernel with 128-deep
+// stages and the 16x16x128 FP8 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4 with
+// unit block scales, twice the bf16 rate). A (row-major E4M3 [M][K]) and W
+// (16 x 128 fragments in two 1 KiB halves) reach LDS as 1 KiB DMA chunks;
+// lane l of an MFMA operand holds row (or column) l%16 and inputs
+// 32*(l/16) .. +31 of the 128, bytes 0-15 from the first chunk and 16-31
+// from the second (the instruction pairs the two operands by lane group and
+// byte, checked on the device). out = acc * a_scale[row] * w_scale[col].
+// ---------------------------------------------------------------------------
+constexpr int GEMM8_KT = 128;
+
+template <int MT, int NT>
+struct Gemm8Shape {
+    static constexpr int ACH = MT / 16 * 2, BCH = NT / 16 * 2;   // 1 KiB DMA chunks per stage
+    static constexpr int STAGE = (ACH + BCH) * 1024;
+    static constexpr int S = 147456 / STAGE >= 3 ? 3 : 147456 / STAGE;
+    static constexpr int LA = (ACH + GEMM_WAVES - 1) / GEMM_WAVES;  // DMA loads per wave and stage
+    static constexpr int LB = (BCH + GEMM_WAVES - 1) / GEMM_WAVES;
+    static constexpr int LPW = LA + LB;
+    static_assert(S >= 2, "tile too large for two LDS stages");
+};
+
+VLA_DEV i32x8 frag32(const uint8_t* lo, const uint8_t* hi) {
+    const u32x4 a = *(const u32x4*)lo, b = *(const u32x4*)hi;
+    return (i32x8){(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+}
+
+template <int MT, int NT, int EPI>
+__global__ __launch_bounds__(64 * GEMM_WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm8_kernel(GemmParams p) {
+    using G = Gemm8Shape<MT, NT>;
+    constexpr int S = G::S, ACH = G::ACH, BCH = G::BCH, LA = G::LA, LB = G::LB, LPW = G::LPW, STAGE = G::STAGE;
+    constexpr int WGN = 4, WM = MT / 2, WN = NT / WGN, FM = WM / 16, FN = WN / 16;
+    static_assert(FM >= 1 && FN >= 1, "tile smaller than the wave grid");
+    __shared__ __attribute__((aligned(1024))) uint8_t lds[S * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave / WGN, wn = wave % WGN;
+    // tile of this workgroup: as in gemm_kernel's data-parallel mapping
+    const int ntn = p.N / NT;
+    int mt_i, nt_i;
+    if (p.tile_map == 1) {
+        const int w = blockIdx.x, s = w >> 3;
+        mt_i = (w & 7) + 8 * (s / ntn);
+        nt_i = s % ntn;
+        if (mt_i * MT >= p.M) return;  // padding of the last group of 8 row tiles
+    } else if (ntn % 8 == 0) {
+        const int w = blockIdx.x, per = ntn / 8, s = w >> 3;
+        mt_i = s / per;
+        nt_i = (w & 7) * per + s % per;
+    } else {
+        mt_i = blockIdx.x / ntn;
+        nt_i = blockIdx.x % ntn;
+    }
+    const int m0 = mt_i * MT, n0 = nt_i * NT;
+    const int nk = p.K / GEMM8_KT;
+    const uint32_t lbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
+    const uint8_t* A = (const uint8_t*)p.A;
+
+    // chunk c of A = (row block c/2, half c%2): lane slot i takes row i%16
+    // (rows past M read row M-1, never stored), inputs 32*(i/16) + 16*half;
+    // chunk c of B = half c%2 of the fragment of column block c/2
+    const uint8_t* asrc[LA];
+    uint32_t adst[LA];
+#pragma unroll
+    for (int i = 0; i < LA; ++i) {
+        const int c = (wave * LA + i) % ACH, rb = c / 2, half = c % 2;
+        const int row = min(m0 + rb * 16 + (lane & 15), p.M - 1);
+        asrc[i] = A + (size_t)row * p.lda + 32 * (lane >> 4) + 16 * half;
+        adst[i] = (uint32_t)c * 1024;
+    }
+    const uint8_t* bsrc[LB];
+    uint32_t bdst[LB];
+#pragma unroll
+    for (int i = 0; i < LB; ++i) {
+        const int c = (wave * LB + i) % BCH;
+        bsrc[i] = (const uint8_t*)p.W + ((size_t)(n0 / 16 + c / 2) * nk) * 2048 + (c % 2) * 1024 + lane * 16;
+        bdst[i] = (uint32_t)(ACH + c) * 1024;
+    }
+    // stage kt into ring slot kt % S; past the last stage the loads repeat it
+    auto issue = [&](int kt_raw) {
+        const uint32_t sb = lbase + (uint32_t)((kt_raw % S) * STAGE);
+        const int kt = min(kt_raw, nk - 1);
+#pragma unroll
+        for (int i = 0; i < LA; ++i) lds_dma16(asrc[i] + (size_t)kt * GEMM8_KT, sb + adst[i]);
+#pragma unroll
+        for (int i = 0; i < LB; ++i) lds_dma16(bsrc[i] + (size_t)kt * 2048, sb + bdst[i]);
+    };
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int s = 0; s < S; ++s) issue(s);
+    vm_wait<(S - 1) * LPW>();
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const uint8_t* st = lds + (kt % S) * STAGE;
+        // the wave's B fragments of the stage, then its A fragments one row
+        // block at a time, the next one read while the current multiplies
+        i32x8 bf[FN], af[2];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const int cb = 2 * (wn * FN + fn);
+            bf[fn] = frag32(st + (ACH + cb) * 1024 + lane * 16, st + (ACH + cb + 1) * 1024 + lane * 16);
+        }
+        af[0] = frag32(st + (2 * wm * FM) * 1024 + lane * 16, st + (2 * wm * FM + 1) * 1024 + lane * 16);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            if (fm + 1 < FM) {
+                const int ca = 2 * (wm * FM + fm + 1);
+                af[(fm + 1) & 1] = frag32(st + ca * 1024 + lane * 16, st + (ca + 1) * 1024 + lane * 16);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[fm & 1], bf[fn], acc[fm][fn], 0, 0,
+                                                                              0, 127, 0, 127);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // stage kt+1 landed (this wave's loads), then every wave's loads
+        // landed and every wave is done with stage kt's slot
+        vm_wait<(S - 2) * LPW>();
+        __syncthreads();
+        issue(kt + S);
+    }
+    vm_wait<0>();      // the repeated tail loads land before the LDS is reused
+    __syncthreads();
+
+    // epilogue through LDS as in gemm_kernel, with the row and column scales
+    constexpr int CLD = NT + 4;
+    constexpr int PPW = FM / 4;
+    constexpr int UPR = NT / 16;
+    static_assert(FM % 4 == 0 && 64 * CLD * 4 <= S * STAGE, "epilogue pass does not fit the ring");
+    float* ct = (float*)lds;
+    float wsc[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) wsc[fn] = p.wscale[n0 + wn * WN + fn * 16 + (lane & 15)];
+#pragma unroll
+    for (int pass = 0; pass < MT / 64; ++pass) {
+        if (wm == pass / PPW) {
+#pragma unroll
+            for (int f = 0; f < 4; ++f)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        ct[(f * 16 + 4 * (lane >> 4) + r) * CLD + wn * WN + fn * 16 + (lane & 15)] =
+                            acc[(pass % PPW) * 4 + f][fn][r] * wsc[fn];
+        }
+        __syncthreads();
+        for (int u = tid; u < 64 * UPR; u += 64 * GEMM_WAVES) {
+            const int lr = u / UPR, uc = u % UPR;
+            const int row = m0 + pass * 64 + lr;
+            if (row < p.M) {
+                const float as = p.ascale[row];
+                float v[16];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 t = *(const f32x4*)(ct + lr * CLD + uc * 16 + 4 * q);
+                    v[4 * q] = t[0] * as; v[4 * q + 1] = t[1] * as; v[4 * q + 2] = t[2] * as; v[4 * q + 3] = t[3] * as;
                 }
                 epilogue16<EPI>(p, row, n0 + uc * 16, v);
             }
