@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "denoise steps/s & chunks/s (36L bf16, chunk 50×75, b=1/64); % HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
 
 # HBM traffic of the dominant batch-1 kernel (the gate_up + SwiGLU skinny GEMM,
 # skinny_gemm_kernel<false, 3>) from rocprofv3 FETCH_SIZE / WRITE_SIZE counter
@@ -103,7 +104,7 @@ def kernel_rooflines(ex, cfg, iters):
     return res
 
 
-def dominant(res, bound):
+def dominant(res, bound, mfma_peak=BF16_PEAK_TFLOPS):
     """The kernel family carrying the largest share of the path's algorithmic
     bytes (HBM-bound) or flops (MFMA-bound); every family runs once per layer."""
     key = "bytes" if bound == "hbm" else "flops"
@@ -112,7 +113,7 @@ def dominant(res, bound):
     if bound == "hbm":
         ach, peak, unit = r["GBps"], HBM_PEAK_GBS, "GB/s"
     else:
-        ach, peak, unit = r["TFLOPs"], BF16_PEAK_TFLOPS, "TFLOP/s"
+        ach, peak, unit = r["TFLOPs"], mfma_peak, "TFLOP/s"
     return name, {"bound": bound, "kernel": name, "achieved": round(ach, 2), "peak": peak, "unit": unit,
                   "frac": round(ach / peak, 4), "traffic": None, "us_per_launch": round(r["us"], 3),
                   "algorithmic_bytes_per_launch": int(r["bytes"]), "algorithmic_flops_per_launch": int(r["flops"])}
@@ -364,6 +365,25 @@ def main():
             "call_mfma_frac": round(f5 / t5 / 1e12 / BF16_PEAK_TFLOPS, 4), "algorithmic_tflop": round(f5 / 1e12, 3),
             "roofline": roof5,
             "kernels": {k: {"us": round(v["us"], 2), "TFLOPs": round(v["TFLOPs"], 1)} for k, v in kr5.items()},
+        }
+        # the same batch with E4M3 block weights: per-token E4M3 activations and
+        # the FP8 MFMA (its own tier; the bf16 figures above are the metric's)
+        cfg8 = synth.config(4).replace(batch=cfg5.batch, n_steps=cfg5.n_steps)
+        log("[bench] batch-64 E4M3 workload")
+        ex8 = Expert(synth.make_weights(cfg8, seed=0), dims_from_config(cfg8))
+        dev8, _ = build_inputs(cfg8)
+        wall8, _, _ = time_calls(ex8, dev8, cfg8.n_steps, 2, n5)
+        t8 = wall8 / n5
+        _, f8 = call_work(cfg8)
+        kr8 = kernel_rooflines(ex8, cfg8, 36)
+        _, roof8 = dominant(kr8, "mfma", FP8_PEAK_TFLOPS)
+        ex8.close()
+        result["batch64_e4m3"] = {
+            "workload": "lingbot_36L_h1024_chunk50x75_euler10_b64_e4m3_weights_per_token_e4m3_activations",
+            "dtype": "e4m3 x e4m3 -> f32", "steps_per_s": round(cfg8.n_steps / t8, 3),
+            "chunks_per_s": round(cfg8.batch / t8, 3), "ms_per_call": round(t8 * 1e3, 3),
+            "call_mfma_frac": round(f8 / t8 / 1e12 / FP8_PEAK_TFLOPS, 4), "roofline": roof8,
+            "kernels": {k: {"us": round(v["us"], 2), "TFLOPs": round(v["TFLOPs"], 1)} for k, v in kr8.items()},
         }
 
     if not args.no_cpu_baseline:
