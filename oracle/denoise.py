@@ -31,8 +31,9 @@ design notes of this repository:
     [af, bf] = W_modf c + b_modf
     v = (RMSNorm(h) * (1 + af) + bf) W_out^T + b_out
 
-Weights arrive as raw encodings (bf16 bit patterns, or OCP E4M3FN codes with
-per-output-row float32 scales); this module decodes them itself.
+Weights arrive as raw encodings (bf16 bit patterns, OCP E4M3FN codes with
+per-output-row float32 scales, or OCP MXFP4 blocks: E2M1 codes with one E8M0
+scale per 32 inputs); this module decodes them itself.
 """
 from __future__ import annotations
 
@@ -47,7 +48,7 @@ __all__ = [
     "sinusoidal_embedding", "silu", "time_condition", "modulation",
     "rms_normalize", "ada_rms_norm", "rope_rotate_half", "softmax",
     "gqa_attention", "expert_layer", "velocity", "denoise", "denoise_varlen", "cosine",
-    "quantize_e4m3fn", "quantize_per_token_e4m3",
+    "quantize_e4m3fn", "quantize_per_token_e4m3", "decode_e2m1", "decode_mxfp4",
 ]
 
 
@@ -147,12 +148,43 @@ def quantize_per_token_e4m3(a: np.ndarray) -> np.ndarray:
     return quantize_e4m3fn(a / s) * s
 
 
+def decode_e2m1(codes: np.ndarray) -> np.ndarray:
+    """OCP 4-bit E2M1 codes (0..15) -> floats.
+
+    Format (OCP Microscaling Formats (MX) specification, FP4 E2M1): 1 sign
+    bit, 2 exponent bits with bias 1, 1 mantissa bit; exponent field 0 holds
+    the subnormal m * 0.5; no infinities or NaN; largest magnitude 6.
+    """
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 8, -1.0, 1.0)
+    e = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    mag = np.where(e == 0, 0.5 * m, (1.0 + 0.5 * m) * np.exp2(e.astype(np.float64) - 1.0))
+    return sign * mag
+
+
+def decode_mxfp4(packed: np.ndarray, scales: np.ndarray, dtype=np.float64) -> np.ndarray:
+    """MXFP4 weights -> floats [N, K]: E2M1 codes two per byte (element 2j in
+    the low nibble) [N, K/2], and one E8M0 scale per 32 inputs [N, K/32]
+    (value 2^(e - 127), the MX shared exponent; e = 255 is NaN)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    codes = np.empty((p.shape[0], p.shape[1] * 2), dtype=np.uint8)
+    codes[:, 0::2] = p & 0xF
+    codes[:, 1::2] = p >> 4
+    e = np.asarray(scales, dtype=np.int64)
+    x = np.where(e == 255, np.nan, np.exp2(e.astype(np.float64) - 127.0))
+    vals = decode_e2m1(codes).reshape(codes.shape[0], -1, 32) * x[:, :, None]
+    return vals.reshape(codes.shape).astype(dtype)
+
+
 def _linear(raw: dict, name: str, l: Optional[int], dtype):
     w = raw[name] if l is None else raw[name][l]
     if w.dtype == np.uint16:
         return decode_bf16(w, dtype)
     if w.dtype == np.uint8:
         s = raw["s" + name[1]][l]
+        if np.asarray(s).dtype == np.uint8:            # MXFP4: E8M0 scale per 32 inputs
+            return decode_mxfp4(w, s, dtype)
         return (decode_e4m3fn(w, np.float64) * np.asarray(s, np.float64)[:, None]).astype(dtype)
     raise TypeError(f"{name}: unsupported encoding {w.dtype}")
 

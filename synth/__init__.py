@@ -15,6 +15,12 @@ Encodings returned:
     scale per output row (``s_n = max_k |W[n,k]| / 448``, ``s_n = 1`` for an
     all-zero row, codes by torch's round-to-nearest-even cast of ``W / s_n``
     clamped to +-448);
+  * MXFP4 tensors (the gate and up linears of the ``fp8_mxfp4gu`` tier) as
+    ``uint8`` arrays of OCP E2M1 codes, two per byte (element 2j in the low
+    nibble), ``[N, K/2]``, plus one E8M0 block scale per 32 inputs
+    ``uint8 [N, K/32]`` (value 2^(e - 127)): per block, X = 2^(floor(log2
+    max|W|) - 2) (X = 1 for an all-zero block) and codes = nearest E2M1 value
+    of W / X, ties to even, clamped to +-6 (the OCP MX conversion);
   * biases, noise and schedules as float32.
 
 Random streams: every tensor has its own ``numpy.random.default_rng`` stream
@@ -55,7 +61,7 @@ class ExpertConfig:
     action_dim: int
     n_steps: int
     batch: int
-    weight_dtype: str = "bf16"      # "bf16" or "fp8_e4m3" for the block linears
+    weight_dtype: str = "bf16"      # "bf16", "fp8_e4m3", or "fp8_mxfp4gu" (E4M3, gate/up MXFP4)
     time_emb_dim: int = 256
     rope_theta: float = 1.0e6
     rms_eps: float = 1.0e-6
@@ -117,6 +123,30 @@ def to_e4m3_rowwise(x: np.ndarray):
     return q, s
 
 
+_E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def to_mxfp4_blocks(x: np.ndarray):
+    """float32 [N, K] (K % 32 == 0) -> (packed E2M1 codes uint8 [N, K/2],
+    E8M0 scales uint8 [N, K/32]); see the module docstring."""
+    x = np.asarray(x, dtype=np.float64)
+    N, K = x.shape
+    blk = x.reshape(N, K // 32, 32)
+    amax = np.max(np.abs(blk), axis=2)
+    e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 2, 0).astype(np.int64)
+    v = np.abs(blk) / np.exp2(e)[:, :, None]
+    v = np.minimum(v, 6.0)
+    d = np.abs(v[..., None] - _E2M1_VALUES)                   # distance to each of the 8 magnitudes
+    best = d.min(axis=-1, keepdims=True)
+    cand = (d == best)
+    # ties: the even code (codes 0..7 in increasing magnitude order)
+    even = cand & (np.arange(8) % 2 == 0)
+    idx = np.where(even.any(axis=-1), even.argmax(axis=-1), cand.argmax(axis=-1))
+    code = (idx | np.where(blk < 0, 8, 0)).astype(np.uint8).reshape(N, K)
+    packed = (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8)
+    return packed, (e + 127).astype(np.uint8)
+
+
 def make_weights(cfg: ExpertConfig, seed: int = 0, weight_dtype: Optional[str] = None) -> dict:
     """All weights of one expert, as raw encodings (see the module docstring).
 
@@ -144,7 +174,7 @@ def make_weights(cfg: ExpertConfig, seed: int = 0, weight_dtype: Optional[str] =
     W["mod_w"], W["mod_b"] = [], []
     for name in BLOCK_LINEARS:
         W[name] = []
-        if wd == "fp8_e4m3":
+        if wd in ("fp8_e4m3", "fp8_mxfp4gu"):
             W["s" + name[1]] = []
     for l in range(L):
         W["mod_w"].append(to_bf16_bits(_draw(cfg, seed, "mod_w", l, (6 * H, H))))
@@ -153,8 +183,12 @@ def make_weights(cfg: ExpertConfig, seed: int = 0, weight_dtype: Optional[str] =
             x = _draw(cfg, seed, name, l, shapes[name])
             if wd == "bf16":
                 W[name].append(to_bf16_bits(x))
-            elif wd == "fp8_e4m3":
+            elif wd == "fp8_e4m3" or (wd == "fp8_mxfp4gu" and name not in ("wg", "wu")):
                 q, s = to_e4m3_rowwise(x)
+                W[name].append(q)
+                W["s" + name[1]].append(s)
+            elif wd == "fp8_mxfp4gu":
+                q, s = to_mxfp4_blocks(x)
                 W[name].append(q)
                 W["s" + name[1]].append(s)
             else:

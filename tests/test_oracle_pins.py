@@ -583,3 +583,53 @@ def test_act_quant_wiring_in_the_layer(monkeypatch):
     assert shapes == [(T, H), (T, d.n_q_heads * d.head_dim), (T, H), (T, d.intermediate)]
     rel = np.linalg.norm(out - base) / np.linalg.norm(base - h)
     assert 1e-4 < rel < 0.2, rel
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 gate/up weights (the E4M3 + MXFP4 gate_up tier)
+# ---------------------------------------------------------------------------
+
+def test_e2m1_decode_table():
+    """The 16 E2M1 codes against the value list of the OCP MX specification
+    (0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives). Catches a wrong bias or
+    subnormal rule."""
+    want = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    got = oracle.decode_e2m1(np.arange(16))
+    np.testing.assert_array_equal(got[:8], want)
+    np.testing.assert_array_equal(got[8:], [-v for v in want])
+
+
+def test_mxfp4_decode_layout_and_scales():
+    """Nibble order (element 2j low), one E8M0 scale per 32 inputs (2^(e-127),
+    255 = NaN), on a hand-built row."""
+    codes = np.zeros((1, 64), dtype=np.uint8)
+    codes[0, 0], codes[0, 1], codes[0, 31], codes[0, 32], codes[0, 63] = 2, 7, 9, 5, 15
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    got = oracle.decode_mxfp4(packed, np.array([[127 - 3, 127 + 1]], dtype=np.uint8))
+    want = np.zeros((1, 64))
+    want[0, 0], want[0, 1], want[0, 31] = 1.0 / 8, 6.0 / 8, -0.5 / 8
+    want[0, 32], want[0, 63] = 3.0 * 2, -6.0 * 2
+    np.testing.assert_array_equal(got, want)
+    assert np.all(np.isnan(oracle.decode_mxfp4(packed, np.array([[255, 127]], dtype=np.uint8))[0, :32]))
+
+
+def test_mxfp4_generated_weights_within_the_format_bound():
+    """The generator's MXFP4 blocks decode to values within one E2M1 step of
+    the float draws (half a step where no clamping occurs): per block with
+    scale X, |decoded - w| <= X for |w / X| <= 6 (steps are 0.5 X below 2 X,
+    X up to 4 X, 2 X above), and the clamped top values decode to +-6 X.
+    Catches a wrong scale exponent or a dropped nibble."""
+    cfg = synth.config(1).replace(weight_dtype="fp8_mxfp4gu")
+    raw = synth.make_weights(cfg, seed=3)
+    ref = synth.make_weights(cfg, seed=3, weight_dtype="bf16")
+    for name in ("wg", "wu"):
+        deq = oracle.decode_mxfp4(raw[name][0], raw["s" + name[1]][0])
+        w = oracle.decode_bf16(ref[name][0])
+        X = np.repeat(np.exp2(raw["s" + name[1]][0].astype(np.float64) - 127.0), 32, axis=1)
+        r = np.abs(w) / X
+        step = np.where(r < 2, 0.5, np.where(r < 4, 1.0, 2.0))
+        # the bf16 reference rounds the draws; allow its 2^-8 relative error
+        err = np.abs(deq - w)
+        assert np.all(err[r <= 6] <= (step[r <= 6] / 2 + np.abs(w[r <= 6]) / X[r <= 6] * 2 ** -8) * X[r <= 6] + 1e-12)
+        assert np.all(np.abs(deq[r > 6]) == 6 * X[r > 6])
+        assert np.corrcoef(deq.ravel(), w.ravel())[0, 1] > 0.98
