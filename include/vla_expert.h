@@ -46,6 +46,10 @@ extern "C" {
 /* Block-linear weight encodings. */
 #define VLA_BF16 0
 #define VLA_FP8_E4M3 1 /* OCP E4M3FN codes, one fp32 scale per output row */
+/* E4M3 as above for wq, wk, wv, wo, wd; OCP MXFP4 for wg and wu (the expert's
+ * "FP8 + FP4 gate_up" of "LingBot-VLA on Thor (sm_110)", section 1, in the
+ * FP4 format gfx950 takes natively). batch * horizon <= 64 only. */
+#define VLA_FP8_E4M3_MXFP4_GU 2
 
 /* Return codes. */
 #define VLA_OK 0
@@ -95,7 +99,7 @@ typedef struct vla_dims {
     float rope_theta;      /* 1e6 */
     float rms_eps;         /* 1e-6 */
     float time_scale;      /* 1000: the embedding's argument is time_scale * t */
-    int32_t weight_dtype;  /* VLA_BF16 or VLA_FP8_E4M3 (block linears only) */
+    int32_t weight_dtype;  /* VLA_BF16, VLA_FP8_E4M3 or VLA_FP8_E4M3_MXFP4_GU (block linears only) */
 } vla_dims;
 
 /*
@@ -110,6 +114,10 @@ typedef struct vla_dims {
  *   wg[l], wu[l] [I, H]  wd[l] [H, I]     — bf16, or E4M3FN bytes when
  *   weight_dtype == VLA_FP8_E4M3, then sq..sd[l] hold one fp32 scale per
  *   output row (the dequantized weight is code * scale); NULL for bf16.
+ *   With VLA_FP8_E4M3_MXFP4_GU, wg[l] and wu[l] hold OCP E2M1 codes two per
+ *   byte (element 2j in the low nibble), [I, H/2] bytes, and sg[l], su[l]
+ *   point to one E8M0 scale byte per 32 inputs, [I, H/32] bytes (value
+ *   2^(e - 127)); the dequantized weight is E2M1 value * block scale.
  */
 typedef struct vla_weights {
     const void* in_w;  const float* in_b;

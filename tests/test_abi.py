@@ -62,3 +62,18 @@ def test_unsupported_dims_are_rejected_before_any_device_work(lib, field, value)
     w = B.VlaWeights()
     assert lib.vla_expert_create(ctypes.byref(w), ctypes.byref(d)) is None
     assert B.vla_last_error() != ""
+
+
+def test_mxfp4_gate_up_tier_rejects_more_than_64_rows(lib):
+    """The E4M3 + MXFP4 gate_up tier has only the weight-streaming kernel:
+    creation fails, before any device work, above 64 rows, and passes the dims
+    check at 64."""
+    from vla_flow_matching_denoise_amd import binding as B
+    from vla_flow_matching_denoise_amd.expert import make_dims
+    w = B.VlaWeights()
+    d = make_dims(2, 256, 4, 2, 64, 704, 7, 16, 32, 5, weight_dtype="fp8_mxfp4gu")   # 80 rows
+    assert lib.vla_expert_create(ctypes.byref(w), ctypes.byref(d)) is None
+    assert "MXFP4" in B.vla_last_error()
+    d = make_dims(2, 256, 4, 2, 64, 704, 7, 16, 32, 4, weight_dtype="fp8_mxfp4gu")   # 64 rows
+    assert lib.vla_expert_create(ctypes.byref(w), ctypes.byref(d)) is None
+    assert "MXFP4" not in B.vla_last_error()          # fails later, on the NULL weight pointers

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libvla_expert.so")
 
 VLA_BF16 = 0
 VLA_FP8_E4M3 = 1
+VLA_FP8_E4M3_MXFP4_GU = 2
 VLA_OK = 0
 VLA_ERR_ARG = -1
 VLA_ERR_SHAPE = -2

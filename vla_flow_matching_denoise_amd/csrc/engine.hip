@@ -123,6 +123,8 @@ GemmCfg choose_gemm(int M, int N, int K, bool allow_split, int ncu, int force_ti
 struct Linear {
     void* w = nullptr;        // packed fragments
     float* scale = nullptr;   // per packed row (E4M3 only)
+    uint8_t* bscale = nullptr; // MXFP4: E8M0 scale per (packed row, 32 inputs), [N/16][K/32][16]
+    int fmt = 0;              // 0 bf16, 1 E4M3, 2 MXFP4
     int N = 0, K = 0;
     GemmCfg cfg;
 };
@@ -138,6 +140,7 @@ struct vla_ctx {
     hipStream_t stream = nullptr;
     bool use_graph = true;
     bool w8 = false;
+    bool gu4 = false;   // gate/up in MXFP4 (the other block linears E4M3)
     int M = 0, qd = 0, kvd = 0, mod_ld = 0;
     int afrag = 0;      // M <= 64: activations y, o, act kept in A-fragment order (64 zero-padded rows)
     int64_t bytes = 0;
@@ -248,8 +251,13 @@ int validate_dims(const vla_dims* d) {
         set_err("rms_eps and rope_theta must be positive, time_scale finite");
         return VLA_ERR_SHAPE;
     }
-    if (d->weight_dtype != VLA_BF16 && d->weight_dtype != VLA_FP8_E4M3) {
+    if (d->weight_dtype != VLA_BF16 && d->weight_dtype != VLA_FP8_E4M3 && d->weight_dtype != VLA_FP8_E4M3_MXFP4_GU) {
         set_err("unknown weight_dtype %d", d->weight_dtype);
+        return VLA_ERR_SHAPE;
+    }
+    if (d->weight_dtype == VLA_FP8_E4M3_MXFP4_GU && ((long)d->batch * d->horizon > 64 || d->hidden % 32)) {
+        set_err("the MXFP4 gate_up tier runs batch*horizon <= 64 with hidden %% 32 == 0 (got %d rows, hidden %d)",
+                d->batch * d->horizon, d->hidden);
         return VLA_ERR_SHAPE;
     }
     if ((long)d->batch * d->horizon > (1L << 24)) {
@@ -298,6 +306,37 @@ int pack_linear(vla_ctx* c, Linear& lin, int N, int K, const void* const* srcs, 
         if (rc) return rc;
         HIPC(hipMemcpy(lin.scale, hs.data(), N * sizeof(float), hipMemcpyHostToDevice));
     }
+    return VLA_OK;
+}
+
+// gate and up in MXFP4 (codes two per byte, E8M0 scale per 32 inputs),
+// interleaved by row (gate even, up odd) like the bf16 / E4M3 packing.
+int pack_linear_mxfp4(vla_ctx* c, Linear& lin, int I, int K, const void* wg, const void* wu, const void* sg,
+                      const void* su) {
+    lin.N = 2 * I;
+    lin.K = K;
+    lin.fmt = 2;
+    int rc = c->alloc(&lin.w, (size_t)lin.N * K / 2);
+    if (rc) return rc;
+    const void* srcs[2] = {wg, wu};
+    const long total = (long)I * (K / 8);
+    for (int s = 0; s < 2; ++s) {
+        hipLaunchKernelGGL(pack_weight_kernel, dim3((int)((total + 255) / 256)), dim3(256), 0, c->stream,
+                           (const uint8_t*)srcs[s], I, K, 1, (uint8_t*)lin.w, 2, 0, 1, s, 2);
+        HIPC(hipGetLastError());
+    }
+    const int Kb = K / 32;
+    std::vector<uint8_t> hg((size_t)I * Kb), hu((size_t)I * Kb), hp((size_t)lin.N * Kb);
+    HIPC(hipMemcpy(hg.data(), sg, hg.size(), hipMemcpyDeviceToHost));
+    HIPC(hipMemcpy(hu.data(), su, hu.size(), hipMemcpyDeviceToHost));
+    for (int r = 0; r < I; ++r)
+        for (int s = 0; s < 2; ++s) {
+            const int drow = 2 * r + s;
+            for (int kb = 0; kb < Kb; ++kb)
+                hp[((size_t)(drow / 16) * Kb + kb) * 16 + drow % 16] = (s ? hu : hg)[(size_t)r * Kb + kb];
+        }
+    if ((rc = c->alloc((void**)&lin.bscale, hp.size()))) return rc;
+    HIPC(hipMemcpy(lin.bscale, hp.data(), hp.size(), hipMemcpyHostToDevice));
     return VLA_OK;
 }
 
@@ -389,14 +428,14 @@ int launch_tiled8_t(int epi, const GemmParams& p, dim3 grid, hipStream_t s) {
     return VLA_OK;
 }
 
-template <bool W8>
+template <int WF>
 int launch_skinny_t(int epi, const GemmParams& p, dim3 grid, hipStream_t s) {
     switch (epi) {
-        case EPI_BIAS_F32: VLA_LAUNCH((skinny_gemm_kernel<W8, EPI_BIAS_F32>), grid, dim3(512), 0, s, p); break;
-        case EPI_RESID: VLA_LAUNCH((skinny_gemm_kernel<W8, EPI_RESID>), grid, dim3(512), 0, s, p); break;
-        case EPI_QKV_ROPE: VLA_LAUNCH((skinny_gemm_kernel<W8, EPI_QKV_ROPE>), grid, dim3(512), 0, s, p); break;
-        case EPI_SWIGLU: VLA_LAUNCH((skinny_gemm_kernel<W8, EPI_SWIGLU>), grid, dim3(512), 0, s, p); break;
-        case EPI_PARTIAL: VLA_LAUNCH((skinny_gemm_kernel<W8, EPI_PARTIAL>), grid, dim3(512), 0, s, p); break;
+        case EPI_BIAS_F32: VLA_LAUNCH((skinny_gemm_kernel<WF, EPI_BIAS_F32>), grid, dim3(512), 0, s, p); break;
+        case EPI_RESID: VLA_LAUNCH((skinny_gemm_kernel<WF, EPI_RESID>), grid, dim3(512), 0, s, p); break;
+        case EPI_QKV_ROPE: VLA_LAUNCH((skinny_gemm_kernel<WF, EPI_QKV_ROPE>), grid, dim3(512), 0, s, p); break;
+        case EPI_SWIGLU: VLA_LAUNCH((skinny_gemm_kernel<WF, EPI_SWIGLU>), grid, dim3(512), 0, s, p); break;
+        case EPI_PARTIAL: VLA_LAUNCH((skinny_gemm_kernel<WF, EPI_PARTIAL>), grid, dim3(512), 0, s, p); break;
         default: set_err("bad skinny epilogue %d", epi); return VLA_ERR_ARG;
     }
     HIPC(hipGetLastError());
@@ -421,7 +460,15 @@ int launch_gemm(vla_ctx* c, const Linear& lin, const GemmCfg& cfg, bool w8, int 
             epi = EPI_PARTIAL;
         }
         dim3 grid(cfg.gx, cfg.ksplit);
-        return w8 ? launch_skinny_t<true>(epi, p, grid, c->stream) : launch_skinny_t<false>(epi, p, grid, c->stream);
+        if (lin.fmt == 2) {
+            p.bscale = lin.bscale;
+            return launch_skinny_t<2>(epi, p, grid, c->stream);
+        }
+        return w8 ? launch_skinny_t<1>(epi, p, grid, c->stream) : launch_skinny_t<0>(epi, p, grid, c->stream);
+    }
+    if (lin.fmt == 2) {
+        set_err("MXFP4 weights run the weight-streaming kernel only (batch*horizon <= 64)");
+        return VLA_ERR_SHAPE;
     }
     if (lin.K % GEMM_KT != 0) {
         set_err("tiled GEMM needs K %% %d == 0 (K = %d)", GEMM_KT, lin.K);
@@ -859,7 +906,8 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
     const vla_dims& d = c->d;
     const int H = d.hidden, A = d.action_dim, E = d.time_emb_dim, L = d.n_layers, I = d.intermediate;
     const int dh = d.head_dim;
-    c->w8 = d.weight_dtype == VLA_FP8_E4M3;
+    c->w8 = d.weight_dtype == VLA_FP8_E4M3 || d.weight_dtype == VLA_FP8_E4M3_MXFP4_GU;
+    c->gu4 = d.weight_dtype == VLA_FP8_E4M3_MXFP4_GU;
     c->M = d.batch * d.horizon;
     c->qd = d.n_q_heads * dh;
     c->kvd = d.n_kv_heads * dh;
@@ -940,7 +988,9 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
             int rows[1] = {H};
             if ((rc = pack_linear(c, c->wo[l], H, c->qd, srcs, scs, 1, rows, 0, dh))) return rc;
         }
-        {
+        if (c->gu4) {
+            if ((rc = pack_linear_mxfp4(c, c->gu[l], I, H, w->wg[l], w->wu[l], w->sg[l], w->su[l]))) return rc;
+        } else {
             const void* srcs[2] = {w->wg[l], w->wu[l]};
             const float* scs[2] = {c->w8 ? w->sg[l] : nullptr, c->w8 ? w->su[l] : nullptr};
             int rows[2] = {I, I};
@@ -1339,7 +1389,8 @@ int vla_profile_kernel(vla_ctx* c, int kernel, int iters, double* us_per_launch,
             flops = 2.0 * M * (double)H * c->qd;
             break;
         case VLA_KERNEL_GATE_UP:
-            bytes = wb * 2.0 * I * H + 2.0 * M * H + 2.0 * M * I;
+            // MXFP4: half a byte per weight plus one scale byte per 32
+            bytes = (c->gu4 ? 0.5 + 1.0 / 32 : wb) * 2.0 * I * H + 2.0 * M * H + 2.0 * M * I;
             flops = 4.0 * M * (double)I * H;
             break;
         case VLA_KERNEL_DOWN:

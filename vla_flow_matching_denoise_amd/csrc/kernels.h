@@ -56,6 +56,14 @@ __global__ void pack_weight_kernel(const uint8_t* __restrict__ src, int R, int K
     }
     int k = kc * 8;
     size_t dst_off_b;
+    if (layout == 2) {
+        // E2M1 codes (two per byte, element 2j low): the 16 x 32 fragments of
+        // layout 0 with 4 bytes (8 codes) per lane
+        const int Kf = K / 32, lane = (drow % 16) + 16 * ((k % 32) / 8);
+        const size_t frag = (size_t)(drow / 16) * Kf + k / 32;
+        *(uint32_t*)(dst + (frag * 64 + lane) * 4) = *(const uint32_t*)(src + ((size_t)r * K + k) / 2);
+        return;
+    }
     if (layout == 1) {
         // E4M3 fragments of the 16x16x128 FP8 MFMA: 16 rows x 128 inputs, two
         // 1 KiB halves; lane l = row%16 + 16*(w/32) holds inputs w%32 of the

@@ -189,6 +189,7 @@ struct GemmParams {
     int afrag;           // act (SwiGLU output) written in A-fragment order
     int tile_map;        // tiled kernel: 1 = row tiles split over the XCDs (grid padded to 8 row-tile groups)
     const float* ascale; // FP8 tiled kernel: per-row scales of the E4M3 A operand
+    const uint8_t* bscale; // MXFP4 weights: E8M0 scale per (packed row, 32 inputs), [N/16][K/32][16]
     const void* W;       // packed fragments
     const float* wscale; // per packed row (E4M3), else null
     int M, N, K;
@@ -358,8 +359,35 @@ VLA_DEV void epilogue16(const GemmParams& p, int row, int col0, const float (&v)
 constexpr int SK_WAVES = 8;
 constexpr int SK_MAXS = 6;  // k-steps (of 32) per wave: K split <= 8 * 6 * 32 = 1536
 
-template <bool W8, int EPI>
+// Eight E2M1 codes (element j in bits 4j..4j+3) times the E8M0 block scale
+// 2^(e - 127) as bf16: a nonzero E2M1 magnitude (1 + m/2) * 2^(x - 1) (x >= 1)
+// or 0.5 (x = 0, m = 1) has bf16 exponent field 126 + x (126 for 0.5) and
+// mantissa m at the top bit; the scale adds e - 127 to the exponent field
+// (exact while the result stays a normal bf16, as for weights of any
+// reasonable size).
+VLA_DEV bf16x8 e2m1x8_to_bf16x8(uint32_t w, uint32_t e) {
+    const int sh = ((int)e - 127) << 7;
+    uint32_t r[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t h[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint32_t c = (w >> (8 * j + 4 * t)) & 15u, m = c & 7u, x = m >> 1;
+            uint32_t b = m == 1u ? 0x3F00u : (((126u + x) << 7) | ((m & 1u) << 6));
+            b = m == 0u ? 0u : (uint32_t)((int)b + sh);
+            h[t] = b | ((c >> 3) << 15);
+        }
+        r[j] = h[0] | (h[1] << 16);
+    }
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+// WF: weight format, 0 bf16, 1 E4M3 (fp32 scale per output row), 2 MXFP4
+// (E2M1 codes, E8M0 scale per 32 inputs).
+template <int WF, int EPI>
 __global__ __launch_bounds__(512) void skinny_gemm_kernel(GemmParams p) {
+    constexpr bool W8 = WF == 1;
     __shared__ __attribute__((aligned(16))) float red[2][SK_WAVES][4][64][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int kz = blockIdx.y;
@@ -382,14 +410,21 @@ __global__ __launch_bounds__(512) void skinny_gemm_kernel(GemmParams p) {
             af[i][mt] = i < ns ? *(const bf16x8*)(p.A + ((size_t)((kt0 + s_beg + i) * 4 + mt) * 64 + lane) * 8)
                                : (bf16x8){};
 
-    constexpr int WREG = W8 ? 2 : 4;  // dwords of one weight fragment slice per lane
-    typedef __attribute__((ext_vector_type(WREG))) unsigned wvec;
+    constexpr int WREG = WF == 2 ? 1 : (W8 ? 2 : 4);  // dwords of one weight fragment slice per lane
+    typedef __attribute__((ext_vector_type(WREG == 1 ? 2 : WREG))) unsigned wvec;
+    // MXFP4: the block scale of the lane's row (l%16) rides in the second dword
     auto load_w = [&](int nt, wvec* dst) {
 #pragma unroll
         for (int i = 0; i < SK_MAXS; ++i)
-            if (i < ns)
-                dst[i] = *(const wvec*)((const uint8_t*)p.W +
-                                        (((size_t)nt * Kf + kt0 + s_beg + i) * 64 + lane) * (W8 ? 8 : 16));
+            if (i < ns) {
+                const size_t frag = (size_t)nt * Kf + kt0 + s_beg + i;
+                if constexpr (WF == 2) {
+                    dst[i][0] = *(const uint32_t*)((const uint8_t*)p.W + (frag * 64 + lane) * 4);
+                    dst[i][1] = p.bscale[frag * 16 + (lane & 15)];
+                } else {
+                    dst[i] = *(const wvec*)((const uint8_t*)p.W + (frag * 64 + lane) * (W8 ? 8 : 16));
+                }
+            }
     };
 
     wvec wcur[SK_MAXS], wnext[SK_MAXS];
@@ -406,7 +441,8 @@ __global__ __launch_bounds__(512) void skinny_gemm_kernel(GemmParams p) {
         for (int i = 0; i < SK_MAXS; ++i) {
             if (i < ns) {
                 bf16x8 b;
-                if constexpr (W8) b = e4m3x8_to_bf16x8(wcur[i]);
+                if constexpr (WF == 2) b = e2m1x8_to_bf16x8(wcur[i][0], wcur[i][1]);
+                else if constexpr (W8) b = e4m3x8_to_bf16x8(wcur[i]);
                 else b = __builtin_bit_cast(bf16x8, wcur[i]);
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt) acc[mt] = mfma_16x16x32(af[i][mt], b, acc[mt]);

@@ -21,7 +21,8 @@ BLOCK = ("wq", "wk", "wv", "wo", "wg", "wu", "wd")
 def make_dims(n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate, action_dim, horizon,
               prefix_len, batch, time_emb_dim=256, rope_theta=1.0e6, rms_eps=1.0e-6, time_scale=1000.0,
               weight_dtype="bf16") -> B.VlaDims:
-    wd = {"bf16": B.VLA_BF16, "fp8_e4m3": B.VLA_FP8_E4M3}[weight_dtype] if isinstance(weight_dtype, str) \
+    wd = {"bf16": B.VLA_BF16, "fp8_e4m3": B.VLA_FP8_E4M3,
+          "fp8_mxfp4gu": B.VLA_FP8_E4M3_MXFP4_GU}[weight_dtype] if isinstance(weight_dtype, str) \
         else int(weight_dtype)
     return B.VlaDims(n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate, action_dim, horizon,
                      prefix_len, batch, time_emb_dim, rope_theta, rms_eps, time_scale, wd)
