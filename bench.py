@@ -318,6 +318,21 @@ def main():
                       "p50_ms": round(float(np.percentile(pc_p, 50)), 4)}
     ex.set_option(B.VLA_OPT_PERSISTENT, 0)
     ex.close()
+    # the same batch-1 workload with E4M3 block linears and MXFP4 gate/up
+    cfg4 = synth.config(4).replace(weight_dtype="fp8_mxfp4gu", n_steps=cfg.n_steps)
+    log("[bench] batch-1 E4M3 + MXFP4 gate_up workload")
+    ex4 = Expert(synth.make_weights(cfg4, seed=0), dims_from_config(cfg4))
+    dev4, _ = build_inputs(cfg4)
+    wall4, _, _ = time_calls(ex4, dev4, cfg4.n_steps, args.warmup, args.steps)
+    t4 = wall4 / args.steps
+    kr4 = kernel_rooflines(ex4, cfg4, args.profile_iters)
+    ex4.close()
+    mxfp4 = {"workload": "lingbot_36L_h1024_chunk50x75_euler10_b1_e4m3_mxfp4_gate_up",
+             "ms_per_call": round(t4 * 1e3, 4), "steps_per_s": round(cfg4.n_steps / t4, 3),
+             "gate_up": {"us": round(kr4["gate_up_swiglu_gemm"]["us"], 3),
+                         "algorithmic_bytes": int(kr4["gate_up_swiglu_gemm"]["bytes"]),
+                         "GBps": round(kr4["gate_up_swiglu_gemm"]["GBps"], 1),
+                         "frac": round(kr4["gate_up_swiglu_gemm"]["GBps"] / HBM_PEAK_GBS, 4)}}
 
     result = {
         "metric": METRIC,
@@ -345,6 +360,7 @@ def main():
         "kernels": {k: {"us": round(v["us"], 3), "GBps": round(v["GBps"], 1), "TFLOPs": round(v["TFLOPs"], 2)}
                     for k, v in kr.items()},
         "persistent_b1": persistent,
+        "b1_e4m3_mxfp4_gate_up": mxfp4,
     }
 
     if not args.no_batch64:
