@@ -49,6 +49,8 @@ __all__ = [
     "rms_normalize", "ada_rms_norm", "rope_rotate_half", "softmax",
     "gqa_attention", "expert_layer", "velocity", "denoise", "denoise_varlen", "cosine",
     "quantize_e4m3fn", "quantize_per_token_e4m3", "decode_e2m1", "decode_mxfp4",
+    "BackboneDims", "decode_backbone_weights", "rms_norm_weighted", "causal_gqa_attention",
+    "backbone_layer", "prefill",
 ]
 
 
@@ -403,3 +405,100 @@ def cosine(a: np.ndarray, b: np.ndarray) -> float:
     a = np.asarray(a, np.float64).ravel()
     b = np.asarray(b, np.float64).ravel()
     return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+
+
+# ----------------------------------------------------------------------------
+# The step before the loop: prefix K/V construction ("LingBot-VLA on Thor
+# (sm_110)", section 1: a 36-layer Qwen2.5-VL prefix whose self-attention
+# builds the cache; "LingBot-VLA v2 Examples", section "Configuration / CUDA
+# Graph": the 36-layer KV-cache construction runs eagerly per request before
+# the denoise loop).  The pages give no layer equations; the reading taken is
+# the plain pre-norm decoder layer of that backbone family:
+#   y = RMSNorm(x) * n1;  q, k, v = y Wq^T, y Wk^T, y Wv^T (no biases);
+#   q, k <- rotate-half RoPE at positions 0..P-1;  o = causal GQA attention;
+#   x = x + o Wo^T;  y = RMSNorm(x) * n2;  x = x + (SiLU(y Wg^T) * (y Wu^T)) Wd^T
+# and the cache of layer l is (roped k, v) of that layer.
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class BackboneDims:
+    n_layers: int
+    hidden: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    intermediate: int
+    prefix_len: int
+    rope_theta: float = 1.0e6
+    rms_eps: float = 1.0e-6
+
+    @classmethod
+    def from_config(cls, cfg) -> "BackboneDims":
+        return cls(cfg.n_layers, cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.intermediate,
+                   cfg.prefix_len, cfg.rope_theta, cfg.rms_eps)
+
+
+def decode_backbone_weights(raw: dict, dtype=np.float64) -> Dict[str, list]:
+    out: Dict[str, list] = {}
+    for name in ("n1", "n2"):
+        out[name] = [np.asarray(w, np.float64).astype(dtype) for w in raw[name]]
+    for name in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"):
+        out[name] = [decode_bf16(w, dtype) for w in raw[name]]
+    return out
+
+
+def rms_norm_weighted(x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm with a learned per-channel weight: x / sqrt(mean(x^2) + eps) * w."""
+    return rms_normalize(x, eps) * w
+
+
+def causal_gqa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """q [n_q, P, d_h], k/v [n_kv, P, d_h]: query i attends to keys j <= i;
+    head j reads KV head j // (n_q / n_kv); scale 1/sqrt(d_h)."""
+    nq, P, dh = q.shape
+    G = nq // k.shape[0]
+    out = np.empty_like(q)
+    mask = np.tril(np.ones((P, P), dtype=bool))
+    for j in range(nq):
+        g = j // G
+        s = (q[j] @ k[g].T) / math.sqrt(dh)
+        s = np.where(mask, s, -np.inf)
+        out[j] = softmax(s) @ v[g]
+    return out
+
+
+def backbone_layer(x: np.ndarray, W: dict, l: int, dims: BackboneDims):
+    """One prefix decoder layer on x [P, H]; returns (x, k, v) with k (roped)
+    and v [n_kv, P, d_h]."""
+    P = x.shape[0]
+    nq, nkv, dh = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    y = rms_norm_weighted(x, W["n1"][l], dims.rms_eps)
+    q = (y @ W["wq"][l].T).reshape(P, nq, dh).transpose(1, 0, 2)
+    k = (y @ W["wk"][l].T).reshape(P, nkv, dh).transpose(1, 0, 2)
+    v = (y @ W["wv"][l].T).reshape(P, nkv, dh).transpose(1, 0, 2)
+    pos = np.arange(P)
+    q = rope_rotate_half(q, pos, dims.rope_theta)
+    k = rope_rotate_half(k, pos, dims.rope_theta)
+    o = causal_gqa_attention(q, k, v).transpose(1, 0, 2).reshape(P, nq * dh)
+    x = x + o @ W["wo"][l].T
+    y = rms_norm_weighted(x, W["n2"][l], dims.rms_eps)
+    x = x + (silu(y @ W["wg"][l].T) * (y @ W["wu"][l].T)) @ W["wd"][l].T
+    return x, k, v
+
+
+def prefill(W: dict, dims: BackboneDims, emb: np.ndarray, n_layers: Optional[int] = None):
+    """Prefix cache of every request: emb [B, P, H] (decoded floats) ->
+    (prefix_k, prefix_v) [B, L, P, n_kv, d_h] in W's dtype (the layout
+    ``denoise`` takes).  ``n_layers`` limits the layers computed."""
+    L = dims.n_layers if n_layers is None else n_layers
+    B, P = emb.shape[0], emb.shape[1]
+    dtype = W["wq"][0].dtype
+    pk = np.empty((B, L, P, dims.n_kv_heads, dims.head_dim), dtype=dtype)
+    pv = np.empty_like(pk)
+    for b in range(B):
+        x = np.asarray(emb[b], dtype=dtype)
+        for l in range(L):
+            x, k, v = backbone_layer(x, W, l, dims)
+            pk[b, l] = k.transpose(1, 0, 2)
+            pv[b, l] = v.transpose(1, 0, 2)
+    return pk, pv

@@ -39,6 +39,7 @@ import torch
 __all__ = [
     "ExpertConfig", "CONFIGS", "config", "make_weights", "make_prefix",
     "make_noise", "make_schedule", "apply_variant", "BLOCK_LINEARS",
+    "BackboneConfig", "BACKBONES", "backbone", "make_backbone_weights", "make_embeddings",
 ]
 
 # Per-layer linears of the expert block that the fp8 tier quantizes.
@@ -283,3 +284,76 @@ def make_schedule(n_steps: int, batch: int, kind: str = "uniform", seed: int = 0
         out[:, -1] = 1.0
         return out
     raise ValueError(f"unknown schedule kind {kind!r}")
+
+
+# ----------------------------------------------------------------------------
+# The prefix backbone (the step before the loop): a decoder whose per-layer
+# K/V become the expert's prefix cache, so its n_layers, n_kv_heads and
+# head_dim equal the expert's.
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class BackboneConfig:
+    name: str
+    model_tag: int
+    n_layers: int
+    hidden: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    intermediate: int
+    prefix_len: int
+    batch: int
+    rope_theta: float = 1.0e6
+    rms_eps: float = 1.0e-6
+    weight_std: float = 0.02
+
+    def replace(self, **kw) -> "BackboneConfig":
+        return dataclasses.replace(self, **kw)
+
+
+# tiny (for the tiny expert) and the LingBot-shaped 36-layer prefix backbone
+# (Qwen2.5-VL-3B text widths: hidden 2048, 16 query / 2 KV heads of 128,
+# SwiGLU 11008; prefix 256 = 3 views x 64 merged patches + 64 text tokens)
+BACKBONES: Dict[int, BackboneConfig] = {
+    1: BackboneConfig("backbone_tiny_2L_h256", 11, 2, 256, 4, 2, 64, 704, 32, 1),
+    2: BackboneConfig("backbone_lingbot_36L_h2048", 12, 36, 2048, 16, 2, 128, 11008, 256, 1),
+}
+
+
+def backbone(i: int) -> BackboneConfig:
+    return BACKBONES[i]
+
+
+_BB_IDS = {"n1": 1, "n2": 2, "wq": 3, "wk": 4, "wv": 5, "wo": 6, "wg": 7, "wu": 8, "wd": 9}
+
+
+def make_backbone_weights(cfg: BackboneConfig, seed: int = 0) -> dict:
+    """Per-layer lists: ``n1``, ``n2`` RMSNorm weights float32 [H] (1 + N(0, 0.1^2));
+    ``wq`` [n_q*d_h, H], ``wk``, ``wv`` [n_kv*d_h, H], ``wo`` [H, n_q*d_h],
+    ``wg``, ``wu`` [I, H], ``wd`` [H, I] as bf16 bits, N(0, std^2)."""
+    H, I = cfg.hidden, cfg.intermediate
+    qd, kvd = cfg.n_q_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+    shapes = {"wq": (qd, H), "wk": (kvd, H), "wv": (kvd, H), "wo": (H, qd), "wg": (I, H), "wu": (I, H),
+              "wd": (H, I)}
+    W: Dict[str, list] = {k: [] for k in _BB_IDS}
+    for l in range(cfg.n_layers):
+        for name in ("n1", "n2"):
+            r = np.random.default_rng([seed, cfg.model_tag, _BB_IDS[name], l])
+            W[name].append((1.0 + 0.1 * r.standard_normal(H)).astype(np.float32))
+        for name, shp in shapes.items():
+            r = np.random.default_rng([seed, cfg.model_tag, _BB_IDS[name], l])
+            x = r.standard_normal(size=shp, dtype=np.float32) * np.float32(cfg.weight_std)
+            W[name].append(to_bf16_bits(x))
+    return W
+
+
+def make_embeddings(cfg: BackboneConfig, seed: int = 0, requests: Optional[List[int]] = None) -> np.ndarray:
+    """Prefix token embeddings (vision patches + text), bf16 bits ``[B, P, H]``,
+    N(0, 1); request b from its own stream."""
+    reqs = list(range(cfg.batch)) if requests is None else list(requests)
+    out = np.empty((len(reqs), cfg.prefix_len, cfg.hidden), dtype=np.uint16)
+    for i, b in enumerate(reqs):
+        r = np.random.default_rng([seed, cfg.model_tag, 5000 + b])
+        out[i] = to_bf16_bits(r.standard_normal(size=(cfg.prefix_len, cfg.hidden), dtype=np.float32))
+    return out

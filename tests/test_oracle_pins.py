@@ -5,6 +5,7 @@ pages print no worked numerical example of the action expert, so the pins are
 library routines (torch, scipy), closed forms that follow from the method's
 structure, invariants and brute force on tiny inputs.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -633,3 +634,65 @@ def test_mxfp4_generated_weights_within_the_format_bound():
         assert np.all(err[r <= 6] <= (step[r <= 6] / 2 + np.abs(w[r <= 6]) / X[r <= 6] * 2 ** -8) * X[r <= 6] + 1e-12)
         assert np.all(np.abs(deq[r > 6]) == 6 * X[r > 6])
         assert np.corrcoef(deq.ravel(), w.ravel())[0, 1] > 0.98
+
+
+# ---------------------------------------------------------------------------
+# Prefix K/V construction (backbone prefill)
+# ---------------------------------------------------------------------------
+
+def test_causal_attention_matches_torch_sdpa():
+    """Causal GQA attention against torch's scaled_dot_product_attention with
+    is_causal (fp64, KV heads repeated per group). Catches an off-by-one in
+    the mask or a wrong group mapping."""
+    nq, nkv, P, dh = 6, 2, 9, 8
+    q, k, v = (RNG.standard_normal(s) for s in ((nq, P, dh), (nkv, P, dh), (nkv, P, dh)))
+    got = oracle.causal_gqa_attention(q, k, v)
+    G = nq // nkv
+    kt = torch.tensor(k).repeat_interleave(G, dim=0)
+    vt = torch.tensor(v).repeat_interleave(G, dim=0)
+    want = torch.nn.functional.scaled_dot_product_attention(torch.tensor(q)[None], kt[None], vt[None],
+                                                            is_causal=True)[0].numpy()
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    # the last query sees every key: the unmasked attention's last row
+    np.testing.assert_allclose(got[:, -1], oracle.gqa_attention(q, k, v)[:, -1], rtol=1e-12, atol=1e-12)
+
+
+def test_weighted_rms_norm_matches_torch():
+    x = RNG.standard_normal((5, 24))
+    w = RNG.standard_normal(24)
+    want = torch.nn.functional.rms_norm(torch.tensor(x), (24,), torch.tensor(w), eps=1e-6).numpy()
+    np.testing.assert_allclose(oracle.rms_norm_weighted(x, w, 1e-6), want, rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_is_causal_in_its_tokens():
+    """The cache of the first n tokens does not depend on later tokens (every
+    layer): prefill of a truncated prefix equals the first n positions of the
+    full one. Also why a prefix padded at its end gives exact caches for its
+    valid tokens."""
+    bcfg = synth.backbone(1).replace(prefix_len=12, batch=2)
+    W = oracle.decode_backbone_weights(synth.make_backbone_weights(bcfg, seed=2))
+    d = oracle.BackboneDims.from_config(bcfg)
+    emb = oracle.decode_bf16(synth.make_embeddings(bcfg, seed=3))
+    pk, pv = oracle.prefill(W, d, emb)
+    n = 7
+    pk7, pv7 = oracle.prefill(W, dataclasses.replace(d, prefix_len=n), emb[:, :n])
+    np.testing.assert_allclose(pk7, pk[:, :, :n], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(pv7, pv[:, :, :n], rtol=1e-12, atol=1e-12)
+    # and a later token does change later positions (the mask is not all-blocking)
+    emb2 = emb.copy()
+    emb2[:, n] += 1.0
+    pk2, _ = oracle.prefill(W, d, emb2)
+    assert np.abs(pk2[:, 1, n + 1:] - pk[:, 1, n + 1:]).max() > 1e-3
+
+
+def test_prefill_position_zero_key_is_unrotated():
+    """RoPE at position 0 is the identity: layer 0's first key equals the
+    normalized first embedding times Wk (a special case of the layer)."""
+    bcfg = synth.backbone(1).replace(prefix_len=4)
+    W = oracle.decode_backbone_weights(synth.make_backbone_weights(bcfg, seed=1))
+    d = oracle.BackboneDims.from_config(bcfg)
+    emb = oracle.decode_bf16(synth.make_embeddings(bcfg, seed=1))
+    pk, _ = oracle.prefill(W, d, emb, n_layers=1)
+    x0 = emb[0, 0]
+    y0 = x0 / np.sqrt(np.mean(x0 ** 2) + d.rms_eps) * W["n1"][0]
+    np.testing.assert_allclose(pk[0, 0, 0].ravel(), W["wk"][0] @ y0, rtol=1e-10, atol=1e-12)
