@@ -70,7 +70,7 @@ extern "C" {
  * not spread 32 per XCD. After 1-3 the call's output holds NaN. */
 #define VLA_OPT_PERSISTENT_STATUS 4
 /* Tile shape of the tiled GEMM (used where batch*horizon > 64): 0 (default) picks one per linear from
- * a cost model; 1, 2, 3 force 256x256, 128x128, 128x64 tiles where they divide the output width, also
+ * a cost model; 1, 2, 3, 4 force 256x256, 128x128, 128x64, 256x128 tiles where they divide the output width, also
  * for batch*horizon <= 64 (in place of the weight-streaming kernel). For testing and tuning; setting it
  * waits for the ctx stream and drops captured graphs. */
 #define VLA_OPT_GEMM_TILE 5

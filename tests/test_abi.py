@@ -1,19 +1,22 @@
 """The C-ABI library loads and exports every entry point its header declares;
 argument validation that runs before any HIP call works without a GPU."""
 import ctypes
+import glob
 import os
 import re
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "vla_expert.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(vla_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(vla_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -27,7 +30,8 @@ def lib():
 
 def test_header_declares_the_product_calls():
     names = declared_functions()
-    for n in ("vla_expert_create", "vla_denoise", "vla_set_stream", "vla_expert_destroy", "vla_last_error"):
+    for n in ("vla_expert_create", "vla_denoise", "vla_set_stream", "vla_expert_destroy", "vla_last_error",
+              "vla_prefill_create", "vla_prefill", "vla_prefill_destroy"):
         assert n in names
 
 
@@ -77,3 +81,28 @@ def test_mxfp4_gate_up_tier_rejects_more_than_64_rows(lib):
     d = make_dims(2, 256, 4, 2, 64, 704, 7, 16, 32, 4, weight_dtype="fp8_mxfp4gu")   # 64 rows
     assert lib.vla_expert_create(ctypes.byref(w), ctypes.byref(d)) is None
     assert "MXFP4" not in B.vla_last_error()          # fails later, on the NULL weight pointers
+
+
+def test_prefill_host_side_argument_errors(lib):
+    from vla_flow_matching_denoise_amd import binding as B
+    assert lib.vla_prefill(None, None, None, None) == B.VLA_ERR_ARG
+    assert "NULL" in B.vla_last_error()
+    assert lib.vla_prefill_set_option(None, B.VLA_OPT_USE_GRAPH, 1) == B.VLA_ERR_ARG
+    assert lib.vla_prefill_set_stream(None, None) == B.VLA_ERR_ARG
+    assert lib.vla_prefill_create(None, None) is None
+    assert "weights" in B.vla_last_error()
+    lib.vla_prefill_destroy(None)                      # NULL-safe
+    assert lib.vla_prefill_device_bytes(None) == 0
+
+
+@pytest.mark.parametrize("field,value", [("head_dim", 96), ("hidden", 1000), ("hidden", 8192), ("n_kv_heads", 3),
+                                         ("intermediate", 100), ("prefix_len", 0), ("prefix_len", 9000),
+                                         ("batch", 0), ("rms_eps", 0.0)])
+def test_prefill_unsupported_dims_are_rejected_before_any_device_work(lib, field, value):
+    from vla_flow_matching_denoise_amd import binding as B
+    from vla_flow_matching_denoise_amd.prefill import backbone_dims
+    d = backbone_dims(2, 256, 4, 2, 64, 704, 32, 1)
+    setattr(d, field, value)
+    w = B.VlaBackboneWeights()
+    assert lib.vla_prefill_create(ctypes.byref(w), ctypes.byref(d)) is None
+    assert "unsupported" in B.vla_last_error() or "must" in B.vla_last_error()

@@ -1,0 +1,181 @@
+"""GPU parity of the prefix K/V construction (the backbone prefill) against the
+oracle's ``prefill``, through the C ABI (vla_prefill_create / vla_prefill).
+
+Every layer's keys and values are compared element by element: cosine >=
+0.9995 and max-abs <= 2e-2 * sqrt(l + 1) x the RMS of layer l. The bf16
+max-abs gate grows with depth because the cache of layer l carries the
+rounding of l + 1 layers (bf16 GEMM/attention inputs, bf16 outputs; fp32
+accumulation and residual stream), independent errors that add in
+quadrature: the oracle with bf16 rounding inserted where the GPU path rounds
+differs from the exact oracle by max-abs 0.012-0.014 x RMS at layer 0, 0.023
+at layer 3 and 0.030 at layer 7 of the 36-layer backbone. Cases:
+the tiny backbone at ragged prefix lengths and batches (causal tiles that
+straddle two heads, a one-token prefix), the 36-layer LingBot-shaped backbone
+at P = 256 (the full workload), eager launches against the graph replay,
+every GEMM tile, and the prefill output fed to the expert's denoise loop.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import BF16_COS, BF16_MAXABS, say
+
+pytestmark = pytest.mark.gpu
+
+
+class _Lazy:
+    """Per-layer decode on access (the 36-layer backbone in fp64 would not fit at once)."""
+
+    def __init__(self, seq, fn):
+        self.seq, self.fn = seq, fn
+
+    def __getitem__(self, l):
+        return self.fn(self.seq[l])
+
+    def __len__(self):
+        return len(self.seq)
+
+
+def lazy_weights(raw):
+    return {k: _Lazy(v, (lambda a: np.asarray(a, np.float64)) if k in ("n1", "n2") else oracle.decode_bf16)
+            for k, v in raw.items()}
+
+
+def run_gpu(bcfg, raw, embs, graph=True, tile=0):
+    """One Prefill context, one call per embedding tensor; returns [(k, v)] as float arrays."""
+    import torch
+    from vla_flow_matching_denoise_amd import binding as B
+    from vla_flow_matching_denoise_amd.expert import to_device
+    from vla_flow_matching_denoise_amd.prefill import Prefill, backbone_dims_from_config
+    pf = Prefill(raw, backbone_dims_from_config(bcfg))
+    out = []
+    try:
+        if not graph:
+            pf.set_option(B.VLA_OPT_USE_GRAPH, 0)
+        if tile:
+            pf.set_option(B.VLA_OPT_GEMM_TILE, tile)
+        for e in embs:
+            k, v = pf(to_device(e))
+            torch.cuda.synchronize()
+            out.append((oracle.decode_bf16(k.cpu().numpy().view(np.uint16)),
+                        oracle.decode_bf16(v.cpu().numpy().view(np.uint16))))
+    finally:
+        pf.close()
+    return out
+
+
+def check(tag, got, ref):
+    """got/ref: [B, L, P, n_kv, d_h]; per layer gates (module docstring)."""
+    worst = (1.0, 0.0)
+    for l in range(ref.shape[1]):
+        g, r = got[:, l], ref[:, l]
+        rms = float(np.sqrt(np.mean(r ** 2)))
+        cos = oracle.cosine(g, r)
+        mx = float(np.max(np.abs(g - r)) / rms)
+        worst = (min(worst[0], cos), max(worst[1], mx / np.sqrt(l + 1)))
+        assert cos >= BF16_COS and mx <= BF16_MAXABS * np.sqrt(l + 1), (tag, l, cos, mx)
+    say(f"[prefill] {tag}: worst layer cosine {worst[0]:.6f}, max over layers of "
+        f"max-abs/RMS/sqrt(l+1) {worst[1]:.2e}; last layer cosine {cos:.6f}, max-abs/RMS {mx:.2e}")
+
+
+def oracle_prefill(bcfg, raw, emb):
+    return oracle.prefill(lazy_weights(raw), oracle.BackboneDims.from_config(bcfg), oracle.decode_bf16(emb))
+
+
+@pytest.mark.parametrize("batch,P", [(2, 32), (3, 45), (1, 1), (2, 100)])
+def test_prefill_tiny(batch, P):
+    bcfg = synth.backbone(1).replace(batch=batch, prefix_len=P)
+    raw = synth.make_backbone_weights(bcfg, seed=3)
+    emb = synth.make_embeddings(bcfg, seed=4)
+    say(f"[prefill] tiny backbone, batch {batch}, P {P}")
+    (k, v), = run_gpu(bcfg, raw, [emb])
+    rk, rv = oracle_prefill(bcfg, raw, emb)
+    check(f"tiny b{batch} P{P} keys", k, rk)
+    check(f"tiny b{batch} P{P} values", v, rv)
+
+
+@pytest.mark.timeout(600)
+def test_prefill_lingbot_36_layers():
+    """The LingBot-shaped backbone (36 layers, hidden 2048, 16 q / 2 KV heads
+    of 128, SwiGLU 11008) at P = 256, batch 1: all 36 layers' caches."""
+    bcfg = synth.backbone(2)
+    say("[prefill] LingBot backbone, 36 layers, P 256: generating weights")
+    raw = synth.make_backbone_weights(bcfg, seed=0)
+    emb = synth.make_embeddings(bcfg, seed=0)
+    (k, v), = run_gpu(bcfg, raw, [emb])
+    say("[prefill] GPU done; oracle")
+    rk, rv = oracle_prefill(bcfg, raw, emb)
+    check("LingBot 36L keys", k, rk)
+    check("LingBot 36L values", v, rv)
+
+
+def test_prefill_graph_replay_and_eager_agree():
+    """Two calls on one context (the second replays the captured graph with new
+    pointers) match the oracle, and eager launches give the same bits."""
+    bcfg = synth.backbone(1).replace(batch=2, prefix_len=70)
+    raw = synth.make_backbone_weights(bcfg, seed=7)
+    e1 = synth.make_embeddings(bcfg, seed=8)
+    e2 = synth.make_embeddings(bcfg, seed=9)
+    (k1, v1), (k2, v2) = run_gpu(bcfg, raw, [e1, e2])
+    rk2, rv2 = oracle_prefill(bcfg, raw, e2)
+    check("replayed graph keys", k2, rk2)
+    check("replayed graph values", v2, rv2)
+    (ek1, ev1), = run_gpu(bcfg, raw, [e1], graph=False)
+    assert np.array_equal(ek1, k1) and np.array_equal(ev1, v1)
+
+
+def _mid():
+    """3 layers at widths where the library splits K for O, down and QKV at
+    M = 192 rows (two requests of 96 tokens, not a multiple of the 128-row tile)."""
+    return synth.backbone(2).replace(n_layers=3, hidden=1024, n_q_heads=8, intermediate=2816, prefix_len=96,
+                                     batch=2)
+
+
+@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4])
+def test_prefill_every_gemm_tile(tile):
+    """Every tile shape (0: the library's choice, with split K; 1 = 256x256
+    also splits gate_up, so its SwiGLU runs in the split-K finish kernel)."""
+    bcfg = _mid()
+    raw = synth.make_backbone_weights(bcfg, seed=11)
+    emb = synth.make_embeddings(bcfg, seed=12)
+    (k, v), = run_gpu(bcfg, raw, [emb], tile=tile)
+    rk, rv = oracle_prefill(bcfg, raw, emb)
+    check(f"tile {tile} keys", k, rk)
+    check(f"tile {tile} values", v, rv)
+
+
+def test_prefill_feeds_the_denoise_loop():
+    """Prefill then denoise on the GPU (the cache stays on the device) against
+    the oracle's prefill then denoise: the two halves of a request."""
+    import torch
+    from vla_flow_matching_denoise_amd.expert import Expert, dims_from_config, to_device
+    from vla_flow_matching_denoise_amd.prefill import Prefill, backbone_dims_from_config
+    cfg = synth.config(1).replace(batch=2)
+    bcfg = synth.backbone(1).replace(batch=2)
+    assert (bcfg.n_layers, bcfg.n_kv_heads, bcfg.head_dim, bcfg.prefix_len) == \
+        (cfg.n_layers, cfg.n_kv_heads, cfg.head_dim, cfg.prefix_len)
+    raw_b = synth.make_backbone_weights(bcfg, seed=1)
+    emb = synth.make_embeddings(bcfg, seed=2)
+    raw_e = synth.make_weights(cfg, seed=3)
+    x0 = synth.make_noise(cfg, seed=4)
+    ts = synth.make_schedule(cfg.n_steps, cfg.batch)
+    pf = Prefill(raw_b, backbone_dims_from_config(bcfg))
+    ex = Expert(raw_e, dims_from_config(cfg))
+    try:
+        k, v = pf(to_device(emb))
+        out = ex.denoise(k, v, to_device(x0), to_device(ts), cfg.n_steps)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+    finally:
+        ex.close()
+        pf.close()
+    rk, rv = oracle_prefill(bcfg, raw_b, emb)
+    # the expert takes the cache in bf16, as the GPU hands it over
+    rk = oracle.decode_bf16(synth.to_bf16_bits(rk.astype(np.float32)))
+    rv = oracle.decode_bf16(synth.to_bf16_bits(rv.astype(np.float32)))
+    ref = oracle.denoise(oracle.decode_weights(raw_e), oracle.ExpertDims.from_config(cfg), rk, rv, x0, ts)
+    cos = oracle.cosine(got, ref)
+    mx = float(np.max(np.abs(got - ref)) / np.sqrt(np.mean(ref ** 2)))
+    say(f"[prefill -> denoise] cosine {cos:.7f}, max-abs/RMS {mx:.2e}")
+    assert cos >= BF16_COS and mx <= BF16_MAXABS, (cos, mx)

@@ -34,6 +34,8 @@ EXPORTED = (
     "vla_expert_destroy",
     "vla_last_error", "vla_device_bytes", "vla_test_modulation", "vla_test_layer",
     "vla_test_attention", "vla_profile_kernel",
+    "vla_prefill_create", "vla_prefill", "vla_prefill_set_stream", "vla_prefill_set_option", "vla_prefill_destroy",
+    "vla_prefill_device_bytes",
 )
 VLA_KERNEL_QKV, VLA_KERNEL_ATTN, VLA_KERNEL_O, VLA_KERNEL_GATE_UP, VLA_KERNEL_DOWN = range(5)
 
@@ -59,6 +61,22 @@ class VlaWeights(ctypes.Structure):
         ("mod_w", _PP), ("mod_b", _PP), ("modf_w", _P), ("modf_b", _P),
         ("wq", _PP), ("wk", _PP), ("wv", _PP), ("wo", _PP), ("wg", _PP), ("wu", _PP), ("wd", _PP),
         ("sq", _PP), ("sk", _PP), ("sv", _PP), ("so", _PP), ("sg", _PP), ("su", _PP), ("sd", _PP),
+    ]
+
+
+class VlaBackboneDims(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", ctypes.c_int32), ("hidden", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("intermediate", ctypes.c_int32),
+        ("prefix_len", ctypes.c_int32), ("batch", ctypes.c_int32), ("rope_theta", ctypes.c_float),
+        ("rms_eps", ctypes.c_float),
+    ]
+
+
+class VlaBackboneWeights(ctypes.Structure):
+    _fields_ = [
+        ("norm1", _PP), ("norm2", _PP), ("wq", _PP), ("wk", _PP), ("wv", _PP), ("wo", _PP), ("wg", _PP),
+        ("wu", _PP), ("wd", _PP),
     ]
 
 
@@ -98,6 +116,18 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.vla_profile_kernel.restype = ctypes.c_int
     lib.vla_profile_kernel.argtypes = [_P, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double),
                                        ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    lib.vla_prefill_create.restype = ctypes.c_void_p
+    lib.vla_prefill_create.argtypes = [ctypes.POINTER(VlaBackboneWeights), ctypes.POINTER(VlaBackboneDims)]
+    lib.vla_prefill.restype = ctypes.c_int
+    lib.vla_prefill.argtypes = [_P, _P, _P, _P]
+    lib.vla_prefill_set_stream.restype = ctypes.c_int
+    lib.vla_prefill_set_stream.argtypes = [_P, _P]
+    lib.vla_prefill_set_option.restype = ctypes.c_int
+    lib.vla_prefill_set_option.argtypes = [_P, ctypes.c_int, ctypes.c_int]
+    lib.vla_prefill_destroy.restype = None
+    lib.vla_prefill_destroy.argtypes = [_P]
+    lib.vla_prefill_device_bytes.restype = ctypes.c_int64
+    lib.vla_prefill_device_bytes.argtypes = [_P]
     return lib
 
 
@@ -192,3 +222,31 @@ def vla_profile_kernel(ctx: int, kernel: int, iters: int):
     _check(lib().vla_profile_kernel(ctx, int(kernel), int(iters), ctypes.byref(us), ctypes.byref(by),
                                     ctypes.byref(fl)))
     return us.value, by.value, fl.value
+
+
+def vla_prefill_create(weights: VlaBackboneWeights, dims: VlaBackboneDims) -> int:
+    h = lib().vla_prefill_create(ctypes.byref(weights), ctypes.byref(dims))
+    if not h:
+        raise VlaError(-1, vla_last_error())
+    return h
+
+
+def vla_prefill(ctx: int, embeddings: int, prefix_k: int, prefix_v: int, check: bool = True) -> int:
+    rc = lib().vla_prefill(ctx, embeddings, prefix_k, prefix_v)
+    return _check(rc) if check else rc
+
+
+def vla_prefill_set_stream(ctx: int, stream: Optional[int]) -> int:
+    return _check(lib().vla_prefill_set_stream(ctx, stream))
+
+
+def vla_prefill_set_option(ctx: int, option: int, value: int) -> int:
+    return _check(lib().vla_prefill_set_option(ctx, option, value))
+
+
+def vla_prefill_destroy(ctx: Optional[int]) -> None:
+    lib().vla_prefill_destroy(ctx)
+
+
+def vla_prefill_device_bytes(ctx: int) -> int:
+    return int(lib().vla_prefill_device_bytes(ctx))

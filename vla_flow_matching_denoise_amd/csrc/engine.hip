@@ -16,8 +16,10 @@
 #include <vector>
 
 #include "../../include/vla_expert.h"
+#include "../../include/vla_prefill.h"
 #include "kernels.h"
 #include "kernels_persist.h"
+#include "kernels_prefill.h"
 
 namespace {
 
@@ -79,9 +81,9 @@ struct GemmCfg {
 // the tile shape of least modelled time: rounds of `ncu` tiles times the
 // time of one tile relative to a 128x128 tile (measured at K = 1024: a
 // 256x256 tile takes 2.75 times as long, a 128x64 tile about 0.65).
-GemmCfg choose_gemm(int M, int N, int K, bool allow_split, int ncu, int force_tile = 0) {
+GemmCfg choose_gemm(int M, int N, int K, bool allow_split, int ncu, int force_tile = 0, bool tiled_only = false) {
     GemmCfg c;
-    if (M <= 64 && force_tile == 0) {
+    if (M <= 64 && force_tile == 0 && !tiled_only) {
         c.skinny = true;
         c.NT = 16;
         const int tiles = N / 16;
@@ -102,11 +104,11 @@ GemmCfg choose_gemm(int M, int N, int K, bool allow_split, int ncu, int force_ti
     c.ksplit = 1;
     c.kw = K;
     struct Cand { int MT, NT; double rel; };
-    const Cand cands[3] = {{256, 256, 2.75}, {128, 128, 1.0}, {128, 64, 0.65}};
+    const Cand cands[4] = {{256, 256, 2.75}, {128, 128, 1.0}, {128, 64, 0.65}, {256, 128, 1.9}};
     double best = 0.0;
-    // force_tile 1..3 picks cands[force_tile - 1] where it divides N
-    const bool forced = force_tile >= 1 && force_tile <= 3 && N % cands[force_tile - 1].NT == 0;
-    for (int i = 0; i < 3; ++i) {
+    // force_tile 1..4 picks cands[force_tile - 1] where it divides N
+    const bool forced = force_tile >= 1 && force_tile <= 4 && N % cands[force_tile - 1].NT == 0;
+    for (int i = 0; i < 4; ++i) {
         const Cand& t = cands[i];
         if (forced ? i != force_tile - 1 : (N % t.NT != 0 || (t.MT == 256 && M <= 128))) continue;
         const long tiles = (long)((M + t.MT - 1) / t.MT) * (N / t.NT);
@@ -117,6 +119,22 @@ GemmCfg choose_gemm(int M, int N, int K, bool allow_split, int ncu, int force_ti
             c.NT = t.NT;
         }
     }
+    return c;
+}
+
+// Tiled GEMM with the K range split over gridDim.y when its tiles alone
+// fill less than half of the CUs: the largest power-of-two split that keeps
+// the grid within one round of `ncu` workgroups and every split at least
+// 512 deep (8 stages). The partials go to a workspace and are summed by the
+// consumer (a norm, or splitk_finish_kernel).
+GemmCfg choose_gemm_split(int M, int N, int K, int ncu, int force_tile) {
+    GemmCfg c = choose_gemm(M, N, K, false, ncu, force_tile, true);
+    const long tiles = (long)((M + c.MT - 1) / c.MT) * (N / c.NT);
+    int ks = 1;
+    while (tiles * ks * 2 <= ncu && (K / (ks * 2)) % GEMM_KT == 0 && K / (ks * 2) >= 512 && K % (ks * 2) == 0)
+        ks *= 2;
+    c.ksplit = ks;
+    c.kw = K / ks;
     return c;
 }
 
@@ -409,6 +427,8 @@ int launch_tiled_t(int epi, const GemmParams& p, dim3 grid, hipStream_t s) {
         case EPI_RESID: VLA_LAUNCH((gemm_kernel<MT, NT, W8, EPI_RESID>), grid, blk, 0, s, p); break;
         case EPI_QKV_ROPE: VLA_LAUNCH((gemm_kernel<MT, NT, W8, EPI_QKV_ROPE>), grid, blk, 0, s, p); break;
         case EPI_SWIGLU: VLA_LAUNCH((gemm_kernel<MT, NT, W8, EPI_SWIGLU>), grid, blk, 0, s, p); break;
+        case EPI_ADD: VLA_LAUNCH((gemm_kernel<MT, NT, W8, EPI_ADD>), grid, blk, 0, s, p); break;
+        case EPI_PARTIAL: VLA_LAUNCH((gemm_kernel<MT, NT, W8, EPI_PARTIAL>), grid, blk, 0, s, p); break;
         default: set_err("bad tiled epilogue %d", epi); return VLA_ERR_ARG;
     }
     HIPC(hipGetLastError());
@@ -479,7 +499,39 @@ int launch_gemm(vla_ctx* c, const Linear& lin, const GemmCfg& cfg, bool w8, int 
     // the XCD with an extra row tile behind)
     const int ntm = (p.M + cfg.MT - 1) / cfg.MT;
     p.tile_map = p.M > lin.N && ntm >= 8 && (ntm + 7) / 8 * 8 * (lin.N / cfg.NT) <= c->ncu ? 1 : 0;
-    dim3 grid((lin.N / cfg.NT) * (p.tile_map ? (ntm + 7) / 8 * 8 : ntm));  // tile from the linear id
+    dim3 grid((lin.N / cfg.NT) * (p.tile_map ? (ntm + 7) / 8 * 8 : ntm), cfg.ksplit);  // tile from the linear id
+    if (cfg.ksplit > 1) {
+        // split K: partials into ws; EPI_ADD / EPI_RESID partials are summed
+        // by the caller's next norm, the other epilogues by a finish kernel
+        if (w8) {
+            set_err("split-K tiled GEMM takes bf16 weights only");
+            return VLA_ERR_SHAPE;
+        }
+        if (!p.ws) {
+            set_err("split-K tiled GEMM without a workspace");
+            return VLA_ERR_ARG;
+        }
+        int rc;
+        if (cfg.MT == 256 && cfg.NT == 256) rc = launch_tiled_t<256, 256, false>(EPI_PARTIAL, p, grid, c->stream);
+        else if (cfg.MT == 256 && cfg.NT == 128) rc = launch_tiled_t<256, 128, false>(EPI_PARTIAL, p, grid, c->stream);
+        else if (cfg.MT == 128 && cfg.NT == 128) rc = launch_tiled_t<128, 128, false>(EPI_PARTIAL, p, grid, c->stream);
+        else if (cfg.MT == 128 && cfg.NT == 64) rc = launch_tiled_t<128, 64, false>(EPI_PARTIAL, p, grid, c->stream);
+        else {
+            set_err("no GEMM tile %dx%d", cfg.MT, cfg.NT);
+            return VLA_ERR_SHAPE;
+        }
+        if (rc || epi == EPI_ADD || epi == EPI_RESID) return rc;
+        const long units = (long)p.M * (lin.N / 16);
+        const dim3 fg((unsigned)((units + 255) / 256));
+        switch (epi) {
+            case EPI_BIAS_F32: hipLaunchKernelGGL(splitk_finish_kernel<EPI_BIAS_F32>, fg, dim3(256), 0, c->stream, p, cfg.ksplit); break;
+            case EPI_QKV_ROPE: hipLaunchKernelGGL(splitk_finish_kernel<EPI_QKV_ROPE>, fg, dim3(256), 0, c->stream, p, cfg.ksplit); break;
+            case EPI_SWIGLU: hipLaunchKernelGGL(splitk_finish_kernel<EPI_SWIGLU>, fg, dim3(256), 0, c->stream, p, cfg.ksplit); break;
+            default: set_err("bad split-K epilogue %d", epi); return VLA_ERR_ARG;
+        }
+        HIPC(hipGetLastError());
+        return VLA_OK;
+    }
     if (w8 && c->a8) {
         if (lin.K % GEMM8_KT != 0) {
             set_err("FP8 GEMM needs K %% %d == 0 (K = %d)", GEMM8_KT, lin.K);
@@ -488,6 +540,7 @@ int launch_gemm(vla_ctx* c, const Linear& lin, const GemmCfg& cfg, bool w8, int 
         if (cfg.MT == 256 && cfg.NT == 256) return launch_tiled8_t<256, 256>(epi, p, grid, c->stream);
         if (cfg.MT == 128 && cfg.NT == 128) return launch_tiled8_t<128, 128>(epi, p, grid, c->stream);
         if (cfg.MT == 128 && cfg.NT == 64) return launch_tiled8_t<128, 64>(epi, p, grid, c->stream);
+        if (cfg.MT == 256 && cfg.NT == 128) return launch_tiled8_t<256, 128>(epi, p, grid, c->stream);
         set_err("no FP8 GEMM tile %dx%d", cfg.MT, cfg.NT);
         return VLA_ERR_SHAPE;
     }
@@ -497,6 +550,8 @@ int launch_gemm(vla_ctx* c, const Linear& lin, const GemmCfg& cfg, bool w8, int 
                                                   : launch_tiled_t<128, 128, false>(epi, p, grid, c->stream);
     if (cfg.MT == 128 && cfg.NT == 64) return w8 ? launch_tiled_t<128, 64, true>(epi, p, grid, c->stream)
                                                  : launch_tiled_t<128, 64, false>(epi, p, grid, c->stream);
+    if (cfg.MT == 256 && cfg.NT == 128) return w8 ? launch_tiled_t<256, 128, true>(epi, p, grid, c->stream)
+                                                  : launch_tiled_t<256, 128, false>(epi, p, grid, c->stream);
     set_err("no GEMM tile %dx%d", cfg.MT, cfg.NT);
     return VLA_ERR_SHAPE;
 }
@@ -1198,8 +1253,8 @@ int vla_set_option(vla_ctx* c, int option, int value) {
         return VLA_OK;
     }
     if (option == VLA_OPT_GEMM_TILE) {
-        if (value < 0 || value > 3) {
-            set_err("VLA_OPT_GEMM_TILE takes 0..3, not %d", value);
+        if (value < 0 || value > 4) {
+            set_err("VLA_OPT_GEMM_TILE takes 0..4, not %d", value);
             return VLA_ERR_ARG;
         }
         HIPC(hipSetDevice(c->device));
@@ -1402,5 +1457,403 @@ int vla_profile_kernel(vla_ctx* c, int kernel, int iters, double* us_per_launch,
     if (flops_per_launch) *flops_per_launch = flops;
     return VLA_OK;
 }
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Prefix K/V construction (see include/vla_prefill.h): the backbone prefill.
+// One graph per context replays, per layer, weighted RMSNorm -> QKV GEMM with
+// the RoPE epilogue (keys/values into the attention layout of that layer) ->
+// causal attention -> O GEMM (+ residual) -> RMSNorm -> gate_up GEMM (SwiGLU)
+// -> down GEMM (+ residual); the last layer stops after its QKV, since its
+// attention and MLP feed no cache. An export kernel then writes every layer's
+// keys and values in the caller's layout.
+// ---------------------------------------------------------------------------
+struct vla_prefill_ctx {
+    vla_backbone_dims d{};
+    vla_ctx* c = nullptr;  // device, streams and allocations (no expert state)
+    bool use_graph = true;
+    int gemm_tile = 0;
+    int M = 0, qd = 0, kvd = 0;
+    std::vector<Linear> qkv, wo, gu, wd;
+    float* norms = nullptr;  // [L][2][H]: norm1, norm2 of each layer
+    float* h = nullptr;      // residual stream [M][H] fp32
+    uint16_t *y = nullptr, *q = nullptr, *o = nullptr, *act = nullptr;
+    uint16_t *kcat = nullptr, *vcat = nullptr;  // every layer's keys / values
+    KVLayout kv{};
+    float2* rope = nullptr;  // [P][d_h/2]
+    int* zeros = nullptr;    // [B] RoPE position offsets (0: token t at position t)
+    size_t ws_elems = 0;     // split-K workspace (c->ws) in floats
+    PrefillArgs* args = nullptr;
+    hipGraphExec_t graph = nullptr;
+};
+
+namespace {
+
+int validate_backbone(const vla_backbone_dims* d) {
+    if (!d) {
+        set_err("dims is NULL");
+        return VLA_ERR_ARG;
+    }
+    if (d->n_layers < 1 || d->hidden < 64 || d->hidden % 64 || d->hidden > 4096 || d->intermediate < 64 ||
+        d->intermediate % 64) {
+        set_err("unsupported backbone n_layers/hidden/intermediate (%d/%d/%d)", d->n_layers, d->hidden,
+                d->intermediate);
+        return VLA_ERR_SHAPE;
+    }
+    if (d->head_dim != 64 && d->head_dim != 128) {
+        set_err("head_dim must be 64 or 128 (got %d)", d->head_dim);
+        return VLA_ERR_SHAPE;
+    }
+    if (d->n_kv_heads < 1 || d->n_q_heads < 1 || d->n_q_heads % d->n_kv_heads) {
+        set_err("unsupported head counts (%d q / %d kv)", d->n_q_heads, d->n_kv_heads);
+        return VLA_ERR_SHAPE;
+    }
+    if (d->prefix_len < 1 || d->prefix_len > 8192 || d->batch < 1 || (long)d->batch * d->prefix_len > (1L << 24)) {
+        set_err("unsupported prefix_len/batch (%d/%d)", d->prefix_len, d->batch);
+        return VLA_ERR_SHAPE;
+    }
+    if (!(d->rms_eps > 0.f) || !(d->rope_theta > 0.f)) {
+        set_err("rms_eps and rope_theta must be positive");
+        return VLA_ERR_SHAPE;
+    }
+    return VLA_OK;
+}
+
+// GEMM configurations and the split-K workspace they need (reallocated when
+// it grows; the caller has synchronized and dropped the graph).
+int prefill_choose(vla_prefill_ctx* x) {
+    vla_ctx* c = x->c;
+    size_t need = 16;
+    for (int l = 0; l < x->d.n_layers; ++l)
+        for (Linear* ln : {&x->qkv[l], &x->wo[l], &x->gu[l], &x->wd[l]}) {
+            ln->cfg = choose_gemm_split(x->M, ln->N, ln->K, c->ncu, x->gemm_tile);
+            if (ln->cfg.ksplit > 1) need = std::max(need, (size_t)ln->cfg.ksplit * x->M * ln->N);
+        }
+    if (need > x->ws_elems) {
+        if (c->ws) c->release(c->ws, x->ws_elems * 4);
+        c->ws = nullptr;
+        x->ws_elems = 0;
+        int rc;
+        if ((rc = c->alloc((void**)&c->ws, need * 4))) return rc;
+        x->ws_elems = need;
+    }
+    return VLA_OK;
+}
+
+int prefill_create_impl(vla_prefill_ctx* x, const vla_backbone_weights* w) {
+    vla_ctx* c = x->c;
+    const vla_backbone_dims& d = x->d;
+    const int H = d.hidden, L = d.n_layers, I = d.intermediate, dh = d.head_dim, B = d.batch, P = d.prefix_len;
+    x->M = B * P;
+    x->qd = d.n_q_heads * dh;
+    x->kvd = d.n_kv_heads * dh;
+    HIPC(hipGetDevice(&c->device));
+    HIPC(hipDeviceGetAttribute(&c->ncu, hipDeviceAttributeMultiprocessorCount, c->device));
+    HIPC(hipStreamCreateWithFlags(&c->own_stream, hipStreamNonBlocking));
+    c->stream = nullptr;
+
+    int rc;
+    const void* const* per[] = {(const void* const*)w->norm1, (const void* const*)w->norm2, w->wq, w->wk, w->wv,
+                                w->wo, w->wg, w->wu, w->wd};
+    const char* pnames[] = {"norm1", "norm2", "wq", "wk", "wv", "wo", "wg", "wu", "wd"};
+    for (int i = 0; i < 9; ++i) {
+        if (!per[i]) {
+            set_err("%s array is NULL", pnames[i]);
+            return VLA_ERR_ARG;
+        }
+        for (int l = 0; l < L; ++l)
+            if ((rc = check_ptr(per[i][l], pnames[i], i >= 2 ? 8 : 4))) return rc;
+    }
+    if ((rc = c->alloc((void**)&x->norms, (size_t)L * 2 * H * 4))) return rc;
+    for (int l = 0; l < L; ++l) {
+        HIPC(hipMemcpyAsync(x->norms + (size_t)(2 * l) * H, w->norm1[l], (size_t)H * 4, hipMemcpyDeviceToDevice,
+                            c->stream));
+        HIPC(hipMemcpyAsync(x->norms + (size_t)(2 * l + 1) * H, w->norm2[l], (size_t)H * 4, hipMemcpyDeviceToDevice,
+                            c->stream));
+    }
+    x->qkv.resize(L);
+    x->wo.resize(L);
+    x->gu.resize(L);
+    x->wd.resize(L);
+    for (int l = 0; l < L; ++l) {
+        {
+            const void* srcs[3] = {w->wq[l], w->wk[l], w->wv[l]};
+            const float* scs[3] = {nullptr, nullptr, nullptr};
+            int rows[3] = {x->qd, x->kvd, x->kvd};
+            if ((rc = pack_linear(c, x->qkv[l], x->qd + 2 * x->kvd, H, srcs, scs, 3, rows, 1, dh))) return rc;
+        }
+        {
+            const void* srcs[1] = {w->wo[l]};
+            const float* scs[1] = {nullptr};
+            int rows[1] = {H};
+            if ((rc = pack_linear(c, x->wo[l], H, x->qd, srcs, scs, 1, rows, 0, dh))) return rc;
+        }
+        {
+            const void* srcs[2] = {w->wg[l], w->wu[l]};
+            const float* scs[2] = {nullptr, nullptr};
+            int rows[2] = {I, I};
+            if ((rc = pack_linear(c, x->gu[l], 2 * I, H, srcs, scs, 2, rows, 2, dh))) return rc;
+        }
+        {
+            const void* srcs[1] = {w->wd[l]};
+            const float* scs[1] = {nullptr};
+            int rows[1] = {H};
+            if ((rc = pack_linear(c, x->wd[l], H, I, srcs, scs, 1, rows, 0, dh))) return rc;
+        }
+    }
+    if ((rc = prefill_choose(x))) return rc;
+
+    if ((rc = c->alloc((void**)&x->rope, (size_t)P * (dh / 2) * sizeof(float2)))) return rc;
+    hipLaunchKernelGGL(rope_table_kernel, dim3((P * (dh / 2) + 255) / 256), dim3(256), 0, c->stream, x->rope, P, dh,
+                       (double)d.rope_theta);
+    HIPC(hipGetLastError());
+    if ((rc = c->alloc((void**)&x->zeros, (size_t)B * sizeof(int)))) return rc;
+    HIPC(hipMemsetAsync(x->zeros, 0, (size_t)B * sizeof(int), c->stream));
+    const size_t M = x->M;
+    if ((rc = c->alloc((void**)&x->h, M * H * 4))) return rc;
+    if ((rc = c->alloc((void**)&x->y, M * H * 2))) return rc;
+    if ((rc = c->alloc((void**)&x->q, M * x->qd * 2))) return rc;
+    if ((rc = c->alloc((void**)&x->o, M * x->qd * 2))) return rc;
+    if ((rc = c->alloc((void**)&x->act, M * I * 2))) return rc;
+    x->kv.L = L;
+    x->kv.nkv = d.n_kv_heads;
+    x->kv.dh = dh;
+    x->kv.S_pad = (P + 31) / 32 * 32;
+    const size_t kv_elems = (size_t)B * L * d.n_kv_heads * x->kv.S_pad * dh;
+    if ((rc = c->alloc((void**)&x->kcat, kv_elems * 2))) return rc;
+    if ((rc = c->alloc((void**)&x->vcat, kv_elems * 2))) return rc;
+    // keys past P stay zero (masked; zero values keep 0 * v finite)
+    HIPC(hipMemsetAsync(x->kcat, 0, kv_elems * 2, c->stream));
+    HIPC(hipMemsetAsync(x->vcat, 0, kv_elems * 2, c->stream));
+    if ((rc = c->alloc((void**)&x->args, sizeof(PrefillArgs)))) return rc;
+    HIPC(hipMemsetAsync(x->args, 0, sizeof(PrefillArgs), c->stream));
+    HIPC(hipStreamSynchronize(c->stream));
+    return VLA_OK;
+}
+
+// Weighted RMSNorm `which` (2l: norm1 of layer l, 2l + 1: norm2), first
+// adding the S split-K partials left in ws by the preceding residual GEMM.
+int prefill_norm(vla_prefill_ctx* x, bool first, int which, int S) {
+    const vla_backbone_dims& d = x->d;
+    hipLaunchKernelGGL(rmsnorm_w_kernel, dim3(x->M), dim3(256), 0, x->c->stream, first ? x->args : nullptr, x->h,
+                       x->c->ws, S, x->M, x->norms + (size_t)which * d.hidden, x->y, d.hidden, d.rms_eps);
+    HIPC(hipGetLastError());
+    return VLA_OK;
+}
+
+int enqueue_prefill(vla_prefill_ctx* x) {
+    vla_ctx* c = x->c;
+    const vla_backbone_dims& d = x->d;
+    const int H = d.hidden, L = d.n_layers, P = d.prefix_len, B = d.batch, dh = d.head_dim;
+    const int G = d.n_q_heads / d.n_kv_heads;
+    int rc, S = 0;  // split-K partials of the last residual GEMM, pending in ws
+    for (int l = 0; l < L; ++l) {
+        if ((rc = prefill_norm(x, l == 0, 2 * l, S))) return rc;
+        {
+            GemmParams p{};
+            p.A = x->y;
+            p.lda = H;
+            p.M = x->M;
+            p.B = B;
+            p.T = P;
+            p.inv_T = 1.0f / (float)P;
+            p.q = x->q;
+            p.kcat = x->kcat;
+            p.vcat = x->vcat;
+            p.kv = x->kv;
+            p.layer = l;
+            p.P = 0;
+            p.rope = x->rope;
+            p.pvalid = x->zeros;
+            p.nq = d.n_q_heads;
+            p.nkv = d.n_kv_heads;
+            p.dh = dh;
+            p.dh_shift = dh == 128 ? 7 : 6;
+            if ((rc = launch_gemm(c, x->qkv[l], x->qkv[l].cfg, false, EPI_QKV_ROPE, p))) return rc;
+        }
+        if (l + 1 == L) break;  // the last layer's attention and MLP feed no cache
+        {
+            AttnParams ap{};
+            ap.q = x->q;
+            ap.kcat = x->kcat;
+            ap.vcat = x->vcat;
+            ap.o = x->o;
+            ap.kv = x->kv;
+            ap.layer = l;
+            ap.S = P;
+            ap.T = P;
+            ap.P = 0;
+            ap.pvalid = x->zeros;
+            ap.nq = d.n_q_heads;
+            ap.ofrag = 0;
+            ap.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
+            const dim3 rg((G * P + 63) / 64, d.n_kv_heads, B);
+            if (dh == 128) hipLaunchKernelGGL((attn_rows_kernel<128, 1, true>), rg, dim3(256), 0, c->stream, ap);
+            else hipLaunchKernelGGL((attn_rows_kernel<64, 1, true>), rg, dim3(256), 0, c->stream, ap);
+            HIPC(hipGetLastError());
+        }
+        {
+            GemmParams p{};
+            p.A = x->o;
+            p.lda = x->qd;
+            p.M = x->M;
+            p.out_f32 = x->h;
+            if ((rc = launch_gemm(c, x->wo[l], x->wo[l].cfg, false, EPI_ADD, p))) return rc;
+            S = x->wo[l].cfg.ksplit > 1 ? x->wo[l].cfg.ksplit : 0;
+        }
+        if ((rc = prefill_norm(x, false, 2 * l + 1, S))) return rc;
+        {
+            GemmParams p{};
+            p.A = x->y;
+            p.lda = H;
+            p.M = x->M;
+            p.act = x->act;
+            if ((rc = launch_gemm(c, x->gu[l], x->gu[l].cfg, false, EPI_SWIGLU, p))) return rc;
+        }
+        {
+            GemmParams p{};
+            p.A = x->act;
+            p.lda = d.intermediate;
+            p.M = x->M;
+            p.out_f32 = x->h;
+            if ((rc = launch_gemm(c, x->wd[l], x->wd[l].cfg, false, EPI_ADD, p))) return rc;
+            S = x->wd[l].cfg.ksplit > 1 ? x->wd[l].cfg.ksplit : 0;
+        }
+    }
+    const long total = (long)B * L * P * d.n_kv_heads * (dh / 8);
+    hipLaunchKernelGGL(prefix_export_kernel, dim3((int)((total + 255) / 256)), dim3(256), 0, c->stream, x->args,
+                       x->kcat, x->vcat, x->kv, B, P);
+    HIPC(hipGetLastError());
+    return VLA_OK;
+}
+
+void prefill_drop_graph(vla_prefill_ctx* x) {
+    if (x->graph) (void)hipGraphExecDestroy(x->graph);
+    x->graph = nullptr;
+}
+
+void prefill_destroy(vla_prefill_ctx* x) {
+    if (!x) return;
+    if (x->c) {
+        (void)hipStreamSynchronize(x->c->stream);
+        prefill_drop_graph(x);
+        destroy_ctx(x->c);
+    }
+    delete x;
+}
+
+}  // namespace
+
+extern "C" {
+
+vla_prefill_ctx* vla_prefill_create(const vla_backbone_weights* weights, const vla_backbone_dims* dims) {
+    g_err.clear();
+    if (!weights) {
+        set_err("weights is NULL");
+        return nullptr;
+    }
+    if (validate_backbone(dims)) return nullptr;
+    vla_prefill_ctx* x = new vla_prefill_ctx();
+    x->d = *dims;
+    x->c = new vla_ctx();
+    if (prefill_create_impl(x, weights) != VLA_OK) {
+        std::string keep = g_err;
+        prefill_destroy(x);
+        g_err = keep;
+        return nullptr;
+    }
+    return x;
+}
+
+int vla_prefill(vla_prefill_ctx* x, const void* embeddings, void* prefix_k, void* prefix_v) {
+    g_err.clear();
+    if (!x) {
+        set_err("ctx is NULL");
+        return VLA_ERR_ARG;
+    }
+    int rc;
+    if ((rc = check_ptr(embeddings, "embeddings"))) return rc;
+    if ((rc = check_ptr(prefix_k, "prefix_k"))) return rc;
+    if ((rc = check_ptr(prefix_v, "prefix_v"))) return rc;
+    vla_ctx* c = x->c;
+    HIPC(hipSetDevice(c->device));
+    hipLaunchKernelGGL(set_prefill_args_kernel, dim3(1), dim3(1), 0, c->stream, x->args,
+                       (const uint16_t*)embeddings, (uint16_t*)prefix_k, (uint16_t*)prefix_v);
+    HIPC(hipGetLastError());
+    if (!x->use_graph) return enqueue_prefill(x);
+    if (!x->graph) {
+        // captured on the library's stream (the legacy default stream cannot
+        // capture), replayed on the caller's
+        const hipStream_t run = c->stream;
+        c->stream = run ? run : c->own_stream;
+        hipGraph_t g = nullptr;
+        hipError_t e = hipStreamBeginCapture(c->stream, hipStreamCaptureModeRelaxed);
+        if (e != hipSuccess) {
+            c->stream = run;
+            set_err("graph capture failed to start: %s", hipGetErrorString(e));
+            return VLA_ERR_HIP;
+        }
+        rc = enqueue_prefill(x);
+        e = hipStreamEndCapture(c->stream, &g);
+        c->stream = run;
+        if (rc) {
+            if (g) (void)hipGraphDestroy(g);
+            return rc;
+        }
+        if (e != hipSuccess) {
+            set_err("graph capture failed: %s", hipGetErrorString(e));
+            return VLA_ERR_HIP;
+        }
+        e = hipGraphInstantiate(&x->graph, g, nullptr, nullptr, 0);
+        (void)hipGraphDestroy(g);
+        if (e != hipSuccess) {
+            x->graph = nullptr;
+            set_err("graph instantiate failed: %s", hipGetErrorString(e));
+            return VLA_ERR_HIP;
+        }
+    }
+    HIPC(hipGraphLaunch(x->graph, c->stream));
+    return VLA_OK;
+}
+
+int vla_prefill_set_stream(vla_prefill_ctx* x, void* stream) {
+    g_err.clear();
+    if (!x) {
+        set_err("ctx is NULL");
+        return VLA_ERR_ARG;
+    }
+    x->c->stream = (hipStream_t)stream;
+    return VLA_OK;
+}
+
+int vla_prefill_set_option(vla_prefill_ctx* x, int option, int value) {
+    g_err.clear();
+    if (!x) {
+        set_err("ctx is NULL");
+        return VLA_ERR_ARG;
+    }
+    if (option == VLA_OPT_USE_GRAPH) {
+        x->use_graph = value != 0;
+        return VLA_OK;
+    }
+    if (option == VLA_OPT_GEMM_TILE) {
+        if (value < 0 || value > 4) {
+            set_err("VLA_OPT_GEMM_TILE takes 0..4, not %d", value);
+            return VLA_ERR_ARG;
+        }
+        HIPC(hipSetDevice(x->c->device));
+        HIPC(hipStreamSynchronize(x->c->stream));
+        x->gemm_tile = value;
+        prefill_drop_graph(x);
+        return prefill_choose(x);
+    }
+    set_err("unknown prefill option %d", option);
+    return VLA_ERR_ARG;
+}
+
+void vla_prefill_destroy(vla_prefill_ctx* x) { prefill_destroy(x); }
+
+int64_t vla_prefill_device_bytes(const vla_prefill_ctx* x) { return x && x->c ? x->c->bytes : 0; }
 
 }  // extern "C"

@@ -180,7 +180,7 @@ __global__ void chunk_kv_store_kernel(const uint16_t* __restrict__ kn, const uin
 // ---------------------------------------------------------------------------
 // GEMM epilogues, shared by the skinny and the tiled kernels
 // ---------------------------------------------------------------------------
-enum { EPI_BIAS_F32 = 0, EPI_RESID = 1, EPI_QKV_ROPE = 2, EPI_SWIGLU = 3, EPI_PARTIAL = 4 };
+enum { EPI_BIAS_F32 = 0, EPI_RESID = 1, EPI_QKV_ROPE = 2, EPI_SWIGLU = 3, EPI_PARTIAL = 4, EPI_ADD = 5 };
 
 struct GemmParams {
     const uint16_t* A;   // [M, lda] bf16: row-major (tiled kernel) or A-fragment order (skinny kernel)
@@ -195,7 +195,7 @@ struct GemmParams {
     int M, N, K;
     int kw;              // K per split (skinny kernel)
     float* ws;           // EPI_PARTIAL: [ksplit][M][N]
-    float* out_f32;      // EPI_BIAS_F32: [M][N]; EPI_RESID: h [M][N]
+    float* out_f32;      // EPI_BIAS_F32: [M][N]; EPI_RESID, EPI_ADD: h [M][N]
     const float* bias;
     const float* mod;    // EPI_RESID gate source
     int mod_ld, gate_off, step, B, T;
@@ -274,8 +274,13 @@ VLA_DEV void epilogue_store(const GemmParams& p, int row, int col, float v, floa
 // multiple of 16) for the tiled kernel: the same results as epilogue_store
 // column by column, with 16-byte global accesses.
 template <int EPI>
-VLA_DEV void epilogue16(const GemmParams& p, int row, int col0, const float (&v)[16]) {
-    if constexpr (EPI == EPI_BIAS_F32) {
+VLA_DEV void epilogue16(const GemmParams& p, int row, int col0, const float (&v)[16], int kz = 0) {
+    if constexpr (EPI == EPI_PARTIAL) {  // split-K partial kz: ws[kz][row][col]
+        float* o = p.ws + ((size_t)kz * p.M + row) * p.N + col0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            *(f32x4*)(o + 4 * q) = (f32x4){v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+    } else if constexpr (EPI == EPI_BIAS_F32) {
         float* o = p.out_f32 + (size_t)row * p.N + col0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -293,6 +298,14 @@ VLA_DEV void epilogue16(const GemmParams& p, int row, int col0, const float (&v)
             const f32x4 hq = *(const f32x4*)(hp + 4 * q);
             *(f32x4*)(hp + 4 * q) = (f32x4){hq[0] + gq[0] * v[4 * q], hq[1] + gq[1] * v[4 * q + 1],
                                             hq[2] + gq[2] * v[4 * q + 2], hq[3] + gq[3] * v[4 * q + 3]};
+        }
+    } else if constexpr (EPI == EPI_ADD) {  // plain residual: h += v
+        float* hp = p.out_f32 + (size_t)row * p.N + col0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 hq = *(const f32x4*)(hp + 4 * q);
+            *(f32x4*)(hp + 4 * q) = (f32x4){hq[0] + v[4 * q], hq[1] + v[4 * q + 1], hq[2] + v[4 * q + 2],
+                                            hq[3] + v[4 * q + 3]};
         }
     } else if constexpr (EPI == EPI_SWIGLU) {
         // columns alternate gate (even) and up (odd) of outputs col0/2 .. col0/2 + 7
@@ -548,7 +561,10 @@ void gemm_kernel(GemmParams p) {
         nt_i = blockIdx.x % ntn;
     }
     const int m0 = mt_i * MT, n0 = nt_i * NT;
-    const int nk = p.K / GEMM_KT, Kf = p.K / 32;
+    // split K (gridDim.y > 1, EPI_PARTIAL): this workgroup sums inputs
+    // [kz * kw, (kz + 1) * kw) and writes partial kz
+    const int kz = blockIdx.y, kf0 = kz * (p.kw / 32);
+    const int nk = p.kw / GEMM_KT, Kf = p.K / 32;
     const uint32_t lbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
 
     // Per-lane source of each DMA load of this wave (stage 0) and the stride
@@ -562,11 +578,11 @@ void gemm_kernel(GemmParams p) {
         if (p.a_frag) {
             // A-fragment order of <= 64 rows: fragment (k-step, row block) is 1 KiB
             const int rbc = min(rb + m0 / 16, 3);
-            asrc[i] = p.A + ((size_t)(ks * 4 + rbc) * 64 + lane) * 8;
+            asrc[i] = p.A + ((size_t)((kf0 + ks) * 4 + rbc) * 64 + lane) * 8;
         } else {
             // rows past M read row M-1; their results are never stored
             const int row = min(m0 + rb * 16 + (lane & 15), p.M - 1);
-            asrc[i] = p.A + (size_t)row * p.lda + ks * 32 + 8 * (lane >> 4);
+            asrc[i] = p.A + (size_t)row * p.lda + (kf0 + ks) * 32 + 8 * (lane >> 4);
         }
         adst[i] = (uint32_t)f * 1024;
     }
@@ -578,10 +594,10 @@ void gemm_kernel(GemmParams p) {
         const int c = (wave * LB + i) % BCH;
         if constexpr (W8) {
             // one chunk = the 2 k-steps (512 bytes each) of one 16-column tile
-            bsrc[i] = (const uint8_t*)p.W + ((size_t)(n0 / 16 + c) * Kf) * 512 + lane * 16;
+            bsrc[i] = (const uint8_t*)p.W + ((size_t)(n0 / 16 + c) * Kf + kf0) * 512 + lane * 16;
         } else {
             const int fn = c / KS, ks = c % KS;
-            bsrc[i] = (const uint8_t*)p.W + ((size_t)(n0 / 16 + fn) * Kf + ks) * 1024 + lane * 16;
+            bsrc[i] = (const uint8_t*)p.W + ((size_t)(n0 / 16 + fn) * Kf + kf0 + ks) * 1024 + lane * 16;
         }
         bdst[i] = (uint32_t)(AF * 1024 + c * 1024);
     }
@@ -686,11 +702,33 @@ void gemm_kernel(GemmParams p) {
                     const f32x4 t = *(const f32x4*)(ct + lr * CLD + uc * 16 + 4 * q);
                     v[4 * q] = t[0]; v[4 * q + 1] = t[1]; v[4 * q + 2] = t[2]; v[4 * q + 3] = t[3];
                 }
-                epilogue16<EPI>(p, row, n0 + uc * 16, v);
+                epilogue16<EPI>(p, row, n0 + uc * 16, v, kz);
             }
         }
         __syncthreads();
     }
+}
+
+// The epilogue of a split-K tiled GEMM: sums the S partials of 16 columns of
+// one row (one thread each) and applies epilogue EPI to them.
+template <int EPI>
+__global__ __launch_bounds__(256) void splitk_finish_kernel(GemmParams p, int S) {
+    const int units = p.N / 16;
+    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (long)p.M * units) return;
+    const int row = (int)(idx / units), col0 = (int)(idx % units) * 16;
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = 0.f;
+    for (int z = 0; z < S; ++z) {
+        const float* w = p.ws + ((size_t)z * p.M + row) * p.N + col0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x4 t = *(const f32x4*)(w + 4 * q);
+            v[4 * q] += t[0]; v[4 * q + 1] += t[1]; v[4 * q + 2] += t[2]; v[4 * q + 3] += t[3];
+        }
+    }
+    epilogue16<EPI>(p, row, col0, v);
 }
 
 // ---------------------------------------------------------------------------
@@ -1048,10 +1086,14 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
 // 2^ATT_SLACK, well inside bf16 and fp32 range.
 // LDS: K rows padded by 16 bytes so the 16 lanes that read one fragment hit
 // distinct banks; V kept in PV-operand order.
+// CAUSAL (prefix self-attention, keys = the T tokens themselves, P = 0):
+// query token i sees keys 0..i. The workgroup stops after the block holding
+// its last row's token, and only blocks that reach past the smallest token of
+// a wave's rows are masked per key.
 // ---------------------------------------------------------------------------
 constexpr float ATT_SLACK = 8.0f;
 
-template <int DH, int RT>
+template <int DH, int RT, bool CAUSAL = false>
 __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
     constexpr int KROW = DH * 2 + 16;            // padded K row in LDS, bytes
     constexpr int KCH = DH * 2 / 16;             // 16-byte chunks per key row
@@ -1067,7 +1109,22 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
     const int rows_total = G * p.T;
     const int g = blockIdx.y, b = blockIdx.z;
     const int r0 = blockIdx.x * 64 * RT + wave * 16 * RT;
-    const int nblk = p.kv.S_pad / 32;
+    int nblk = p.kv.S_pad / 32;
+    // causal: token of each of this lane's rows, the smallest token of the
+    // wave's rows (0 when they span two heads), and the last block any row of
+    // the workgroup needs (rows are head-major: row = head_in_group * T + token)
+    int tok[RT][4], tmin = 0;
+    if constexpr (CAUSAL) {
+        const int R0 = blockIdx.x * 64 * RT, R1 = min(R0 + 64 * RT, rows_total) - 1;
+        const int tmax = R0 / p.T == R1 / p.T ? R1 % p.T : p.T - 1;
+        nblk = min(nblk, tmax / 32 + 1);
+        const int w1 = min(r0 + 16 * RT, rows_total) - 1;
+        tmin = r0 <= w1 && r0 / p.T == w1 / p.T ? r0 % p.T : 0;
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tok[t][r] = (r0 + t * 16 + 4 * (lane >> 4) + r) % p.T;
+    }
     const size_t base = p.kv.base(b, p.layer, g);
     const uint8_t* K = (const uint8_t*)(p.kcat + base);
     const uint8_t* V = (const uint8_t*)(p.vcat + base);
@@ -1139,7 +1196,8 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
             }
         }
         // every key of the block real (a uniform test): no per-key mask
-        const bool whole = (kb * 32 + 32 <= pvb) || (kb * 32 >= p.P && kb * 32 + 32 <= p.S);
+        bool whole = (kb * 32 + 32 <= pvb) || (kb * 32 >= p.P && kb * 32 + 32 <= p.S);
+        if constexpr (CAUSAL) whole = whole && kb * 32 + 31 <= tmin;
         float s0[RT][4], s1[RT][4], mx[RT][4];
         bool grow = false;
 #pragma unroll
@@ -1152,6 +1210,10 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
                     const int key0 = kb * 32 + (lane & 15), key1 = key0 + 16;
                     if (key0 >= p.S || (key0 < p.P && key0 >= pvb)) s0[t][r] = -INFINITY;
                     if (key1 >= p.S || (key1 < p.P && key1 >= pvb)) s1[t][r] = -INFINITY;
+                    if constexpr (CAUSAL) {
+                        if (key0 > tok[t][r]) s0[t][r] = -INFINITY;
+                        if (key1 > tok[t][r]) s1[t][r] = -INFINITY;
+                    }
                 }
                 mx[t][r] = group16_max(fmaxf(s0[t][r], s1[t][r]));
                 grow |= mx[t][r] > mrow[t][r] + ATT_SLACK;

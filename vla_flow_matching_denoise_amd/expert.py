@@ -34,8 +34,11 @@ def dims_from_config(cfg, batch: Optional[int] = None) -> B.VlaDims:
                      cfg.time_emb_dim, cfg.rope_theta, cfg.rms_eps, cfg.time_scale, cfg.weight_dtype)
 
 
-def to_device(a: np.ndarray, device="cuda"):
+def to_device(a, device="cuda"):
+    """numpy array (uint16 = bf16 bits, kept as int16) or torch tensor -> contiguous device tensor."""
     import torch
+    if isinstance(a, torch.Tensor):
+        return a.to(device).contiguous()
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         return torch.from_numpy(a.view(np.int16)).to(device)
