@@ -515,7 +515,7 @@ VLA_DEV void vm_wait() {
 // most 3 (one workgroup per CU).
 template <int MT, int NT, bool W8>
 struct GemmShape {
-    static constexpr int AF = MT / 16 * GEMM_KS;                 // A fragments per stage (1 KiB each)
+    static constexpr int AF = MT / 16 * GEMM_KS;                 // A loads per stage (8 rows x 128 B = 1 KiB each)
     static constexpr int BBYTES = NT / 16 * GEMM_KS * (W8 ? 512 : 1024);
     static constexpr int BCH = BBYTES / 1024;                    // 1 KiB DMA chunks of B per stage
     static constexpr int STAGE = AF * 1024 + BBYTES;
@@ -568,23 +568,31 @@ void gemm_kernel(GemmParams p) {
     const uint32_t lbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
 
     // Per-lane source of each DMA load of this wave (stage 0) and the stride
-    // per stage. Fragment f = (row block, k-step) of A, chunk c of B. Waves
-    // with fewer fragments than loads repeat one (same bytes, same place).
+    // per stage. A stage holds A as MT rows of 128 bytes (64 inputs), the
+    // 16-byte chunk c of row r at chunk position c ^ ((r >> 1) & 7): one DMA
+    // load fills 8 whole rows, each from one contiguous 128-byte line (a
+    // load of 16 half lines moves about 40 % fewer bytes per clock), and the
+    // 16 lanes that read one MFMA fragment (16 rows, one chunk) meet 16
+    // distinct bank groups. Load j of A covers rows 8j .. 8j + 7; chunk c of
+    // B is one 1 KiB weight fragment. Waves with fewer chunks than loads
+    // repeat one (same bytes, same place).
     const uint16_t* asrc[LA];
     uint32_t adst[LA];
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-        const int f = (wave * LA + i) % AF, rb = f / KS, ks = f % KS;
+        const int j = (wave * LA + i) % AF, r = j * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
         if (p.a_frag) {
-            // A-fragment order of <= 64 rows: fragment (k-step, row block) is 1 KiB
-            const int rbc = min(rb + m0 / 16, 3);
-            asrc[i] = p.A + ((size_t)((kf0 + ks) * 4 + rbc) * 64 + lane) * 8;
+            // A-fragment order of <= 64 rows: fragment (k-step, row block) is
+            // 1 KiB, lane l holding row l % 16 at inputs 8 (l / 16) .. + 7
+            const int row = min(m0 + r, 63);
+            asrc[i] = p.A + ((size_t)((kf0 + (c >> 2)) * 4 + (row >> 4)) * 64 + (row & 15) + 16 * (c & 3)) * 8;
         } else {
             // rows past M read row M-1; their results are never stored
-            const int row = min(m0 + rb * 16 + (lane & 15), p.M - 1);
-            asrc[i] = p.A + (size_t)row * p.lda + (kf0 + ks) * 32 + 8 * (lane >> 4);
+            const int row = min(m0 + r, p.M - 1);
+            asrc[i] = p.A + (size_t)row * p.lda + kf0 * 32 + c * 8;
         }
-        adst[i] = (uint32_t)f * 1024;
+        adst[i] = (uint32_t)j * 1024;
     }
     const size_t astride = p.a_frag ? (size_t)KS * 4 * 512 : (size_t)GEMM_KT;
     const uint8_t* bsrc[LB];
@@ -619,12 +627,15 @@ void gemm_kernel(GemmParams p) {
     for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    // fragments of k-step ks + 1 are read while k-step ks is multiplied
+    // fragments of k-step ks + 1 are read while k-step ks is multiplied; lane
+    // l reads row l % 16 of each row block at chunk 4 ks + l / 16 (swizzled)
     bf16x8 fa[2][FM], fb[2][FN];
+    const int arow = (wm * FM * 16 + (lane & 15)) * 128;
+    const int achunk = (lane >> 4) ^ ((lane & 15) >> 1);
     auto read_frags = [&](int buf, const uint8_t* st, int ks) {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
-            fa[buf][fm] = *(const bf16x8*)(st + ((wm * FM + fm) * KS + ks) * 1024 + lane * 16);
+            fa[buf][fm] = *(const bf16x8*)(st + arow + fm * 16 * 128 + ((achunk ^ (ks * 4)) << 4));
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             const int frag = (wn * FN + fn) * KS + ks;
@@ -676,6 +687,12 @@ void gemm_kernel(GemmParams p) {
     constexpr int UPR = NT / 16;   // 16-column units per row
     static_assert(FM % 4 == 0 && 64 * CLD * 4 <= S * STAGE, "epilogue pass does not fit the ring");
     float* ct = (float*)lds;
+    // Column col of a row sits at col ^ (4 s): s = ((col / 64) * (256 / NT)) % 4
+    // permutes the 4-float chunks of each 16-column unit, so that the 16
+    // threads reading one unit's chunk q (16 units of one row for NT = 256,
+    // 8 units of two rows for NT = 128) meet 16 distinct bank groups; a
+    // fragment write (16 consecutive columns) stays within one unit.
+    auto swz = [](int col) { return col ^ ((((col >> 6) * (256 / NT)) & 3) << 2); };
     float wsc[FN];
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) wsc[fn] = W8 ? p.wscale[n0 + wn * WN + fn * 16 + (lane & 15)] : 1.0f;
@@ -688,7 +705,7 @@ void gemm_kernel(GemmParams p) {
                 for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        ct[(f * 16 + 4 * (lane >> 4) + r) * CLD + wn * WN + fn * 16 + (lane & 15)] =
+                        ct[(f * 16 + 4 * (lane >> 4) + r) * CLD + swz(wn * WN + fn * 16 + (lane & 15))] =
                             acc[(pass % PPW) * 4 + f][fn][r] * wsc[fn];
         }
         __syncthreads();
@@ -699,7 +716,7 @@ void gemm_kernel(GemmParams p) {
                 float v[16];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const f32x4 t = *(const f32x4*)(ct + lr * CLD + uc * 16 + 4 * q);
+                    const f32x4 t = *(const f32x4*)(ct + lr * CLD + swz(uc * 16 + 4 * q));
                     v[4 * q] = t[0]; v[4 * q + 1] = t[1]; v[4 * q + 2] = t[2]; v[4 * q + 3] = t[3];
                 }
                 epilogue16<EPI>(p, row, n0 + uc * 16, v, kz);
@@ -746,7 +763,7 @@ constexpr int GEMM8_KT = 128;
 
 template <int MT, int NT>
 struct Gemm8Shape {
-    static constexpr int ACH = MT / 16 * 2, BCH = NT / 16 * 2;   // 1 KiB DMA chunks per stage
+    static constexpr int ACH = MT / 8, BCH = NT / 16 * 2;        // 1 KiB DMA loads per stage (A: 8 rows each)
     static constexpr int STAGE = (ACH + BCH) * 1024;
     static constexpr int S = 147456 / STAGE >= 3 ? 3 : 147456 / STAGE;
     static constexpr int LA = (ACH + GEMM_WAVES - 1) / GEMM_WAVES;  // DMA loads per wave and stage
@@ -793,17 +810,19 @@ void gemm8_kernel(GemmParams p) {
     const uint32_t lbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
     const uint8_t* A = (const uint8_t*)p.A;
 
-    // chunk c of A = (row block c/2, half c%2): lane slot i takes row i%16
-    // (rows past M read row M-1, never stored), inputs 32*(i/16) + 16*half;
-    // chunk c of B = half c%2 of the fragment of column block c/2
+    // A in the stage as MT rows of 128 bytes (128 inputs) with the 16-byte
+    // chunk swizzle of gemm_kernel: load j fills rows 8j .. 8j + 7 from whole
+    // 128-byte lines (rows past M read row M-1, never stored); chunk c of B =
+    // half c%2 of the fragment of column block c/2
     const uint8_t* asrc[LA];
     uint32_t adst[LA];
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-        const int c = (wave * LA + i) % ACH, rb = c / 2, half = c % 2;
-        const int row = min(m0 + rb * 16 + (lane & 15), p.M - 1);
-        asrc[i] = A + (size_t)row * p.lda + 32 * (lane >> 4) + 16 * half;
-        adst[i] = (uint32_t)c * 1024;
+        const int j = (wave * LA + i) % ACH, r = j * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        const int row = min(m0 + r, p.M - 1);
+        asrc[i] = A + (size_t)row * p.lda + c * 16;
+        adst[i] = (uint32_t)j * 1024;
     }
     const uint8_t* bsrc[LB];
     uint32_t bdst[LB];
@@ -836,20 +855,22 @@ void gemm8_kernel(GemmParams p) {
     for (int kt = 0; kt < nk; ++kt) {
         const uint8_t* st = lds + (kt % S) * STAGE;
         // the wave's B fragments of the stage, then its A fragments one row
-        // block at a time, the next one read while the current multiplies
+        // block at a time, the next one read while the current multiplies;
+        // lane l takes row l % 16 of the block, bytes 32 (l / 16) .. + 31
+        // (chunks a_lo, a_lo + 1, swizzled)
         i32x8 bf[FN], af[2];
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             const int cb = 2 * (wn * FN + fn);
             bf[fn] = frag32(st + (ACH + cb) * 1024 + lane * 16, st + (ACH + cb + 1) * 1024 + lane * 16);
         }
-        af[0] = frag32(st + (2 * wm * FM) * 1024 + lane * 16, st + (2 * wm * FM + 1) * 1024 + lane * 16);
+        const uint8_t* arow = st + (wm * FM * 16 + (lane & 15)) * 128;
+        const int a_lo = ((2 * (lane >> 4)) ^ ((lane & 15) >> 1)) << 4;
+        const int a_hi = ((2 * (lane >> 4) + 1) ^ ((lane & 15) >> 1)) << 4;
+        af[0] = frag32(arow + a_lo, arow + a_hi);
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
-            if (fm + 1 < FM) {
-                const int ca = 2 * (wm * FM + fm + 1);
-                af[(fm + 1) & 1] = frag32(st + ca * 1024 + lane * 16, st + (ca + 1) * 1024 + lane * 16);
-            }
+            if (fm + 1 < FM) af[(fm + 1) & 1] = frag32(arow + (fm + 1) * 2048 + a_lo, arow + (fm + 1) * 2048 + a_hi);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
@@ -872,6 +893,7 @@ void gemm8_kernel(GemmParams p) {
     constexpr int UPR = NT / 16;
     static_assert(FM % 4 == 0 && 64 * CLD * 4 <= S * STAGE, "epilogue pass does not fit the ring");
     float* ct = (float*)lds;
+    auto swz = [](int col) { return col ^ ((((col >> 6) * (256 / NT)) & 3) << 2); };  // as in gemm_kernel
     float wsc[FN];
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) wsc[fn] = p.wscale[n0 + wn * WN + fn * 16 + (lane & 15)];
@@ -884,7 +906,7 @@ void gemm8_kernel(GemmParams p) {
                 for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        ct[(f * 16 + 4 * (lane >> 4) + r) * CLD + wn * WN + fn * 16 + (lane & 15)] =
+                        ct[(f * 16 + 4 * (lane >> 4) + r) * CLD + swz(wn * WN + fn * 16 + (lane & 15))] =
                             acc[(pass % PPW) * 4 + f][fn][r] * wsc[fn];
         }
         __syncthreads();
@@ -896,7 +918,7 @@ void gemm8_kernel(GemmParams p) {
                 float v[16];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const f32x4 t = *(const f32x4*)(ct + lr * CLD + uc * 16 + 4 * q);
+                    const f32x4 t = *(const f32x4*)(ct + lr * CLD + swz(uc * 16 + 4 * q));
                     v[4 * q] = t[0] * as; v[4 * q + 1] = t[1] * as; v[4 * q + 2] = t[2] * as; v[4 * q + 3] = t[3] * as;
                 }
                 epilogue16<EPI>(p, row, n0 + uc * 16, v);
