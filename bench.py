@@ -13,7 +13,11 @@ Also reported:
   * ``roofline``: the dominant kernel's algorithmic bytes (or flops) per launch
     over its mean launch time, measured with HIP events around each launch;
   * ``cpu_baseline``: the fp64 CPU oracle timed on a bounded sample;
-  * ``batch64``: the batched-replica workload (64 requests, GEMM M = 3200).
+  * ``batch64``: the batched-replica workload (64 requests, GEMM M = 3200);
+  * ``prefill``: the prefix K/V construction that precedes the loop (the
+    36-layer LingBot-shaped backbone over a 256-token prefix) at 1 and 16
+    requests per call, as tokens per second with its weight-streaming and
+    MFMA fractions.
 """
 import argparse
 import csv
@@ -35,12 +39,12 @@ BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
 
 # HBM traffic of the dominant batch-1 kernel (the gate_up + SwiGLU skinny GEMM,
-# skinny_gemm_kernel<false, 3>) from rocprofv3 FETCH_SIZE / WRITE_SIZE counter
+# skinny_gemm_kernel<0, 3>) from rocprofv3 FETCH_SIZE / WRITE_SIZE counter
 # runs, scaled by what the counters read for a plain copy of known size. The
 # summary records a hash of the kernel sources; once they change, the figure
 # no longer describes the kernel and `traffic` is reported as null.
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gate_up_swiglu_gemm_lingbot_b1_counters.txt")
-TRAFFIC_KERNEL = "skinny_gemm_kernel<false, 3>"
+TRAFFIC_KERNEL = "skinny_gemm_kernel<0, 3>"
 KERNEL_SOURCES = ("vla_flow_matching_denoise_amd/csrc/common.h", "vla_flow_matching_denoise_amd/csrc/kernels_layer.h")
 COPY_BYTES = 256 << 20
 
@@ -201,7 +205,7 @@ def traffic_from(fetch_dir, write_dir, cmd_fetch, cmd_write):
                      "gemm_bytes": float(np.mean(gemm)) * scale * 1024.0, "n": len(gemm)}
     total = out["FETCH_SIZE"]["gemm_bytes"] + out["WRITE_SIZE"]["gemm_bytes"]
     lines = [
-        "# HBM traffic of the gate_up + SwiGLU skinny GEMM (skinny_gemm_kernel<false, 3>),",
+        "# HBM traffic of the gate_up + SwiGLU skinny GEMM (skinny_gemm_kernel<0, 3>),",
         "# LingBot-shaped batch-1 workload (M = 50 rows, N = 8192, K = 1024, bf16 weights).",
         "# Two rocprofv3 counter runs of `python bench.py --counter-run`, each scaled by the",
         "# counter's reading for a plain device copy of 256 MiB (read 256 MiB, write 256 MiB).",
@@ -223,6 +227,68 @@ def traffic_from(fetch_dir, write_dir, cmd_fetch, cmd_write):
     with open(TRAFFIC_SUMMARY, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+def prefill_work(bcfg):
+    """Weight bytes read and GEMM + attention flops of one prefill call (the
+    last layer stops after its QKV projection)."""
+    H, I, L, P, B = bcfg.hidden, bcfg.intermediate, bcfg.n_layers, bcfg.prefix_len, bcfg.batch
+    qd, kvd = bcfg.n_q_heads * bcfg.head_dim, bcfg.n_kv_heads * bcfg.head_dim
+    per_layer = H * (qd + 2 * kvd) + H * qd + 2 * H * I + H * I
+    params = per_layer * (L - 1) + H * (qd + 2 * kvd)
+    M = B * P
+    attn = (L - 1) * B * bcfg.n_q_heads * 2 * P * (P + 1) * bcfg.head_dim  # causal: P(P+1)/2 pairs, 2 products
+    return 2 * params + 2 * L * H * 4, 2 * M * params + attn
+
+
+def gpu_backbone_weights(bcfg, seed=0):
+    """Random-init backbone weights drawn on the GPU (the values do not change
+    the timing): N(0, std^2) linears in bf16, 1 + N(0, 0.1^2) norm weights."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    H, I = bcfg.hidden, bcfg.intermediate
+    qd, kvd = bcfg.n_q_heads * bcfg.head_dim, bcfg.n_kv_heads * bcfg.head_dim
+    shapes = {"wq": (qd, H), "wk": (kvd, H), "wv": (kvd, H), "wo": (H, qd), "wg": (I, H), "wu": (I, H),
+              "wd": (H, I)}
+    W = {k: [] for k in ("n1", "n2", *shapes)}
+    for _ in range(bcfg.n_layers):
+        for n in ("n1", "n2"):
+            W[n].append(1.0 + 0.1 * torch.randn(H, device="cuda", generator=g))
+        for n, shp in shapes.items():
+            w = bcfg.weight_std * torch.randn(shp, device="cuda", generator=g)
+            W[n].append(w.to(torch.bfloat16).view(torch.int16))
+    return W
+
+
+def bench_prefill(batches, warmup, steps):
+    import torch
+    import synth
+    from vla_flow_matching_denoise_amd.prefill import Prefill, backbone_dims_from_config
+    base = synth.backbone(2)
+    W = gpu_backbone_weights(base)
+    out = {}
+    for b in batches:
+        bcfg = base.replace(batch=b)
+        pf = Prefill(W, backbone_dims_from_config(bcfg))
+        emb = torch.randn((b, bcfg.prefix_len, bcfg.hidden), device="cuda").to(torch.bfloat16).view(torch.int16)
+        k, v = pf(emb)                                    # first call captures the graph (untimed)
+        for _ in range(warmup):
+            pf(emb, k, v)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            pf(emb, k, v)
+        torch.cuda.synchronize()
+        t = (time.perf_counter() - t0) / steps
+        pf.close()
+        wbytes, flops = prefill_work(bcfg)
+        out[f"b{b}"] = {"ms_per_call": round(t * 1e3, 4), "tokens_per_s": round(b * bcfg.prefix_len / t, 1),
+                        "weights_GBps": round(wbytes / t / 1e9, 1),
+                        "weights_hbm_frac": round(wbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                        "TFLOPs": round(flops / t / 1e12, 1),
+                        "mfma_frac": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    del W
+    return out
 
 
 def build_inputs(cfg, seed=0):
@@ -270,6 +336,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch64", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true", help="time only the prefill leg (for kernel profiles)")
     ap.add_argument("--counter-run", action="store_true",
                     help="run only the workload of the rocprofv3 counter runs (copy calibration + layers)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -295,6 +363,9 @@ def main():
     from vla_flow_matching_denoise_amd import binding as B
     from vla_flow_matching_denoise_amd.expert import Expert, dims_from_config
     torch.cuda.set_device(0)
+    if args.prefill_only:
+        print(json.dumps({"prefill": bench_prefill((1, 16), args.warmup, args.steps)}), flush=True)
+        return
 
     cfg = synth.config(2)
     log(f"[bench] generating weights for {cfg.name}")
@@ -400,6 +471,15 @@ def main():
             "chunks_per_s": round(cfg8.batch / t8, 3), "ms_per_call": round(t8 * 1e3, 3),
             "call_mfma_frac": round(f8 / t8 / 1e12 / FP8_PEAK_TFLOPS, 4), "roofline": roof8,
             "kernels": {k: {"us": round(v["us"], 2), "TFLOPs": round(v["TFLOPs"], 1)} for k, v in kr8.items()},
+        }
+
+    if not args.no_prefill:
+        log("[bench] prefix K/V construction (36-layer backbone prefill)")
+        result["prefill"] = {
+            "workload": "lingbot_backbone_36L_h2048_gqa16x2x128_swiglu11008_prefix256",
+            "unit": "prefix tokens/s", "dtype": "bf16",
+            "data": "synthetic (N(0,0.02^2) bf16 weights drawn on the GPU, N(0,1) embeddings)",
+            **bench_prefill((1, 16), 3, max(5, args.steps // 3)),
         }
 
     if not args.no_cpu_baseline:
