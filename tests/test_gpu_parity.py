@@ -273,6 +273,24 @@ def test_lingbot_b1_end_to_end():
     _gate_bf16(metrics(out, ref), "cfg2")
 
 
+@pytest.mark.timeout(600)
+def test_v2_b1_end_to_end():
+    """The V2-shaped loop: 36 layers, hidden 1536, SwiGLU 6144, prefix 512,
+    chunk 50x55, 50 Euler steps, batch 1 (its weights are its own model)."""
+    cfg = synth.config(3)
+    pk, pv, x0, ts = _inputs(cfg)
+    say("[cfg3] 36 layers, h1536, prefix 512, chunk 50x55, 50 steps, batch 1: generating weights")
+    raw = synth.make_weights(cfg, seed=0)
+    case = GpuCase(cfg, raw, pk, pv, x0, ts)
+    try:
+        out = case.run()
+    finally:
+        case.close()
+    say("[cfg3] GPU done; oracle")
+    ref = run_oracle(cfg, oracle.decode_weights(raw), pk, pv, x0, ts)
+    _gate_bf16(metrics(out, ref), "cfg3")
+
+
 def test_batch64_sampled_requests_warped():
     """Batch 64, per-request warped schedules; requests sampled for the oracle."""
     cfg = synth.config(5)
