@@ -74,6 +74,12 @@ extern "C" {
  * for batch*horizon <= 64 (in place of the weight-streaming kernel). For testing and tuning; setting it
  * waits for the ctx stream and drops captured graphs. */
 #define VLA_OPT_GEMM_TILE 5
+/* With batch*horizon <= 64, workgroups appended to the attention and norm kernels (on CUs those leave
+ * idle) load the next weight-streaming GEMMs' weights into the L2 of the XCD that will read them. Bits:
+ * 1 the attention prefetches O, 2 the attention prefetches gate_up, 4 the norm before a layer prefetches
+ * its QKV, 8 the norm before gate_up prefetches down; 0 off. Default 3. For measurement; setting it
+ * waits for the ctx stream and drops captured graphs. */
+#define VLA_OPT_L2_PREFETCH 6
 
 typedef struct vla_ctx vla_ctx;
 

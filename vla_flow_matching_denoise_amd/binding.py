@@ -27,6 +27,7 @@ VLA_OPT_PERSISTENT = 2
 VLA_OPT_PERSISTENT_ACTIVE = 3
 VLA_OPT_PERSISTENT_STATUS = 4
 VLA_OPT_GEMM_TILE = 5
+VLA_OPT_L2_PREFETCH = 6
 
 # every symbol include/vla_expert.h declares
 EXPORTED = (

@@ -192,6 +192,11 @@ struct vla_ctx {
 
     std::map<int, hipGraphExec_t> graphs;
 
+    // batch <= 64 rows: idle workgroups of the attention and norm kernels
+    // prefetch the next skinny GEMMs' weights into the right XCD's L2
+    int l2_prefetch = 3;  // VLA_OPT_L2_PREFETCH bits
+    uint32_t* pf_sink = nullptr;
+
     // persistent small-batch path (one resident launch per call)
     bool persist_ok = false, use_persist = false;
     int pn_cap = 0;                // 1 once the exchange buffers exist
@@ -590,7 +595,26 @@ int enqueue_prefix_repack(vla_ctx* c, const uint16_t* pk, const uint16_t* pv) {
     return VLA_OK;
 }
 
-int launch_attention(vla_ctx* c, int l, const uint16_t* q, uint16_t* o, int ofrag) {
+// Prefetch plan for up to two skinny GEMMs (see L2Prefetch): only GEMMs run by
+// the weight-streaming kernel whose grid width is a multiple of 8 (so XCD x
+// reads the tiles nt % 8 == x) and whose weights are bf16 or E4M3.
+L2Prefetch make_prefetch(vla_ctx* c, const Linear* a, const Linear* b) {
+    L2Prefetch pf{};
+    pf.sink = c->pf_sink;
+    if (!c->pf_sink) return pf;
+    const Linear* ls[2] = {a, b};
+    int k = 0;
+    for (const Linear* ln : ls) {
+        if (!ln || !ln->cfg.skinny || ln->cfg.gx % 8 != 0 || ln->fmt == 2) continue;
+        pf.w[k] = (const uint8_t*)ln->w;
+        pf.tile_bytes[k] = (ln->K / 32) * (c->w8 ? 512 : 1024);
+        pf.n_tiles[k] = ln->N / 16;
+        ++k;
+    }
+    return pf;
+}
+
+int launch_attention(vla_ctx* c, int l, const uint16_t* q, uint16_t* o, int ofrag, const L2Prefetch* pf = nullptr) {
     ProfScope prof(VLA_KERNEL_ATTN);
     const vla_dims& d = c->d;
     AttnParams ap{};
@@ -612,6 +636,13 @@ int launch_attention(vla_ctx* c, int l, const uint16_t* q, uint16_t* o, int ofra
     // few workgroups (small batch): 8 waves per workgroup split the keys finer
     const bool wide = (long)ag.x * ag.y * ag.z < 512;
     if (wide) {
+        // slices of workgroups past the requests take the idle CUs to prefetch
+        if (pf && pf->w[0]) {
+            ap.pf = *pf;
+            const int n_attn = (int)(ag.x * ag.y * ag.z);
+            ap.pf_slices = c->ncu > n_attn ? (c->ncu - n_attn) / (int)(ag.x * ag.y) : 0;
+            ag.z += ap.pf_slices;
+        }
         if (d.head_dim == 128) VLA_LAUNCH((attn_kernel<128, 8>), ag, dim3(512), 0, c->stream, ap);
         else VLA_LAUNCH((attn_kernel<64, 8>), ag, dim3(512), 0, c->stream, ap);
     } else {
@@ -635,14 +666,17 @@ int launch_attention(vla_ctx* c, int l, const uint16_t* q, uint16_t* o, int ofra
 // Residual + AdaRMSNorm over all rows (see resnorm_kernel); skipped when it
 // would do nothing.
 int launch_resnorm(vla_ctx* c, int step, int S, int gate_off, int scale_off, int shift_off, uint16_t* y,
-                   float* yf = nullptr) {
+                   float* yf = nullptr, const L2Prefetch* pf = nullptr) {
     if (S == 0 && !y && !yf) return VLA_OK;
     const vla_dims& d = c->d;
     // the batched E4M3 tier takes y as per-token E4M3 codes instead of bf16
     uint8_t* y8 = c->a8 && y ? c->y8 : nullptr;
-    hipLaunchKernelGGL(resnorm_kernel, dim3(c->M), dim3(256), 0, c->stream, c->h, c->ws, S, c->modtab, gate_off,
+    // workgroups past the M rows (on otherwise idle CUs) prefetch, if asked
+    L2Prefetch none{};
+    const int npf = pf && pf->w[0] && c->ncu > c->M ? (c->ncu - c->M) & ~7 : 0;
+    hipLaunchKernelGGL(resnorm_kernel, dim3(c->M + npf), dim3(256), 0, c->stream, c->h, c->ws, S, c->modtab, gate_off,
                        scale_off, shift_off, y8 ? nullptr : y, yf, c->M, d.hidden, d.horizon, d.batch, step, c->mod_ld,
-                       d.rms_eps, c->afrag, y8, c->y8s);
+                       d.rms_eps, c->afrag, y8, c->y8s, npf ? *pf : none);
     HIPC(hipGetLastError());
     return VLA_OK;
 }
@@ -721,14 +755,23 @@ int enqueue_layer(vla_ctx* c, int step, int l, bool norm_next, float* yf_final =
     const int H = c->d.hidden, L = c->d.n_layers;
     int rc, S = 0;
     if ((rc = launch_block_gemm(c, VLA_KERNEL_QKV, step, l, nullptr))) return rc;
-    if ((rc = launch_attention(c, l, c->q, c->o, c->afrag))) return rc;
+    // weight streaming: the attention's idle CUs prefetch O and gate_up, the
+    // norm before the next layer that layer's QKV
+    const int pfb = c->l2_prefetch;
+    const L2Prefetch pf_attn = make_prefetch(c, pfb & 1 ? &c->wo[l] : nullptr, pfb & 2 ? &c->gu[l] : nullptr);
+    const L2Prefetch pf_mid = make_prefetch(c, pfb & 8 ? &c->wd[l] : nullptr, nullptr);
+    const L2Prefetch pf_next = make_prefetch(c, pfb & 4 && l + 1 < L ? &c->qkv[l + 1] : nullptr, nullptr);
+    if ((rc = launch_attention(c, l, c->q, c->o, c->afrag, &pf_attn))) return rc;
     if (c->a8 && (rc = launch_quant(c, c->o, c->qd, c->o8, c->o8s))) return rc;
     if ((rc = launch_block_gemm(c, VLA_KERNEL_O, step, l, &S))) return rc;
-    if ((rc = launch_resnorm(c, step, S, (6 * l + 2) * H, (6 * l + 3) * H, (6 * l + 4) * H, c->y))) return rc;
+    if ((rc = launch_resnorm(c, step, S, (6 * l + 2) * H, (6 * l + 3) * H, (6 * l + 4) * H, c->y, nullptr, &pf_mid)))
+        return rc;
     if ((rc = launch_block_gemm(c, VLA_KERNEL_GATE_UP, step, l, nullptr))) return rc;
     if (c->a8 && (rc = launch_quant(c, c->act, c->d.intermediate, c->act8, c->act8s))) return rc;
     if ((rc = launch_block_gemm(c, VLA_KERNEL_DOWN, step, l, &S))) return rc;
-    if (norm_next) return launch_resnorm(c, step, S, (6 * l + 5) * H, (6 * (l + 1)) * H, (6 * (l + 1) + 1) * H, c->y);
+    if (norm_next)
+        return launch_resnorm(c, step, S, (6 * l + 5) * H, (6 * (l + 1)) * H, (6 * (l + 1) + 1) * H, c->y, nullptr,
+                              &pf_next);
     if (yf_final) return launch_resnorm(c, step, S, (6 * l + 5) * H, 6 * L * H, (6 * L + 1) * H, nullptr, yf_final);
     return launch_resnorm(c, step, S, (6 * l + 5) * H, 0, 0, nullptr);
 }
@@ -1122,6 +1165,7 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
         if ((rc = c->alloc((void**)&c->gflag, 512 * sizeof(unsigned)))) return rc;
         if ((rc = c->alloc((void**)&c->perr, 64))) return rc;
     }
+    if ((rc = c->alloc((void**)&c->pf_sink, 64))) return rc;
     if ((rc = c->alloc((void**)&c->ab, sizeof(ArgBlock)))) return rc;
     HIPC(hipMemsetAsync(c->ab, 0, sizeof(ArgBlock), c->stream));
     if ((rc = ensure_capacity(c, 10))) return rc;
@@ -1252,6 +1296,18 @@ int vla_set_option(vla_ctx* c, int option, int value) {
         c->use_persist = value != 0;
         return VLA_OK;
     }
+    if (option == VLA_OPT_L2_PREFETCH) {
+        HIPC(hipSetDevice(c->device));
+        HIPC(hipStreamSynchronize(c->stream));
+        if (value < 0 || value > 15) {
+            set_err("VLA_OPT_L2_PREFETCH takes bits 0..15, not %d", value);
+            return VLA_ERR_ARG;
+        }
+        c->l2_prefetch = value;
+        for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);  // they hold the old launches
+        c->graphs.clear();
+        return VLA_OK;
+    }
     if (option == VLA_OPT_GEMM_TILE) {
         if (value < 0 || value > 4) {
             set_err("VLA_OPT_GEMM_TILE takes 0..4, not %d", value);
@@ -1285,6 +1341,7 @@ int vla_get_option(const vla_ctx* c, int option, int* value) {
         case VLA_OPT_USE_GRAPH: *value = c->use_graph ? 1 : 0; return VLA_OK;
         case VLA_OPT_PERSISTENT: *value = c->use_persist ? 1 : 0; return VLA_OK;
         case VLA_OPT_GEMM_TILE: *value = c->gemm_tile; return VLA_OK;
+        case VLA_OPT_L2_PREFETCH: *value = c->l2_prefetch; return VLA_OK;
         case VLA_OPT_PERSISTENT_ACTIVE: *value = (c->persist_ok && c->use_persist) ? 1 : 0; return VLA_OK;
         case VLA_OPT_PERSISTENT_STATUS: {
             int e = 0;
