@@ -439,11 +439,12 @@ class BackboneDims:
 
 
 def decode_backbone_weights(raw: dict, dtype=np.float64) -> Dict[str, list]:
+    """bf16 or per-row E4M3 (codes times row scale) linears, fp32 norm weights."""
     out: Dict[str, list] = {}
     for name in ("n1", "n2"):
         out[name] = [np.asarray(w, np.float64).astype(dtype) for w in raw[name]]
     for name in ("wq", "wk", "wv", "wo", "wg", "wu", "wd"):
-        out[name] = [decode_bf16(w, dtype) for w in raw[name]]
+        out[name] = [_linear(raw, name, l, dtype) for l in range(len(raw[name]))]
     return out
 
 
@@ -467,29 +468,35 @@ def causal_gqa_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndar
     return out
 
 
-def backbone_layer(x: np.ndarray, W: dict, l: int, dims: BackboneDims):
+def backbone_layer(x: np.ndarray, W: dict, l: int, dims: BackboneDims, act_quant: bool = False):
     """One prefix decoder layer on x [P, H]; returns (x, k, v) with k (roped)
-    and v [n_kv, P, d_h]."""
+    and v [n_kv, P, d_h]. ``act_quant``: the input of each linear (y before
+    QKV and gate_up, the attention output before O, the SwiGLU output before
+    down) is taken through per-token E4M3 (``quantize_per_token_e4m3``), as
+    the expert's batched E4M3 tier does."""
     P = x.shape[0]
     nq, nkv, dh = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
-    y = rms_norm_weighted(x, W["n1"][l], dims.rms_eps)
+    aq = quantize_per_token_e4m3 if act_quant else (lambda z: z)
+    y = aq(rms_norm_weighted(x, W["n1"][l], dims.rms_eps))
     q = (y @ W["wq"][l].T).reshape(P, nq, dh).transpose(1, 0, 2)
     k = (y @ W["wk"][l].T).reshape(P, nkv, dh).transpose(1, 0, 2)
     v = (y @ W["wv"][l].T).reshape(P, nkv, dh).transpose(1, 0, 2)
     pos = np.arange(P)
     q = rope_rotate_half(q, pos, dims.rope_theta)
     k = rope_rotate_half(k, pos, dims.rope_theta)
-    o = causal_gqa_attention(q, k, v).transpose(1, 0, 2).reshape(P, nq * dh)
+    o = aq(causal_gqa_attention(q, k, v).transpose(1, 0, 2).reshape(P, nq * dh))
     x = x + o @ W["wo"][l].T
-    y = rms_norm_weighted(x, W["n2"][l], dims.rms_eps)
-    x = x + (silu(y @ W["wg"][l].T) * (y @ W["wu"][l].T)) @ W["wd"][l].T
+    y = aq(rms_norm_weighted(x, W["n2"][l], dims.rms_eps))
+    x = x + aq(silu(y @ W["wg"][l].T) * (y @ W["wu"][l].T)) @ W["wd"][l].T
     return x, k, v
 
 
-def prefill(W: dict, dims: BackboneDims, emb: np.ndarray, n_layers: Optional[int] = None):
+def prefill(W: dict, dims: BackboneDims, emb: np.ndarray, n_layers: Optional[int] = None,
+            act_quant: bool = False):
     """Prefix cache of every request: emb [B, P, H] (decoded floats) ->
     (prefix_k, prefix_v) [B, L, P, n_kv, d_h] in W's dtype (the layout
-    ``denoise`` takes).  ``n_layers`` limits the layers computed."""
+    ``denoise`` takes).  ``n_layers`` limits the layers computed;
+    ``act_quant`` as in ``backbone_layer``."""
     L = dims.n_layers if n_layers is None else n_layers
     B, P = emb.shape[0], emb.shape[1]
     dtype = W["wq"][0].dtype
@@ -498,7 +505,7 @@ def prefill(W: dict, dims: BackboneDims, emb: np.ndarray, n_layers: Optional[int
     for b in range(B):
         x = np.asarray(emb[b], dtype=dtype)
         for l in range(L):
-            x, k, v = backbone_layer(x, W, l, dims)
+            x, k, v = backbone_layer(x, W, l, dims, act_quant)
             pk[b, l] = k.transpose(1, 0, 2)
             pv[b, l] = v.transpose(1, 0, 2)
     return pk, pv

@@ -307,6 +307,7 @@ class BackboneConfig:
     rope_theta: float = 1.0e6
     rms_eps: float = 1.0e-6
     weight_std: float = 0.02
+    weight_dtype: str = "bf16"   # or "fp8_e4m3": per-row E4M3 linears as for the expert
 
     def replace(self, **kw) -> "BackboneConfig":
         return dataclasses.replace(self, **kw)
@@ -328,15 +329,23 @@ def backbone(i: int) -> BackboneConfig:
 _BB_IDS = {"n1": 1, "n2": 2, "wq": 3, "wk": 4, "wv": 5, "wo": 6, "wg": 7, "wu": 8, "wd": 9}
 
 
-def make_backbone_weights(cfg: BackboneConfig, seed: int = 0) -> dict:
+def make_backbone_weights(cfg: BackboneConfig, seed: int = 0, weight_dtype: Optional[str] = None) -> dict:
     """Per-layer lists: ``n1``, ``n2`` RMSNorm weights float32 [H] (1 + N(0, 0.1^2));
     ``wq`` [n_q*d_h, H], ``wk``, ``wv`` [n_kv*d_h, H], ``wo`` [H, n_q*d_h],
-    ``wg``, ``wu`` [I, H], ``wd`` [H, I] as bf16 bits, N(0, std^2)."""
+    ``wg``, ``wu`` [I, H], ``wd`` [H, I], N(0, std^2), as bf16 bits, or for
+    ``fp8_e4m3`` as per-row E4M3FN codes with fp32 row scales ``sq`` .. ``sd``
+    (the rule of the expert's E4M3 tier) from the same draws."""
+    wd = weight_dtype or cfg.weight_dtype
     H, I = cfg.hidden, cfg.intermediate
     qd, kvd = cfg.n_q_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
     shapes = {"wq": (qd, H), "wk": (kvd, H), "wv": (kvd, H), "wo": (H, qd), "wg": (I, H), "wu": (I, H),
               "wd": (H, I)}
     W: Dict[str, list] = {k: [] for k in _BB_IDS}
+    if wd == "fp8_e4m3":
+        for name in shapes:
+            W["s" + name[1]] = []
+    elif wd != "bf16":
+        raise ValueError(f"unknown backbone weight dtype {wd!r}")
     for l in range(cfg.n_layers):
         for name in ("n1", "n2"):
             r = np.random.default_rng([seed, cfg.model_tag, _BB_IDS[name], l])
@@ -344,7 +353,12 @@ def make_backbone_weights(cfg: BackboneConfig, seed: int = 0) -> dict:
         for name, shp in shapes.items():
             r = np.random.default_rng([seed, cfg.model_tag, _BB_IDS[name], l])
             x = r.standard_normal(size=shp, dtype=np.float32) * np.float32(cfg.weight_std)
-            W[name].append(to_bf16_bits(x))
+            if wd == "bf16":
+                W[name].append(to_bf16_bits(x))
+            else:
+                q, sc = to_e4m3_rowwise(x)
+                W[name].append(q)
+                W["s" + name[1]].append(sc)
     return W
 
 

@@ -7,6 +7,7 @@ structure, invariants and brute force on tiny inputs.
 """
 import dataclasses
 import math
+import sys
 
 import numpy as np
 import pytest
@@ -696,3 +697,46 @@ def test_prefill_position_zero_key_is_unrotated():
     x0 = emb[0, 0]
     y0 = x0 / np.sqrt(np.mean(x0 ** 2) + d.rms_eps) * W["n1"][0]
     np.testing.assert_allclose(pk[0, 0, 0].ravel(), W["wk"][0] @ y0, rtol=1e-10, atol=1e-12)
+
+
+def test_prefill_act_quant_wiring():
+    """act_quant takes exactly the four linear inputs through per-token E4M3:
+    with the quantizer replaced by the identity the result is the plain
+    prefill bitwise, and with it on the result moves by a rounding-sized
+    amount (so the switch is wired)."""
+    bcfg = synth.backbone(1).replace(prefix_len=9, batch=1)
+    W = oracle.decode_backbone_weights(synth.make_backbone_weights(bcfg, seed=5))
+    d = oracle.BackboneDims.from_config(bcfg)
+    emb = oracle.decode_bf16(synth.make_embeddings(bcfg, seed=6))
+    pk, pv = oracle.prefill(W, d, emb)
+    mod = sys.modules["oracle.denoise"]
+    calls = []
+    orig = mod.quantize_per_token_e4m3
+    try:
+        mod.quantize_per_token_e4m3 = lambda a: (calls.append(a.shape), a)[1]
+        qk, qv = oracle.prefill(W, d, emb, act_quant=True)
+    finally:
+        mod.quantize_per_token_e4m3 = orig
+    assert np.array_equal(qk, pk) and np.array_equal(qv, pv)
+    H, I, qd = bcfg.hidden, bcfg.intermediate, bcfg.n_q_heads * bcfg.head_dim
+    assert calls == [(9, H), (9, qd), (9, H), (9, I)] * bcfg.n_layers
+    qk, qv = oracle.prefill(W, d, emb, act_quant=True)
+    rel = np.linalg.norm(qk - pk) / np.linalg.norm(pk)
+    assert 1e-4 < rel < 0.1
+
+
+def test_backbone_fp8_weights_decode_to_row_scaled_codes():
+    """The E4M3 backbone linears decode to code value x row scale within one
+    E4M3 rounding of the same float32 draws (relative 2^-4 per element, the
+    row maximum exact to 2^-4 of itself)."""
+    bcfg = synth.backbone(1)
+    raw8 = synth.make_backbone_weights(bcfg, seed=2, weight_dtype="fp8_e4m3")
+    rawb = synth.make_backbone_weights(bcfg, seed=2)
+    W8 = oracle.decode_backbone_weights(raw8)
+    Wb = oracle.decode_backbone_weights(rawb)
+    for name in ("wq", "wo", "wd"):
+        a, b = W8[name][1], Wb[name][1]
+        assert a.shape == b.shape
+        row_max = np.abs(b).max(axis=1, keepdims=True)
+        assert np.all(np.abs(a - b) <= 2.0 ** -4 * np.abs(b) + 2.0 ** -9 * row_max / 448 * 2 + 2.0 ** -8 * row_max)
+        np.testing.assert_allclose(np.abs(a).max(axis=1), row_max[:, 0], rtol=2.0 ** -4)
