@@ -21,8 +21,9 @@
  * later tokens: a prefix padded at its end gives exact caches for its valid
  * tokens (vla_denoise_varlen then ignores the rest).
  *
- * Precision: weights and GEMM/attention inputs bf16, every accumulation
- * fp32, the residual stream fp32, keys/values out bf16.
+ * Precision: weights and GEMM/attention inputs bf16 (or, with
+ * VLA_FP8_E4M3, E4M3 weights and per-token E4M3 linear inputs), every
+ * accumulation fp32, the residual stream fp32, keys/values out bf16.
  * Threading and errors as in vla_expert.h (shared VLA_ERR_* codes and
  * vla_last_error()).
  */
@@ -57,13 +58,21 @@ typedef struct vla_backbone_dims {
     int32_t batch;         /* B requests per call */
     float rope_theta;
     float rms_eps;
+    int32_t weight_dtype;  /* VLA_BF16, or VLA_FP8_E4M3 (hidden, n_q_heads*head_dim and
+                              intermediate multiples of 128) */
 } vla_backbone_dims;
 
 /*
  * Weights, all DEVICE pointers, one array entry per layer (n_layers each):
  *   norm1, norm2  [H] fp32 RMSNorm weights (4-byte aligned)
  *   wq [n_q*d_h, H], wk, wv [n_kv*d_h, H], wo [H, n_q*d_h],
- *   wg, wu [I, H], wd [H, I]   bf16, row-major (out, in), 8-byte aligned.
+ *   wg, wu [I, H], wd [H, I]   row-major (out, in), 8-byte aligned: bf16, or
+ *                              for VLA_FP8_E4M3 OCP E4M3FN codes with
+ *   sq, sk, sv, so, sg, su, sd  fp32 per-output-row scales (weight = code *
+ *                              scale; unused and may be NULL for bf16).
+ * The E4M3 tier also takes each linear's input per token in E4M3 (codes
+ * RNE(x * 448 / max|x_row|), row scale max|x_row| / 448), as the expert's
+ * batched E4M3 tier does; accumulation stays fp32.
  */
 typedef struct vla_backbone_weights {
     const float* const* norm1;
@@ -71,6 +80,9 @@ typedef struct vla_backbone_weights {
     const void* const* wq; const void* const* wk; const void* const* wv;
     const void* const* wo; const void* const* wg; const void* const* wu;
     const void* const* wd;
+    const float* const* sq; const float* const* sk; const float* const* sv;
+    const float* const* so; const float* const* sg; const float* const* su;
+    const float* const* sd;
 } vla_backbone_weights;
 
 /*

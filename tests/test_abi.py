@@ -106,3 +106,18 @@ def test_prefill_unsupported_dims_are_rejected_before_any_device_work(lib, field
     w = B.VlaBackboneWeights()
     assert lib.vla_prefill_create(ctypes.byref(w), ctypes.byref(d)) is None
     assert "unsupported" in B.vla_last_error() or "must" in B.vla_last_error()
+
+
+def test_prefill_e4m3_needs_multiples_of_128(lib):
+    from vla_flow_matching_denoise_amd import binding as B
+    from vla_flow_matching_denoise_amd.prefill import backbone_dims
+    w = B.VlaBackboneWeights()
+    d = backbone_dims(2, 256, 4, 2, 64, 704, 32, 1, weight_dtype="fp8_e4m3")     # I = 704: not a multiple of 128
+    assert lib.vla_prefill_create(ctypes.byref(w), ctypes.byref(d)) is None
+    assert "128" in B.vla_last_error()
+    d = backbone_dims(2, 256, 4, 2, 64, 768, 32, 1, weight_dtype="fp8_e4m3")
+    assert lib.vla_prefill_create(ctypes.byref(w), ctypes.byref(d)) is None
+    assert "128" not in B.vla_last_error()          # fails later, on the NULL weight pointers
+    d = backbone_dims(2, 256, 4, 2, 64, 768, 32, 1, weight_dtype=7)
+    assert lib.vla_prefill_create(ctypes.byref(w), ctypes.byref(d)) is None
+    assert "weight_dtype" in B.vla_last_error()

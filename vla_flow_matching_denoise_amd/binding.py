@@ -70,7 +70,7 @@ class VlaBackboneDims(ctypes.Structure):
         ("n_layers", ctypes.c_int32), ("hidden", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
         ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("intermediate", ctypes.c_int32),
         ("prefix_len", ctypes.c_int32), ("batch", ctypes.c_int32), ("rope_theta", ctypes.c_float),
-        ("rms_eps", ctypes.c_float),
+        ("rms_eps", ctypes.c_float), ("weight_dtype", ctypes.c_int32),
     ]
 
 
@@ -78,6 +78,7 @@ class VlaBackboneWeights(ctypes.Structure):
     _fields_ = [
         ("norm1", _PP), ("norm2", _PP), ("wq", _PP), ("wk", _PP), ("wv", _PP), ("wo", _PP), ("wg", _PP),
         ("wu", _PP), ("wd", _PP),
+        ("sq", _PP), ("sk", _PP), ("sv", _PP), ("so", _PP), ("sg", _PP), ("su", _PP), ("sd", _PP),
     ]
 
 

@@ -127,11 +127,11 @@ GemmCfg choose_gemm(int M, int N, int K, bool allow_split, int ncu, int force_ti
 // the grid within one round of `ncu` workgroups and every split at least
 // 512 deep (8 stages). The partials go to a workspace and are summed by the
 // consumer (a norm, or splitk_finish_kernel).
-GemmCfg choose_gemm_split(int M, int N, int K, int ncu, int force_tile) {
+GemmCfg choose_gemm_split(int M, int N, int K, int ncu, int force_tile, int kt = GEMM_KT) {
     GemmCfg c = choose_gemm(M, N, K, false, ncu, force_tile, true);
     const long tiles = (long)((M + c.MT - 1) / c.MT) * (N / c.NT);
     int ks = 1;
-    while (tiles * ks * 2 <= ncu && (K / (ks * 2)) % GEMM_KT == 0 && K / (ks * 2) >= 512 && K % (ks * 2) == 0)
+    while (tiles * ks * 2 <= ncu && (K / (ks * 2)) % kt == 0 && K / (ks * 2) >= 512 && K % (ks * 2) == 0)
         ks *= 2;
     c.ksplit = ks;
     c.kw = K / ks;
@@ -447,6 +447,8 @@ int launch_tiled8_t(int epi, const GemmParams& p, dim3 grid, hipStream_t s) {
         case EPI_RESID: VLA_LAUNCH((gemm8_kernel<MT, NT, EPI_RESID>), grid, blk, 0, s, p); break;
         case EPI_QKV_ROPE: VLA_LAUNCH((gemm8_kernel<MT, NT, EPI_QKV_ROPE>), grid, blk, 0, s, p); break;
         case EPI_SWIGLU: VLA_LAUNCH((gemm8_kernel<MT, NT, EPI_SWIGLU>), grid, blk, 0, s, p); break;
+        case EPI_ADD: VLA_LAUNCH((gemm8_kernel<MT, NT, EPI_ADD>), grid, blk, 0, s, p); break;
+        case EPI_PARTIAL: VLA_LAUNCH((gemm8_kernel<MT, NT, EPI_PARTIAL>), grid, blk, 0, s, p); break;
         default: set_err("bad FP8 tiled epilogue %d", epi); return VLA_ERR_ARG;
     }
     HIPC(hipGetLastError());
@@ -508,8 +510,8 @@ int launch_gemm(vla_ctx* c, const Linear& lin, const GemmCfg& cfg, bool w8, int 
     if (cfg.ksplit > 1) {
         // split K: partials into ws; EPI_ADD / EPI_RESID partials are summed
         // by the caller's next norm, the other epilogues by a finish kernel
-        if (w8) {
-            set_err("split-K tiled GEMM takes bf16 weights only");
+        if (w8 && !c->a8) {
+            set_err("split-K tiled GEMM takes bf16 weights or the per-token E4M3 tier");
             return VLA_ERR_SHAPE;
         }
         if (!p.ws) {
@@ -517,7 +519,20 @@ int launch_gemm(vla_ctx* c, const Linear& lin, const GemmCfg& cfg, bool w8, int 
             return VLA_ERR_ARG;
         }
         int rc;
-        if (cfg.MT == 256 && cfg.NT == 256) rc = launch_tiled_t<256, 256, false>(EPI_PARTIAL, p, grid, c->stream);
+        if (w8) {
+            if (cfg.kw % GEMM8_KT != 0) {
+                set_err("FP8 split-K GEMM needs K per split %% %d == 0 (%d)", GEMM8_KT, cfg.kw);
+                return VLA_ERR_SHAPE;
+            }
+            if (cfg.MT == 256 && cfg.NT == 256) rc = launch_tiled8_t<256, 256>(EPI_PARTIAL, p, grid, c->stream);
+            else if (cfg.MT == 256 && cfg.NT == 128) rc = launch_tiled8_t<256, 128>(EPI_PARTIAL, p, grid, c->stream);
+            else if (cfg.MT == 128 && cfg.NT == 128) rc = launch_tiled8_t<128, 128>(EPI_PARTIAL, p, grid, c->stream);
+            else if (cfg.MT == 128 && cfg.NT == 64) rc = launch_tiled8_t<128, 64>(EPI_PARTIAL, p, grid, c->stream);
+            else {
+                set_err("no FP8 GEMM tile %dx%d", cfg.MT, cfg.NT);
+                return VLA_ERR_SHAPE;
+            }
+        } else if (cfg.MT == 256 && cfg.NT == 256) rc = launch_tiled_t<256, 256, false>(EPI_PARTIAL, p, grid, c->stream);
         else if (cfg.MT == 256 && cfg.NT == 128) rc = launch_tiled_t<256, 128, false>(EPI_PARTIAL, p, grid, c->stream);
         else if (cfg.MT == 128 && cfg.NT == 128) rc = launch_tiled_t<128, 128, false>(EPI_PARTIAL, p, grid, c->stream);
         else if (cfg.MT == 128 && cfg.NT == 64) rc = launch_tiled_t<128, 64, false>(EPI_PARTIAL, p, grid, c->stream);
@@ -1574,6 +1589,15 @@ int validate_backbone(const vla_backbone_dims* d) {
         set_err("rms_eps and rope_theta must be positive");
         return VLA_ERR_SHAPE;
     }
+    if (d->weight_dtype != VLA_BF16 && d->weight_dtype != VLA_FP8_E4M3) {
+        set_err("backbone weight_dtype must be VLA_BF16 or VLA_FP8_E4M3 (got %d)", d->weight_dtype);
+        return VLA_ERR_SHAPE;
+    }
+    if (d->weight_dtype == VLA_FP8_E4M3 &&
+        (d->hidden % 128 || (d->n_q_heads * d->head_dim) % 128 || d->intermediate % 128)) {
+        set_err("the E4M3 backbone needs hidden, n_q_heads*head_dim and intermediate multiples of 128");
+        return VLA_ERR_SHAPE;
+    }
     return VLA_OK;
 }
 
@@ -1584,7 +1608,7 @@ int prefill_choose(vla_prefill_ctx* x) {
     size_t need = 16;
     for (int l = 0; l < x->d.n_layers; ++l)
         for (Linear* ln : {&x->qkv[l], &x->wo[l], &x->gu[l], &x->wd[l]}) {
-            ln->cfg = choose_gemm_split(x->M, ln->N, ln->K, c->ncu, x->gemm_tile);
+            ln->cfg = choose_gemm_split(x->M, ln->N, ln->K, c->ncu, x->gemm_tile, c->a8 ? GEMM8_KT : GEMM_KT);
             if (ln->cfg.ksplit > 1) need = std::max(need, (size_t)ln->cfg.ksplit * x->M * ln->N);
         }
     if (need > x->ws_elems) {
@@ -1605,6 +1629,8 @@ int prefill_create_impl(vla_prefill_ctx* x, const vla_backbone_weights* w) {
     x->M = B * P;
     x->qd = d.n_q_heads * dh;
     x->kvd = d.n_kv_heads * dh;
+    // E4M3 tier: weights packed as 16 x 128 FP8 fragments, per-token E4M3 inputs
+    c->w8 = c->a8 = d.weight_dtype == VLA_FP8_E4M3;
     HIPC(hipGetDevice(&c->device));
     HIPC(hipDeviceGetAttribute(&c->ncu, hipDeviceAttributeMultiprocessorCount, c->device));
     HIPC(hipStreamCreateWithFlags(&c->own_stream, hipStreamNonBlocking));
@@ -1622,6 +1648,17 @@ int prefill_create_impl(vla_prefill_ctx* x, const vla_backbone_weights* w) {
         for (int l = 0; l < L; ++l)
             if ((rc = check_ptr(per[i][l], pnames[i], i >= 2 ? 8 : 4))) return rc;
     }
+    const float* const* scales[7] = {w->sq, w->sk, w->sv, w->so, w->sg, w->su, w->sd};
+    if (c->w8)
+        for (int i = 0; i < 7; ++i) {
+            if (!scales[i]) {
+                set_err("E4M3 backbone weights need all seven per-layer scale arrays");
+                return VLA_ERR_ARG;
+            }
+            for (int l = 0; l < L; ++l)
+                if ((rc = check_ptr(scales[i][l], "E4M3 scale", 4))) return rc;
+        }
+    auto sc = [&](int i, int l) -> const float* { return c->w8 ? scales[i][l] : nullptr; };
     if ((rc = c->alloc((void**)&x->norms, (size_t)L * 2 * H * 4))) return rc;
     for (int l = 0; l < L; ++l) {
         HIPC(hipMemcpyAsync(x->norms + (size_t)(2 * l) * H, w->norm1[l], (size_t)H * 4, hipMemcpyDeviceToDevice,
@@ -1636,25 +1673,25 @@ int prefill_create_impl(vla_prefill_ctx* x, const vla_backbone_weights* w) {
     for (int l = 0; l < L; ++l) {
         {
             const void* srcs[3] = {w->wq[l], w->wk[l], w->wv[l]};
-            const float* scs[3] = {nullptr, nullptr, nullptr};
+            const float* scs[3] = {sc(0, l), sc(1, l), sc(2, l)};
             int rows[3] = {x->qd, x->kvd, x->kvd};
             if ((rc = pack_linear(c, x->qkv[l], x->qd + 2 * x->kvd, H, srcs, scs, 3, rows, 1, dh))) return rc;
         }
         {
             const void* srcs[1] = {w->wo[l]};
-            const float* scs[1] = {nullptr};
+            const float* scs[1] = {sc(3, l)};
             int rows[1] = {H};
             if ((rc = pack_linear(c, x->wo[l], H, x->qd, srcs, scs, 1, rows, 0, dh))) return rc;
         }
         {
             const void* srcs[2] = {w->wg[l], w->wu[l]};
-            const float* scs[2] = {nullptr, nullptr};
+            const float* scs[2] = {sc(4, l), sc(5, l)};
             int rows[2] = {I, I};
             if ((rc = pack_linear(c, x->gu[l], 2 * I, H, srcs, scs, 2, rows, 2, dh))) return rc;
         }
         {
             const void* srcs[1] = {w->wd[l]};
-            const float* scs[1] = {nullptr};
+            const float* scs[1] = {sc(6, l)};
             int rows[1] = {H};
             if ((rc = pack_linear(c, x->wd[l], H, I, srcs, scs, 1, rows, 0, dh))) return rc;
         }
@@ -1673,6 +1710,14 @@ int prefill_create_impl(vla_prefill_ctx* x, const vla_backbone_weights* w) {
     if ((rc = c->alloc((void**)&x->q, M * x->qd * 2))) return rc;
     if ((rc = c->alloc((void**)&x->o, M * x->qd * 2))) return rc;
     if ((rc = c->alloc((void**)&x->act, M * I * 2))) return rc;
+    if (c->a8) {
+        if ((rc = c->alloc((void**)&c->y8, M * H))) return rc;
+        if ((rc = c->alloc((void**)&c->o8, M * x->qd))) return rc;
+        if ((rc = c->alloc((void**)&c->act8, M * I))) return rc;
+        if ((rc = c->alloc((void**)&c->y8s, M * 4))) return rc;
+        if ((rc = c->alloc((void**)&c->o8s, M * 4))) return rc;
+        if ((rc = c->alloc((void**)&c->act8s, M * 4))) return rc;
+    }
     x->kv.L = L;
     x->kv.nkv = d.n_kv_heads;
     x->kv.dh = dh;
@@ -1693,8 +1738,10 @@ int prefill_create_impl(vla_prefill_ctx* x, const vla_backbone_weights* w) {
 // adding the S split-K partials left in ws by the preceding residual GEMM.
 int prefill_norm(vla_prefill_ctx* x, bool first, int which, int S) {
     const vla_backbone_dims& d = x->d;
-    hipLaunchKernelGGL(rmsnorm_w_kernel, dim3(x->M), dim3(256), 0, x->c->stream, first ? x->args : nullptr, x->h,
-                       x->c->ws, S, x->M, x->norms + (size_t)which * d.hidden, x->y, d.hidden, d.rms_eps);
+    vla_ctx* c = x->c;
+    hipLaunchKernelGGL(rmsnorm_w_kernel, dim3(x->M), dim3(256), 0, c->stream, first ? x->args : nullptr, x->h, c->ws,
+                       S, x->M, x->norms + (size_t)which * d.hidden, x->y, d.hidden, d.rms_eps,
+                       c->a8 ? c->y8 : nullptr, c->y8s);
     HIPC(hipGetLastError());
     return VLA_OK;
 }
@@ -1709,7 +1756,8 @@ int enqueue_prefill(vla_prefill_ctx* x) {
         if ((rc = prefill_norm(x, l == 0, 2 * l, S))) return rc;
         {
             GemmParams p{};
-            p.A = x->y;
+            p.A = c->a8 ? (const uint16_t*)c->y8 : x->y;
+            p.ascale = c->y8s;
             p.lda = H;
             p.M = x->M;
             p.B = B;
@@ -1727,7 +1775,7 @@ int enqueue_prefill(vla_prefill_ctx* x) {
             p.nkv = d.n_kv_heads;
             p.dh = dh;
             p.dh_shift = dh == 128 ? 7 : 6;
-            if ((rc = launch_gemm(c, x->qkv[l], x->qkv[l].cfg, false, EPI_QKV_ROPE, p))) return rc;
+            if ((rc = launch_gemm(c, x->qkv[l], x->qkv[l].cfg, c->w8, EPI_QKV_ROPE, p))) return rc;
         }
         if (l + 1 == L) break;  // the last layer's attention and MLP feed no cache
         {
@@ -1750,31 +1798,43 @@ int enqueue_prefill(vla_prefill_ctx* x) {
             else hipLaunchKernelGGL((attn_rows_kernel<64, 1, true>), rg, dim3(256), 0, c->stream, ap);
             HIPC(hipGetLastError());
         }
+        if (c->a8) {
+            hipLaunchKernelGGL(quant_rows_kernel, dim3(x->M), dim3(256), 0, c->stream, x->o, x->qd, c->o8, c->o8s);
+            HIPC(hipGetLastError());
+        }
         {
             GemmParams p{};
-            p.A = x->o;
+            p.A = c->a8 ? (const uint16_t*)c->o8 : x->o;
+            p.ascale = c->o8s;
             p.lda = x->qd;
             p.M = x->M;
             p.out_f32 = x->h;
-            if ((rc = launch_gemm(c, x->wo[l], x->wo[l].cfg, false, EPI_ADD, p))) return rc;
+            if ((rc = launch_gemm(c, x->wo[l], x->wo[l].cfg, c->w8, EPI_ADD, p))) return rc;
             S = x->wo[l].cfg.ksplit > 1 ? x->wo[l].cfg.ksplit : 0;
         }
         if ((rc = prefill_norm(x, false, 2 * l + 1, S))) return rc;
         {
             GemmParams p{};
-            p.A = x->y;
+            p.A = c->a8 ? (const uint16_t*)c->y8 : x->y;
+            p.ascale = c->y8s;
             p.lda = H;
             p.M = x->M;
             p.act = x->act;
-            if ((rc = launch_gemm(c, x->gu[l], x->gu[l].cfg, false, EPI_SWIGLU, p))) return rc;
+            if ((rc = launch_gemm(c, x->gu[l], x->gu[l].cfg, c->w8, EPI_SWIGLU, p))) return rc;
+        }
+        if (c->a8) {
+            hipLaunchKernelGGL(quant_rows_kernel, dim3(x->M), dim3(256), 0, c->stream, x->act, d.intermediate,
+                               c->act8, c->act8s);
+            HIPC(hipGetLastError());
         }
         {
             GemmParams p{};
-            p.A = x->act;
+            p.A = c->a8 ? (const uint16_t*)c->act8 : x->act;
+            p.ascale = c->act8s;
             p.lda = d.intermediate;
             p.M = x->M;
             p.out_f32 = x->h;
-            if ((rc = launch_gemm(c, x->wd[l], x->wd[l].cfg, false, EPI_ADD, p))) return rc;
+            if ((rc = launch_gemm(c, x->wd[l], x->wd[l].cfg, c->w8, EPI_ADD, p))) return rc;
             S = x->wd[l].cfg.ksplit > 1 ? x->wd[l].cfg.ksplit : 0;
         }
     }

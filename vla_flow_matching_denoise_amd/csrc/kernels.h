@@ -86,7 +86,7 @@ __global__ void pack_weight_kernel(const uint8_t* __restrict__ src, int R, int K
 }
 
 // ---------------------------------------------------------------------------
-// Per-token E4M3 activations: row r of a bf16 [M][K] matrix (K <= 8192, a
+// Per-token E4M3 activations: row r of a bf16 [M][K] matrix (K <= 16384, a
 // multiple of 8) becomes codes q = RNE(x * 448 / max|x_r|) with the row
 // scale max|x_r| / 448 (1 for an all-zero row), so x ~ q * scale.
 // ---------------------------------------------------------------------------
@@ -95,10 +95,10 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
     __shared__ float red[4];
     const int row = blockIdx.x, tid = threadIdx.x;
     const uint16_t* sr = src + (size_t)row * K;
-    float v[4][8];
+    float v[8][8];
     float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
         const int c = (tid + 256 * i) * 8;
         if (c < K) {
             const u32x4 w = *(const u32x4*)(sr + c);
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
     const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
     if (tid == 0) scale[row] = amax > 0.f ? amax / 448.0f : 1.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 8; ++i) {
         const int c = (tid + 256 * i) * 8;
         if (c < K) {
             u32x2 q;

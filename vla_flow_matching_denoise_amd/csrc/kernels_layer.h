@@ -869,9 +869,11 @@ void gemm8_kernel(GemmParams p) {
         nt_i = blockIdx.x % ntn;
     }
     const int m0 = mt_i * MT, n0 = nt_i * NT;
-    const int nk = p.K / GEMM8_KT;
+    // split K (gridDim.y > 1, EPI_PARTIAL): inputs [kz * kw, (kz + 1) * kw)
+    const int kz = blockIdx.y, kt0 = kz * (p.kw / GEMM8_KT);
+    const int nk = p.kw / GEMM8_KT, Kt = p.K / GEMM8_KT;
     const uint32_t lbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
-    const uint8_t* A = (const uint8_t*)p.A;
+    const uint8_t* A = (const uint8_t*)p.A + (size_t)kt0 * GEMM8_KT;
 
     // A in the stage as MT rows of 128 bytes (128 inputs) with the 16-byte
     // chunk swizzle of gemm_kernel: load j fills rows 8j .. 8j + 7 from whole
@@ -892,7 +894,7 @@ void gemm8_kernel(GemmParams p) {
 #pragma unroll
     for (int i = 0; i < LB; ++i) {
         const int c = (wave * LB + i) % BCH;
-        bsrc[i] = (const uint8_t*)p.W + ((size_t)(n0 / 16 + c / 2) * nk) * 2048 + (c % 2) * 1024 + lane * 16;
+        bsrc[i] = (const uint8_t*)p.W + ((size_t)(n0 / 16 + c / 2) * Kt + kt0) * 2048 + (c % 2) * 1024 + lane * 16;
         bdst[i] = (uint32_t)(ACH + c) * 1024;
     }
     // stage kt into ring slot kt % S; past the last stage the loads repeat it
@@ -984,7 +986,7 @@ void gemm8_kernel(GemmParams p) {
                     const f32x4 t = *(const f32x4*)(ct + lr * CLD + swz(uc * 16 + 4 * q));
                     v[4 * q] = t[0] * as; v[4 * q + 1] = t[1] * as; v[4 * q + 2] = t[2] * as; v[4 * q + 3] = t[3] * as;
                 }
-                epilogue16<EPI>(p, row, n0 + uc * 16, v);
+                epilogue16<EPI>(p, row, n0 + uc * 16, v, kz);
             }
         }
         __syncthreads();

@@ -33,11 +33,14 @@ __global__ void set_prefill_args_kernel(PrefillArgs* a, const uint16_t* emb, uin
 // first layer) the row comes from the bf16 embeddings and is also written to
 // the fp32 residual stream h. With S > 0 the S split-K partials ws[s][M][H]
 // of the preceding residual GEMM are first added to h (and h written back).
+// With y8 (the E4M3 tier) the output is instead per-token E4M3: codes
+// RNE(y * 448 / max|y|) and the row scale max|y| / 448 (1 for a zero row).
 __global__ __launch_bounds__(256) void rmsnorm_w_kernel(const PrefillArgs* args, float* __restrict__ h,
                                                         const float* __restrict__ ws, int S, int M,
                                                         const float* __restrict__ w, uint16_t* __restrict__ y,
-                                                        int H, float eps) {
-    __shared__ float red[4];
+                                                        int H, float eps, uint8_t* __restrict__ y8,
+                                                        float* __restrict__ y8s) {
+    __shared__ float red[4], red8[4];
     const int row = blockIdx.x, tid = threadIdx.x;
     float* hr = h + (size_t)row * H;
     f32x4 v[4];
@@ -68,15 +71,39 @@ __global__ __launch_bounds__(256) void rmsnorm_w_kernel(const PrefillArgs* args,
     if ((tid & 63) == 0) red[tid >> 6] = ss;
     __syncthreads();
     const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + eps);
+    float amax = 0.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int c = (tid + 256 * j) * 4;
         if (c < H) {
             const f32x4 wq = *(const f32x4*)(w + c);
-            u32x2 o;
-            o[0] = pack_bf16x2(v[j][0] * inv * wq[0], v[j][1] * inv * wq[1]);
-            o[1] = pack_bf16x2(v[j][2] * inv * wq[2], v[j][3] * inv * wq[3]);
-            *(u32x2*)(y + (size_t)row * H + c) = o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[j][e] = v[j][e] * inv * wq[e];
+                amax = fmaxf(amax, fabsf(v[j][e]));
+            }
+            if (!y8) {
+                u32x2 o;
+                o[0] = pack_bf16x2(v[j][0], v[j][1]);
+                o[1] = pack_bf16x2(v[j][2], v[j][3]);
+                *(u32x2*)(y + (size_t)row * H + c) = o;
+            }
+        }
+    }
+    if (y8) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        if ((tid & 63) == 0) red8[tid >> 6] = amax;
+        __syncthreads();
+        amax = fmaxf(fmaxf(red8[0], red8[1]), fmaxf(red8[2], red8[3]));
+        const float qs = amax > 0.f ? 448.0f / amax : 1.0f;
+        if (tid == 0) y8s[row] = amax > 0.f ? amax / 448.0f : 1.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = (tid + 256 * j) * 4;
+            if (c < H)
+                *(uint32_t*)(y8 + (size_t)row * H + c) =
+                    f32x4_to_e4m3x4(v[j][0] * qs, v[j][1] * qs, v[j][2] * qs, v[j][3] * qs);
         }
     }
 }

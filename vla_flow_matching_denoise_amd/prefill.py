@@ -1,7 +1,7 @@
 """``Prefill``: owns one prefix K/V construction context (argument marshalling only).
 
-Backbone weights arrive as raw encodings (bf16 bit patterns as uint16, fp32
-RMSNorm weights), are placed in device memory by torch, handed to
+Backbone weights arrive as raw encodings (bf16 bit patterns as uint16, or
+E4M3 codes as uint8 with fp32 row scales; fp32 RMSNorm weights), are placed in device memory by torch, handed to
 ``vla_prefill_create`` (which repacks and copies them) and released.
 ``__call__`` passes device pointers of torch tensors to ``vla_prefill`` on
 torch's current stream; every step runs in the HIP library.
@@ -18,15 +18,17 @@ LINEARS = ("wq", "wk", "wv", "wo", "wg", "wu", "wd")
 
 
 def backbone_dims(n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate, prefix_len, batch,
-                  rope_theta=1.0e6, rms_eps=1.0e-6) -> B.VlaBackboneDims:
+                  rope_theta=1.0e6, rms_eps=1.0e-6, weight_dtype="bf16") -> B.VlaBackboneDims:
+    wd = {"bf16": B.VLA_BF16, "fp8_e4m3": B.VLA_FP8_E4M3}[weight_dtype] if isinstance(weight_dtype, str) \
+        else int(weight_dtype)
     return B.VlaBackboneDims(n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate, prefix_len, batch,
-                             rope_theta, rms_eps)
+                             rope_theta, rms_eps, wd)
 
 
 def backbone_dims_from_config(cfg, batch: Optional[int] = None, prefix_len: Optional[int] = None):
     return backbone_dims(cfg.n_layers, cfg.hidden, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.intermediate,
                          cfg.prefix_len if prefix_len is None else prefix_len,
-                         cfg.batch if batch is None else batch, cfg.rope_theta, cfg.rms_eps)
+                         cfg.batch if batch is None else batch, cfg.rope_theta, cfg.rms_eps, cfg.weight_dtype)
 
 
 class Prefill:
@@ -48,6 +50,9 @@ class Prefill:
         w.norm2 = arr("n2")
         for name in LINEARS:
             setattr(w, name, arr(name))
+            sname = "s" + name[1]
+            if sname in raw:                   # E4M3 row scales
+                setattr(w, sname, arr(sname))
         torch.cuda.synchronize()
         self.ctx = B.vla_prefill_create(w, dims)
         del keep
