@@ -236,14 +236,17 @@ def prefill_work(bcfg):
     qd, kvd = bcfg.n_q_heads * bcfg.head_dim, bcfg.n_kv_heads * bcfg.head_dim
     per_layer = H * (qd + 2 * kvd) + H * qd + 2 * H * I + H * I
     params = per_layer * (L - 1) + H * (qd + 2 * kvd)
+    rows = (qd + 2 * kvd + H + 2 * I + H) * (L - 1) + qd + 2 * kvd   # output rows (E4M3 scales)
     M = B * P
     attn = (L - 1) * B * bcfg.n_q_heads * 2 * P * (P + 1) * bcfg.head_dim  # causal: P(P+1)/2 pairs, 2 products
-    return 2 * params + 2 * L * H * 4, 2 * M * params + attn
+    wbytes = params * (1 if bcfg.weight_dtype == "fp8_e4m3" else 2) + (rows * 4 if bcfg.weight_dtype == "fp8_e4m3" else 0)
+    return wbytes + 2 * L * H * 4, 2 * M * params + attn
 
 
 def gpu_backbone_weights(bcfg, seed=0):
     """Random-init backbone weights drawn on the GPU (the values do not change
-    the timing): N(0, std^2) linears in bf16, 1 + N(0, 0.1^2) norm weights."""
+    the timing): N(0, std^2) linears in bf16 (or per-row E4M3 codes with
+    max|row| / 448 scales), 1 + N(0, 0.1^2) norm weights."""
     import torch
     g = torch.Generator(device="cuda").manual_seed(seed)
     H, I = bcfg.hidden, bcfg.intermediate
@@ -256,15 +259,20 @@ def gpu_backbone_weights(bcfg, seed=0):
             W[n].append(1.0 + 0.1 * torch.randn(H, device="cuda", generator=g))
         for n, shp in shapes.items():
             w = bcfg.weight_std * torch.randn(shp, device="cuda", generator=g)
-            W[n].append(w.to(torch.bfloat16).view(torch.int16))
+            if bcfg.weight_dtype == "fp8_e4m3":
+                sc = (w.abs().amax(dim=1) / 448.0).clamp_min(1e-30)
+                W[n].append((w / sc[:, None]).to(torch.float8_e4m3fn).view(torch.uint8))
+                W.setdefault("s" + n[1], []).append(sc.float().contiguous())
+            else:
+                W[n].append(w.to(torch.bfloat16).view(torch.int16))
     return W
 
 
-def bench_prefill(batches, warmup, steps):
+def bench_prefill(batches, warmup, steps, weight_dtype="bf16"):
     import torch
     import synth
     from vla_flow_matching_denoise_amd.prefill import Prefill, backbone_dims_from_config
-    base = synth.backbone(2)
+    base = synth.backbone(2).replace(weight_dtype=weight_dtype)
     W = gpu_backbone_weights(base)
     out = {}
     for b in batches:
@@ -282,11 +290,12 @@ def bench_prefill(batches, warmup, steps):
         t = (time.perf_counter() - t0) / steps
         pf.close()
         wbytes, flops = prefill_work(bcfg)
+        peak = FP8_PEAK_TFLOPS if weight_dtype == "fp8_e4m3" else BF16_PEAK_TFLOPS
         out[f"b{b}"] = {"ms_per_call": round(t * 1e3, 4), "tokens_per_s": round(b * bcfg.prefix_len / t, 1),
                         "weights_GBps": round(wbytes / t / 1e9, 1),
                         "weights_hbm_frac": round(wbytes / t / 1e9 / HBM_PEAK_GBS, 4),
                         "TFLOPs": round(flops / t / 1e12, 1),
-                        "mfma_frac": round(flops / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+                        "mfma_frac": round(flops / t / 1e12 / peak, 4)}
     del W
     return out
 
@@ -364,7 +373,8 @@ def main():
     from vla_flow_matching_denoise_amd.expert import Expert, dims_from_config
     torch.cuda.set_device(0)
     if args.prefill_only:
-        print(json.dumps({"prefill": bench_prefill((1, 16), args.warmup, args.steps)}), flush=True)
+        print(json.dumps({"prefill": bench_prefill((1, 16), args.warmup, args.steps),
+                          "prefill_e4m3": bench_prefill((1, 16), args.warmup, args.steps, "fp8_e4m3")}), flush=True)
         return
 
     cfg = synth.config(2)
@@ -480,6 +490,9 @@ def main():
             "unit": "prefix tokens/s", "dtype": "bf16",
             "data": "synthetic (N(0,0.02^2) bf16 weights drawn on the GPU, N(0,1) embeddings)",
             **bench_prefill((1, 16), 3, max(5, args.steps // 3)),
+            # the pages' prefix runs FP8: E4M3 weights and per-token E4M3 inputs
+            # (mfma_frac against the 5 PFLOP/s FP8 peak)
+            "e4m3": bench_prefill((1, 16), 3, max(5, args.steps // 3), "fp8_e4m3"),
         }
 
     if not args.no_cpu_baseline:
