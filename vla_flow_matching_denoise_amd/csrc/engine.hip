@@ -612,7 +612,8 @@ int enqueue_prefix_repack(vla_ctx* c, const uint16_t* pk, const uint16_t* pv) {
 
 // Prefetch plan for up to two skinny GEMMs (see L2Prefetch): only GEMMs run by
 // the weight-streaming kernel whose grid width is a multiple of 8 (so XCD x
-// reads the tiles nt % 8 == x) and whose weights are bf16 or E4M3.
+// reads the tiles nt % 8 == x); an MXFP4 GEMM takes two targets, its codes
+// and its block scales (both laid out per 16-column tile).
 L2Prefetch make_prefetch(vla_ctx* c, const Linear* a, const Linear* b) {
     L2Prefetch pf{};
     pf.sink = c->pf_sink;
@@ -620,11 +621,22 @@ L2Prefetch make_prefetch(vla_ctx* c, const Linear* a, const Linear* b) {
     const Linear* ls[2] = {a, b};
     int k = 0;
     for (const Linear* ln : ls) {
-        if (!ln || !ln->cfg.skinny || ln->cfg.gx % 8 != 0 || ln->fmt == 2) continue;
-        pf.w[k] = (const uint8_t*)ln->w;
-        pf.tile_bytes[k] = (ln->K / 32) * (c->w8 ? 512 : 1024);
-        pf.n_tiles[k] = ln->N / 16;
-        ++k;
+        if (!ln || !ln->cfg.skinny || ln->cfg.gx % 8 != 0) continue;
+        const int Kf = ln->K / 32;
+        if (ln->fmt == 2) {
+            if (k + 2 > PF_MAX) continue;
+            pf.w[k] = (const uint8_t*)ln->w;
+            pf.tile_bytes[k] = Kf * 256;
+            pf.n_tiles[k++] = ln->N / 16;
+            pf.w[k] = ln->bscale;
+            pf.tile_bytes[k] = Kf * 16;
+            pf.n_tiles[k++] = ln->N / 16;
+        } else {
+            if (k + 1 > PF_MAX) continue;
+            pf.w[k] = (const uint8_t*)ln->w;
+            pf.tile_bytes[k] = Kf * (c->w8 ? 512 : 1024);
+            pf.n_tiles[k++] = ln->N / 16;
+        }
     }
     return pf;
 }

@@ -16,19 +16,20 @@
 // XCD, so the GEMM starts with its weights in L2 (a probe: a 16.8 MB gate_up
 // 9.6 -> 8.4 us; the same prefetch on the wrong XCDs gains nothing).
 // ---------------------------------------------------------------------------
+constexpr int PF_MAX = 3;
 struct L2Prefetch {
-    const uint8_t* w[2];  // packed weights of up to two GEMMs (null: none)
-    int tile_bytes[2];    // bytes of one 16-column tile over all of K
-    int n_tiles[2];
-    uint32_t* sink;       // 16 bytes no realistic load result is written to
+    const uint8_t* w[PF_MAX];  // packed weights (or MXFP4 block scales) per 16-column tile (null: none)
+    int tile_bytes[PF_MAX];    // bytes of one 16-column tile over all of K
+    int n_tiles[PF_MAX];
+    uint32_t* sink;            // 16 bytes no realistic load result is written to
 };
 
 // Prefetcher `rank` of the `per_xcd` prefetching workgroups on XCD `xcd`
-// (nthreads threads each) loads its share of the XCD's tiles of both GEMMs.
+// (nthreads threads each) loads its share of the XCD's tiles of each target.
 VLA_DEV void l2_prefetch(const L2Prefetch& pf, int xcd, int rank, int per_xcd, int nthreads, int tid) {
     u32x4 acc = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
+    for (int g = 0; g < PF_MAX; ++g) {
         if (!pf.w[g] || rank >= per_xcd) continue;
         const int ppt = pf.tile_bytes[g] / 16;  // 16-byte pieces per tile
         const int ntx = (pf.n_tiles[g] - xcd + 7) / 8;
