@@ -241,3 +241,44 @@ def test_prefill_e4m3_lingbot_36_layers():
     del raw
     bk, bv = oracle_prefill(bcfg, synth.make_backbone_weights(bcfg, seed=0, weight_dtype="bf16"), emb)
     _check_e4m3("LingBot 36L", k, v, sk, sv, bk, bv, sharp_layers=2)
+
+
+def test_padded_prefix_prefill_then_varlen_denoise():
+    """A prefix padded at its end (request 1: 20 real tokens of 32) through the
+    GPU prefill and vla_denoise_varlen equals the oracle's chain on the
+    truncated prefix: causal attention makes the first 20 tokens' caches
+    exact, and the loop ignores the rest (readings R19 and R24)."""
+    import torch
+    from vla_flow_matching_denoise_amd.expert import Expert, dims_from_config, to_device
+    from vla_flow_matching_denoise_amd.prefill import Prefill, backbone_dims_from_config
+    cfg = synth.config(1).replace(batch=2)
+    bcfg = synth.backbone(1).replace(batch=2)
+    valid = [32, 20]
+    raw_b = synth.make_backbone_weights(bcfg, seed=21)
+    emb = synth.make_embeddings(bcfg, seed=22)
+    raw_e = synth.make_weights(cfg, seed=23)
+    x0 = synth.make_noise(cfg, seed=24)
+    ts = synth.make_schedule(cfg.n_steps, cfg.batch)
+    pf = Prefill(raw_b, backbone_dims_from_config(bcfg))
+    ex = Expert(raw_e, dims_from_config(cfg))
+    try:
+        k, v = pf(to_device(emb))
+        pvalid = torch.tensor(valid, dtype=torch.int32, device="cuda")
+        out = ex.denoise(k, v, to_device(x0), to_device(ts), cfg.n_steps, prefix_valid=pvalid)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+    finally:
+        ex.close()
+        pf.close()
+    We = oracle.decode_weights(raw_e)
+    for b, n in enumerate(valid):
+        bc = bcfg.replace(batch=1, prefix_len=n)
+        rk, rv = oracle_prefill(bc, raw_b, emb[b:b + 1, :n])
+        rk = oracle.decode_bf16(synth.to_bf16_bits(rk.astype(np.float32)))
+        rv = oracle.decode_bf16(synth.to_bf16_bits(rv.astype(np.float32)))
+        ref = oracle.denoise(We, oracle.ExpertDims.from_config(cfg.replace(batch=1, prefix_len=n)), rk, rv,
+                             x0[b:b + 1], ts[b:b + 1])
+        cos = oracle.cosine(got[b:b + 1], ref)
+        mx = float(np.max(np.abs(got[b:b + 1] - ref)) / np.sqrt(np.mean(ref ** 2)))
+        say(f"[padded prefill -> varlen denoise] request {b} ({n} tokens): cosine {cos:.7f}, max-abs/RMS {mx:.2e}")
+        assert cos >= BF16_COS and mx <= BF16_MAXABS, (b, cos, mx)
