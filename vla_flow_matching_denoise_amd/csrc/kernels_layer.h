@@ -1183,8 +1183,17 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
 // than ATT_SLACK (log2 units), so most blocks skip the rescale of the
 // accumulators and its exponentials; the unnormalised weights stay below
 // 2^ATT_SLACK, well inside bf16 and fp32 range.
-// LDS: K rows padded by 16 bytes so the 16 lanes that read one fragment hit
-// distinct banks; V kept in PV-operand order.
+// The scores are computed transposed (K as the MFMA's A operand, Q as B), so
+// lane l holds, for the query l % 16 of each of its tiles, the scores of the
+// keys 8 (l / 16) + j, j = 0..7, of a block: the K fragment of sub-block sb
+// takes key rows 8 ((l % 16) / 4) + 4 sb + l % 4. Those eight exponentials
+// are then directly the A operand of the PV MFMA (no trip through LDS), the
+// row sum stays a per-lane partial until the end, and the row maximum needs
+// the other three lanes of the query only when some lane's block maximum
+// exceeds the running maximum by ATT_SLACK.
+// LDS: K rows unpadded with the 16-byte chunk c of key row w at
+// c ^ h(w) (h spreads the 16 rows a fragment reads over 16 bank groups);
+// V kept in PV-operand order.
 // CAUSAL (prefix self-attention, keys = the T tokens themselves, P = 0):
 // query token i sees keys 0..i. The workgroup stops after the block holding
 // its last row's token, and only blocks that reach past the smallest token of
@@ -1192,16 +1201,23 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
 // ---------------------------------------------------------------------------
 constexpr float ATT_SLACK = 8.0f;
 
+// chunk swizzle of key row w (within a 32-key block) for rows of DH values
+template <int DH>
+VLA_DEV int kswz(int w) {
+    if constexpr (DH == 128) return (((w >> 3) & 3) << 2) | (w & 3);
+    else return (((w >> 3) & 3) << 1) | ((w >> 1) & 1);
+}
+
 template <int DH, int RT, bool CAUSAL = false>
 __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
-    constexpr int KROW = DH * 2 + 16;            // padded K row in LDS, bytes
-    constexpr int KCH = DH * 2 / 16;             // 16-byte chunks per key row
-    constexpr int BLK = 32 * DH * 2;             // one 32-key block of K (or V), bytes
+    constexpr int RB = DH * 2;                   // bytes of one key row
+    constexpr int KCH = RB / 16;                 // 16-byte chunks per key row
+    constexpr int BLK = 32 * RB;                 // one 32-key block of K (or V), bytes
     constexpr int CH = BLK / 16 / 256;           // chunks of a block per thread
     static_assert(CH >= 1, "head too small");
-    __shared__ __attribute__((aligned(16))) uint8_t Ks[2][32 * KROW];
+    static_assert(DH == 64 || DH == 128, "head_dim 64 or 128");
+    __shared__ __attribute__((aligned(16))) uint8_t Ks[2][BLK];
     __shared__ __attribute__((aligned(16))) uint8_t Vs[2][BLK];
-    __shared__ __attribute__((aligned(16))) uint16_t Ps[4][RT * 16][40];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int G = p.nq / p.kv.nkv;
@@ -1209,10 +1225,10 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
     const int g = blockIdx.y, b = blockIdx.z;
     const int r0 = blockIdx.x * 64 * RT + wave * 16 * RT;
     int nblk = p.kv.S_pad / 32;
-    // causal: token of each of this lane's rows, the smallest token of the
-    // wave's rows (0 when they span two heads), and the last block any row of
-    // the workgroup needs (rows are head-major: row = head_in_group * T + token)
-    int tok[RT][4], tmin = 0;
+    // causal: token of this lane's query in each tile, the smallest token of
+    // the wave's rows (0 when they span two heads), and the last block any row
+    // of the workgroup needs (rows are head-major: row = head_in_group * T + token)
+    int tok[RT], tmin = 0;
     if constexpr (CAUSAL) {
         const int R0 = blockIdx.x * 64 * RT, R1 = min(R0 + 64 * RT, rows_total) - 1;
         const int tmax = R0 / p.T == R1 / p.T ? R1 % p.T : p.T - 1;
@@ -1220,9 +1236,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
         const int w1 = min(r0 + 16 * RT, rows_total) - 1;
         tmin = r0 <= w1 && r0 / p.T == w1 / p.T ? r0 % p.T : 0;
 #pragma unroll
-        for (int t = 0; t < RT; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) tok[t][r] = (r0 + t * 16 + 4 * (lane >> 4) + r) % p.T;
+        for (int t = 0; t < RT; ++t) tok[t] = (r0 + t * 16 + (lane & 15)) % p.T;
     }
     const size_t base = p.kv.base(b, p.layer, g);
     const uint8_t* K = (const uint8_t*)(p.kcat + base);
@@ -1244,15 +1258,17 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
         }
     }
 
-    float mrow[RT][4], lrow[RT][4];
+    // per lane: the running maximum and the partial sum (over this lane's
+    // keys) of its query in each tile; oacc rows are the queries 4 (l / 16) + r
+    float mrow[RT], lrow[RT];
     f32x4 oacc[RT][DH / 16];
     // running max starts finite: a block whose keys are all masked (padding)
     // then leaves m finite and adds weight 0, where -inf would give
     // exp2(-inf - -inf) = NaN
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) { mrow[t][r] = -1e30f; lrow[t][r] = 0.f; }
+        mrow[t] = -1e30f;
+        lrow[t] = 0.f;
 #pragma unroll
         for (int dn = 0; dn < DH / 16; ++dn) oacc[t][dn] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
@@ -1269,11 +1285,14 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
     auto sstore = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            const int c = tid + i * 256;
-            *(u32x4*)(&Ks[buf][(c / KCH) * KROW + (c % KCH) * 16]) = rk[i];
+            const int c = tid + i * 256, w = c / KCH;
+            *(u32x4*)(&Ks[buf][w * RB + (((c % KCH) ^ kswz<DH>(w)) << 4)]) = rk[i];
             *(u32x4*)(&Vs[buf][c * 16]) = rv[i];
         }
     };
+    // this lane's K fragment rows (sub-block sb adds 4) and chunk swizzle
+    const int krow = 8 * ((lane & 15) >> 2) + (lane & 3);
+    const int ksw = kswz<DH>(krow);
 
     gload(0);
     sstore(0);
@@ -1281,6 +1300,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
     for (int kb = 0; kb < nblk; ++kb) {
         const int buf = kb & 1;
         if (kb + 1 < nblk) gload(kb + 1);   // next block in flight during this one
+        // s[t][sb][r]: query (tile t, lane & 15) against key 8 (lane / 16) + 4 sb + r
         f32x4 s[RT][2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
@@ -1288,81 +1308,89 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
             for (int t = 0; t < RT; ++t) s[t][sb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < DH / 32; ++ks) {
-                const bf16x8 kf =
-                    *(const bf16x8*)(&Ks[buf][(sb * 16 + (lane & 15)) * KROW + ks * 64 + 16 * (lane >> 4)]);
+                const bf16x8 kf = *(const bf16x8*)(&Ks[buf][(krow + 4 * sb) * RB +
+                                                            (((ks * 4 + (lane >> 4)) ^ ksw) << 4)]);
 #pragma unroll
-                for (int t = 0; t < RT; ++t) s[t][sb] = mfma_16x16x32(qf[t][ks], kf, s[t][sb]);
+                for (int t = 0; t < RT; ++t) s[t][sb] = mfma_16x16x32(kf, qf[t][ks], s[t][sb]);
             }
         }
         // every key of the block real (a uniform test): no per-key mask
         bool whole = (kb * 32 + 32 <= pvb) || (kb * 32 >= p.P && kb * 32 + 32 <= p.S);
         if constexpr (CAUSAL) whole = whole && kb * 32 + 31 <= tmin;
-        float s0[RT][4], s1[RT][4], mx[RT][4];
+        float v[RT][8], lmax[RT];
         bool grow = false;
 #pragma unroll
-        for (int t = 0; t < RT; ++t)
+        for (int t = 0; t < RT; ++t) {
+            lmax[t] = -INFINITY;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                s0[t][r] = s[t][0][r] * p.scale_log2;
-                s1[t][r] = s[t][1][r] * p.scale_log2;
+            for (int j = 0; j < 8; ++j) {
+                v[t][j] = s[t][j >> 2][j & 3] * p.scale_log2;
                 if (!whole) {  // a block with padded prefix keys or keys past P + T
-                    const int key0 = kb * 32 + (lane & 15), key1 = key0 + 16;
-                    if (key0 >= p.S || (key0 < p.P && key0 >= pvb)) s0[t][r] = -INFINITY;
-                    if (key1 >= p.S || (key1 < p.P && key1 >= pvb)) s1[t][r] = -INFINITY;
+                    const int key = kb * 32 + 8 * (lane >> 4) + j;
+                    if (key >= p.S || (key < p.P && key >= pvb)) v[t][j] = -INFINITY;
                     if constexpr (CAUSAL) {
-                        if (key0 > tok[t][r]) s0[t][r] = -INFINITY;
-                        if (key1 > tok[t][r]) s1[t][r] = -INFINITY;
+                        if (key > tok[t]) v[t][j] = -INFINITY;
                     }
                 }
-                mx[t][r] = group16_max(fmaxf(s0[t][r], s1[t][r]));
-                grow |= mx[t][r] > mrow[t][r] + ATT_SLACK;
+                lmax[t] = fmaxf(lmax[t], v[t][j]);
             }
+            grow |= lmax[t] > mrow[t] + ATT_SLACK;
+        }
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {  // uniform: move the maxima, rescale
 #pragma unroll
-            for (int t = 0; t < RT; ++t)
+            for (int t = 0; t < RT; ++t) {
+                // the query's block maximum over its four lanes (l, l ^ 16, l ^ 32, l ^ 48)
+                float bm = fmaxf(lmax[t], __shfl_xor(lmax[t], 16, 64));
+                bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+                const float mnew = fmaxf(mrow[t], bm);
+                const float alpha = attn_exp2(mrow[t] - mnew);
+                lrow[t] *= alpha;
+                mrow[t] = mnew;
+                // oacc row r is the query 4 (l / 16) + r: its factor from that query's lane
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float mnew = fmaxf(mrow[t][r], mx[t][r]);
-                    const float alpha = attn_exp2(mrow[t][r] - mnew);
-                    lrow[t][r] *= alpha;
-                    mrow[t][r] = mnew;
+                    const float ar = __shfl(alpha, 4 * (lane >> 4) + r, 64);
 #pragma unroll
-                    for (int dn = 0; dn < DH / 16; ++dn) oacc[t][dn][r] *= alpha;
+                    for (int dn = 0; dn < DH / 16; ++dn) oacc[t][dn][r] *= ar;
                 }
-        }
-#pragma unroll
-        for (int t = 0; t < RT; ++t)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float p0 = attn_exp2(s0[t][r] - mrow[t][r]), p1 = attn_exp2(s1[t][r] - mrow[t][r]);
-                lrow[t][r] += group16_sum(p0 + p1);
-                Ps[wave][t * 16 + 4 * (lane >> 4) + r][lane & 15] = f32_to_bf16(p0);
-                Ps[wave][t * 16 + 4 * (lane >> 4) + r][16 + (lane & 15)] = f32_to_bf16(p1);
             }
-        // the P tiles are private to this wave: LDS ops of one wave complete in order
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
+        }
+        // the eight weights of lane l are the PV A operand: query l % 16, keys
+        // 8 (l / 16) + j, which is the row order of V's PV fragments
         bf16x8 pa[RT];
 #pragma unroll
-        for (int t = 0; t < RT; ++t) pa[t] = *(const bf16x8*)(&Ps[wave][t * 16 + (lane & 15)][8 * (lane >> 4)]);
+        for (int t = 0; t < RT; ++t) {
+            float e[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                e[j] = attn_exp2(v[t][j] - mrow[t]);
+                lrow[t] += e[j];
+            }
+            u32x4 w;
+#pragma unroll
+            for (int q2 = 0; q2 < 4; ++q2) w[q2] = pack_bf16x2(e[2 * q2], e[2 * q2 + 1]);
+            pa[t] = __builtin_bit_cast(bf16x8, w);
+        }
 #pragma unroll
         for (int dn = 0; dn < DH / 16; ++dn) {
             const bf16x8 vf = *(const bf16x8*)(&Vs[buf][(dn * 64 + lane) * 16]);
 #pragma unroll
             for (int t = 0; t < RT; ++t) oacc[t][dn] = mfma_16x16x32(pa[t], vf, oacc[t][dn]);
         }
-        __builtin_amdgcn_wave_barrier();
         if (kb + 1 < nblk) sstore(buf ^ 1);  // that buffer was last read before the previous barrier
         __syncthreads();
     }
 
 #pragma unroll
-    for (int t = 0; t < RT; ++t)
+    for (int t = 0; t < RT; ++t) {
+        // the query's total weight over its four lanes
+        float lt = lrow[t] + __shfl_xor(lrow[t], 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = r0 + t * 16 + 4 * (lane >> 4) + r;
+            const float inv = 1.0f / __shfl(lt, 4 * (lane >> 4) + r, 64);
             if (row < rows_total) {
-                const float inv = 1.0f / lrow[t][r];
                 const int hh = row / p.T, i = row % p.T;
 #pragma unroll
                 for (int dn = 0; dn < DH / 16; ++dn)
@@ -1370,4 +1398,5 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
                         f32_to_bf16(oacc[t][dn][r] * inv);
             }
         }
+    }
 }
