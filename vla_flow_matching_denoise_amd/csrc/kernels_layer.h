@@ -1017,9 +1017,13 @@ struct AttnParams {
     L2Prefetch pf;
 };
 
+// The running maximum of a query moves only when a block's maximum exceeds it
+// by more than ATT_SLACK (log2 units), so most blocks skip the rescale; the
+// unnormalised weights stay below 2^ATT_SLACK, well inside bf16 and fp32.
+constexpr float ATT_SLACK = 8.0f;
+
 template <int DH, int AT_WAVES>
 __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t Ps[AT_WAVES][16][40];
     __shared__ __attribute__((aligned(16))) float Om[AT_WAVES][64][DH / 16 * 4 + 8];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1052,15 +1056,15 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
                                       : (bf16x8){};
     }
 
-    float mrow[4], lrow[4];
+    // scores transposed as in attn_rows_kernel: lane l holds, for its query
+    // l % 16, keys 8 (l / 16) + j of a block; mrow / lrow are that query's
+    // running maximum and this lane's partial sum; oacc rows are the queries
+    // 4 (l / 16) + r
+    float mrow = -1e30f, lrow = 0.f;  // finite start: an all-masked block adds weight 0, never NaN
     f32x4 oacc[DH / 16];
 #pragma unroll
-    // running max starts finite: a block whose keys are all masked (padding)
-    // then leaves m finite and adds weight 0, where -inf would give
-    // exp2(-inf - -inf) = NaN
-    for (int r = 0; r < 4; ++r) { mrow[r] = -1e30f; lrow[r] = 0.f; }
-#pragma unroll
     for (int dn = 0; dn < DH / 16; ++dn) oacc[dn] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    const int krow = 8 * ((lane & 15) >> 2) + (lane & 3);  // K fragment row of sub-block 0 (+4 for 1)
 
     bf16x8 kf[2][DH / 32], vf[DH / 16], kf_n[2][DH / 32], vf_n[DH / 16];
     auto load_kv = [&](int kb, bf16x8 (*kd)[DH / 32], bf16x8* vd) {
@@ -1068,7 +1072,7 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
             for (int ks = 0; ks < DH / 32; ++ks)
-                kd[sb][ks] = *(const bf16x8*)(K + (size_t)(kb * 32 + sb * 16 + (lane & 15)) * DH + ks * 32 +
+                kd[sb][ks] = *(const bf16x8*)(K + (size_t)(kb * 32 + krow + 4 * sb) * DH + ks * 32 +
                                               8 * (lane >> 4));
 #pragma unroll
         for (int dn = 0; dn < DH / 16; ++dn)
@@ -1077,44 +1081,52 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
     if (wave < nblk) load_kv(wave, kf, vf);
     for (int kb = wave; kb < nblk; kb += AT_WAVES) {
         if (kb + AT_WAVES < nblk) load_kv(kb + AT_WAVES, kf_n, vf_n);   // next block of this wave, in flight
+        // s[sb][r]: query lane & 15 against key 8 (lane / 16) + 4 sb + r
         f32x4 s[2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             s[sb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < DH / 32; ++ks) s[sb] = mfma_16x16x32(qf[ks], kf[sb][ks], s[sb]);
+            for (int ks = 0; ks < DH / 32; ++ks) s[sb] = mfma_16x16x32(kf[sb][ks], qf[ks], s[sb]);
         }
         // every key of the block real (a uniform test): no per-key mask
         const bool whole = (kb * 32 + 32 <= pvb) || (kb * 32 >= p.P && kb * 32 + 32 <= p.S);
-        float alpha[4];
+        float v[8], lmax = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float s0 = s[0][r] * p.scale_log2, s1 = s[1][r] * p.scale_log2;
+        for (int j = 0; j < 8; ++j) {
+            v[j] = s[j >> 2][j & 3] * p.scale_log2;
             if (!whole) {  // a block with padded prefix keys or keys past P + T
-                const int key0 = kb * 32 + (lane & 15), key1 = key0 + 16;
-                if (key0 >= p.S || (key0 < p.P && key0 >= pvb)) s0 = -INFINITY;
-                if (key1 >= p.S || (key1 < p.P && key1 >= pvb)) s1 = -INFINITY;
+                const int key = kb * 32 + 8 * (lane >> 4) + j;
+                if (key >= p.S || (key < p.P && key >= pvb)) v[j] = -INFINITY;
             }
-            const float mx = group16_max(fmaxf(s0, s1));
-            const float mnew = fmaxf(mrow[r], mx);
-            alpha[r] = attn_exp2(mrow[r] - mnew);
-            const float p0 = attn_exp2(s0 - mnew), p1 = attn_exp2(s1 - mnew);
-            lrow[r] = lrow[r] * alpha[r] + group16_sum(p0 + p1);
-            mrow[r] = mnew;
-            Ps[wave][4 * (lane >> 4) + r][lane & 15] = f32_to_bf16(p0);
-            Ps[wave][4 * (lane >> 4) + r][16 + (lane & 15)] = f32_to_bf16(p1);
+            lmax = fmaxf(lmax, v[j]);
         }
+        if (__builtin_amdgcn_ballot_w64(lmax > mrow + ATT_SLACK) != 0) {  // uniform: move the maxima, rescale
+            float bm = fmaxf(lmax, __shfl_xor(lmax, 16, 64));  // over the query's four lanes
+            bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
+            const float mnew = fmaxf(mrow, bm);
+            const float alpha = attn_exp2(mrow - mnew);
+            lrow *= alpha;
+            mrow = mnew;
 #pragma unroll
-        for (int dn = 0; dn < DH / 16; ++dn)
+            for (int r = 0; r < 4; ++r) {  // oacc row r is the query 4 (l / 16) + r
+                const float ar = __shfl(alpha, 4 * (lane >> 4) + r, 64);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) oacc[dn][r] *= alpha[r];
-        // the P tile is private to this wave: LDS ops of one wave complete in order
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
-        const bf16x8 pa = *(const bf16x8*)(&Ps[wave][lane & 15][8 * (lane >> 4)]);
+                for (int dn = 0; dn < DH / 16; ++dn) oacc[dn][r] *= ar;
+            }
+        }
+        float e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            e[j] = attn_exp2(v[j] - mrow);
+            lrow += e[j];
+        }
+        u32x4 pw;
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) pw[q2] = pack_bf16x2(e[2 * q2], e[2 * q2 + 1]);
+        const bf16x8 pa = __builtin_bit_cast(bf16x8, pw);  // the PV A operand: keys 8 (l / 16) + j
 #pragma unroll
         for (int dn = 0; dn < DH / 16; ++dn) oacc[dn] = mfma_16x16x32(pa, vf[dn], oacc[dn]);
-        __builtin_amdgcn_wave_barrier();
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
@@ -1123,11 +1135,22 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
         for (int dn = 0; dn < DH / 16; ++dn) vf[dn] = vf_n[dn];
     }
 
-    // merge the four waves' partial results
+    // merge the waves' partial results: each lane takes the maximum and the
+    // total weight (over the query's four lanes) of its oacc rows 4 (l / 16) + r
+    {
+        float lt = lrow + __shfl_xor(lrow, 16, 64);
+        lt += __shfl_xor(lt, 32, 64);
+        f32x4 m4, l4;
 #pragma unroll
-    for (int dn = 0; dn < DH / 16; ++dn) *(f32x4*)(&Om[wave][lane][dn * 4]) = oacc[dn];
-    *(f32x4*)(&Om[wave][lane][DH / 16 * 4]) = (f32x4){mrow[0], mrow[1], mrow[2], mrow[3]};
-    *(f32x4*)(&Om[wave][lane][DH / 16 * 4 + 4]) = (f32x4){lrow[0], lrow[1], lrow[2], lrow[3]};
+        for (int r = 0; r < 4; ++r) {
+            m4[r] = __shfl(mrow, 4 * (lane >> 4) + r, 64);
+            l4[r] = __shfl(lt, 4 * (lane >> 4) + r, 64);
+        }
+#pragma unroll
+        for (int dn = 0; dn < DH / 16; ++dn) *(f32x4*)(&Om[wave][lane][dn * 4]) = oacc[dn];
+        *(f32x4*)(&Om[wave][lane][DH / 16 * 4]) = m4;
+        *(f32x4*)(&Om[wave][lane][DH / 16 * 4 + 4]) = l4;
+    }
     __syncthreads();
     // wave w finishes d-column tiles dn = w, w + AT_WAVES, ...
     float mw[AT_WAVES][4], lw[AT_WAVES][4];
@@ -1199,7 +1222,6 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
 // its last row's token, and only blocks that reach past the smallest token of
 // a wave's rows are masked per key.
 // ---------------------------------------------------------------------------
-constexpr float ATT_SLACK = 8.0f;
 
 // chunk swizzle of key row w (within a 32-key block) for rows of DH values
 template <int DH>
