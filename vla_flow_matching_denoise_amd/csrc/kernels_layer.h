@@ -174,18 +174,32 @@ __global__ __launch_bounds__(256) void resnorm_kernel(float* __restrict__ h, con
 // Per-layer K/V of the attention, [prefix ; chunk] concatenated on the key
 // axis and padded to a multiple of 32 keys (S_pad), per (request, layer, KV
 // head):
-//   kcat [B][L][n_kv][S_pad][d_h]  row-major (the QK^T B operand reads
-//                                  16 bytes of one key row per lane)
+//   kcat [B][L][n_kv][S_pad/32][d_h/16][64][8]  the K operand of the
+//                                  transposed scores S^T = K Q^T: lane l of
+//                                  fragment f = sb * (d_h/32) + ks of block kb
+//                                  holds key kb*32 + 8*((l%16)/4) + 4*sb + l%4
+//                                  at d = ks*32 + 8*(l/16) + j (kfrag_off), so
+//                                  every fragment is one contiguous 1 KiB
 //   vcat [B][L][n_kv][S_pad/32][d_h/16][64][8]  the PV B operand: lane l of
 //                                  fragment (kb, dn) holds keys
 //                                  kb*32 + 8*(l/16) + j at d = dn*16 + l%16
 // The prefix part is copied in once per call; the chunk part is written by
 // the QKV epilogue of each layer.
 // ---------------------------------------------------------------------------
+// Element offset, within a 32-key block of K, of key w (0..31) and the 8 head
+// dims 8c .. 8c+7 (kept contiguous), in the fragment order above.
+VLA_DEV int kfrag_off(int w, int c, int dh) {
+    const int sb = (w >> 2) & 1, ks = c >> 2;
+    const int lane = ((c & 3) << 4) | ((w >> 3) << 2) | (w & 3);
+    return ((sb * (dh >> 5) + ks) * 64 + lane) * 8;
+}
+
 struct KVLayout {
     int L, nkv, dh, S_pad;
     VLA_DEV size_t base(int b, int l, int g) const { return (((size_t)b * L + l) * nkv + g) * (size_t)S_pad * dh; }
-    VLA_DEV size_t k_at(int b, int l, int g, int key, int d) const { return base(b, l, g) + (size_t)key * dh + d; }
+    VLA_DEV size_t k_at(int b, int l, int g, int key, int d) const {
+        return base(b, l, g) + (size_t)(key >> 5) * 32 * dh + kfrag_off(key & 31, d >> 3, dh) + (d & 7);
+    }
     VLA_DEV size_t v_at(int b, int l, int g, int key, int d) const {
         const int kb = key >> 5, w = key & 31;
         return base(b, l, g) + (size_t)kb * 32 * dh +
@@ -401,16 +415,23 @@ VLA_DEV void epilogue16(const GemmParams& p, int row, int col0, const float (&v)
             for (int j = 0; j < 8; ++j) { lo[j] = v[2 * j]; hi[j] = v[2 * j + 1]; }
         }
         if (sec < 2) {
-            uint16_t* dst = sec == 0 ? p.q + ((size_t)(b * p.nq + head) * p.T + i) * p.dh
-                                     : p.kcat + p.kv.k_at(b, p.layer, head, p.P + i, 0);
+            uint16_t* dlo;
+            uint16_t* dhi;
+            if (sec == 0) {
+                dlo = p.q + ((size_t)(b * p.nq + head) * p.T + i) * p.dh + m0;
+                dhi = dlo + p.dh / 2;
+            } else {
+                dlo = p.kcat + p.kv.k_at(b, p.layer, head, p.P + i, m0);
+                dhi = p.kcat + p.kv.k_at(b, p.layer, head, p.P + i, m0 + p.dh / 2);
+            }
             u32x4 a, c;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 a[j] = pack_bf16x2(lo[2 * j], lo[2 * j + 1]);
                 c[j] = pack_bf16x2(hi[2 * j], hi[2 * j + 1]);
             }
-            *(u32x4*)(dst + m0) = a;
-            *(u32x4*)(dst + m0 + p.dh / 2) = c;
+            *(u32x4*)dlo = a;
+            *(u32x4*)dhi = c;
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -1024,7 +1045,12 @@ constexpr float ATT_SLACK = 8.0f;
 
 template <int DH, int AT_WAVES>
 __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
-    __shared__ __attribute__((aligned(16))) float Om[AT_WAVES][64][DH / 16 * 4 + 8];
+    // the waves' partial outputs (lane rows padded by 4 floats: a 16-byte read
+    // of 16 consecutive lanes meets 64 distinct banks) and per-query maxima
+    // and total weights
+    __shared__ __attribute__((aligned(16))) float Om[AT_WAVES][64][DH / 16 * 4 + 4];
+    __shared__ __attribute__((aligned(16))) float Ml[AT_WAVES][2][16];
+    __shared__ __attribute__((aligned(16))) uint8_t Qs[16 * DH * 2];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int g = blockIdx.y, b = blockIdx.z;
@@ -1046,15 +1072,17 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
     const uint16_t* V = p.vcat + base;
     const int pvb = p.pvalid[b];  // prefix keys past this are padding
 
-    bf16x8 qf[DH / 32];
-    {
-        const uint16_t* qg = p.q + (size_t)(b * p.nq + g * G) * p.T * DH;
-        const int row = r0 + (lane & 15);
-#pragma unroll
-        for (int ks = 0; ks < DH / 32; ++ks)
-            qf[ks] = row < rows_total ? *(const bf16x8*)(qg + (size_t)row * DH + ks * 32 + 8 * (lane >> 4))
-                                      : (bf16x8){};
-    }
+    // the workgroup's 16 query rows are contiguous in q (rows of a KV group
+    // are head-major, heads consecutive): one 16-byte chunk per thread into
+    // LDS, chunk c of row r at c ^ qswz(r) so the fragment reads below (16
+    // rows, one chunk column) meet distinct banks
+    constexpr int QCH = DH / 8;  // 16-byte chunks per row
+    static_assert(16 * QCH <= AT_WAVES * 64, "one query chunk per thread");
+    auto qswz = [](int r) { return (DH == 128 ? r : r >> 1) & (QCH - 1); };
+    u32x4 qv = (u32x4){0u, 0u, 0u, 0u};
+    const int qr = tid / QCH, qc = tid % QCH;
+    if (tid < 16 * QCH && r0 + qr < rows_total)
+        qv = *(const u32x4*)(p.q + ((size_t)(b * p.nq + g * G) * p.T + r0 + qr) * DH + qc * 8);
 
     // scores transposed as in attn_rows_kernel: lane l holds, for its query
     // l % 16, keys 8 (l / 16) + j of a block; mrow / lrow are that query's
@@ -1064,21 +1092,25 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
     f32x4 oacc[DH / 16];
 #pragma unroll
     for (int dn = 0; dn < DH / 16; ++dn) oacc[dn] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    const int krow = 8 * ((lane & 15) >> 2) + (lane & 3);  // K fragment row of sub-block 0 (+4 for 1)
-
+    // K and V blocks are stored as MFMA fragments: every load is 1 KiB contiguous
     bf16x8 kf[2][DH / 32], vf[DH / 16], kf_n[2][DH / 32], vf_n[DH / 16];
     auto load_kv = [&](int kb, bf16x8 (*kd)[DH / 32], bf16x8* vd) {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
             for (int ks = 0; ks < DH / 32; ++ks)
-                kd[sb][ks] = *(const bf16x8*)(K + (size_t)(kb * 32 + krow + 4 * sb) * DH + ks * 32 +
-                                              8 * (lane >> 4));
+                kd[sb][ks] = *(const bf16x8*)(K + (size_t)kb * 32 * DH + ((size_t)(sb * (DH / 32) + ks) * 64 + lane) * 8);
 #pragma unroll
         for (int dn = 0; dn < DH / 16; ++dn)
             vd[dn] = *(const bf16x8*)(V + (size_t)kb * 32 * DH + ((size_t)dn * 64 + lane) * 8);
     };
     if (wave < nblk) load_kv(wave, kf, vf);
+    if (tid < 16 * QCH) *(u32x4*)(&Qs[qr * DH * 2 + ((qc ^ qswz(qr)) << 4)]) = qv;
+    __syncthreads();
+    bf16x8 qf[DH / 32];
+#pragma unroll
+    for (int ks = 0; ks < DH / 32; ++ks)
+        qf[ks] = *(const bf16x8*)(&Qs[(lane & 15) * DH * 2 + (((ks * 4 + (lane >> 4)) ^ qswz(lane & 15)) << 4)]);
     for (int kb = wave; kb < nblk; kb += AT_WAVES) {
         if (kb + AT_WAVES < nblk) load_kv(kb + AT_WAVES, kf_n, vf_n);   // next block of this wave, in flight
         // s[sb][r]: query lane & 15 against key 8 (lane / 16) + 4 sb + r
@@ -1105,15 +1137,17 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
             float bm = fmaxf(lmax, __shfl_xor(lmax, 16, 64));  // over the query's four lanes
             bm = fmaxf(bm, __shfl_xor(bm, 32, 64));
             const float mnew = fmaxf(mrow, bm);
-            const float alpha = attn_exp2(mrow - mnew);
-            lrow *= alpha;
-            mrow = mnew;
+            if (kb != wave) {  // (the wave's first block: oacc and lrow are still zero)
+                const float alpha = attn_exp2(mrow - mnew);
+                lrow *= alpha;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {  // oacc row r is the query 4 (l / 16) + r
-                const float ar = __shfl(alpha, 4 * (lane >> 4) + r, 64);
+                for (int r = 0; r < 4; ++r) {  // oacc row r is the query 4 (l / 16) + r
+                    const float ar = __shfl(alpha, 4 * (lane >> 4) + r, 64);
 #pragma unroll
-                for (int dn = 0; dn < DH / 16; ++dn) oacc[dn][r] *= ar;
+                    for (int dn = 0; dn < DH / 16; ++dn) oacc[dn][r] *= ar;
+                }
             }
+            mrow = mnew;
         }
         float e[8];
 #pragma unroll
@@ -1135,33 +1169,32 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
         for (int dn = 0; dn < DH / 16; ++dn) vf[dn] = vf_n[dn];
     }
 
-    // merge the waves' partial results: each lane takes the maximum and the
-    // total weight (over the query's four lanes) of its oacc rows 4 (l / 16) + r
+    // merge the waves' partial results: lanes 0..15 publish their query's
+    // maximum and total weight (over the query's four lanes); every lane then
+    // reads those of its oacc rows 4 (l / 16) + r (16-lane broadcasts)
     {
         float lt = lrow + __shfl_xor(lrow, 16, 64);
         lt += __shfl_xor(lt, 32, 64);
-        f32x4 m4, l4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            m4[r] = __shfl(mrow, 4 * (lane >> 4) + r, 64);
-            l4[r] = __shfl(lt, 4 * (lane >> 4) + r, 64);
+        if (lane < 16) {
+            Ml[wave][0][lane] = mrow;
+            Ml[wave][1][lane] = lt;
         }
 #pragma unroll
         for (int dn = 0; dn < DH / 16; ++dn) *(f32x4*)(&Om[wave][lane][dn * 4]) = oacc[dn];
-        *(f32x4*)(&Om[wave][lane][DH / 16 * 4]) = m4;
-        *(f32x4*)(&Om[wave][lane][DH / 16 * 4 + 4]) = l4;
     }
     __syncthreads();
     // wave w finishes d-column tiles dn = w, w + AT_WAVES, ...
     float mw[AT_WAVES][4], lw[AT_WAVES][4];
 #pragma unroll
     for (int w = 0; w < AT_WAVES; ++w) {
-        f32x4 m4 = *(const f32x4*)(&Om[w][lane][DH / 16 * 4]);
-        f32x4 l4 = *(const f32x4*)(&Om[w][lane][DH / 16 * 4 + 4]);
+        const f32x4 m4 = *(const f32x4*)(&Ml[w][0][4 * (lane >> 4)]);
+        const f32x4 l4 = *(const f32x4*)(&Ml[w][1][4 * (lane >> 4)]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) { mw[w][r] = m4[r]; lw[w][r] = l4[r]; }
     }
-    float scale[AT_WAVES][4], inv[4];
+    // per row: the waves' weights exp2(m_w - M) with 1 / L folded in (the
+    // total weight L >= 1: the row's maximum key contributes 1)
+    float scale[AT_WAVES][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         float M = mw[0][r];
@@ -1173,8 +1206,13 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
             scale[w][r] = attn_exp2(mw[w][r] - M);
             L += scale[w][r] * lw[w][r];
         }
-        inv[r] = 1.0f / L;
+        const float inv = __builtin_amdgcn_rcpf(L);
+#pragma unroll
+        for (int w = 0; w < AT_WAVES; ++w) scale[w][r] *= inv;
     }
+    // (head in group, token) of the lane's first row; the next three follow
+    const int row0 = r0 + 4 * (lane >> 4);
+    const int hh0 = row0 / p.T, i0 = row0 - hh0 * p.T;
     for (int dn = wave; dn < DH / 16; dn += AT_WAVES) {
         f32x4 o = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1183,14 +1221,13 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) o[r] += scale[w][r] * t[r];
         }
+        int hh = hh0, i = i0;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int row = r0 + 4 * (lane >> 4) + r;
-            if (row < rows_total) {
-                const int hh = row / p.T, i = row % p.T;
+            if (row0 + r < rows_total)
                 p.o[act_index(b * p.T + i, (g * G + hh) * DH + dn * 16 + (lane & 15), p.nq * DH, p.ofrag)] =
-                    f32_to_bf16(o[r] * inv[r]);
-            }
+                    f32_to_bf16(o[r]);
+            if (++i == p.T) { i = 0; ++hh; }
         }
     }
 }
@@ -1214,27 +1251,17 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
 // row sum stays a per-lane partial until the end, and the row maximum needs
 // the other three lanes of the query only when some lane's block maximum
 // exceeds the running maximum by ATT_SLACK.
-// LDS: K rows unpadded with the 16-byte chunk c of key row w at
-// c ^ h(w) (h spreads the 16 rows a fragment reads over 16 bank groups);
-// V kept in PV-operand order.
+// LDS: K and V blocks copied as they are stored (MFMA fragments, 1 KiB each),
+// so every fragment read is 64 lanes x 16 contiguous bytes.
 // CAUSAL (prefix self-attention, keys = the T tokens themselves, P = 0):
 // query token i sees keys 0..i. The workgroup stops after the block holding
 // its last row's token, and only blocks that reach past the smallest token of
 // a wave's rows are masked per key.
 // ---------------------------------------------------------------------------
 
-// chunk swizzle of key row w (within a 32-key block) for rows of DH values
-template <int DH>
-VLA_DEV int kswz(int w) {
-    if constexpr (DH == 128) return (((w >> 3) & 3) << 2) | (w & 3);
-    else return (((w >> 3) & 3) << 1) | ((w >> 1) & 1);
-}
-
 template <int DH, int RT, bool CAUSAL = false>
 __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
-    constexpr int RB = DH * 2;                   // bytes of one key row
-    constexpr int KCH = RB / 16;                 // 16-byte chunks per key row
-    constexpr int BLK = 32 * RB;                 // one 32-key block of K (or V), bytes
+    constexpr int BLK = 32 * DH * 2;             // one 32-key block of K (or V), bytes
     constexpr int CH = BLK / 16 / 256;           // chunks of a block per thread
     static_assert(CH >= 1, "head too small");
     static_assert(DH == 64 || DH == 128, "head_dim 64 or 128");
@@ -1307,14 +1334,11 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
     auto sstore = [&](int buf) {
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
-            const int c = tid + i * 256, w = c / KCH;
-            *(u32x4*)(&Ks[buf][w * RB + (((c % KCH) ^ kswz<DH>(w)) << 4)]) = rk[i];
+            const int c = tid + i * 256;
+            *(u32x4*)(&Ks[buf][c * 16]) = rk[i];
             *(u32x4*)(&Vs[buf][c * 16]) = rv[i];
         }
     };
-    // this lane's K fragment rows (sub-block sb adds 4) and chunk swizzle
-    const int krow = 8 * ((lane & 15) >> 2) + (lane & 3);
-    const int ksw = kswz<DH>(krow);
 
     gload(0);
     sstore(0);
@@ -1330,8 +1354,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
             for (int t = 0; t < RT; ++t) s[t][sb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < DH / 32; ++ks) {
-                const bf16x8 kf = *(const bf16x8*)(&Ks[buf][(krow + 4 * sb) * RB +
-                                                            (((ks * 4 + (lane >> 4)) ^ ksw) << 4)]);
+                const bf16x8 kf = *(const bf16x8*)(&Ks[buf][((sb * (DH / 32) + ks) * 64 + lane) * 16]);
 #pragma unroll
                 for (int t = 0; t < RT; ++t) s[t][sb] = mfma_16x16x32(kf, qf[t][ks], s[t][sb]);
             }

@@ -276,11 +276,14 @@ VLA_DEV void p_attention(const PersistParams& p, const uint16_t* qg, int r0, con
         const uint16_t* Kb = pre ? Kp + (size_t)kb * 32 * DH : Kc + (size_t)(kb - nbp) * 32 * DH;
         const uint16_t* Vb = pre ? Vp + (size_t)kb * 32 * DH : Vc + (size_t)(kb - nbp) * 32 * DH;
         bf16x8 kf[2][DH / 32], vf[DH / 16];
+        // key sb*16 + l%16, dims ks*32 + 8*(l/16) + j: prefix blocks are in the
+        // K fragment order of the cache, chunk blocks (kc) row-major
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
             for (int ks = 0; ks < DH / 32; ++ks)
-                kf[sb][ks] = *(const bf16x8*)(Kb + (size_t)(sb * 16 + (lane & 15)) * DH + ks * 32 + 8 * (lane >> 4));
+                kf[sb][ks] = *(const bf16x8*)(Kb + (pre ? (size_t)kfrag_off(sb * 16 + (lane & 15), ks * 4 + (lane >> 4), DH)
+                                                        : (size_t)(sb * 16 + (lane & 15)) * DH + ks * 32 + 8 * (lane >> 4)));
 #pragma unroll
         for (int dn = 0; dn < DH / 16; ++dn) vf[dn] = *(const bf16x8*)(Vb + ((size_t)dn * 64 + lane) * 8);
         f32x4 s[2];
