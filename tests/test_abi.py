@@ -121,3 +121,19 @@ def test_prefill_e4m3_needs_multiples_of_128(lib):
     d = backbone_dims(2, 256, 4, 2, 64, 768, 32, 1, weight_dtype=7)
     assert lib.vla_prefill_create(ctypes.byref(w), ctypes.byref(d)) is None
     assert "weight_dtype" in B.vla_last_error()
+
+
+def test_header_constants_match_the_binding():
+    """Every integer constant the headers define has the same value in the binding."""
+    import glob
+    import os
+    import re
+    from vla_flow_matching_denoise_amd import binding as B
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    seen = 0
+    for path in glob.glob(os.path.join(root, "include", "*.h")):
+        for m in re.finditer(r"#define\s+(VLA_\w+)\s+\(?(-?\d+)\)?", open(path).read()):
+            name, value = m.group(1), int(m.group(2))
+            assert getattr(B, name, None) == value, (path, name, value)
+            seen += 1
+    assert seen >= 10
