@@ -306,9 +306,11 @@ VLA_DEV int qkv_row_pos(const GemmParams& p, int row) {
     return p.pvalid[b] + row - b * p.T;
 }
 
-// rpos: qkv_row_pos(p, row) for EPI_QKV_ROPE (callers hoist it per row).
+// rpos: qkv_row_pos(p, row) for EPI_QKV_ROPE (callers hoist it per row);
+// rope_cs: that row's RoPE factors for this column when already loaded.
 template <int EPI>
-VLA_DEV void epilogue_store(const GemmParams& p, int row, int col, float v, float partner, int kz, int rpos) {
+VLA_DEV void epilogue_store(const GemmParams& p, int row, int col, float v, float partner, int kz, int rpos,
+                            const float2* rope_cs = nullptr) {
     if (row >= p.M) return;
     if constexpr (EPI == EPI_PARTIAL) {
         p.ws[((size_t)kz * p.M + row) * p.N + col] = v;
@@ -332,7 +334,7 @@ VLA_DEV void epilogue_store(const GemmParams& p, int row, int col, float v, floa
         const int b = div_T(row, p), i = row - b * p.T;
         float outv = v;
         if (sec < 2) {
-            const float2 cs = p.rope[rpos * (p.dh / 2) + m];
+            const float2 cs = rope_cs ? *rope_cs : p.rope[rpos * (p.dh / 2) + m];
             const float u1 = second ? partner : v;
             const float u2 = second ? v : partner;
             outv = second ? (u2 * cs.x + u1 * cs.y) : (u1 * cs.x - u2 * cs.y);
@@ -528,6 +530,28 @@ __global__ __launch_bounds__(512) void skinny_gemm_kernel(GemmParams p) {
     wvec wcur[SK_MAXS], wnext[SK_MAXS];
     int nt = blockIdx.x;
     if (nt < n_tiles) load_w(nt, wcur);
+
+    // epilogue operands of the first tile that do not depend on the sums (the
+    // E4M3 column scale; the QKV rows' RoPE positions and factors) are loaded
+    // now, so the epilogue does not wait on dependent loads
+    const int nt0 = blockIdx.x;
+    float wsc0 = 1.0f;
+    int rpos0[4] = {0, 0, 0, 0};
+    float2 cs0[4];
+    if (wave < 4 && nt0 < n_tiles) {
+        const int col = nt0 * 16 + (lane & 15);
+        if constexpr (W8) wsc0 = p.wscale[col];
+        if constexpr (EPI == EPI_QKV_ROPE) {
+            const bool roped = col < (p.nq + p.nkv) * p.dh;  // q and k columns
+            const int m = (col & (p.dh - 1)) >> 1;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = wave * 16 + 4 * (lane >> 4) + r;
+                rpos0[r] = row < p.M ? qkv_row_pos(p, row) : 0;
+                cs0[r] = roped && row < p.M ? p.rope[rpos0[r] * (p.dh / 2) + m] : make_float2(0.f, 0.f);
+            }
+        }
+    }
     int buf = 0;
     for (; nt < n_tiles; nt += gridDim.x) {
         const int nt_next = nt + gridDim.x;
@@ -554,14 +578,18 @@ __global__ __launch_bounds__(512) void skinny_gemm_kernel(GemmParams p) {
 #pragma unroll
             for (int w = 1; w < SK_WAVES; ++w) sum += *(const f32x4*)(&red[buf][w][wave][lane][0]);
             const int col = nt * 16 + (lane & 15);
-            const float wsc = W8 ? p.wscale[col] : 1.0f;
+            const bool first = nt == nt0;
+            const float wsc = W8 ? (first ? wsc0 : p.wscale[col]) : 1.0f;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = wave * 16 + 4 * (lane >> 4) + r;
                 const float v = sum[r] * wsc;
                 const float partner = __shfl_xor(v, 1, 64);
-                epilogue_store<EPI>(p, row, col, v, partner, kz,
-                                    EPI == EPI_QKV_ROPE && row < p.M ? qkv_row_pos(p, row) : 0);
+                if (EPI == EPI_QKV_ROPE && first)
+                    epilogue_store<EPI>(p, row, col, v, partner, kz, rpos0[r], &cs0[r]);
+                else
+                    epilogue_store<EPI>(p, row, col, v, partner, kz,
+                                        EPI == EPI_QKV_ROPE && row < p.M ? qkv_row_pos(p, row) : 0);
             }
         }
         buf ^= 1;
