@@ -218,12 +218,19 @@ def test_single_layer_stage(cfg_id):
 
 # small grids take the key-split kernel; (2, 12) and (1, 130) have enough
 # 16-row tiles (>= 512) to take the 64-rows-per-workgroup kernel (d_h 128 / 64)
-@pytest.mark.parametrize("cfg_id,batch", [(1, 1), (2, 1), (3, 1), (2, 3), (2, 12), (1, 130)])
-def test_attention_stage(cfg_id, batch):
+# (cfg, batch, prefix): few rows take the 8-wave kernel (prefix 280 with
+# T = 16 and prefix 320 with T = 50 give 10 and 12 key blocks: some waves
+# take two, and the last block is partly padding); many rows take the
+# row-tile kernel
+@pytest.mark.parametrize("cfg_id,batch,prefix", [(1, 1, None), (2, 1, None), (3, 1, None), (2, 3, None),
+                                                 (2, 12, None), (1, 130, None), (1, 1, 280), (2, 1, 320)])
+def test_attention_stage(cfg_id, batch, prefix):
     import torch
     from vla_flow_matching_denoise_amd import binding as B
     from vla_flow_matching_denoise_amd.expert import Expert, dims_from_config, to_device
     cfg = synth.config(cfg_id).replace(n_layers=2, batch=batch)
+    if prefix is not None:
+        cfg = cfg.replace(prefix_len=prefix)
     raw = synth.make_weights(cfg.replace(n_layers=2), seed=0)
     pk, pv = synth.make_prefix(cfg)
     rng = np.random.default_rng(11)
