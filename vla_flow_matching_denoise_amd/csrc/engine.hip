@@ -701,9 +701,21 @@ int launch_resnorm(vla_ctx* c, int step, int S, int gate_off, int scale_off, int
     // workgroups past the M rows (on otherwise idle CUs) prefetch, if asked
     L2Prefetch none{};
     const int npf = pf && pf->w[0] && c->ncu > c->M ? (c->ncu - c->M) & ~7 : 0;
-    hipLaunchKernelGGL(resnorm_kernel, dim3(c->M + npf), dim3(256), 0, c->stream, c->h, c->ws, S, c->modtab, gate_off,
-                       scale_off, shift_off, y8 ? nullptr : y, yf, c->M, d.hidden, d.horizon, d.batch, step, c->mod_ld,
-                       d.rms_eps, c->afrag, y8, c->y8s, npf ? *pf : none);
+    if (c->M > 64) {  // many rows: a wave per row
+        const dim3 g((c->M + 3) / 4);
+        if (d.hidden <= 1024)
+            hipLaunchKernelGGL(resnorm_rows_kernel<4>, g, dim3(256), 0, c->stream, c->h, c->ws, S, c->modtab,
+                               gate_off, scale_off, shift_off, y8 ? nullptr : y, yf, c->M, d.hidden, d.horizon,
+                               d.batch, step, c->mod_ld, d.rms_eps, c->afrag, y8, c->y8s);
+        else
+            hipLaunchKernelGGL(resnorm_rows_kernel<8>, g, dim3(256), 0, c->stream, c->h, c->ws, S, c->modtab,
+                               gate_off, scale_off, shift_off, y8 ? nullptr : y, yf, c->M, d.hidden, d.horizon,
+                               d.batch, step, c->mod_ld, d.rms_eps, c->afrag, y8, c->y8s);
+    } else {
+        hipLaunchKernelGGL(resnorm_kernel, dim3(c->M + npf), dim3(256), 0, c->stream, c->h, c->ws, S, c->modtab,
+                           gate_off, scale_off, shift_off, y8 ? nullptr : y, yf, c->M, d.hidden, d.horizon, d.batch,
+                           step, c->mod_ld, d.rms_eps, c->afrag, y8, c->y8s, npf ? *pf : none);
+    }
     HIPC(hipGetLastError());
     return VLA_OK;
 }
@@ -771,11 +783,19 @@ int launch_block_gemm(vla_ctx* c, int which, int step, int l, int* S) {
 // Layer l of Euler step `step`. On entry y holds the layer's first AdaRMSNorm
 // output; on exit h holds the layer output and, when norm_next, y holds the
 // next layer's first AdaRMSNorm output.
-// Per-token E4M3 copy of a bf16 [M][K] activation (batched E4M3 tier).
-int launch_quant(vla_ctx* c, const uint16_t* src, int K, uint8_t* dst, float* scale) {
-    hipLaunchKernelGGL(quant_rows_kernel, dim3(c->M), dim3(256), 0, c->stream, src, K, dst, scale);
+// Per-token E4M3 copy of a bf16 [M][K] activation (batched E4M3 tiers): a
+// wave per row up to K = 4096, else a workgroup per row.
+int launch_quant_rows(hipStream_t s, const uint16_t* src, int K, int M, uint8_t* dst, float* scale) {
+    const dim3 g((M + 3) / 4);
+    if (K <= 2048) hipLaunchKernelGGL(quant_rows_wave_kernel<4>, g, dim3(256), 0, s, src, K, M, dst, scale);
+    else if (K <= 4096) hipLaunchKernelGGL(quant_rows_wave_kernel<8>, g, dim3(256), 0, s, src, K, M, dst, scale);
+    else hipLaunchKernelGGL(quant_rows_kernel, dim3(M), dim3(256), 0, s, src, K, dst, scale);
     HIPC(hipGetLastError());
     return VLA_OK;
+}
+
+int launch_quant(vla_ctx* c, const uint16_t* src, int K, uint8_t* dst, float* scale) {
+    return launch_quant_rows(c->stream, src, K, c->M, dst, scale);
 }
 
 int enqueue_layer(vla_ctx* c, int step, int l, bool norm_next, float* yf_final = nullptr) {
@@ -1810,10 +1830,7 @@ int enqueue_prefill(vla_prefill_ctx* x) {
             else hipLaunchKernelGGL((attn_rows_kernel<64, 1, true>), rg, dim3(256), 0, c->stream, ap);
             HIPC(hipGetLastError());
         }
-        if (c->a8) {
-            hipLaunchKernelGGL(quant_rows_kernel, dim3(x->M), dim3(256), 0, c->stream, x->o, x->qd, c->o8, c->o8s);
-            HIPC(hipGetLastError());
-        }
+        if (c->a8 && (rc = launch_quant_rows(c->stream, x->o, x->qd, x->M, c->o8, c->o8s))) return rc;
         {
             GemmParams p{};
             p.A = c->a8 ? (const uint16_t*)c->o8 : x->o;
@@ -1834,11 +1851,8 @@ int enqueue_prefill(vla_prefill_ctx* x) {
             p.act = x->act;
             if ((rc = launch_gemm(c, x->gu[l], x->gu[l].cfg, c->w8, EPI_SWIGLU, p))) return rc;
         }
-        if (c->a8) {
-            hipLaunchKernelGGL(quant_rows_kernel, dim3(x->M), dim3(256), 0, c->stream, x->act, d.intermediate,
-                               c->act8, c->act8s);
-            HIPC(hipGetLastError());
-        }
+        if (c->a8 && (rc = launch_quant_rows(c->stream, x->act, d.intermediate, x->M, c->act8, c->act8s)))
+            return rc;
         {
             GemmParams p{};
             p.A = c->a8 ? (const uint16_t*)c->act8 : x->act;

@@ -129,6 +129,48 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
     }
 }
 
+// The same per-token E4M3 conversion with one wave per row (four rows per
+// 256-thread workgroup) for K <= 512 NC: the row stays in the wave's
+// registers and its maximum is reduced within the wave (no LDS, no barrier),
+// which suits many short rows better than a workgroup per row.
+template <int NC>
+__global__ __launch_bounds__(256) void quant_rows_wave_kernel(const uint16_t* __restrict__ src, int K, int M,
+                                                              uint8_t* __restrict__ dst, float* __restrict__ scale) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    const uint16_t* sr = src + (size_t)row * K;
+    float v[NC][8];
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int c = (lane + 64 * i) * 8;
+        if (c < K) {
+            const u32x4 w = *(const u32x4*)(sr + c);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[i][2 * j] = __uint_as_float(w[j] << 16);
+                v[i][2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+                amax = fmaxf(amax, fmaxf(fabsf(v[i][2 * j]), fabsf(v[i][2 * j + 1])));
+            }
+        }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
+    if (lane == 0) scale[row] = amax > 0.f ? amax / 448.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int c = (lane + 64 * i) * 8;
+        if (c < K) {
+            u32x2 q;
+            q[0] = f32x4_to_e4m3x4(v[i][0] * inv, v[i][1] * inv, v[i][2] * inv, v[i][3] * inv);
+            q[1] = f32x4_to_e4m3x4(v[i][4] * inv, v[i][5] * inv, v[i][6] * inv, v[i][7] * inv);
+            *(u32x2*)(dst + (size_t)row * K + c) = q;
+        }
+    }
+}
+
 // cos/sin of the rotary angle (P + i) * theta^(-2m/d_h), i < T, m < d_h/2,
 // evaluated in double precision once at create time.
 // cos/sin of every absolute position 0..npos-1 (the chunk of request b sits

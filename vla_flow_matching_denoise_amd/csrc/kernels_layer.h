@@ -170,6 +170,88 @@ __global__ __launch_bounds__(256) void resnorm_kernel(float* __restrict__ h, con
     }
 }
 
+// The same residual + AdaRMSNorm for many rows (batched workloads, where a
+// workgroup per row spends more time starting than working): one wave per
+// row, four rows per 256-thread workgroup, NC float4 chunks per lane (H <=
+// 256 NC), every load of the row issued before the first use, and the sums
+// and the maximum reduced within the wave (no LDS, no barrier).
+template <int NC>
+__global__ __launch_bounds__(256) void resnorm_rows_kernel(float* __restrict__ h, const float* __restrict__ ws, int S,
+                                                           const float* __restrict__ mod, int gate_off, int scale_off,
+                                                           int shift_off, uint16_t* __restrict__ y,
+                                                           float* __restrict__ yf, int M, int H, int T, int B,
+                                                           int step, int mod_ld, float eps, int afrag,
+                                                           uint8_t* __restrict__ y8, float* __restrict__ y8s) {
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;
+    float* hr = h + (size_t)row * H;
+    const float* mr = mod + (size_t)(step * B + row / T) * mod_ld;
+    const bool norm = y || yf || y8;
+    f32x4 v[NC], g[NC], sc[NC], sh[NC];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        const int c = (lane + 64 * j) * 4;
+        if (c < H) {
+            v[j] = *(const f32x4*)(hr + c);
+            if (S > 0) g[j] = *(const f32x4*)(mr + gate_off + c);
+            if (norm) {
+                sc[j] = *(const f32x4*)(mr + scale_off + c);
+                sh[j] = *(const f32x4*)(mr + shift_off + c);
+            }
+        }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        const int c = (lane + 64 * j) * 4;
+        if (c < H) {
+            if (S > 0) {
+                f32x4 acc = *(const f32x4*)(ws + (size_t)row * H + c);
+                for (int z = 1; z < S; ++z) acc += *(const f32x4*)(ws + ((size_t)z * M + row) * H + c);
+                v[j] += g[j] * acc;
+                *(f32x4*)(hr + c) = v[j];
+            }
+            ss += v[j][0] * v[j][0] + v[j][1] * v[j][1] + v[j][2] * v[j][2] + v[j][3] * v[j][3];
+        }
+    }
+    if (!norm) return;
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+        const int c = (lane + 64 * j) * 4;
+        if (c < H) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[j][e] = v[j][e] * inv * (1.f + sc[j][e]) + sh[j][e];
+                amax = fmaxf(amax, fabsf(v[j][e]));
+            }
+            if (y) {
+                u32x2 ob;
+                ob[0] = pack_bf16x2(v[j][0], v[j][1]);
+                ob[1] = pack_bf16x2(v[j][2], v[j][3]);
+                *(u32x2*)(y + act_index(row, c, H, afrag)) = ob;
+            }
+            if (yf) *(f32x4*)(yf + (size_t)row * H + c) = v[j];
+        }
+    }
+    if (y8) {  // per-token E4M3 copy of y, as in resnorm_kernel
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        const float qs = amax > 0.f ? 448.0f / amax : 1.0f;
+        if (lane == 0) y8s[row] = amax > 0.f ? amax / 448.0f : 1.0f;
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+            const int c = (lane + 64 * j) * 4;
+            if (c < H)
+                *(uint32_t*)(y8 + (size_t)row * H + c) =
+                    f32x4_to_e4m3x4(v[j][0] * qs, v[j][1] * qs, v[j][2] * qs, v[j][3] * qs);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Per-layer K/V of the attention, [prefix ; chunk] concatenated on the key
 // axis and padded to a multiple of 32 keys (S_pad), per (request, layer, KV
