@@ -1126,12 +1126,14 @@ void gemm8_kernel(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Grouped-query attention, no mask, scale 1/sqrt(d_h), online softmax.
-// Workgroup = (16 query rows of one KV group, group g, request b); the G query
-// heads of a group are packed: group row = head_in_group*T + token. The
-// AT_WAVES waves (8 for few workgroups, 4 otherwise) take interleaved 32-key blocks of the layer's concatenated K/V
-// (prefetching their next block), keep their own running max / sum / output,
-// and merge them through LDS at the end.
+// Grouped-query attention, no mask, scale 1/sqrt(d_h), online softmax, for
+// few query rows (batch 1). Workgroup = (16 query rows of one KV group, group
+// g, request b); the G query heads of a group are packed: group row =
+// head_in_group*T + token, so the workgroup's rows are one contiguous run of
+// q, loaded once into LDS. Its AT_WAVES waves take interleaved 32-key blocks
+// of the layer's concatenated K/V straight from the cache (fragment order:
+// 1 KiB loads), prefetch their next block, keep their own running max / sum
+// / output, and merge them through LDS at the end.
 // ---------------------------------------------------------------------------
 struct AttnParams {
     const uint16_t* q;      // [B, nq, T, dh]
