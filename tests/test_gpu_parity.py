@@ -149,6 +149,25 @@ def test_ragged_shapes(prefix_len, horizon, batch):
     _gate_bf16(metrics(out, ref), f"ragged P={prefix_len} T={horizon} B={batch}")
 
 
+@pytest.mark.parametrize("hidden,intermediate", [(1536, 6144), (2048, 5632)])
+def test_wide_hidden_batched_rows(hidden, intermediate):
+    """Hidden above 1024 (up to the 2048 maximum) with more than 64 rows: the
+    tiled GEMMs and the wave-per-row residual + norm with 8 float4 chunks per
+    lane. Two layers, two requests on warped schedules, three steps."""
+    cfg = synth.config(3).replace(n_layers=2, hidden=hidden, intermediate=intermediate, prefix_len=64,
+                                  horizon=50, batch=2, n_steps=3)
+    raw = synth.make_weights(cfg, seed=5)
+    pk, pv, x0, ts = _inputs(cfg, schedule="warped")
+    say(f"[wide] hidden {hidden}, SwiGLU {intermediate}, 2 layers, B=2 (M=100), 3 steps")
+    case = GpuCase(cfg, raw, pk, pv, x0, ts)
+    try:
+        out = case.run()
+    finally:
+        case.close()
+    ref = run_oracle(cfg, oracle.decode_weights(raw), pk, pv, x0, ts)
+    _gate_bf16(metrics(out, ref), f"wide h{hidden}")
+
+
 # ---------------------------------------------------------------------------
 # stage parity
 # ---------------------------------------------------------------------------
