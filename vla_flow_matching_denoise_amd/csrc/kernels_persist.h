@@ -424,21 +424,21 @@ __global__ __launch_bounds__(PWAVES * 64) void persist_kernel(PersistParams p) {
     // Reduce / norm columns: f = sub*cpt + c of the workgroup's 16*nto O / down
     // columns, i.e. global column pcol(f).
 #define P_PHASE_VARS                                                                                  \
-    const int tid = p_opaque_v((int)threadIdx.x), lane = tid & 63, wave = tid >> 6;                   \
+    [[maybe_unused]] const int tid = p_opaque_v((int)threadIdx.x), lane = tid & 63, wave = tid >> 6;  \
     const int x = p_opaque_s(x_id), j = p_opaque_s(j_id);                                             \
     const int g = (x * hq) / p.G;                                                                     \
     const int nqt = hq * dh / 16, nkt = dh / 16, n_qkv = nqt + 2 * nkt;                               \
     const int gbase = x * (2 * p.Ix) / 16, gcount = 2 * p.Ix / 16;                                    \
     auto ntiles = [&](int count) { return count > j ? (count - j + PJ - 1) / PJ : 0; };               \
     const int ntq = ntiles(n_qkv), nto = ntiles(H / 16), ntg = ntiles(gcount);                        \
-    auto tq = [&](int t) {                                                                            \
+    [[maybe_unused]] auto tq = [&](int t) {                                                                            \
         const int lt = min(j + t * PJ, n_qkv - 1);                                                    \
         if (lt < nqt) return (x * hq * dh) / 16 + lt;                                                 \
         if (lt < nqt + nkt) return (p.nq * dh + g * dh) / 16 + (lt - nqt);                            \
         return (p.nq * dh + p.nkv * dh + g * dh) / 16 + (lt - nqt - nkt);                             \
     };                                                                                                \
-    auto to = [&](int t) { return min(j + t * PJ, H / 16 - 1); };                                     \
-    auto tg = [&](int t) { return gbase + min(j + t * PJ, gcount - 1); };                             \
+    [[maybe_unused]] auto to = [&](int t) { return min(j + t * PJ, H / 16 - 1); };                                     \
+    [[maybe_unused]] auto tg = [&](int t) { return gbase + min(j + t * PJ, gcount - 1); };                             \
     auto pcol = [&](int f) { return (j + (f >> 4) * PJ) * 16 + (f & 15); };                           \
     const PSplit sp_qkv = p_split(H / 32, wave), sp_o = p_split(hq * dh / 32, wave), sp_gu = sp_qkv,  \
                  sp_d = p_split(p.Ix / 32, wave);                                                     \
