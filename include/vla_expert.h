@@ -77,7 +77,7 @@ extern "C" {
 /* With batch*horizon <= 64, workgroups appended to the attention and norm kernels (on CUs those leave
  * idle) load the next weight-streaming GEMMs' weights into the L2 of the XCD that will read them. Bits:
  * 1 the attention prefetches O, 2 the attention prefetches gate_up, 4 the norm before a layer prefetches
- * its QKV, 8 the norm before gate_up prefetches down; 0 off. Default 3. For measurement; setting it
+ * its QKV, 8 the norm before gate_up prefetches down; 0 off. Default 7. For measurement; setting it
  * waits for the ctx stream and drops captured graphs. */
 #define VLA_OPT_L2_PREFETCH 6
 

@@ -194,7 +194,7 @@ struct vla_ctx {
 
     // batch <= 64 rows: idle workgroups of the attention and norm kernels
     // prefetch the next skinny GEMMs' weights into the right XCD's L2
-    int l2_prefetch = 3;  // VLA_OPT_L2_PREFETCH bits
+    int l2_prefetch = 7;  // VLA_OPT_L2_PREFETCH bits
     uint32_t* pf_sink = nullptr;
 
     // persistent small-batch path (one resident launch per call)
