@@ -357,6 +357,119 @@ def test_mlp_block_closed_form():
 
 
 # ---------------------------------------------------------------------------
+# The block's rotary positions: a closed form with one-hot weights
+# ("LingBot-VLA on Thor (sm_110)", section 2: the QKV projection with RoPE;
+# chunk tokens sit after the cached prefix, at positions P + i)
+# ---------------------------------------------------------------------------
+
+def _rope_probe_layer(d: ExpertDims, m: int):
+    """One layer whose attention scores can be written out by hand.
+
+    Modulation: scale_1 = -1 and shift_1 = e_0, so every chunk row's normed
+    input is exactly e_0; gate_1 = 1; the MLP gate is closed.  W_q and W_k
+    send e_0 to e_m in every head, W_v sends it to e_2, W_o is the identity.
+    Prefix keys: key 0 = e_m, key 1 = e_{m+d/2}, the rest zero; prefix values
+    e_0, e_1, then e_3.  Before the rotation every chunk query and key is e_m,
+    so each score is a cosine or sine of the rotation angle."""
+    H, dh, nq, nkv = d.hidden, d.head_dim, d.n_q_heads, d.n_kv_heads
+    assert nq * dh == H
+    W = _tiny_weights(d)
+    for name, n_heads, unit in (("wq", nq, m), ("wk", nkv, m), ("wv", nkv, 2)):
+        w = RNG.standard_normal((n_heads * dh, H))
+        w[:, 0] = 0.0
+        w[[h * dh + unit for h in range(n_heads)], 0] = 1.0
+        W[name] = [w]
+    W["wo"] = [np.eye(H)]
+    e0 = np.zeros(H)
+    e0[0] = 1.0
+    _only_bias_chunks(d, W, {0: -np.ones(H), 1: e0, 2: np.ones(H)})
+    P = d.prefix_len
+    pk = np.zeros((P, nkv, dh))
+    pv = np.zeros((P, nkv, dh))
+    pk[0, :, m] = 1.0
+    pk[1, :, m + dh // 2] = 1.0
+    pv[0, :, 0] = 1.0
+    pv[1, :, 1] = 1.0
+    pv[2:, :, 3] = 1.0
+    return W, pk, pv
+
+
+def _rope_probe_expect(d: ExpertDims, m: int, h: np.ndarray, positions, chunk_rotated=True):
+    """h + o for the probe layer, o written out with math.cos / math.sin: the
+    query of chunk token i (at positions[i]) scores cos(phi_i) and sin(phi_i)
+    against the two prefix keys, 0 against the other prefix keys, and
+    cos(phi_i - phi_j) against chunk key j (its own rotation, phi at that
+    key's position), where phi = position * theta^(-2m/d_h)."""
+    dh, P, T = d.head_dim, d.prefix_len, h.shape[0]
+    w_m = d.rope_theta ** (-2.0 * m / dh)
+    phi = [positions[i] * w_m for i in range(T)]
+    out = np.empty_like(h)
+    for i in range(T):
+        s = [math.cos(phi[i]), math.sin(phi[i])] + [0.0] * (P - 2)
+        s += [math.cos(phi[i] - phi[j]) if chunk_rotated else math.cos(phi[i]) for j in range(T)]
+        s = [x / math.sqrt(dh) for x in s]
+        mx = max(s)
+        e = [math.exp(x - mx) for x in s]
+        z = sum(e)
+        o_head = np.zeros(dh)
+        o_head[0] = e[0] / z
+        o_head[1] = e[1] / z
+        o_head[3] = sum(e[2:P]) / z
+        o_head[2] = sum(e[P:]) / z
+        out[i] = h[i] + np.tile(o_head, d.n_q_heads)
+    return out
+
+
+@pytest.mark.parametrize("m", [0, 1])
+@pytest.mark.parametrize("P", [7, 19])
+def test_block_rope_positions_closed_form(m, P):
+    """The chunk's queries and keys are rotated at positions P + i: the
+    oracle's layer equals the hand-written scores above, and differs from
+    the two plausible mistakes (positions 0..T-1, or chunk keys left
+    unrotated)."""
+    d = _tiny_dims(n_layers=1, hidden=32, n_q_heads=4, n_kv_heads=2, head_dim=8, prefix_len=P)
+    W, pk, pv = _rope_probe_layer(d, m)
+    h = RNG.standard_normal((d.horizon, d.hidden))
+    mod = oracle.modulation(np.ones(d.hidden), W["mod_w"][0], W["mod_b"][0], 6)
+    got = oracle.expert_layer(h, W, 0, mod, pk, pv, d)
+    T = d.horizon
+    want = _rope_probe_expect(d, m, h, [P + i for i in range(T)])
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-13)
+    wrong_pos = _rope_probe_expect(d, m, h, list(range(T)))
+    unrotated = _rope_probe_expect(d, m, h, [P + i for i in range(T)], chunk_rotated=False)
+    assert np.abs(got - wrong_pos).max() > 1e-3
+    assert np.abs(got - unrotated).max() > 1e-3
+
+
+def test_varlen_block_positions_follow_the_valid_length():
+    """A prefix padded to P with n valid tokens puts the chunk at positions
+    n + i: one Euler step of a one-layer probe model (x-independent input
+    rows, output projection reading the probe's attention) through
+    denoise_varlen equals the hand-written scores at positions n + i."""
+    P, n, m = 19, 7, 0
+    d = _tiny_dims(n_layers=1, hidden=32, n_q_heads=4, n_kv_heads=2, head_dim=8, prefix_len=P)
+    W, pk, pv = _rope_probe_layer(d, m)
+    # x enters only through W_in = 0, so h = b_in for every row; the final
+    # norm is the plain RMSNorm (closed final gate) and W_out reads it back
+    W["in_w"] = np.zeros_like(W["in_w"])
+    W["modf_w"] = np.zeros_like(W["modf_w"])
+    W["modf_b"] = np.zeros_like(W["modf_b"])
+    A, H = d.action_dim, d.hidden
+    W["out_w"] = RNG.standard_normal((A, H))
+    W["out_b"] = np.zeros(A)
+    x0 = RNG.standard_normal((1, d.horizon, A))
+    ts = np.array([[0.0, 1.0]])
+    pk_pad = np.concatenate([pk[:n], RNG.standard_normal((P - n, d.n_kv_heads, d.head_dim))])[None, None]
+    pv_pad = np.concatenate([pv[:n], RNG.standard_normal((P - n, d.n_kv_heads, d.head_dim))])[None, None]
+    got = oracle.denoise_varlen(W, d, pk_pad, pv_pad, x0, ts, [n])[0]
+    h0 = np.tile(W["in_b"], (d.horizon, 1))
+    hd = dataclasses.replace(d, prefix_len=n)
+    h1 = _rope_probe_expect(hd, m, h0, [n + i for i in range(d.horizon)])
+    hn = h1 / np.sqrt(np.mean(h1 ** 2, axis=1, keepdims=True) + d.rms_eps)
+    np.testing.assert_allclose(got, x0[0] + hn @ W["out_w"].T, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
 # Euler loop
 # ---------------------------------------------------------------------------
 
@@ -740,3 +853,169 @@ def test_backbone_fp8_weights_decode_to_row_scaled_codes():
         row_max = np.abs(b).max(axis=1, keepdims=True)
         assert np.all(np.abs(a - b) <= 2.0 ** -4 * np.abs(b) + 2.0 ** -9 * row_max / 448 * 2 + 2.0 ** -8 * row_max)
         np.testing.assert_allclose(np.abs(a).max(axis=1), row_max[:, 0], rtol=2.0 ** -4)
+
+
+# ---------------------------------------------------------------------------
+# The backbone layer's body: closed forms and a composition of torch routines
+# ("LingBot-VLA on Thor (sm_110)", section 1: the prefix model whose per-layer
+# self-attention builds the cache; the layer reading is the plain pre-norm
+# decoder layer)
+# ---------------------------------------------------------------------------
+
+def _bb_dims(**kw):
+    base = dict(n_layers=1, hidden=24, n_q_heads=4, n_kv_heads=2, head_dim=8, intermediate=40, prefix_len=9)
+    base.update(kw)
+    return oracle.BackboneDims(**base)
+
+
+def _bb_weights(d, seed=0, std=0.3):
+    r = np.random.default_rng(seed)
+    H, I = d.hidden, d.intermediate
+    qd, kvd = d.n_q_heads * d.head_dim, d.n_kv_heads * d.head_dim
+    g = lambda *s: r.standard_normal(s) * std
+    W = {"n1": [1.0 + 0.5 * r.standard_normal(H)], "n2": [1.0 + 0.5 * r.standard_normal(H)],
+         "wq": [g(qd, H)], "wk": [g(kvd, H)], "wv": [g(kvd, H)], "wo": [g(H, qd)], "wg": [g(I, H)],
+         "wu": [g(I, H)], "wd": [g(H, I)]}
+    return W
+
+
+def _rms_rows(x, w, eps):
+    """x / rms(x) * w with the RMS from numpy.linalg.norm."""
+    return x / np.sqrt(np.linalg.norm(x, axis=1, keepdims=True) ** 2 / x.shape[1] + eps) * w
+
+
+def test_backbone_uniform_causal_attention_closed_form():
+    """W_q = W_k = 0: every score is 0, so token t's head output is the mean of
+    the values of tokens 0..t of its KV group; W_g = 0 closes the MLP (SiLU(0)
+    = 0).  The layer adds exactly that mean times W_o, its keys are zero, and
+    its values are W_v applied to the first norm (weight n1, not n2)."""
+    d = _bb_dims()
+    W = _bb_weights(d)
+    W["wq"][0][:] = 0.0
+    W["wk"][0][:] = 0.0
+    W["wg"][0][:] = 0.0
+    x = RNG.standard_normal((d.prefix_len, d.hidden)) * 2.0
+    xo, k, v = oracle.backbone_layer(x, W, 0, d)
+    y = _rms_rows(x, W["n1"][0], d.rms_eps)
+    vv = (y @ W["wv"][0].T).reshape(d.prefix_len, d.n_kv_heads, d.head_dim)
+    grp = d.n_q_heads // d.n_kv_heads
+    o = np.empty((d.prefix_len, d.n_q_heads * d.head_dim))
+    for t in range(d.prefix_len):
+        mean_t = vv[:t + 1].mean(axis=0)
+        o[t] = np.concatenate([mean_t[j // grp] for j in range(d.n_q_heads)])
+    np.testing.assert_allclose(xo, x + o @ W["wo"][0].T, rtol=0, atol=1e-12)
+    assert np.all(k == 0.0)
+    np.testing.assert_allclose(v, vv.transpose(1, 0, 2), rtol=0, atol=1e-13)
+
+
+def test_backbone_zeroed_outputs_are_identity():
+    """W_o = W_d = 0: both residual branches add nothing, x passes unchanged."""
+    d = _bb_dims()
+    W = _bb_weights(d)
+    W["wo"][0][:] = 0.0
+    W["wd"][0][:] = 0.0
+    x = RNG.standard_normal((d.prefix_len, d.hidden))
+    xo, _, _ = oracle.backbone_layer(x, W, 0, d)
+    assert np.array_equal(xo, x)
+
+
+def test_backbone_mlp_reads_the_second_norm_of_the_attention_residual():
+    """The MLP branch takes RMSNorm(x + attention) * n2.  With W_q = W_k = 0 the
+    attention residual has the closed form of the uniform causal mean, so the
+    whole layer is written out here; a mix-up of n1 and n2, or an MLP reading
+    x before the attention residual, fails."""
+    d = _bb_dims()
+    W = _bb_weights(d)
+    W["wq"][0][:] = 0.0
+    W["wk"][0][:] = 0.0
+    x = RNG.standard_normal((d.prefix_len, d.hidden))
+    xo, _, _ = oracle.backbone_layer(x, W, 0, d)
+    y = _rms_rows(x, W["n1"][0], d.rms_eps)
+    vv = (y @ W["wv"][0].T).reshape(d.prefix_len, d.n_kv_heads, d.head_dim)
+    grp = d.n_q_heads // d.n_kv_heads
+    o = np.stack([np.concatenate([vv[:t + 1].mean(axis=0)[j // grp] for j in range(d.n_q_heads)])
+                  for t in range(d.prefix_len)])
+    x1 = x + o @ W["wo"][0].T
+
+    def mlp(xin, nw):
+        y2 = _rms_rows(xin, nw, d.rms_eps)
+        gz = y2 @ W["wg"][0].T
+        return (gz * scipy.special.expit(gz) * (y2 @ W["wu"][0].T)) @ W["wd"][0].T
+
+    np.testing.assert_allclose(xo, x1 + mlp(x1, W["n2"][0]), rtol=0, atol=1e-12)
+    assert np.abs(xo - (x1 + mlp(x1, W["n1"][0]))).max() > 1e-3       # n1 in the MLP
+    assert np.abs(xo - (x1 + mlp(x, W["n2"][0]))).max() > 1e-3         # MLP on pre-attention x
+
+
+def _torch_rope(u: torch.Tensor, pos: torch.Tensor, theta: float) -> torch.Tensor:
+    """Rotary embedding written as complex multiplication: the pair
+    (u_m, u_{m+d/2}) is the complex number u_m + i u_{m+d/2}, turned by
+    exp(i pos theta^(-2m/d))."""
+    d = u.shape[-1]
+    half = d // 2
+    z = torch.complex(u[..., :half], u[..., half:])
+    freq = theta ** (-2.0 * torch.arange(half, dtype=torch.float64) / d)
+    rot = torch.polar(torch.ones(pos.shape[0], half, dtype=torch.float64), pos[:, None].double() * freq[None])
+    w = z * rot
+    return torch.cat([w.real, w.imag], dim=-1)
+
+
+def test_backbone_layer_matches_torch_composition():
+    """The whole layer against torch's own routines (rms_norm, linear,
+    scaled_dot_product_attention with is_causal and grouped KV heads, silu)
+    and the complex-number RoPE at positions 0..P-1, for layer 1 of a
+    two-layer set of weights."""
+    F = torch.nn.functional
+    d = _bb_dims(n_layers=2)
+    W0, W1 = _bb_weights(d, seed=3), _bb_weights(d, seed=4)
+    W = {k: W0[k] + W1[k] for k in W0}
+    x = RNG.standard_normal((d.prefix_len, d.hidden))
+    xo, k, v = oracle.backbone_layer(x, W, 1, d)
+    T = lambda a: torch.tensor(a, dtype=torch.float64)
+    P, H, nq, nkv, dh = d.prefix_len, d.hidden, d.n_q_heads, d.n_kv_heads, d.head_dim
+    xt = T(x)
+    y = F.rms_norm(xt, (H,), T(W1["n1"][0]), eps=d.rms_eps)
+    q = F.linear(y, T(W1["wq"][0])).reshape(P, nq, dh).transpose(0, 1)
+    kt = F.linear(y, T(W1["wk"][0])).reshape(P, nkv, dh).transpose(0, 1)
+    vt = F.linear(y, T(W1["wv"][0])).reshape(P, nkv, dh).transpose(0, 1)
+    pos = torch.arange(P)
+    q, kt = _torch_rope(q, pos, d.rope_theta), _torch_rope(kt, pos, d.rope_theta)
+    o = F.scaled_dot_product_attention(q[None], kt[None], vt[None], is_causal=True, enable_gqa=True)[0]
+    x1 = xt + F.linear(o.transpose(0, 1).reshape(P, nq * dh), T(W1["wo"][0]))
+    y2 = F.rms_norm(x1, (H,), T(W1["n2"][0]), eps=d.rms_eps)
+    x2 = x1 + F.linear(F.silu(F.linear(y2, T(W1["wg"][0]))) * F.linear(y2, T(W1["wu"][0])), T(W1["wd"][0]))
+    np.testing.assert_allclose(xo, x2.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(k, kt.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(v, vt.numpy(), rtol=0, atol=1e-12)
+
+
+def test_expert_layer_matches_torch_composition():
+    """One expert layer against torch's routines: rms_norm with the (1 +
+    scale) / shift modulation, linear, the complex-number RoPE at positions
+    P + i, unmasked scaled_dot_product_attention over [prefix ; chunk] keys
+    with grouped KV heads, the two gated residuals and the SwiGLU MLP."""
+    F = torch.nn.functional
+    d = _tiny_dims(n_layers=2)
+    W = _tiny_weights(d, seed=5)
+    pk, pv, _ = _tiny_inputs(d, seed=6)
+    h = RNG.standard_normal((d.horizon, d.hidden))
+    l = 1
+    mod = oracle.modulation(RNG.standard_normal(d.hidden), W["mod_w"][l], W["mod_b"][l], 6)
+    got = oracle.expert_layer(h, W, l, mod, pk[0, l], pv[0, l], d)
+    T = lambda a: torch.tensor(a, dtype=torch.float64)
+    a1, b1, g1, a2, b2, g2 = (T(z) for z in mod)
+    Tn, H, nq, nkv, dh, P = d.horizon, d.hidden, d.n_q_heads, d.n_kv_heads, d.head_dim, d.prefix_len
+    ht = T(h)
+    y = F.rms_norm(ht, (H,), eps=d.rms_eps) * (1 + a1) + b1
+    q = F.linear(y, T(W["wq"][l])).reshape(Tn, nq, dh).transpose(0, 1)
+    k = F.linear(y, T(W["wk"][l])).reshape(Tn, nkv, dh).transpose(0, 1)
+    v = F.linear(y, T(W["wv"][l])).reshape(Tn, nkv, dh).transpose(0, 1)
+    pos = P + torch.arange(Tn)
+    q, k = _torch_rope(q, pos, d.rope_theta), _torch_rope(k, pos, d.rope_theta)
+    K = torch.cat([T(pk[0, l]).transpose(0, 1), k], dim=1)
+    V = torch.cat([T(pv[0, l]).transpose(0, 1), v], dim=1)
+    o = F.scaled_dot_product_attention(q[None], K[None], V[None], enable_gqa=True)[0]
+    h1 = ht + g1 * F.linear(o.transpose(0, 1).reshape(Tn, nq * dh), T(W["wo"][l]))
+    y2 = F.rms_norm(h1, (H,), eps=d.rms_eps) * (1 + a2) + b2
+    h2 = h1 + g2 * F.linear(F.silu(F.linear(y2, T(W["wg"][l]))) * F.linear(y2, T(W["wu"][l])), T(W["wd"][l]))
+    np.testing.assert_allclose(got, h2.numpy(), rtol=0, atol=1e-12)
