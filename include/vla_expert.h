@@ -150,7 +150,8 @@ vla_ctx* vla_expert_create(const vla_weights* weights, const vla_dims* dims);
 
 /*
  * Run the n_steps-step Euler denoise loop for all dims.batch requests.
- * All pointers are DEVICE pointers, 16-byte aligned:
+ * All pointers are DEVICE pointers; prefix_k and prefix_v 16-byte aligned,
+ * noise, t_schedule and out_actions 4-byte aligned (VLA_ERR_ARG otherwise):
  *   prefix_k, prefix_v  [B, L, P, n_kv, d_h] bf16 — each request's cached
  *                       prefix keys/values per layer, used as given;
  *   noise               [B, T, A] fp32 — the state x at t_0;
@@ -158,7 +159,8 @@ vla_ctx* vla_expert_create(const vla_weights* weights, const vla_dims* dims);
  *   out_actions         [B, T, A] fp32 — x at t_N; may alias noise.
  * Inputs are borrowed until the ctx stream passes this call. Asynchronous on
  * the ctx stream. The first call with a new n_steps captures a graph.
- * Returns VLA_OK or a VLA_ERR_* code.
+ * Returns VLA_OK or a VLA_ERR_* code (VLA_ERR_ARG for n_steps outside
+ * [1, 100000]); argument errors are found before anything is enqueued.
  */
 int vla_denoise(vla_ctx* ctx, const void* prefix_k, const void* prefix_v, const float* noise,
                 const float* t_schedule, int n_steps, float* out_actions);
@@ -180,7 +182,10 @@ int vla_denoise_varlen(vla_ctx* ctx, const void* prefix_k, const void* prefix_v,
 /* Use `stream` (a hipStream_t) for every later call on ctx. NULL (also the
  * state after vla_expert_create) selects the legacy default stream. Graphs
  * are captured once on a library-created stream and replayed on this one.
- * Returns VLA_OK or VLA_ERR_ARG. */
+ * A context's working buffers serve all its calls, so when the stream
+ * changes, the new stream first waits (an event, no host wait) for the work
+ * already enqueued on the previous one. Returns VLA_OK, VLA_ERR_ARG or
+ * VLA_ERR_HIP. */
 int vla_set_stream(vla_ctx* ctx, void* stream);
 
 /* Set an option (VLA_OPT_*). Returns VLA_OK or VLA_ERR_ARG. */

@@ -107,8 +107,10 @@ vla_prefill_ctx* vla_prefill_create(const vla_backbone_weights* weights, const v
 int vla_prefill(vla_prefill_ctx* ctx, const void* embeddings, void* prefix_k, void* prefix_v);
 
 /* Use `stream` (a hipStream_t) for later calls; NULL selects the legacy
- * default stream (the state after vla_prefill_create). Returns VLA_OK or
- * VLA_ERR_ARG. */
+ * default stream (the state after vla_prefill_create). When the stream
+ * changes, the new stream first waits (an event, no host wait) for the work
+ * already enqueued on the previous one, whose buffers later calls reuse.
+ * Returns VLA_OK, VLA_ERR_ARG or VLA_ERR_HIP. */
 int vla_prefill_set_stream(vla_prefill_ctx* ctx, void* stream);
 
 /* VLA_OPT_USE_GRAPH (1 replay a captured graph, the default; 0 launch

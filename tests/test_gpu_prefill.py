@@ -7,11 +7,12 @@ max-abs gate grows with depth because the cache of layer l carries the
 rounding of l + 1 layers (bf16 GEMM/attention inputs, bf16 outputs; fp32
 accumulation and residual stream), independent errors that add in
 quadrature: the oracle with bf16 rounding inserted where the GPU path rounds
-differs from the exact oracle by max-abs 0.012-0.014 x RMS at layer 0, 0.023
-at layer 3 and 0.030 at layer 7 of the 36-layer backbone. Cases:
+(tests/rounding_model.py; ``python -m tests.rounding_model 8`` prints the
+table) differs from the exact oracle by max-abs 0.012-0.014 x RMS at layer 0,
+0.023 at layer 3 and 0.030 at layer 7 of the 36-layer backbone. Cases:
 the tiny backbone at ragged prefix lengths and batches (causal tiles that
 straddle two heads, a one-token prefix), the 36-layer LingBot-shaped backbone
-at P = 256 (the full workload), eager launches against the graph replay,
+at P = 256 (the full workload) and at P = 512, eager launches against the graph replay,
 every GEMM tile, and the prefill output fed to the expert's denoise loop.
 """
 import numpy as np
@@ -113,6 +114,30 @@ def test_prefill_lingbot_36_layers():
     rk, rv = oracle_prefill(bcfg, raw, emb)
     check("LingBot 36L keys", k, rk)
     check("LingBot 36L values", v, rv)
+
+
+@pytest.mark.timeout(900)
+def test_prefill_lingbot_36_layers_p512():
+    """The LingBot-shaped backbone at P = 512 (the V2-shaped loop's prefix
+    length), batch 1: all 36 layers' caches, the oracle run layer by layer."""
+    bcfg = synth.backbone(2).replace(prefix_len=512)
+    say("[prefill] LingBot backbone, 36 layers, P 512: generating weights")
+    raw = synth.make_backbone_weights(bcfg, seed=1)
+    emb = synth.make_embeddings(bcfg, seed=1)
+    (k, v), = run_gpu(bcfg, raw, [emb])
+    say("[prefill] P 512: GPU done; oracle")
+    W = lazy_weights(raw)
+    d = oracle.BackboneDims.from_config(bcfg)
+    x = oracle.decode_bf16(emb)[0]
+    rk = np.empty((1, bcfg.n_layers, 512, bcfg.n_kv_heads, bcfg.head_dim))
+    rv = np.empty_like(rk)
+    for l in range(bcfg.n_layers):
+        x, kl, vl = oracle.backbone_layer(x, W, l, d)
+        rk[0, l], rv[0, l] = kl.transpose(1, 0, 2), vl.transpose(1, 0, 2)
+        if l % 6 == 5:
+            say(f"[prefill] P 512 oracle: {l + 1} layers")
+    check("LingBot 36L P512 keys", k, rk)
+    check("LingBot 36L P512 values", v, rv)
 
 
 def test_prefill_graph_replay_and_eager_agree():

@@ -7,9 +7,10 @@ import of this module raises.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
-from typing import Optional
+from typing import Callable, Dict, Optional
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libvla_expert.so")
@@ -135,11 +136,34 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
 
 _LIB: Optional[ctypes.CDLL] = None
 
+# Contexts created through this module and not yet destroyed, handle -> the
+# destroy function.  They are destroyed at interpreter exit by an atexit hook
+# registered right after the library (and with it torch's HIP runtime) is
+# loaded: Python runs its atexit hooks in reverse order of registration and
+# before the C-level exit handlers, so the contexts' graphs, streams, events
+# and allocations are released while the HIP runtime (and a profiler that
+# intercepts it) is still fully up, instead of being left for the runtime's
+# own exit-time teardown or for a finalizer that runs after it.
+_LIVE: Dict[int, Callable[[int], None]] = {}
+
+
+def close_all() -> int:
+    """Destroy every context still open (in creation order reversed).
+    Returns how many were destroyed."""
+    n = 0
+    for h in reversed(list(_LIVE)):
+        destroy = _LIVE.pop(h, None)
+        if destroy is not None:
+            destroy(h)
+            n += 1
+    return n
+
 
 def lib() -> ctypes.CDLL:
     global _LIB
     if _LIB is None:
         _LIB = load_library()
+        atexit.register(close_all)
     return _LIB
 
 
@@ -165,6 +189,7 @@ def vla_expert_create(weights: VlaWeights, dims: VlaDims) -> int:
     h = lib().vla_expert_create(ctypes.byref(weights), ctypes.byref(dims))
     if not h:
         raise VlaError(-1, vla_last_error())
+    _LIVE[h] = lib().vla_expert_destroy
     return h
 
 
@@ -196,6 +221,8 @@ def vla_get_option(ctx: int, option: int) -> int:
 
 
 def vla_expert_destroy(ctx: Optional[int]) -> None:
+    if ctx:
+        _LIVE.pop(ctx, None)
     lib().vla_expert_destroy(ctx)
 
 
@@ -230,6 +257,7 @@ def vla_prefill_create(weights: VlaBackboneWeights, dims: VlaBackboneDims) -> in
     h = lib().vla_prefill_create(ctypes.byref(weights), ctypes.byref(dims))
     if not h:
         raise VlaError(-1, vla_last_error())
+    _LIVE[h] = lib().vla_prefill_destroy
     return h
 
 
@@ -247,6 +275,8 @@ def vla_prefill_set_option(ctx: int, option: int, value: int) -> int:
 
 
 def vla_prefill_destroy(ctx: Optional[int]) -> None:
+    if ctx:
+        _LIVE.pop(ctx, None)
     lib().vla_prefill_destroy(ctx)
 
 

@@ -156,6 +156,7 @@ struct vla_ctx {
     int gemm_tile = 0;  // VLA_OPT_GEMM_TILE
     hipStream_t own_stream = nullptr;
     hipStream_t stream = nullptr;
+    hipEvent_t switch_ev = nullptr;  // orders a newly set stream after the previous one
     bool use_graph = true;
     bool w8 = false;
     bool gu4 = false;   // gate/up in MXFP4 (the other block linears E4M3)
@@ -1035,6 +1036,19 @@ int set_args(vla_ctx* c, const void* pk, const void* pv, const float* noise, con
     return VLA_OK;
 }
 
+// Make `next` the context's stream. Its buffers (argument block, working
+// buffers, graphs) are shared by every call, so work later enqueued on `next`
+// must not start before what is already enqueued on the previous stream:
+// an event recorded there is waited on by `next`.
+int switch_stream(vla_ctx* c, hipStream_t next) {
+    if (next == c->stream) return VLA_OK;
+    if (!c->switch_ev) HIPC(hipEventCreateWithFlags(&c->switch_ev, hipEventDisableTiming));
+    HIPC(hipEventRecord(c->switch_ev, c->stream));
+    HIPC(hipStreamWaitEvent(next, c->switch_ev, 0));
+    c->stream = next;
+    return VLA_OK;
+}
+
 void destroy_ctx(vla_ctx* c) {
     if (!c) return;
     (void)hipStreamSynchronize(c->stream);  // the caller's stream, or the legacy default stream
@@ -1043,6 +1057,7 @@ void destroy_ctx(vla_ctx* c) {
     c->graphs.clear();
     for (void* p : c->allocs) (void)hipFree(p);
     c->allocs.clear();
+    if (c->switch_ev) (void)hipEventDestroy(c->switch_ev);
     if (c->own_stream) (void)hipStreamDestroy(c->own_stream);
     delete c;
 }
@@ -1325,8 +1340,8 @@ int vla_set_stream(vla_ctx* c, void* stream) {
         set_err("ctx is NULL");
         return VLA_ERR_ARG;
     }
-    c->stream = (hipStream_t)stream;
-    return VLA_OK;
+    HIPC(hipSetDevice(c->device));
+    return switch_stream(c, (hipStream_t)stream);
 }
 
 int vla_set_option(vla_ctx* c, int option, int value) {
@@ -1966,8 +1981,8 @@ int vla_prefill_set_stream(vla_prefill_ctx* x, void* stream) {
         set_err("ctx is NULL");
         return VLA_ERR_ARG;
     }
-    x->c->stream = (hipStream_t)stream;
-    return VLA_OK;
+    HIPC(hipSetDevice(x->c->device));
+    return switch_stream(x->c, (hipStream_t)stream);
 }
 
 int vla_prefill_set_option(vla_prefill_ctx* x, int option, int value) {

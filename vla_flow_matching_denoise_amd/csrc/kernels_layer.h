@@ -64,11 +64,13 @@ VLA_DEV void prefetch_rank(int lin, int base, int n, int* xcd, int* rank, int* p
 
 // ---------------------------------------------------------------------------
 // Fused residual + AdaRMSNorm, one workgroup (256 threads) per token row,
-// H <= 2048, S <= 8:
+// H <= 2048, any number S of split-K partials:
 //   h += gate * sum_z ws[z]        (when S > 0: split-K partials of O or down)
 //   y  = h / sqrt(mean(h^2) + eps) * (1 + scale) + shift  -> bf16 y and/or fp32 yf
-// Every load is issued before the first use, so a row costs one memory round
-// trip plus the reduction.
+// Every load of the first RN_MAXS partials is issued before the first use, so
+// a row costs one memory round trip plus the reduction; partials past
+// RN_MAXS (only very deep or very narrow down projections split that far)
+// are added by a second loop.
 // ---------------------------------------------------------------------------
 constexpr int RN_MAXS = 8;
 
@@ -118,6 +120,10 @@ __global__ __launch_bounds__(256) void resnorm_kernel(float* __restrict__ h, con
                     if (z < S) {
                         acc.x += part[j][z].x; acc.y += part[j][z].y; acc.z += part[j][z].z; acc.w += part[j][z].w;
                     }
+                for (int z = RN_MAXS; z < S; ++z) {
+                    const float4 t = *(const float4*)(ws + ((size_t)z * M + row) * H + c);
+                    acc.x += t.x; acc.y += t.y; acc.z += t.z; acc.w += t.w;
+                }
                 v[j].x += g[j].x * acc.x; v[j].y += g[j].y * acc.y; v[j].z += g[j].z * acc.z; v[j].w += g[j].w * acc.w;
                 *(float4*)(hr + c) = v[j];
             }

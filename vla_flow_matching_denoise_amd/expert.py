@@ -84,7 +84,8 @@ class Expert:
 
     @property
     def persistent_active(self) -> bool:
-        """True when calls run as one persistent cooperative kernel."""
+        """True when calls run as the single persistent kernel (one launch of
+        one workgroup per CU, all resident together)."""
         return B.vla_get_option(self.ctx, B.VLA_OPT_PERSISTENT_ACTIVE) == 1
 
     def denoise(self, prefix_k, prefix_v, noise, t_schedule, n_steps: int, out=None, prefix_valid=None):
