@@ -10,10 +10,20 @@ accumulation). ``value`` is denoise steps per second (Euler steps of the whole
 batch per second); chunks per second are reported beside it.
 
 Also reported:
-  * ``roofline``: the dominant kernel's algorithmic bytes (or flops) per launch
-    over its mean launch time, measured with HIP events around each launch;
-  * ``cpu_baseline``: the fp64 CPU oracle timed on a bounded sample;
-  * ``batch64``: the batched-replica workload (64 requests, GEMM M = 3200);
+  * ``call_roofline``: the whole call's algorithmic bytes (batch 1) or flops
+    (batch 64) over its time, against the HBM or bf16 MFMA peak, with the
+    target fraction beside it;
+  * ``roofline``: the kernel family that takes the largest share of a layer's
+    time, its algorithmic bytes (or flops) per launch over its mean launch
+    time, measured with HIP events around each launch; ``roofline_worst`` is
+    the family furthest below its roofline;
+  * ``cpu_baseline``: the CPU oracle (its fp32 twin: the same code on float32
+    inputs) on a bounded sample of every workload, on all cores of the
+    process's affinity mask and, for the two batch-1 bf16 workloads of the
+    smallest sizes, on one thread; the fp64 oracle once for reference;
+  * ``v2_b1``, ``fp8_b1``, ``batch64``: the V2-shaped 50-step loop, the E4M3
+    weight tier (25 steps) and the batched-replica workload (64 requests,
+    GEMM M = 3200), each with its call roofline;
   * ``prefill``: the prefix K/V construction that precedes the loop (the
     36-layer LingBot-shaped backbone over a 256-token prefix) at 1 and 16
     requests per call, as tokens per second with its weight-streaming and
@@ -38,13 +48,22 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
 
-# HBM traffic of the dominant batch-1 kernel (the gate_up + SwiGLU skinny GEMM,
-# skinny_gemm_kernel<0, 3>) from rocprofv3 FETCH_SIZE / WRITE_SIZE counter
-# runs, scaled by what the counters read for a plain copy of known size. The
-# summary records a hash of the kernel sources; once they change, the figure
-# no longer describes the kernel and `traffic` is reported as null.
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "gate_up_swiglu_gemm_lingbot_b1_counters.txt")
-TRAFFIC_KERNEL = "skinny_gemm_kernel<0, 3>"
+CALL_TARGET = {"hbm": 0.70, "mfma": 0.50}   # batch-1 HBM and batch-64 bf16 MFMA fractions aimed at
+
+# HBM traffic of each kernel family of the batch-1 layer from rocprofv3
+# FETCH_SIZE / WRITE_SIZE counter runs, scaled by what the counters read for a
+# plain copy of known size. The summary records a hash of the kernel sources;
+# once they change, the figures no longer describe the kernels and `traffic`
+# is reported as null.
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "layer_kernels_lingbot_b1_counters.txt")
+# kernel family -> (kernel name in the trace, which of that name's launches per layer)
+TRAFFIC_KERNELS = {
+    "qkv_rope_gemm": ("skinny_gemm_kernel<0, 2>", 0, 1),
+    "gqa_attention": ("attn_kernel<", 0, 1),
+    "o_proj_gemm": ("skinny_gemm_kernel<0, 4>", 0, 2),
+    "gate_up_swiglu_gemm": ("skinny_gemm_kernel<0, 3>", 0, 1),
+    "down_gemm": ("skinny_gemm_kernel<0, 4>", 1, 2),
+}
 KERNEL_SOURCES = ("vla_flow_matching_denoise_amd/csrc/common.h", "vla_flow_matching_denoise_amd/csrc/kernels_layer.h")
 COPY_BYTES = 256 << 20
 
@@ -108,19 +127,22 @@ def kernel_rooflines(ex, cfg, iters):
     return res
 
 
-def dominant(res, bound, mfma_peak=BF16_PEAK_TFLOPS):
-    """The kernel family carrying the largest share of the path's algorithmic
-    bytes (HBM-bound) or flops (MFMA-bound); every family runs once per layer."""
-    key = "bytes" if bound == "hbm" else "flops"
-    name = max(res, key=lambda n: res[n][key])
-    r = res[name]
+def _roof(name, r, bound, mfma_peak):
     if bound == "hbm":
         ach, peak, unit = r["GBps"], HBM_PEAK_GBS, "GB/s"
     else:
         ach, peak, unit = r["TFLOPs"], mfma_peak, "TFLOP/s"
-    return name, {"bound": bound, "kernel": name, "achieved": round(ach, 2), "peak": peak, "unit": unit,
-                  "frac": round(ach / peak, 4), "traffic": None, "us_per_launch": round(r["us"], 3),
-                  "algorithmic_bytes_per_launch": int(r["bytes"]), "algorithmic_flops_per_launch": int(r["flops"])}
+    return {"bound": bound, "kernel": name, "achieved": round(ach, 2), "peak": peak, "unit": unit,
+            "frac": round(ach / peak, 4), "traffic": None, "us_per_launch": round(r["us"], 3),
+            "algorithmic_bytes_per_launch": int(r["bytes"]), "algorithmic_flops_per_launch": int(r["flops"])}
+
+
+def dominant(res, bound, mfma_peak=BF16_PEAK_TFLOPS):
+    """The kernel family with the largest share of a layer's time (every family
+    runs once per layer), and the family furthest below its roofline."""
+    name = max(res, key=lambda n: res[n]["us"])
+    worst = min(res, key=lambda n: _roof(n, res[n], bound, mfma_peak)["frac"])
+    return name, _roof(name, res[name], bound, mfma_peak), _roof(worst, res[worst], bound, mfma_peak)
 
 
 def kernel_source_hash() -> str:
@@ -131,9 +153,9 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic():
-    """Bytes per launch from the committed counter summary, or None when absent
-    or taken on kernel sources other than the current ones."""
+def recorded_traffic(family):
+    """Bytes per launch of a kernel family from the committed counter summary,
+    or None when absent or taken on kernel sources other than the current ones."""
     if not os.path.exists(TRAFFIC_SUMMARY):
         return None
     fields = {}
@@ -145,14 +167,15 @@ def recorded_traffic():
     if fields.get("source_sha256_16") != kernel_source_hash():
         return None
     try:
-        return int(float(fields["traffic_bytes_per_launch"]))
+        return int(float(fields[f"traffic_bytes_per_launch.{family}"]))
     except (KeyError, ValueError):
         return None
 
 
 def counter_run(iters):
     """Workload of the counter runs: a plain copy of COPY_BYTES (calibration),
-    then whole layers of the batch-1 workload with the gate_up GEMM inside."""
+    then `iters` whole layers of the batch-1 workload (every kernel family of
+    the layer launches once per layer)."""
     import torch
     import synth
     from vla_flow_matching_denoise_amd import binding as B
@@ -183,11 +206,13 @@ def _counter_rows(d):
 
 
 def _per_dispatch(rows, counter, match):
+    """Counter value per dispatch (summed over its instances), in dispatch order."""
     vals = {}
     for r in rows:
         if r.get("Counter_Name") == counter and match(r.get("Kernel_Name", "")):
-            vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
-    return list(vals.values())
+            d = int(r["Dispatch_Id"])
+            vals[d] = vals.get(d, 0.0) + float(r["Counter_Value"])
+    return [vals[d] for d in sorted(vals)]
 
 
 def traffic_from(fetch_dir, write_dir, cmd_fetch, cmd_write):
@@ -196,19 +221,21 @@ def traffic_from(fetch_dir, write_dir, cmd_fetch, cmd_write):
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _counter_rows(d)
         copy = _per_dispatch(rows, name, lambda k: "copy" in k.lower())
-        gemm = _per_dispatch(rows, name, lambda k: TRAFFIC_KERNEL in k)
-        if not copy or not gemm:
-            raise SystemExit(f"{name}: copy dispatches {len(copy)}, gate_up dispatches {len(gemm)}")
-        kib_copy = max(copy)
-        scale = (COPY_BYTES / 1024.0) / kib_copy      # bytes of KiB reported, per counted KiB
-        out[name] = {"copy_kib": kib_copy, "scale": scale, "gemm_kib_mean": float(np.mean(gemm)),
-                     "gemm_bytes": float(np.mean(gemm)) * scale * 1024.0, "n": len(gemm)}
-    total = out["FETCH_SIZE"]["gemm_bytes"] + out["WRITE_SIZE"]["gemm_bytes"]
+        if not copy:
+            raise SystemExit(f"{name}: no copy dispatches")
+        scale = (COPY_BYTES / 1024.0) / max(copy)      # bytes of KiB reported, per counted KiB
+        out[name] = {"copy_kib": max(copy), "scale": scale, "fam": {}}
+        for fam, (kname, which, per_layer) in TRAFFIC_KERNELS.items():
+            vals = _per_dispatch(rows, name, lambda k, kname=kname: kname in k)[which::per_layer]
+            if not vals:
+                raise SystemExit(f"{name}: no dispatches of {kname}")
+            out[name]["fam"][fam] = (float(np.mean(vals)), len(vals))
     lines = [
-        "# HBM traffic of the gate_up + SwiGLU skinny GEMM (skinny_gemm_kernel<0, 3>),",
-        "# LingBot-shaped batch-1 workload (M = 50 rows, N = 8192, K = 1024, bf16 weights).",
+        "# HBM traffic per launch of each kernel family of one expert layer,",
+        "# LingBot-shaped batch-1 workload (M = 50 rows, hidden 1024, 16/2 heads of 128, SwiGLU 4096, prefix 256).",
         "# Two rocprofv3 counter runs of `python bench.py --counter-run`, each scaled by the",
         "# counter's reading for a plain device copy of 256 MiB (read 256 MiB, write 256 MiB).",
+        "# O and down share one kernel instance: launches alternate O, down within a layer.",
         f"# fetch command: {cmd_fetch}",
         f"# write command: {cmd_write}",
         f"# summary: python bench.py --traffic-from <fetch dir> <write dir>",
@@ -216,14 +243,14 @@ def traffic_from(fetch_dir, write_dir, cmd_fetch, cmd_write):
         f"copy_write_kib: {out['WRITE_SIZE']['copy_kib']:.1f}",
         f"fetch_scale: {out['FETCH_SIZE']['scale']:.4f}",
         f"write_scale: {out['WRITE_SIZE']['scale']:.4f}",
-        f"gate_up_dispatches: {out['FETCH_SIZE']['n']}",
-        f"gate_up_fetch_kib_mean: {out['FETCH_SIZE']['gemm_kib_mean']:.1f}",
-        f"gate_up_write_kib_mean: {out['WRITE_SIZE']['gemm_kib_mean']:.1f}",
-        f"fetch_bytes_per_launch: {out['FETCH_SIZE']['gemm_bytes']:.0f}",
-        f"write_bytes_per_launch: {out['WRITE_SIZE']['gemm_bytes']:.0f}",
-        f"traffic_bytes_per_launch: {total:.0f}",
-        f"source_sha256_16: {kernel_source_hash()}",
     ]
+    for fam in TRAFFIC_KERNELS:
+        fk, n = out["FETCH_SIZE"]["fam"][fam]
+        wk, _ = out["WRITE_SIZE"]["fam"][fam]
+        fb, wb = fk * out["FETCH_SIZE"]["scale"] * 1024.0, wk * out["WRITE_SIZE"]["scale"] * 1024.0
+        lines += [f"dispatches.{fam}: {n}", f"fetch_kib_mean.{fam}: {fk:.1f}", f"write_kib_mean.{fam}: {wk:.1f}",
+                  f"traffic_bytes_per_launch.{fam}: {fb + wb:.0f}"]
+    lines.append(f"source_sha256_16: {kernel_source_hash()}")
     with open(TRAFFIC_SUMMARY, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -309,34 +336,211 @@ def build_inputs(cfg, seed=0):
     return tuple(to_device(a) for a in (pk, pv, x0, ts)), (pk, pv, x0, ts)
 
 
-def cpu_baseline(cfg, raw, host_inputs, budget_s):
-    """The fp64 oracle, as it stands, on one request: whole denoise calls of the workload's Euler
-    schedule, repeated until about `budget_s` of CPU work (fewer steps if one call alone is longer)."""
+def gpu_inputs(cfg, seed=0):
+    """Inputs of the workload's shapes drawn on the GPU (prefix K/V and noise
+    N(0, 1), the uniform schedule): for legs whose values do not change the
+    timing."""
+    import torch
+    import synth
+    from vla_flow_matching_denoise_amd.expert import to_device
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    shp = (cfg.batch, cfg.n_layers, cfg.prefix_len, cfg.n_kv_heads, cfg.head_dim)
+    pk = torch.randn(shp, device="cuda", generator=g).to(torch.bfloat16).view(torch.int16)
+    pv = torch.randn(shp, device="cuda", generator=g).to(torch.bfloat16).view(torch.int16)
+    x0 = torch.randn((cfg.batch, cfg.horizon, cfg.action_dim), device="cuda", generator=g)
+    return pk, pv, x0, to_device(synth.make_schedule(cfg.n_steps, cfg.batch))
+
+
+def gpu_expert_weights(cfg, seed=0):
+    """Random-init bf16 expert weights of the workload's shapes drawn on the GPU
+    (N(0, std^2) linears and biases; the values do not change the timing)."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    H, A, E, L, I = cfg.hidden, cfg.action_dim, cfg.time_emb_dim, cfg.n_layers, cfg.intermediate
+    qd, kvd = cfg.n_q_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+
+    def w(*shape):
+        return (cfg.weight_std * torch.randn(shape, device="cuda", generator=g)).to(torch.bfloat16).view(torch.int16)
+
+    def b(n):
+        return cfg.weight_std * torch.randn(n, device="cuda", generator=g)
+
+    W = {"in_w": w(H, A), "in_b": b(H), "out_w": w(A, H), "out_b": b(A), "t1_w": w(H, E), "t1_b": b(H),
+         "t2_w": w(H, H), "t2_b": b(H), "modf_w": w(2 * H, H), "modf_b": b(2 * H),
+         "mod_w": [w(6 * H, H) for _ in range(L)], "mod_b": [b(6 * H) for _ in range(L)]}
+    shapes = {"wq": (qd, H), "wk": (kvd, H), "wv": (kvd, H), "wo": (H, qd), "wg": (I, H), "wu": (I, H),
+              "wd": (H, I)}
+    for n, shp in shapes.items():
+        W[n] = [w(*shp) for _ in range(L)]
+    return W
+
+
+def leg(ex, cfg, dev_in, warmup, steps, bound="hbm", peak=None):
+    """Times `steps` calls of one workload; rates and the call roofline."""
+    wall, per_call, _ = time_calls(ex, dev_in, cfg.n_steps, warmup, steps)
+    t = wall / steps
+    by, fl = call_work(cfg)
+    if bound == "hbm":
+        ach, pk, unit, work = by / t / 1e9, HBM_PEAK_GBS, "GB/s", {"algorithmic_bytes": int(by)}
+    else:
+        ach, pk, unit, work = fl / t / 1e12, peak or BF16_PEAK_TFLOPS, "TFLOP/s", {"algorithmic_tflop": round(fl / 1e12, 3)}
+    return {"ms_per_call": round(t * 1e3, 4), "steps_per_s": round(cfg.n_steps / t, 3),
+            "chunks_per_s": round(cfg.batch / t, 3),
+            "p50_ms": round(float(np.percentile(per_call, 50)), 4),
+            "p95_ms": round(float(np.percentile(per_call, 95)), 4),
+            "call_roofline": {"bound": bound, **work, "achieved": round(ach, 1), "peak": pk, "unit": unit,
+                              "frac": round(ach / pk, 4)}}
+
+
+# ------------------------------- CPU baseline --------------------------------
+
+def cpu_model() -> str:
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return "unknown"
+
+
+def random_decoded_weights(cfg, dtype=np.float32, seed=0):
+    """Float weights of the workload's shapes, N(0, std^2), in the layout the
+    oracle takes after decoding (for timing a workload whose encoded weights
+    are not on the host; the values do not change the CPU time)."""
+    r = np.random.default_rng([seed, 7, cfg.model_tag])
+    H, A, E, L, I = cfg.hidden, cfg.action_dim, cfg.time_emb_dim, cfg.n_layers, cfg.intermediate
+    qd, kvd = cfg.n_q_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+
+    def g(*shape):
+        return (r.standard_normal(shape, dtype=np.float32) * np.float32(cfg.weight_std)).astype(dtype)
+
+    W = {"in_w": g(H, A), "in_b": g(H), "out_w": g(A, H), "out_b": g(A), "t1_w": g(H, E), "t1_b": g(H),
+         "t2_w": g(H, H), "t2_b": g(H), "modf_w": g(2 * H, H), "modf_b": g(2 * H),
+         "mod_w": [g(6 * H, H) for _ in range(L)], "mod_b": [g(6 * H) for _ in range(L)]}
+    shapes = {"wq": (qd, H), "wk": (kvd, H), "wv": (kvd, H), "wo": (H, qd), "wg": (I, H), "wu": (I, H),
+              "wd": (H, I)}
+    for n, shp in shapes.items():
+        W[n] = [g(*shp) for _ in range(L)]
+    return W
+
+
+def _oracle_steps_per_s(W, cfg, n_steps, dtype, min_s=2.0):
+    """One request of `cfg` through the oracle: one untimed call, then calls
+    of `n_steps` Euler steps until at least `min_s`; returns (Euler steps per
+    second of one request, seconds, calls)."""
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count()
-    pk, pv, x0, _ = host_inputs
-    W = oracle.decode_weights(raw)
     d = oracle.ExpertDims.from_config(cfg)
-    fpk, fpv = oracle.decode_bf16(pk[:1]), oracle.decode_bf16(pv[:1])
-    one = synth.make_schedule(1, 1)
-    t0 = time.perf_counter()
-    oracle.denoise(W, d, fpk, fpv, x0[:1], one)
-    t1 = max(time.perf_counter() - t0, 1e-3)
-    n = max(1, min(cfg.n_steps, int(budget_s / t1)))
-    reps = max(1, int(budget_s / (t1 * cfg.n_steps))) if n == cfg.n_steps else 1
-    ts = synth.make_schedule(n, 1)
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        oracle.denoise(W, d, fpk, fpv, x0[:1], ts)
-    dt = time.perf_counter() - t0
-    return {"value": round(reps * n / dt, 4), "unit": "denoise_steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"1 request of the {cfg.name} workload, {reps} call(s) of {n} Euler step(s) "
-                      f"(36 layers each), fp64 numpy oracle, {dt:.1f} s"}
+    r = np.random.default_rng(3)
+    pk = r.standard_normal((1, cfg.n_layers, cfg.prefix_len, cfg.n_kv_heads, cfg.head_dim)).astype(dtype)
+    pv = r.standard_normal(pk.shape).astype(dtype)
+    x0 = r.standard_normal((1, cfg.horizon, cfg.action_dim)).astype(np.float32)
+    ts = synth.make_schedule(n_steps, 1)
+    oracle.denoise(W, d, pk, pv, x0, ts)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.denoise(W, d, pk, pv, x0, ts)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_s:
+            return reps * n_steps / dt, dt, reps
+
+
+def cpu_baselines(raw2, raw4):
+    """The oracle as it stands on the host CPU: its fp32 twin (the same code on
+    float32 weights and inputs) on a bounded sample of every workload (one
+    request; whole 10-step calls of the tiny workload, single Euler steps of
+    the 36-layer ones, converted to the workload's steps/s and chunks/s), with
+    the BLAS threads set to every core of the process's affinity mask, and on
+    one thread for the tiny and LingBot batch-1 workloads; the fp64 oracle once
+    on the LingBot workload."""
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_limits
+    cores = len(os.sched_getaffinity(0))
+    model = cpu_model()
+    t_start = time.perf_counter()
+    per, one = {}, {}
+
+    def rates(cfg, sps_one_request):
+        # requests are independent: a batch step of B requests costs B single-request
+        # steps, and a request finishes after the workload's N steps
+        return {"steps_per_s": round(sps_one_request / cfg.batch, 4),
+                "chunks_per_s": round(sps_one_request / cfg.n_steps, 5)}
+
+    c1 = synth.config(1)
+    W1 = oracle.decode_weights(synth.make_weights(c1), np.float32)
+    c2 = synth.config(2)
+    W2 = oracle.decode_weights(raw2, np.float32)
+    with threadpool_limits(cores):
+        sps, dt, n = _oracle_steps_per_s(W1, c1, c1.n_steps, np.float32)
+        per["tiny_b1"] = {**rates(c1, sps), "sample": f"{n} call(s) of 10 steps, {dt:.2f} s"}
+        sps2, dt, n = _oracle_steps_per_s(W2, c2, 1, np.float32)
+        per["lingbot_b1"] = {**rates(c2, sps2), "sample": f"{n} Euler step(s) of 36 layers, {dt:.2f} s"}
+        c5 = synth.config(5)
+        per["lingbot_b64"] = {**rates(c5, sps2), "sample": "one request's Euler step (as lingbot_b1) x 64 requests"}
+        c4 = synth.config(4)
+        W4 = oracle.decode_weights(raw4, np.float32)
+        sps4, dt, n = _oracle_steps_per_s(W4, c4, 1, np.float32)
+        per["lingbot_fp8_b1"] = {**rates(c4, sps4),
+                                 "sample": f"{n} Euler step(s), E4M3 weights decoded to fp32, {dt:.2f} s"}
+        del W4
+        c3 = synth.config(3)
+        W3 = random_decoded_weights(c3, np.float32)
+        sps3, dt, n = _oracle_steps_per_s(W3, c3, 1, np.float32)
+        per["v2_b1"] = {**rates(c3, sps3), "sample": f"{n} Euler step(s) of 36 layers (hidden 1536, prefix 512), "
+                                                     f"{dt:.2f} s"}
+        del W3
+    with threadpool_limits(1):
+        sps, dt, n = _oracle_steps_per_s(W1, c1, c1.n_steps, np.float32)
+        one["tiny_b1"] = {**rates(c1, sps), "sample": f"{n} call(s) of 10 steps, {dt:.2f} s"}
+        sps, dt, n = _oracle_steps_per_s(W2, c2, 1, np.float32)
+        one["lingbot_b1"] = {**rates(c2, sps), "sample": f"{n} Euler step(s), {dt:.2f} s"}
+    del W2
+    W64 = oracle.decode_weights(raw2, np.float64)
+    with threadpool_limits(cores):
+        sps64, dt, n = _oracle_steps_per_s(W64, c2, 1, np.float64)
+    del W64
+    return {"value": per["lingbot_b1"]["steps_per_s"], "unit": "denoise_steps/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "fp32 twin of the oracle, one request of the LingBot batch-1 workload, "
+                      + per["lingbot_b1"]["sample"],
+            "cpu_model": model, "blas_threads": cores,
+            "per_workload": per, "one_thread": one,
+            "fp64_lingbot_b1": {"steps_per_s": round(sps64, 4), "sample": f"{n} Euler step(s), {dt:.2f} s"},
+            "total_s": round(time.perf_counter() - t_start, 1)}
+
+
+# ------------------------------- batch-64 counters ---------------------------
+
+def counter_run_b64(iters):
+    """Workload of the batch-64 MFMA counter runs: whole layers of the batch-64
+    workload with bf16 weights, then with E4M3 weights and per-token E4M3
+    activations (every GEMM of the layer launches once per layer)."""
+    import torch
+    import synth
+    from vla_flow_matching_denoise_amd import binding as B
+    from vla_flow_matching_denoise_amd.expert import Expert, dims_from_config
+    torch.cuda.set_device(0)
+    for wd in ("bf16", "fp8_e4m3"):
+        cfg = synth.config(5).replace(weight_dtype=wd)
+        ex = Expert(synth.make_weights(cfg, seed=0), dims_from_config(cfg))
+        dev_in = gpu_inputs(cfg)
+        ex.denoise(*dev_in, cfg.n_steps)
+        torch.cuda.synchronize()
+        B.vla_profile_kernel(ex.ctx, B.VLA_KERNEL_GATE_UP, iters)
+        torch.cuda.synchronize()
+        ex.close()
+        log(f"[bench] batch-64 counter run ({wd}) done: {iters} layers")
 
 
 def main():
@@ -345,13 +549,15 @@ def main():
     ap.add_argument("--steps", type=int, default=30, help="timed denoise calls")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--profile-iters", type=int, default=144)
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batch64", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the V2, E4M3, MXFP4 and persistent legs")
     ap.add_argument("--prefill-only", action="store_true", help="time only the prefill leg (for kernel profiles)")
     ap.add_argument("--counter-run", action="store_true",
-                    help="run only the workload of the rocprofv3 counter runs (copy calibration + layers)")
+                    help="run only the workload of the batch-1 rocprofv3 counter runs (copy calibration + layers)")
+    ap.add_argument("--counter-run-b64", action="store_true",
+                    help="run only the workload of the batch-64 MFMA counter runs")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from two rocprofv3 --pmc output folders")
     ap.add_argument("--traffic-cmds", nargs=2, metavar=("FETCH_CMD", "WRITE_CMD"), default=("?", "?"))
@@ -368,6 +574,9 @@ def main():
 
     if args.counter_run:
         counter_run(72)
+        return
+    if args.counter_run_b64:
+        counter_run_b64(36)
         return
 
     import torch
@@ -386,38 +595,22 @@ def main():
     ex = Expert(raw, dims_from_config(cfg))
     dev_in, host_in = build_inputs(cfg)
     log(f"[bench] timing {args.steps} calls of {cfg.n_steps} Euler steps (warmup {args.warmup})")
-    wall, per_call, _ = time_calls(ex, dev_in, cfg.n_steps, args.warmup, args.steps)
-    t_call = wall / args.steps
-    bytes_call, flops_call = call_work(cfg)
+    head = leg(ex, cfg, dev_in, args.warmup, args.steps)
+    t_call = head["ms_per_call"] / 1e3
     kr = kernel_rooflines(ex, cfg, args.profile_iters)
-    _, roof = dominant(kr, "hbm")
-    roof["traffic"] = recorded_traffic()
-    # the opt-in persistent single-launch path on the same workload
-    ex.set_option(B.VLA_OPT_PERSISTENT, 1)
+    dom, roof, worst = dominant(kr, "hbm")
+    roof["traffic"] = recorded_traffic(dom)
+    worst["traffic"] = recorded_traffic(worst["kernel"])
     persistent = None
-    if ex.persistent_active:
-        wall_p, pc_p, _ = time_calls(ex, dev_in, cfg.n_steps, args.warmup, args.steps)
-        tp = wall_p / args.steps
-        persistent = {"ms_per_call": round(tp * 1e3, 4), "steps_per_s": round(cfg.n_steps * cfg.batch / tp, 3),
-                      "p50_ms": round(float(np.percentile(pc_p, 50)), 4)}
-    ex.set_option(B.VLA_OPT_PERSISTENT, 0)
+    if not args.no_extra:
+        # the opt-in persistent single-launch path on the same workload
+        ex.set_option(B.VLA_OPT_PERSISTENT, 1)
+        if ex.persistent_active:
+            persistent = leg(ex, cfg, dev_in, args.warmup, args.steps)
+            persistent["status"] = ex.get_option(B.VLA_OPT_PERSISTENT_STATUS)
+        ex.set_option(B.VLA_OPT_PERSISTENT, 0)
     ex.close()
-    # the same batch-1 workload with E4M3 block linears and MXFP4 gate/up
-    cfg4 = synth.config(4).replace(weight_dtype="fp8_mxfp4gu", n_steps=cfg.n_steps)
-    log("[bench] batch-1 E4M3 + MXFP4 gate_up workload")
-    ex4 = Expert(synth.make_weights(cfg4, seed=0), dims_from_config(cfg4))
-    dev4, _ = build_inputs(cfg4)
-    wall4, _, _ = time_calls(ex4, dev4, cfg4.n_steps, args.warmup, args.steps)
-    t4 = wall4 / args.steps
-    kr4 = kernel_rooflines(ex4, cfg4, args.profile_iters)
-    ex4.close()
-    mxfp4 = {"workload": "lingbot_36L_h1024_chunk50x75_euler10_b1_e4m3_mxfp4_gate_up",
-             "ms_per_call": round(t4 * 1e3, 4), "steps_per_s": round(cfg4.n_steps / t4, 3),
-             "gate_up": {"us": round(kr4["gate_up_swiglu_gemm"]["us"], 3),
-                         "algorithmic_bytes": int(kr4["gate_up_swiglu_gemm"]["bytes"]),
-                         "GBps": round(kr4["gate_up_swiglu_gemm"]["GBps"], 1),
-                         "frac": round(kr4["gate_up_swiglu_gemm"]["GBps"] / HBM_PEAK_GBS, 4)}}
-
+    cr = head.pop("call_roofline")
     result = {
         "metric": METRIC,
         "value": round(cfg.n_steps * cfg.batch / t_call, 3),
@@ -434,18 +627,59 @@ def main():
         "config": {"workload": "lingbot_36L_h1024_gqa16x2x128_swiglu4096_prefix256_chunk50x75_euler10_b1",
                    "batch": cfg.batch, "euler_steps": cfg.n_steps, "chunk": [cfg.horizon, cfg.action_dim],
                    "prefix_len": cfg.prefix_len},
-        "chunks_per_s": round(cfg.batch / t_call, 3),
-        "p50_ms": round(float(np.percentile(per_call, 50)), 4),
-        "p95_ms": round(float(np.percentile(per_call, 95)), 4),
-        "call_roofline": {"bound": "hbm", "algorithmic_bytes": int(bytes_call),
-                          "achieved_GBps": round(bytes_call / t_call / 1e9, 1),
-                          "frac": round(bytes_call / t_call / 1e9 / HBM_PEAK_GBS, 4)},
+        "chunks_per_s": head["chunks_per_s"],
+        "p50_ms": head["p50_ms"],
+        "p95_ms": head["p95_ms"],
+        "call_roofline": {**cr, "target_frac": CALL_TARGET["hbm"],
+                          "target_steps_per_s": round(CALL_TARGET["hbm"] * cfg.n_steps / (cr["algorithmic_bytes"]
+                                                      / (HBM_PEAK_GBS * 1e9)), 1)},
         "roofline": roof,
-        "kernels": {k: {"us": round(v["us"], 3), "GBps": round(v["GBps"], 1), "TFLOPs": round(v["TFLOPs"], 2)}
-                    for k, v in kr.items()},
+        "roofline_worst": worst,
+        "kernels": {k: {"us": round(v["us"], 3), "GBps": round(v["GBps"], 1), "TFLOPs": round(v["TFLOPs"], 2),
+                        "hbm_frac": round(v["GBps"] / HBM_PEAK_GBS, 4)} for k, v in kr.items()},
         "persistent_b1": persistent,
-        "b1_e4m3_mxfp4_gate_up": mxfp4,
     }
+
+    if not args.no_extra:
+        # V2-shaped loop: hidden 1536, SwiGLU 6144, prefix 512, chunk 50x55, 50 Euler steps
+        cfg3 = synth.config(3)
+        log("[bench] V2-shaped workload (weights drawn on the GPU)")
+        ex3 = Expert(gpu_expert_weights(cfg3), dims_from_config(cfg3))
+        torch.cuda.synchronize()
+        result["v2_b1"] = {"workload": "v2_36L_h1536_gqa16x2x128_swiglu6144_prefix512_chunk50x55_euler50_b1",
+                           **leg(ex3, cfg3, gpu_inputs(cfg3), 2, max(5, args.steps // 3))}
+        ex3.close()
+        torch.cuda.empty_cache()
+        # E4M3 weight tier: per-row E4M3 block linears, bf16 activations, 25 steps
+        cfg4 = synth.config(4)
+        log("[bench] E4M3-weight batch-1 workload")
+        raw4 = synth.make_weights(cfg4, seed=0)
+        ex4 = Expert(raw4, dims_from_config(cfg4))
+        dev4, _ = build_inputs(cfg4)
+        result["fp8_b1"] = {"workload": "lingbot_36L_h1024_e4m3_weights_bf16_activations_chunk50x75_euler25_b1",
+                            "dtype": "e4m3 weights, bf16 activations, f32 accumulation",
+                            **leg(ex4, cfg4, dev4, args.warmup, args.steps)}
+        kr4 = kernel_rooflines(ex4, cfg4, args.profile_iters)
+        result["fp8_b1"]["kernels"] = {k: {"us": round(v["us"], 3), "GBps": round(v["GBps"], 1)} for k, v in kr4.items()}
+        ex4.close()
+        # the same batch-1 workload with E4M3 block linears and MXFP4 gate/up
+        cfgm = synth.config(4).replace(weight_dtype="fp8_mxfp4gu", n_steps=cfg.n_steps)
+        log("[bench] batch-1 E4M3 + MXFP4 gate_up workload")
+        exm = Expert(synth.make_weights(cfgm, seed=0), dims_from_config(cfgm))
+        devm, _ = build_inputs(cfgm)
+        lm = leg(exm, cfgm, devm, args.warmup, args.steps)
+        krm = kernel_rooflines(exm, cfgm, args.profile_iters)
+        exm.close()
+        lm.pop("call_roofline")
+        result["b1_e4m3_mxfp4_gate_up"] = {
+            "workload": "lingbot_36L_h1024_chunk50x75_euler10_b1_e4m3_mxfp4_gate_up", **lm,
+            "gate_up": {"us": round(krm["gate_up_swiglu_gemm"]["us"], 3),
+                        "algorithmic_bytes": int(krm["gate_up_swiglu_gemm"]["bytes"]),
+                        "GBps": round(krm["gate_up_swiglu_gemm"]["GBps"], 1),
+                        "frac": round(krm["gate_up_swiglu_gemm"]["GBps"] / HBM_PEAK_GBS, 4)},
+            "e4m3_gate_up_us": round(kr4["gate_up_swiglu_gemm"]["us"], 3)}
+    else:
+        raw4 = None
 
     if not args.no_batch64:
         cfg5 = synth.config(5)
@@ -453,36 +687,29 @@ def main():
         ex5 = Expert(raw, dims_from_config(cfg5))
         dev5, _ = build_inputs(cfg5)
         n5 = max(3, args.steps // 5)
-        wall5, pc5, _ = time_calls(ex5, dev5, cfg5.n_steps, 2, n5)
-        t5 = wall5 / n5
-        b5, f5 = call_work(cfg5)
+        l5 = leg(ex5, cfg5, dev5, 2, n5, bound="mfma")
         kr5 = kernel_rooflines(ex5, cfg5, 36)
-        _, roof5 = dominant(kr5, "mfma")
+        _, roof5, worst5 = dominant(kr5, "mfma")
         ex5.close()
         result["batch64"] = {
-            "workload": "lingbot_36L_h1024_chunk50x75_euler10_b64", "steps_per_s": round(cfg5.n_steps / t5, 3),
-            "chunks_per_s": round(cfg5.batch / t5, 3), "ms_per_call": round(t5 * 1e3, 3),
-            "call_mfma_frac": round(f5 / t5 / 1e12 / BF16_PEAK_TFLOPS, 4), "algorithmic_tflop": round(f5 / 1e12, 3),
-            "roofline": roof5,
-            "kernels": {k: {"us": round(v["us"], 2), "TFLOPs": round(v["TFLOPs"], 1)} for k, v in kr5.items()},
+            "workload": "lingbot_36L_h1024_chunk50x75_euler10_b64", **l5,
+            "target_frac": CALL_TARGET["mfma"], "roofline": roof5, "roofline_worst": worst5,
+            "kernels": {k: {"us": round(v["us"], 2), "TFLOPs": round(v["TFLOPs"], 1),
+                            "mfma_frac": round(v["TFLOPs"] / BF16_PEAK_TFLOPS, 4)} for k, v in kr5.items()},
         }
         # the same batch with E4M3 block weights: per-token E4M3 activations and
         # the FP8 MFMA (its own tier; the bf16 figures above are the metric's)
         cfg8 = synth.config(4).replace(batch=cfg5.batch, n_steps=cfg5.n_steps)
         log("[bench] batch-64 E4M3 workload")
-        ex8 = Expert(synth.make_weights(cfg8, seed=0), dims_from_config(cfg8))
+        ex8 = Expert(raw4 if raw4 is not None else synth.make_weights(cfg8, seed=0), dims_from_config(cfg8))
         dev8, _ = build_inputs(cfg8)
-        wall8, _, _ = time_calls(ex8, dev8, cfg8.n_steps, 2, n5)
-        t8 = wall8 / n5
-        _, f8 = call_work(cfg8)
+        l8 = leg(ex8, cfg8, dev8, 2, n5, bound="mfma", peak=FP8_PEAK_TFLOPS)
         kr8 = kernel_rooflines(ex8, cfg8, 36)
-        _, roof8 = dominant(kr8, "mfma", FP8_PEAK_TFLOPS)
+        _, roof8, _ = dominant(kr8, "mfma", FP8_PEAK_TFLOPS)
         ex8.close()
         result["batch64_e4m3"] = {
             "workload": "lingbot_36L_h1024_chunk50x75_euler10_b64_e4m3_weights_per_token_e4m3_activations",
-            "dtype": "e4m3 x e4m3 -> f32", "steps_per_s": round(cfg8.n_steps / t8, 3),
-            "chunks_per_s": round(cfg8.batch / t8, 3), "ms_per_call": round(t8 * 1e3, 3),
-            "call_mfma_frac": round(f8 / t8 / 1e12 / FP8_PEAK_TFLOPS, 4), "roofline": roof8,
+            "dtype": "e4m3 x e4m3 -> f32", **l8, "roofline": roof8,
             "kernels": {k: {"us": round(v["us"], 2), "TFLOPs": round(v["TFLOPs"], 1)} for k, v in kr8.items()},
         }
 
@@ -500,7 +727,9 @@ def main():
 
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
-        result["cpu_baseline"] = cpu_baseline(cfg, raw, host_in, args.cpu_budget)
+        if raw4 is None:
+            raw4 = synth.make_weights(synth.config(4), seed=0)
+        result["cpu_baseline"] = cpu_baselines(raw, raw4)
 
     print(json.dumps(result), flush=True)
 
