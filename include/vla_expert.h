@@ -179,6 +179,24 @@ int vla_denoise(vla_ctx* ctx, const void* prefix_k, const void* prefix_v, const 
 int vla_denoise_varlen(vla_ctx* ctx, const void* prefix_k, const void* prefix_v, const int32_t* prefix_valid,
                        const float* noise, const float* t_schedule, int n_steps, float* out_actions);
 
+/* For callers that cannot allocate device memory during a call: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * The same loop as vla_denoise (same arguments, ownership and errors, same
+ * kernels, so the same bits), launched kernel by kernel on the ctx stream
+ * (no graph of its own, none instantiated), calling no allocator: the call's
+ * scratch (the modulation table of every step, the time-MLP intermediates,
+ * the split-K partials) lives in one library-wide static device array of
+ * VLA_STATIC_SCRATCH_BYTES per device, held until the process ends. Calls
+ * needing more than that (roughly n_steps * batch * (6 n_layers + 2) * hidden
+ * * 4 bytes plus the partials) fail with VLA_ERR_SHAPE before anything is
+ * enqueued; e.g. the 36-layer hidden-1024 expert fits up to about 70 steps
+ * at batch 1. Every call on a device shares that device's array: calls
+ * that overlap on one device (other streams, other contexts) race and must
+ * be serialized by the caller. The persistent path option is ignored. */
+#define VLA_STATIC_SCRATCH_BYTES 67108864 /* 64 MiB */
+int vla_denoise_static(vla_ctx* ctx, const void* prefix_k, const void* prefix_v, const float* noise,
+                       const float* t_schedule, int n_steps, float* out_actions);
+
 /* Use `stream` (a hipStream_t) for every later call on ctx. NULL (also the
  * state after vla_expert_create) selects the legacy default stream. Graphs
  * are captured once on a library-created stream and replayed on this one.

@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -20,6 +21,13 @@
 #include "kernels.h"
 #include "kernels_persist.h"
 #include "kernels_prefill.h"
+
+// Per-call scratch of vla_denoise_static (modulation table, time-MLP
+// intermediates, split-K partials), resident on every device the library runs
+// on until the process ends. Host code never uses this name as an address: it
+// uses the device address hipGetSymbolAddress returns for the current device
+// (static_scratch_ptr below).
+static __device__ __align__(256) uint8_t scratch[VLA_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -67,6 +75,32 @@ void set_err(const char* fmt, ...) {
             return VLA_ERR_HIP;                                                          \
         }                                                                                \
     } while (0)
+
+// Device address of `scratch` on each device, taken once per device (with
+// that device current) by static_scratch_ptr; the array's host-side name is
+// not a device address.
+constexpr int VLA_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[VLA_MAX_DEVICES] = {};
+
+int static_scratch_ptr(int dev, void** out) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (dev < 0 || dev >= VLA_MAX_DEVICES) {
+        set_err("device %d out of range for the static scratch table", dev);
+        return VLA_ERR_ARG;
+    }
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            set_err("hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+            return VLA_ERR_HIP;
+        }
+        g_scratch_dev[dev] = p;
+    }
+    *out = g_scratch_dev[dev];
+    return VLA_OK;
+}
 
 struct GemmCfg {
     bool skinny = true;  // weight-streaming kernel for M <= 64 rows
@@ -184,6 +218,8 @@ struct vla_ctx {
     uint8_t *y8 = nullptr, *o8 = nullptr, *act8 = nullptr;
     float *y8s = nullptr, *o8s = nullptr, *act8s = nullptr;
     float* ws = nullptr;        // split-K partials of O / down, [ksplit][M][H]
+    size_t ws_elems = 0;
+    void* static_scratch = nullptr;  // device address of `scratch` on this ctx's device
     uint16_t *kcat = nullptr, *vcat = nullptr;  // per-layer [prefix ; chunk] K and V
     KVLayout kv{};
     ArgBlock* ab = nullptr;
@@ -1211,6 +1247,8 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
     for (const Linear* ln : {&c->wo[0], &c->wd[0]})
         if (ln->cfg.skinny && ln->cfg.ksplit > 1) ws_elems = std::max(ws_elems, (size_t)ln->cfg.ksplit * M * H);
     if ((rc = c->alloc((void**)&c->ws, ws_elems * 4))) return rc;
+    c->ws_elems = ws_elems;
+    if ((rc = static_scratch_ptr(c->device, &c->static_scratch))) return rc;
     c->persist_ok = persist_supported(c);
     if (c->persist_ok) {
         std::vector<const uint8_t*> hp(4 * (size_t)L);
@@ -1332,6 +1370,72 @@ int vla_denoise_varlen(vla_ctx* c, const void* prefix_k, const void* prefix_v, c
 int vla_denoise(vla_ctx* c, const void* prefix_k, const void* prefix_v, const float* noise, const float* t_schedule,
                 int n_steps, float* out_actions) {
     return vla_denoise_varlen(c, prefix_k, prefix_v, nullptr, noise, t_schedule, n_steps, out_actions);
+}
+
+int vla_denoise_static(vla_ctx* c, const void* prefix_k, const void* prefix_v, const float* noise,
+                       const float* t_schedule, int n_steps, float* out_actions) {
+    g_err.clear();
+    if (!c) {
+        set_err("ctx is NULL");
+        return VLA_ERR_ARG;
+    }
+    int rc;
+    if (c->d.prefix_len > 0) {
+        if ((rc = check_ptr(prefix_k, "prefix_k"))) return rc;
+        if ((rc = check_ptr(prefix_v, "prefix_v"))) return rc;
+    }
+    if ((rc = check_ptr(noise, "noise", 4))) return rc;
+    if ((rc = check_ptr(t_schedule, "t_schedule", 4))) return rc;
+    if ((rc = check_ptr(out_actions, "out_actions", 4))) return rc;
+    if (n_steps < 1 || n_steps > 100000) {
+        set_err("n_steps must be in [1, 100000] (got %d)", n_steps);
+        return VLA_ERR_ARG;
+    }
+    // this call's scratch, carved from the static array in 256-byte aligned pieces
+    const vla_dims& d = c->d;
+    const size_t nb = (size_t)n_steps * d.batch;
+    const size_t H = d.hidden, E = d.time_emb_dim;
+    auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+    const size_t cbf_rows = nb > 64 ? nb : 64;
+    const size_t o_mod = 0, o_e = o_mod + up(nb * c->mod_ld * 4), o_z1 = o_e + up(nb * E * 4),
+                 o_cbf = o_z1 + up(nb * H * 4), o_ws = o_cbf + up(cbf_rows * H * 2),
+                 total = o_ws + up(c->ws_elems * 4);
+    if (total > VLA_STATIC_SCRATCH_BYTES) {
+        set_err("vla_denoise_static needs %zu bytes of scratch for %d steps x %d requests; the static scratch holds "
+                "%zu (use vla_denoise)", total, n_steps, d.batch, (size_t)VLA_STATIC_SCRATCH_BYTES);
+        return VLA_ERR_SHAPE;
+    }
+    if (!c->static_scratch) {
+        set_err("static scratch address not set for device %d", c->device);
+        return VLA_ERR_HIP;
+    }
+    HIPC(hipSetDevice(c->device));
+    uint8_t* base = (uint8_t*)c->static_scratch;
+    float* const keep_mod = c->modtab;
+    float* const keep_e = c->e;
+    float* const keep_z1 = c->z1;
+    uint16_t* const keep_cbf = c->cbf;
+    float* const keep_ws = c->ws;
+    c->modtab = (float*)(base + o_mod);
+    c->e = (float*)(base + o_e);
+    c->z1 = (float*)(base + o_z1);
+    c->cbf = (uint16_t*)(base + o_cbf);
+    c->ws = (float*)(base + o_ws);
+    // the conditioning rows past nb are the A-fragment padding: zero them (a
+    // kernel, not a memset, so that a capturing caller records no memset node)
+    const long words = (long)(cbf_rows * H * 2 / 16);
+    hipLaunchKernelGGL(zero_u32x4_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, c->stream,
+                       (u32x4*)c->cbf, words);
+    rc = hipGetLastError() == hipSuccess ? VLA_OK : VLA_ERR_HIP;
+    if (rc) set_err("zero fill of the static scratch failed to launch");
+    if (!rc) rc = set_args(c, prefix_k, prefix_v, noise, t_schedule, out_actions, nullptr);
+    if (!rc) rc = enqueue_forward(c, n_steps);
+    c->modtab = keep_mod;
+    c->e = keep_e;
+    c->z1 = keep_z1;
+    c->cbf = keep_cbf;
+    c->ws = keep_ws;
+    return rc;
 }
 
 int vla_set_stream(vla_ctx* c, void* stream) {

@@ -350,3 +350,10 @@ __global__ void copy_f32_kernel(const float* src, float* dst, long n) {
     long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) dst[i] = src[i];
 }
+
+// Zero n 16-byte words (clears scratch memory with a kernel, so that callers
+// capturing the launches into a graph record no memset node).
+__global__ void zero_u32x4_kernel(u32x4* dst, long n) {
+    long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = (u32x4){0u, 0u, 0u, 0u};
+}
