@@ -948,7 +948,14 @@ bool persist_supported(const vla_ctx* c) {
     if (d.hidden != 512 && d.hidden != 1024 && d.hidden != 2048) return false;  // H/256 even, divides 16
     if (d.batch > P_BMAX) return false;                       // staged modulation vectors
     if (d.batch * ((hq * d.horizon + 15) / 16) > PJ) return false;  // attention tiles per XCD
-    return persist_shape(d).fn != nullptr;
+    const void* fn = persist_shape(d).fn;
+    if (!fn) return false;
+    // the workgroups wait on each other, so all PX * PJ of them must be able
+    // to be resident at once: the device's occupancy for this kernel decides,
+    // not the launch (a plain launch would queue the rest behind the waiters)
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, PWAVES * 64, 0) != hipSuccess) return false;
+    return (long)per_cu * c->ncu >= (long)PX * PJ;
 }
 
 // Slot strides of the persistent kernel's write-once buffers (elements), and
@@ -1052,10 +1059,12 @@ int enqueue_persist(vla_ctx* c, int n_steps) {
     p.sink = c->gflag + 384;
     p.ticket = c->gflag + 320;
     p.err = c->perr;
-    // A plain launch (stream order and events behave as for any kernel): with
-    // one 512-thread, 100 KiB-LDS workgroup per CU, the 256 workgroups are
-    // resident together on an otherwise idle GPU. If other work holds CUs,
-    // the bounded waits expire and the output is poisoned instead of hanging.
+    // A plain launch (stream order and events behave as for any kernel):
+    // persist_supported checked that the device's occupancy for this kernel
+    // holds all 256 workgroups at once (one 512-thread, ~100 KiB-LDS
+    // workgroup per CU), so on an otherwise idle GPU they are resident
+    // together. If other work holds CUs, the bounded waits expire and the
+    // output is poisoned instead of hanging.
     void* args[] = {&p};
     HIPC(hipLaunchKernel(persist_shape(d).fn, dim3(PX * PJ), dim3(PWAVES * 64), args, 0, c->stream));
     const int n = c->M * d.action_dim;

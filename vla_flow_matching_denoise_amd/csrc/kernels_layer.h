@@ -548,27 +548,18 @@ constexpr int SK_WAVES = 8;
 constexpr int SK_MAXS = 6;  // k-steps (of 32) per wave: K split <= 8 * 6 * 32 = 1536
 
 // Eight E2M1 codes (element j in bits 4j..4j+3) times the E8M0 block scale
-// 2^(e - 127) as bf16: a nonzero E2M1 magnitude (1 + m/2) * 2^(x - 1) (x >= 1)
-// or 0.5 (x = 0, m = 1) has bf16 exponent field 126 + x (126 for 0.5) and
-// mantissa m at the top bit; the scale adds e - 127 to the exponent field
-// (exact while the result stays a normal bf16, as for weights of any
-// reasonable size).
+// 2^(e - 127) as bf16, by gfx950's scaled FP4 conversion: each
+// v_cvt_scalef32_pk_bf16_fp4 takes the two codes of one byte (the low nibble
+// is the lower element) and multiplies them by an fp32 scale. An E2M1 value
+// has at most two significant bits, so the product by a power of two is
+// exact in bf16 while it stays normal, as for weights of any reasonable size.
 VLA_DEV bf16x8 e2m1x8_to_bf16x8(uint32_t w, uint32_t e) {
-    const int sh = ((int)e - 127) << 7;
-    uint32_t r[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        uint32_t h[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const uint32_t c = (w >> (8 * j + 4 * t)) & 15u, m = c & 7u, x = m >> 1;
-            uint32_t b = m == 1u ? 0x3F00u : (((126u + x) << 7) | ((m & 1u) << 6));
-            b = m == 0u ? 0u : (uint32_t)((int)b + sh);
-            h[t] = b | ((c >> 3) << 15);
-        }
-        r[j] = h[0] | (h[1] << 16);
-    }
-    return __builtin_bit_cast(bf16x8, r);
+    const float sc = __uint_as_float(e << 23);  // 2^(e - 127) for e in 1..254
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
+    return (bf16x8){p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
 // WF: weight format, 0 bf16, 1 E4M3 (fp32 scale per output row), 2 MXFP4
