@@ -256,6 +256,79 @@ def traffic_from(fetch_dir, write_dir, cmd_fetch, cmd_write):
     print("\n".join(lines))
 
 
+MFMA_SUMMARY = os.path.join(ROOT, "profiles", "gemm_attention_lingbot_b64_mfma_counters.txt")
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_VALU_MFMA_BUSY_CYCLES",
+                 "SQ_BUSY_CU_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE")
+SIMDS = 256 * 4   # MI355X: 256 CUs of 4 SIMDs
+XCDS = 8          # GRBM_GUI_ACTIVE comes summed over the XCDs' instances
+
+
+def _kernel_durations(d):
+    """Dispatch id -> duration in ns from a rocprofv3 kernel trace under `d`."""
+    files = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not files:
+        return {}
+    out = {}
+    with open(files[0]) as fh:
+        for r in csv.DictReader(fh):
+            try:
+                out[int(r["Dispatch_Id"])] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            except (KeyError, ValueError):
+                pass
+    return out
+
+
+def mfma_from(pmc_dir, cmd):
+    """Summary of the batch-64 MFMA counter run (bench.py --counter-run-b64
+    under rocprofv3 --pmc <MFMA_COUNTERS> --kernel-trace): per kernel of the
+    layer, the hardware's MFMA operations (x 512 flops each) against the
+    algorithmic flops, the MFMA-busy share of all SIMD cycles while the
+    kernel ran (busy cycles / (GRBM_GUI_ACTIVE x SIMDs), as rocprofv3's
+    MfmaUtil), the CU-busy share, achieved TFLOP/s over the traced duration,
+    and LDS bank conflicts per active LDS cycle."""
+    rows = _counter_rows(pmc_dir)
+    dur = _kernel_durations(pmc_dir)
+    per = {}   # dispatch -> {"kernel", counter -> value}
+    for r in rows:
+        d = int(r["Dispatch_Id"])
+        e = per.setdefault(d, {"kernel": r.get("Kernel_Name", "")})
+        e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    fams = {}
+    for d, e in sorted(per.items()):
+        k = e["kernel"]
+        if not any(t in k for t in ("gemm_kernel<", "gemm8_kernel<", "attn_rows_kernel<")):
+            continue
+        fams.setdefault(k, []).append((d, e))
+    lines = [
+        "# MFMA counters per kernel of one expert layer, LingBot-shaped batch-64 workload (M = 3200 rows),",
+        "# bf16 weights (gemm_kernel) and E4M3 weights with per-token E4M3 activations (gemm8_kernel).",
+        f"# command: {cmd}",
+        f"# summary: python bench.py --mfma-from <pmc dir>",
+        "# flops_hw = (MOPS_BF16 + MOPS_F8) x 512 per dispatch; cycles = GRBM_GUI_ACTIVE / 8 (the counter",
+        f"# comes summed over the 8 XCDs); mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x {SIMDS} SIMDs), as",
+        "# rocprofv3's MfmaUtil; cu_busy = SQ_BUSY_CU_CYCLES / (cycles x 256 CUs);",
+        "# lds_conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE; us from the kernel trace of the same run.",
+        "# kernel | dispatches | us | flops_hw (GFLOP) | TFLOP/s | mfma_busy | cu_busy | lds_conflict",
+    ]
+    for k, lst in fams.items():
+        mops = np.mean([e.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + e.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0)
+                        for _, e in lst])
+        cyc = [max(e.get("GRBM_GUI_ACTIVE", 0.0) / XCDS, 1.0) for _, e in lst]   # GPU cycles of the dispatch
+        busy = np.mean([e.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (c * SIMDS) for (_, e), c in zip(lst, cyc)])
+        cu = np.mean([e.get("SQ_BUSY_CU_CYCLES", 0.0) / (c * SIMDS / 4) for (_, e), c in zip(lst, cyc)])
+        conf = np.mean([e.get("SQ_LDS_BANK_CONFLICT", 0.0) / max(e.get("SQ_LDS_IDX_ACTIVE", 1.0), 1.0)
+                        for _, e in lst])
+        ds = [dur[d] for d, _ in lst if d in dur]
+        us = float(np.mean(ds)) / 1e3 if ds else float("nan")
+        fl = mops * 512
+        name = k.split("(")[0].replace("void ", "")
+        lines.append(f"{name} | {len(lst)} | {us:.2f} | {fl / 1e9:.2f} | {fl / us / 1e6:.1f} | {busy:.3f} | "
+                     f"{cu:.3f} | {conf:.3f}")
+    with open(MFMA_SUMMARY, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def prefill_work(bcfg):
     """Weight bytes read and GEMM + attention flops of one prefill call (the
     last layer stops after its QKV projection)."""
@@ -532,7 +605,7 @@ def counter_run_b64(iters):
     from vla_flow_matching_denoise_amd.expert import Expert, dims_from_config
     torch.cuda.set_device(0)
     for wd in ("bf16", "fp8_e4m3"):
-        cfg = synth.config(5).replace(weight_dtype=wd)
+        cfg = synth.config(5).replace(weight_dtype=wd, n_steps=1)   # one step fills the table the layers read
         ex = Expert(synth.make_weights(cfg, seed=0), dims_from_config(cfg))
         dev_in = gpu_inputs(cfg)
         ex.denoise(*dev_in, cfg.n_steps)
@@ -561,9 +634,14 @@ def main():
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write the traffic summary from two rocprofv3 --pmc output folders")
     ap.add_argument("--traffic-cmds", nargs=2, metavar=("FETCH_CMD", "WRITE_CMD"), default=("?", "?"))
+    ap.add_argument("--mfma-from", metavar="PMC_DIR", help="write the batch-64 MFMA counter summary")
+    ap.add_argument("--mfma-cmd", default="?")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(*args.traffic_from, *args.traffic_cmds)
+        return
+    if args.mfma_from:
+        mfma_from(args.mfma_from, args.mfma_cmd)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
