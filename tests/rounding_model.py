@@ -17,7 +17,10 @@ Where the kernels round (expert loop, "LingBot-VLA on Thor (sm_110)", section
 * q, k and v after the RoPE epilogue (the cache layout is bf16);
 * the softmax weights exp(s - m) as the PV MFMA operand (the row sum stays
   fp32, so normalisation uses the unrounded weights);
-* the attention output o (O GEMM input) and the SwiGLU output (down input).
+* the attention output o (O GEMM input) and the SwiGLU output (down input);
+* with E4M3 weights at more than 64 rows (per-token E4M3 linear inputs):
+  the norm outputs are quantized from fp32, the attention and SwiGLU
+  outputs from their bf16 copies.
 
 The residual stream, the final norm, the out-projection and the Euler state
 stay fp32 (here fp64).  The prefix backbone ("LingBot-VLA on Thor (sm_110)",
@@ -73,12 +76,19 @@ def _attention_r(q, k, v, rnd, causal=False):
     return out
 
 
-def expert_layer_r(h, W, l, mod, prefix_k_l, prefix_v_l, dims, rnd=bf16_round):
-    """``oracle.expert_layer`` with the kernels' bf16 stores (``rnd``)."""
+def expert_layer_r(h, W, l, mod, prefix_k_l, prefix_v_l, dims, rnd=bf16_round, act_quant=False):
+    """``oracle.expert_layer`` with the kernels' bf16 stores (``rnd``).
+
+    ``act_quant``: the batched E4M3 tier, whose linears take per-token E4M3
+    inputs. The norm kernels quantize their fp32 output directly; the
+    attention and SwiGLU outputs are stored as bf16 first and then quantized
+    (the quantization itself is the oracle's ``quantize_per_token_e4m3``)."""
+    q8 = oracle.quantize_per_token_e4m3 if act_quant else None
     a1, b1, g1, a2, b2, g2 = mod
     T = h.shape[0]
     nq, nkv, dh = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
-    y = rnd(oracle.ada_rms_norm(h, a1, b1, dims.rms_eps))
+    y = oracle.ada_rms_norm(h, a1, b1, dims.rms_eps)
+    y = q8(y) if q8 else rnd(y)
     q = (y @ W["wq"][l].T).reshape(T, nq, dh).transpose(1, 0, 2)
     k = (y @ W["wk"][l].T).reshape(T, nkv, dh).transpose(1, 0, 2)
     v = (y @ W["wv"][l].T).reshape(T, nkv, dh).transpose(1, 0, 2)
@@ -89,31 +99,36 @@ def expert_layer_r(h, W, l, mod, prefix_k_l, prefix_v_l, dims, rnd=bf16_round):
     K = np.concatenate([prefix_k_l.transpose(1, 0, 2), k], axis=1)
     V = np.concatenate([prefix_v_l.transpose(1, 0, 2), v], axis=1)
     o = rnd(_attention_r(q, K, V, rnd).transpose(1, 0, 2).reshape(T, nq * dh))
+    if q8:
+        o = q8(o)
     h = h + g1 * (o @ W["wo"][l].T)
-    y = rnd(oracle.ada_rms_norm(h, a2, b2, dims.rms_eps))
+    y = oracle.ada_rms_norm(h, a2, b2, dims.rms_eps)
+    y = q8(y) if q8 else rnd(y)
     a = rnd(oracle.silu(y @ W["wg"][l].T) * (y @ W["wu"][l].T))
+    if q8:
+        a = q8(a)
     return h + g2 * (a @ W["wd"][l].T)
 
 
-def velocity_r(x, t, W, prefix_k_b, prefix_v_b, dims, rnd=bf16_round):
+def velocity_r(x, t, W, prefix_k_b, prefix_v_b, dims, rnd=bf16_round, act_quant=False):
     """``oracle.velocity`` with the kernels' bf16 stores."""
     c = rnd(oracle.time_condition(t, W, dims))
     h = x @ W["in_w"].T + W["in_b"]
     for l in range(dims.n_layers):
         mod = oracle.modulation(c, W["mod_w"][l], W["mod_b"][l], 6)
-        h = expert_layer_r(h, W, l, mod, prefix_k_b[l], prefix_v_b[l], dims, rnd)
+        h = expert_layer_r(h, W, l, mod, prefix_k_b[l], prefix_v_b[l], dims, rnd, act_quant)
     af, bf = oracle.modulation(c, W["modf_w"], W["modf_b"], 2)
     return oracle.ada_rms_norm(h, af, bf, dims.rms_eps) @ W["out_w"].T + W["out_b"]
 
 
-def denoise_r(W, dims, prefix_k, prefix_v, noise, t_schedule, rnd=bf16_round):
+def denoise_r(W, dims, prefix_k, prefix_v, noise, t_schedule, rnd=bf16_round, act_quant=False):
     """``oracle.denoise`` (explicit Euler at the left end point) on ``velocity_r``."""
     out = np.empty(noise.shape, dtype=np.float64)
     for b in range(noise.shape[0]):
         x = noise[b].astype(np.float64)
         ts = np.asarray(t_schedule[b], dtype=np.float64)
         for k in range(ts.shape[0] - 1):
-            x = x + (ts[k + 1] - ts[k]) * velocity_r(x, ts[k], W, prefix_k[b], prefix_v[b], dims, rnd)
+            x = x + (ts[k + 1] - ts[k]) * velocity_r(x, ts[k], W, prefix_k[b], prefix_v[b], dims, rnd, act_quant)
         out[b] = x
     return out
 

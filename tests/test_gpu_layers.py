@@ -202,4 +202,3 @@ def test_create_destroy_cycles_release_device_memory():
     free1, _ = torch.cuda.mem_get_info()
     say(f"[create/destroy x50] free before {free0 / 2**20:.1f} MiB, after {free1 / 2**20:.1f} MiB")
     assert free1 >= free0 - (16 << 20), (free0, free1)
-
