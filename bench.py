@@ -368,11 +368,13 @@ def gpu_backbone_weights(bcfg, seed=0):
     return W
 
 
-def bench_prefill(batches, warmup, steps, weight_dtype="bf16"):
+def bench_prefill(batches, warmup, steps, weight_dtype="bf16", prefix_len=None):
     import torch
     import synth
     from vla_flow_matching_denoise_amd.prefill import Prefill, backbone_dims_from_config
     base = synth.backbone(2).replace(weight_dtype=weight_dtype)
+    if prefix_len:
+        base = base.replace(prefix_len=prefix_len)
     W = gpu_backbone_weights(base)
     out = {}
     for b in batches:
@@ -801,6 +803,8 @@ def main():
             # the pages' prefix runs FP8: E4M3 weights and per-token E4M3 inputs
             # (mfma_frac against the 5 PFLOP/s FP8 peak)
             "e4m3": bench_prefill((1, 16), 3, max(5, args.steps // 3), "fp8_e4m3"),
+            # the V2-shaped loop's prefix length
+            "p512": bench_prefill((1,), 3, max(5, args.steps // 3), prefix_len=512),
         }
 
     if not args.no_cpu_baseline:
