@@ -236,6 +236,9 @@ def traffic_from(fetch_dir, write_dir, cmd_fetch, cmd_write):
         "# Two rocprofv3 counter runs of `python bench.py --counter-run`, each scaled by the",
         "# counter's reading for a plain device copy of 256 MiB (read 256 MiB, write 256 MiB).",
         "# O and down share one kernel instance: launches alternate O, down within a layer.",
+        "# The attention launch's extra workgroups load the O and gate_up weights (~21 MB) into L2",
+        "# ahead of those GEMMs, and the norm before a layer the layer's QKV weights: those fetches",
+        "# count against the launch that issues them (attention, resnorm), not the GEMM that uses them.",
         f"# fetch command: {cmd_fetch}",
         f"# write command: {cmd_write}",
         f"# summary: python bench.py --traffic-from <fetch dir> <write dir>",
@@ -681,6 +684,10 @@ def main():
     dom, roof, worst = dominant(kr, "hbm")
     roof["traffic"] = recorded_traffic(dom)
     worst["traffic"] = recorded_traffic(worst["kernel"])
+    for r in (roof, worst):
+        if r["kernel"] == "gqa_attention":
+            r["traffic_note"] = ("includes the O and gate_up weights (about 21 MB) that the launch's idle "
+                                 "workgroups load into L2 for the next GEMMs")
     persistent = None
     if not args.no_extra:
         # the opt-in persistent single-launch path on the same workload
