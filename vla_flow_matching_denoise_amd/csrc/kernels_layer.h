@@ -694,9 +694,15 @@ constexpr int GEMM_WAVES = 8, GEMM_KT = 64, GEMM_KS = GEMM_KT / 32;
 // 16 bytes per lane from global memory into LDS: the 64 lanes fill the
 // 1 KiB at byte offset `lds` (lane i at lds + 16 i). No register receives
 // data; the kernel waits for these loads itself (vm_wait) before the
-// barrier that publishes a stage, and before it exits.
+// barrier that publishes a stage, and before it exits. M0 carries the LDS
+// address; it is a register the compiler reserves (a clobber of it would be
+// ignored), so the block saves and restores it.
 VLA_DEV void lds_dma16(const void* g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+    uint32_t keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep)
+                 : "v"(g), "s"(lds)
+                 : "memory");
 }
 template <int N>
 VLA_DEV void vm_wait() {
