@@ -202,3 +202,46 @@ def test_create_destroy_cycles_release_device_memory():
     free1, _ = torch.cuda.mem_get_info()
     say(f"[create/destroy x50] free before {free0 / 2**20:.1f} MiB, after {free1 / 2**20:.1f} MiB")
     assert free1 >= free0 - (16 << 20), (free0, free1)
+
+
+def test_batch_split_into_concurrent_halves():
+    """VLA_OPT_SPLIT_BATCH = 2 runs the requests as two halves on two streams
+    (child contexts borrowing the weights): 43 requests (halves of 21 and 22),
+    warped per-request schedules and padded prefixes with per-request valid
+    lengths. Each mode repeats bitwise over two calls; the two modes differ
+    only through the fp32 summation order of the modulation GEMM (its row
+    count is steps x requests: 63 rows take the weight-streaming kernel,
+    129 the tiled one), far inside the bf16 gates, and sampled requests of
+    the split run meet the oracle's gates."""
+    import torch
+    from vla_flow_matching_denoise_amd import binding as B
+    from vla_flow_matching_denoise_amd.expert import to_device
+    cfg = synth.config(5).replace(n_layers=4, batch=43, n_steps=3)
+    raw = synth.make_weights(cfg, seed=6)
+    case = GpuCase(cfg, raw, *_inputs(cfg, schedule="warped", seed=3))
+    valid = to_device(np.random.default_rng(4).integers(0, cfg.prefix_len + 1, cfg.batch).astype(np.int32))
+    try:
+        ex = case.expert
+        outs = {}
+        for mode in (0, 2, 0, 2):
+            ex.set_option(B.VLA_OPT_SPLIT_BATCH, mode)
+            assert ex.get_option(B.VLA_OPT_SPLIT_BATCH) == mode
+            a = ex.denoise(case.pk, case.pv, case.x0, case.ts, cfg.n_steps, prefix_valid=valid).clone()
+            b = ex.denoise(case.pk, case.pv, case.x0, case.ts, cfg.n_steps).clone()
+            torch.cuda.synchronize()
+            if mode in outs:
+                assert torch.equal(outs[mode][0], a) and torch.equal(outs[mode][1], b)
+            outs[mode] = (a, b)
+        for i in (0, 1):
+            m = metrics(outs[2][i].cpu().numpy(), outs[0][i].cpu().numpy())
+            say(f"[split] halves vs one batch, call {i}: {m}")
+            assert m["cos"] >= 1 - 1e-8 and m["maxabs_over_rms"] <= 2e-3, m
+        assert not torch.equal(outs[0][0], outs[0][1])     # the valid lengths did matter
+    finally:
+        case.close()
+    W = oracle.decode_weights(raw)
+    pk, pv, x0, ts = _inputs(cfg, schedule="warped", seed=3)
+    for b in (0, 21, 42):
+        ref = run_oracle(cfg.replace(batch=1), W, pk[b:b + 1], pv[b:b + 1], x0[b:b + 1], ts[b:b + 1])
+        m = metrics(outs[2][1][b:b + 1].cpu().numpy(), ref)
+        assert m["cos"] >= BF16_COS and m["maxabs_over_rms"] <= BF16_MAXABS, (b, m)
