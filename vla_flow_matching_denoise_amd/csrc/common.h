@@ -87,7 +87,12 @@ VLA_DEV float group16_max(float v) {
     return v;
 }
 
-VLA_DEV float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+// SiLU z / (1 + e^-z) with the hardware exp2 and reciprocal (about one ulp
+// each, far below the bf16 rounding of every result it feeds) in place of an
+// IEEE division. z -> -inf: e^-z overflows to inf and the reciprocal to 0.
+VLA_DEV float silu_f(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.44269504088896341f));
+}
 
 // 2^x for softmax weights: the hardware v_exp_f32 alone. The library exp2f adds
 // range scaling for results below 2^-126 (six more instructions); softmax

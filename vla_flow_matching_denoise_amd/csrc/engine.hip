@@ -717,13 +717,13 @@ int launch_attention(vla_ctx* c, int l, const uint16_t* q, uint16_t* o, int ofra
         if (d.head_dim == 128) VLA_LAUNCH((attn_kernel<128, 8>), ag, dim3(512), 0, c->stream, ap);
         else VLA_LAUNCH((attn_kernel<64, 8>), ag, dim3(512), 0, c->stream, ap);
     } else {
-        // many rows: 64 or 128 query rows per workgroup (128 when a KV group
-        // has more than 64 rows), K/V staged once through LDS
+        // many rows: 64 or 128 query rows per workgroup (128, as 8 waves of
+        // 16, when a KV group has more than 64 rows), K/V staged once through LDS
         const int rows = G * d.horizon;
         if (rows > 64) {
             const dim3 rg((rows + 127) / 128, d.n_kv_heads, d.batch);
-            if (d.head_dim == 128) VLA_LAUNCH((attn_rows_kernel<128, 2>), rg, dim3(256), 0, c->stream, ap);
-            else VLA_LAUNCH((attn_rows_kernel<64, 2>), rg, dim3(256), 0, c->stream, ap);
+            if (d.head_dim == 128) VLA_LAUNCH((attn_rows_kernel<128, 1, false, 8>), rg, dim3(512), 0, c->stream, ap);
+            else VLA_LAUNCH((attn_rows_kernel<64, 1, false, 8>), rg, dim3(512), 0, c->stream, ap);
         } else {
             const dim3 rg((rows + 63) / 64, d.n_kv_heads, d.batch);
             if (d.head_dim == 128) VLA_LAUNCH((attn_rows_kernel<128, 1>), rg, dim3(256), 0, c->stream, ap);
@@ -810,7 +810,7 @@ int launch_block_gemm(vla_ctx* c, int which, int step, int l, int* S) {
         p.lda = o ? c->qd : d.intermediate;
         p.out_f32 = c->h;
         p.gate_off = (6 * l + (o ? 2 : 5)) * H;
-        if (S && lin.cfg.skinny && lin.cfg.ksplit > 1) *S = lin.cfg.ksplit;
+        if (S && lin.cfg.ksplit > 1) *S = lin.cfg.ksplit;   // partials for the next norm
         return launch_gemm(c, lin, lin.cfg, c->w8, EPI_RESID, p);
     }
     if (which == VLA_KERNEL_GATE_UP) {
@@ -1281,7 +1281,7 @@ int create_buffers(vla_ctx* c) {
     HIPC(hipMemsetAsync(c->vcat, 0, kv_elems * 2, c->stream));
     size_t ws_elems = 16;
     for (const Linear* ln : {&c->wo[0], &c->wd[0]})
-        if (ln->cfg.skinny && ln->cfg.ksplit > 1) ws_elems = std::max(ws_elems, (size_t)ln->cfg.ksplit * M * H);
+        if (ln->cfg.ksplit > 1) ws_elems = std::max(ws_elems, (size_t)ln->cfg.ksplit * M * H);
     if ((rc = c->alloc((void**)&c->ws, ws_elems * 4))) return rc;
     c->ws_elems = ws_elems;
     if ((rc = static_scratch_ptr(c->device, &c->static_scratch))) return rc;

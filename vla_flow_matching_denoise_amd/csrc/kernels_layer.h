@@ -689,7 +689,8 @@ __global__ __launch_bounds__(512) void skinny_gemm_kernel(GemmParams p) {
 // tiles, for half the LDS bytes per MFMA on 128-row tiles, measured no
 // faster: the 128-row tiles are not bound by LDS bandwidth.)
 // ---------------------------------------------------------------------------
-constexpr int GEMM_WAVES = 8, GEMM_KT = 64, GEMM_KS = GEMM_KT / 32;
+constexpr int GEMM_WAVES = 8;
+constexpr int GEMM_KT = 64;   // K granularity of a tiled GEMM (its loop runs k-steps of 32 in pairs)
 
 // 16 bytes per lane from global memory into LDS: the 64 lanes fill the
 // 1 KiB at byte offset `lds` (lane i at lds + 16 i). No register receives
@@ -709,27 +710,88 @@ VLA_DEV void vm_wait() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// LDS stages per tile shape: as many 64-deep stages as fit in 144 KiB, at
-// most 3 (one workgroup per CU).
+// Stage depth and LDS ring per tile shape. A stage holds A as MT rows of
+// RB = 2 KT bytes, each row's 16-byte chunk c at chunk position
+// c ^ ((r / RPB) % CPR) (RPB rows per 256 bytes, i.e. per pass over the 64
+// banks): one DMA load (1 KiB) fills RPL whole rows, each from contiguous
+// global bytes, and the 16 lanes that read one MFMA fragment (16 rows, one
+// chunk) meet 16 distinct bank groups. Stages as many as fit in the LDS
+// budget, at most GEMM_SMAX (one workgroup per CU).
+#ifndef VLA_GEMM_KT
+#define VLA_GEMM_KT 64
+#endif
+#ifndef VLA_GEMM_SMAX
+#define VLA_GEMM_SMAX 3
+#endif
+#ifndef VLA_GEMM_LDS
+#define VLA_GEMM_LDS 147456
+#endif
 template <int MT, int NT, bool W8>
 struct GemmShape {
-    static constexpr int AF = MT / 16 * GEMM_KS;                 // A loads per stage (8 rows x 128 B = 1 KiB each)
-    static constexpr int BBYTES = NT / 16 * GEMM_KS * (W8 ? 512 : 1024);
+    static constexpr int KT = W8 ? 64 : VLA_GEMM_KT;             // inputs per stage
+    static constexpr int KS = KT / 32;                           // MFMA k-steps per stage
+    static constexpr int RB = KT * 2, CPR = RB / 16, RPL = 64 / CPR, RPB = 256 / RB;
+    static constexpr int AF = MT / RPL;                          // A loads per stage (1 KiB each)
+    static constexpr int BBYTES = NT / 16 * KS * (W8 ? 512 : 1024);
     static constexpr int BCH = BBYTES / 1024;                    // 1 KiB DMA chunks of B per stage
     static constexpr int STAGE = AF * 1024 + BBYTES;
-    static constexpr int S = 147456 / STAGE >= 3 ? 3 : 147456 / STAGE;
+    static constexpr int S = VLA_GEMM_LDS / STAGE >= VLA_GEMM_SMAX ? VLA_GEMM_SMAX : VLA_GEMM_LDS / STAGE;
     static constexpr int LA = (AF + GEMM_WAVES - 1) / GEMM_WAVES;   // DMA loads per wave and stage
     static constexpr int LB = (BCH + GEMM_WAVES - 1) / GEMM_WAVES;
     static constexpr int LPW = LA + LB;
+    static_assert(KS == 1 || KS == 2, "stages of one or two k-steps");
     static_assert(S >= 2, "tile too large for two LDS stages");
 };
+
+// SwiGLU epilogue of a tiled GEMM straight from the MFMA accumulators (8
+// waves as 2 x 4 wave tiles of MT/2 x NT/4). The packed weight rows
+// alternate gate (even column) and up (odd column), so lanes l and l ^ 1
+// hold the two halves of the same outputs for the same four rows. One swap
+// of two values between them leaves each lane two outputs (two rows), and a
+// second swap with lane l ^ 2 pairs adjacent outputs of one row as bf16x2,
+// which each lane writes into a bf16 output tile in LDS. The row pitch is
+// NT + 16 bytes, so the 16 rows one write instruction touches meet distinct
+// banks and one row's 16-byte chunks are contiguous; 16-byte chunks then go
+// to global memory, row by row. val(fm, fn, r) is accumulator element r of
+// fragment (fm, fn) with its scales applied. The LDS ring must be free.
+template <int MT, int NT, int FM, int FN, typename Val>
+VLA_DEV void swiglu_epilogue_tile(const GemmParams& p, uint8_t* lds, int m0, int n0, int wm, int wn, int lane,
+                                  int tid, Val val) {
+    constexpr int WM = MT / 2, WN = NT / 4, OP = NT + 16;
+    const bool odd = lane & 1, podd = lane & 2;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            float a[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) a[r] = val(fm, fn, r);
+            // even lanes keep rows 0, 1 (their gate), odd lanes rows 2, 3 (their up)
+            const float y0 = row_dpp<0xB1>(odd ? a[0] : a[2]), y1 = row_dpp<0xB1>(odd ? a[1] : a[3]);
+            const float o0 = silu_f(odd ? y0 : a[0]) * (odd ? a[2] : y0);
+            const float o1 = silu_f(odd ? y1 : a[1]) * (odd ? a[3] : y1);
+            // lanes with bit 1 clear keep the first row, the others the second
+            const float w = row_dpp<0x4E>(podd ? o0 : o1);
+            const uint32_t pk = podd ? pack_bf16x2(w, o1) : pack_bf16x2(o0, w);
+            const int r = wm * WM + fm * 16 + 4 * (lane >> 4) + (odd ? 2 : 0) + (podd ? 1 : 0);
+            const int oc = (wn * WN + fn * 16) / 2 + ((lane & 15) >> 2) * 2;
+            *(uint32_t*)(lds + r * OP + oc * 2) = pk;
+        }
+    __syncthreads();
+    constexpr int CPR = NT / 16;   // 16-byte chunks (8 outputs) per output row
+    for (int u = tid; u < MT * CPR; u += 64 * GEMM_WAVES) {
+        const int r = u / CPR, q = u % CPR;
+        if (m0 + r < p.M)
+            *(u32x4*)(p.act + act_index(m0 + r, n0 / 2 + 8 * q, p.N / 2, p.afrag)) = *(const u32x4*)(lds + r * OP + 16 * q);
+    }
+}
 
 template <int MT, int NT, bool W8, int EPI>
 __global__ __launch_bounds__(64 * GEMM_WAVES) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemm_kernel(GemmParams p) {
     using G = GemmShape<MT, NT, W8>;
     constexpr int S = G::S, AF = G::AF, BCH = G::BCH, LA = G::LA, LB = G::LB, LPW = G::LPW, STAGE = G::STAGE;
-    constexpr int KS = GEMM_KS, WGN = 4;
+    constexpr int KT = G::KT, KS = G::KS, RB = G::RB, CPR = G::CPR, RPL = G::RPL, RPB = G::RPB, WGN = 4;
     constexpr int WM = MT / 2, WN = NT / WGN, FM = WM / 16, FN = WN / 16;
     static_assert(FM >= 1 && FN >= 1, "tile smaller than the wave grid");
     __shared__ __attribute__((aligned(1024))) uint8_t lds[S * STAGE];
@@ -762,24 +824,21 @@ void gemm_kernel(GemmParams p) {
     // split K (gridDim.y > 1, EPI_PARTIAL): this workgroup sums inputs
     // [kz * kw, (kz + 1) * kw) and writes partial kz
     const int kz = blockIdx.y, kf0 = kz * (p.kw / 32);
-    const int nk = p.kw / GEMM_KT, Kf = p.K / 32;
+    const int nk = p.kw / KT, Kf = p.K / 32;
     const uint32_t lbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
 
     // Per-lane source of each DMA load of this wave (stage 0) and the stride
-    // per stage. A stage holds A as MT rows of 128 bytes (64 inputs), the
-    // 16-byte chunk c of row r at chunk position c ^ ((r >> 1) & 7): one DMA
-    // load fills 8 whole rows, each from one contiguous 128-byte line (a
-    // load of 16 half lines moves about 40 % fewer bytes per clock), and the
-    // 16 lanes that read one MFMA fragment (16 rows, one chunk) meet 16
-    // distinct bank groups. Load j of A covers rows 8j .. 8j + 7; chunk c of
-    // B is one 1 KiB weight fragment. Waves with fewer chunks than loads
-    // repeat one (same bytes, same place).
+    // per stage. Load j of A covers rows RPL j .. RPL j + RPL - 1 of the
+    // stage (whole rows from contiguous global bytes: a load of 16 half
+    // lines moves about 40 % fewer bytes per clock); chunk c of B is one
+    // 1 KiB weight fragment. Waves with fewer chunks than loads repeat one
+    // (same bytes, same place).
     const uint16_t* asrc[LA];
     uint32_t adst[LA];
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
-        const int j = (wave * LA + i) % AF, r = j * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        const int j = (wave * LA + i) % AF, r = j * RPL + lane / CPR;
+        const int c = (lane % CPR) ^ ((r / RPB) % CPR);
         if (p.a_frag) {
             // A-fragment order of <= 64 rows: fragment (k-step, row block) is
             // 1 KiB, lane l holding row l % 16 at inputs 8 (l / 16) .. + 7
@@ -792,7 +851,7 @@ void gemm_kernel(GemmParams p) {
         }
         adst[i] = (uint32_t)j * 1024;
     }
-    const size_t astride = p.a_frag ? (size_t)KS * 4 * 512 : (size_t)GEMM_KT;
+    const size_t astride = p.a_frag ? (size_t)KS * 4 * 512 : (size_t)KT;
     const uint8_t* bsrc[LB];
     uint32_t bdst[LB];
 #pragma unroll
@@ -828,12 +887,12 @@ void gemm_kernel(GemmParams p) {
     // fragments of k-step ks + 1 are read while k-step ks is multiplied; lane
     // l reads row l % 16 of each row block at chunk 4 ks + l / 16 (swizzled)
     bf16x8 fa[2][FM], fb[2][FN];
-    const int arow = (wm * FM * 16 + (lane & 15)) * 128;
-    const int achunk = (lane >> 4) ^ ((lane & 15) >> 1);
+    const int arow = (wm * FM * 16 + (lane & 15)) * RB;
+    const int aswz = ((lane & 15) / RPB) % CPR;   // the row's chunk permutation (fm * 16 rows keep it)
     auto read_frags = [&](int buf, const uint8_t* st, int ks) {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
-            fa[buf][fm] = *(const bf16x8*)(st + arow + fm * 16 * 128 + ((achunk ^ (ks * 4)) << 4));
+            fa[buf][fm] = *(const bf16x8*)(st + arow + fm * 16 * RB + (((ks * 4 + (lane >> 4)) ^ aswz) << 4));
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             const int frag = (wn * FN + fn) * KS + ks;
@@ -853,28 +912,45 @@ void gemm_kernel(GemmParams p) {
     vm_wait<(S - 1) * LPW>();
     __syncthreads();
     read_frags(0, lds, 0);
-    for (int kt = 0; kt < nk; ++kt) {
-        const uint8_t* st = lds + (kt % S) * STAGE;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 1 < KS) {
-                read_frags((ks + 1) & 1, st, ks + 1);
-            } else {
-                // stage kt+1 landed (this wave's loads), then every wave's
-                // loads landed and every wave is done reading stage kt
-                vm_wait<(S - 2) * LPW>();
-                __syncthreads();
-                issue(kt + S);
-                read_frags(0, lds + ((kt + 1) % S) * STAGE, 0);
-            }
-            // keep the fragment reads ahead of the multiplies they overlap
-            __builtin_amdgcn_sched_barrier(0);
-            multiply(ks & 1);
-            __builtin_amdgcn_sched_barrier(0);
+    // k-step g (32 inputs) of stage g / KS multiplies fragment buffer g % 2;
+    // the other buffer takes k-step g + 1 meanwhile. Two k-steps per
+    // iteration keep the buffer indexes constant (the k-steps of a split
+    // are a multiple of two).
+    auto step = [&](int g, auto bufc) {
+        constexpr int buf = decltype(bufc)::value, ks = buf % KS;
+        const int kt = g / KS;
+        if (ks + 1 < KS) {
+            read_frags(buf ^ 1, lds + (kt % S) * STAGE, ks + 1);
+        } else {
+            // stage kt+1 landed (this wave's loads), then every wave's
+            // loads landed and every wave is done reading stage kt
+            vm_wait<(S - 2) * LPW>();
+            __syncthreads();
+            issue(kt + S);
+            read_frags(buf ^ 1, lds + ((kt + 1) % S) * STAGE, 0);
         }
+        // keep the fragment reads ahead of the multiplies they overlap
+        __builtin_amdgcn_sched_barrier(0);
+        multiply(buf);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int g = 0; g < nk * KS; g += 2) {
+        step(g, std::integral_constant<int, 0>{});
+        step(g + 1, std::integral_constant<int, 1>{});
     }
     vm_wait<0>();  // the repeated tail loads land before the LDS is reused
     __syncthreads();    // every wave is done with the ring
+
+    if constexpr (EPI == EPI_SWIGLU) {
+        static_assert(MT * (NT + 16) <= S * STAGE, "SwiGLU output tile does not fit the ring");
+        float wsc[FN];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) wsc[fn] = W8 ? p.wscale[n0 + wn * WN + fn * 16 + (lane & 15)] : 1.0f;
+        swiglu_epilogue_tile<MT, NT, FM, FN>(p, lds, m0, n0, wm, wn, lane, tid, [&](int fm, int fn, int r) {
+            return W8 ? acc[fm][fn][r] * wsc[fn] : acc[fm][fn][r];
+        });
+        return;
+    }
 
     // Epilogue through LDS, 64 tile rows per pass: the waves holding those
     // rows write their accumulators (times the E4M3 row scales) as fp32 rows,
@@ -1086,6 +1162,22 @@ void gemm8_kernel(GemmParams p) {
     }
     vm_wait<0>();      // the repeated tail loads land before the LDS is reused
     __syncthreads();
+
+    if constexpr (EPI == EPI_SWIGLU) {
+        static_assert(MT * (NT + 16) <= S * STAGE, "SwiGLU output tile does not fit the ring");
+        float wsc[FN], asc[FM][4];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) wsc[fn] = p.wscale[n0 + wn * WN + fn * 16 + (lane & 15)];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                asc[fm][r] = p.ascale[min(m0 + wm * WM + fm * 16 + 4 * (lane >> 4) + r, p.M - 1)];
+        swiglu_epilogue_tile<MT, NT, FM, FN>(p, lds, m0, n0, wm, wn, lane, tid, [&](int fm, int fn, int r) {
+            return acc[fm][fn][r] * wsc[fn] * asc[fm][r];
+        });
+        return;
+    }
 
     // epilogue through LDS as in gemm_kernel, with the row and column scales
     constexpr int CLD = NT + 4;
@@ -1348,12 +1440,15 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// The same attention for many query rows (large batches): a workgroup of four
-// waves takes 64 * RT query rows of one (request, KV group), each wave owning
-// RT 16-row tiles over the whole key range, and every 32-key K/V block is
-// staged once per workgroup through LDS (double-buffered). K/V is then read
-// from L2 once per 64 * RT query rows, each K or V fragment read from LDS
-// serves RT tiles, and the waves never merge.
+// The same attention for many query rows (large batches): a workgroup of AW
+// waves takes AW * 16 * RT query rows of one (request, KV group), each wave
+// owning RT 16-row tiles over the whole key range, and every 32-key K/V block
+// is staged once per workgroup through LDS. K/V is then read from L2 once per
+// workgroup, each K or V fragment read from LDS serves RT tiles, and the
+// waves never merge. The blocks arrive by global->LDS DMA into a ring of
+// ATT_RING slots, ATT_RING - 1 blocks ahead of the one being multiplied, so
+// the load latency of a block is hidden behind the blocks before it (with
+// one block in flight, each block waited out most of a memory round trip).
 // The running maximum moves only when a block's maximum exceeds it by more
 // than ATT_SLACK (log2 units), so most blocks skip the rescale of the
 // accumulators and its exponentials; the unnormalised weights stay below
@@ -1374,27 +1469,31 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
 // a wave's rows are masked per key.
 // ---------------------------------------------------------------------------
 
-template <int DH, int RT, bool CAUSAL = false>
-__global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
-    constexpr int BLK = 32 * DH * 2;             // one 32-key block of K (or V), bytes
-    constexpr int CH = BLK / 16 / 256;           // chunks of a block per thread
-    static_assert(CH >= 1, "head too small");
-    static_assert(DH == 64 || DH == 128, "head_dim 64 or 128");
-    __shared__ __attribute__((aligned(16))) uint8_t Ks[2][BLK];
-    __shared__ __attribute__((aligned(16))) uint8_t Vs[2][BLK];
+constexpr int ATT_RING = 4;   // K/V block slots of attn_rows_kernel
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+template <int DH, int RT, bool CAUSAL = false, int AW = 4>
+__global__ __launch_bounds__(64 * AW) void attn_rows_kernel(AttnParams p) {
+    constexpr int BLK = 32 * DH * 2;             // one 32-key block of K (or V), bytes
+    constexpr int NCH = 2 * BLK / 1024;          // 1 KiB DMA chunks of a K + V block
+    constexpr int LPW = (NCH + AW - 1) / AW;     // DMA loads per wave and block
+    constexpr int WROWS = AW * 16 * RT;          // query rows of a workgroup
+    static_assert(DH == 64 || DH == 128, "head_dim 64 or 128");
+    // slot s: K block at s * 2 BLK, V block after it
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[ATT_RING * 2 * BLK];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G = p.nq / p.kv.nkv;
     const int rows_total = G * p.T;
     const int g = blockIdx.y, b = blockIdx.z;
-    const int r0 = blockIdx.x * 64 * RT + wave * 16 * RT;
+    const int r0 = blockIdx.x * WROWS + wave * 16 * RT;
     int nblk = p.kv.S_pad / 32;
     // causal: token of this lane's query in each tile, the smallest token of
     // the wave's rows (0 when they span two heads), and the last block any row
     // of the workgroup needs (rows are head-major: row = head_in_group * T + token)
     int tok[RT], tmin = 0;
     if constexpr (CAUSAL) {
-        const int R0 = blockIdx.x * 64 * RT, R1 = min(R0 + 64 * RT, rows_total) - 1;
+        const int R0 = blockIdx.x * WROWS, R1 = min(R0 + WROWS, rows_total) - 1;
         const int tmax = R0 / p.T == R1 / p.T ? R1 % p.T : p.T - 1;
         nblk = min(nblk, tmax / 32 + 1);
         const int w1 = min(r0 + 16 * RT, rows_total) - 1;
@@ -1406,6 +1505,24 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
     const uint8_t* K = (const uint8_t*)(p.kcat + base);
     const uint8_t* V = (const uint8_t*)(p.vcat + base);
     const int pvb = p.pvalid[b];  // prefix keys past this are padding
+    const uint32_t rbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ring;
+
+    // Block kb into slot kb % ATT_RING: chunk j < NCH / 2 of K, the rest of V
+    // (a wave with fewer chunks than loads repeats one: same bytes, same
+    // place). Past the last block the loads repeat it into a slot no later
+    // block uses, so every wave always has the same loads in flight.
+    auto issue = [&](int kb_raw) {
+        const int kb = min(kb_raw, nblk - 1);
+        const uint32_t sb = rbase + (uint32_t)((kb_raw % ATT_RING) * 2 * BLK);
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+            const int j = (wave * LPW + i) % NCH;
+            const uint8_t* src = j < NCH / 2 ? K + (size_t)kb * BLK + j * 1024 : V + (size_t)kb * BLK + (j - NCH / 2) * 1024;
+            lds_dma16(src + lane * 16, sb + (uint32_t)(j * 1024));
+        }
+    };
+#pragma unroll
+    for (int kb = 0; kb < ATT_RING - 1; ++kb) issue(kb);
 
     bf16x8 qf[RT][DH / 32];
     {
@@ -1421,6 +1538,14 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
             }
         }
     }
+    // The compiler counts only its own loads when it places waits: were the
+    // first use of q inside the loop, its wait would also cover the ring
+    // loads issued there. Taking q here (behind the first ring blocks, which
+    // are older and land first) keeps every later wait on the ring explicit.
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int ks = 0; ks < DH / 32; ++ks) asm volatile("" ::"v"(qf[t][ks]));
 
     // per lane: the running maximum and the partial sum (over this lane's
     // keys) of its query in each tile; oacc rows are the queries 4 (l / 16) + r
@@ -1437,30 +1562,15 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
         for (int dn = 0; dn < DH / 16; ++dn) oacc[t][dn] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
 
-    u32x4 rk[CH], rv[CH];
-    auto gload = [&](int kb) {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = tid + i * 256;
-            rk[i] = *(const u32x4*)(K + (size_t)kb * BLK + (size_t)c * 16);
-            rv[i] = *(const u32x4*)(V + (size_t)kb * BLK + (size_t)c * 16);
-        }
-    };
-    auto sstore = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < CH; ++i) {
-            const int c = tid + i * 256;
-            *(u32x4*)(&Ks[buf][c * 16]) = rk[i];
-            *(u32x4*)(&Vs[buf][c * 16]) = rv[i];
-        }
-    };
-
-    gload(0);
-    sstore(0);
-    __syncthreads();
     for (int kb = 0; kb < nblk; ++kb) {
-        const int buf = kb & 1;
-        if (kb + 1 < nblk) gload(kb + 1);   // next block in flight during this one
+        // block kb landed (this wave's loads), then every wave's loads landed
+        // and every wave is done with block kb - 1, whose slot then takes
+        // block kb - 1 + ATT_RING
+        vm_wait<(ATT_RING - 2) * LPW>();
+        __syncthreads();
+        issue(kb - 1 + ATT_RING);
+        const uint8_t* Ks = ring + (kb % ATT_RING) * 2 * BLK;
+        const uint8_t* Vs = Ks + BLK;
         // s[t][sb][r]: query (tile t, lane & 15) against key 8 (lane / 16) + 4 sb + r
         f32x4 s[RT][2];
 #pragma unroll
@@ -1469,7 +1579,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
             for (int t = 0; t < RT; ++t) s[t][sb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < DH / 32; ++ks) {
-                const bf16x8 kf = *(const bf16x8*)(&Ks[buf][((sb * (DH / 32) + ks) * 64 + lane) * 16]);
+                const bf16x8 kf = *(const bf16x8*)(Ks + ((sb * (DH / 32) + ks) * 64 + lane) * 16);
 #pragma unroll
                 for (int t = 0; t < RT; ++t) s[t][sb] = mfma_16x16x32(kf, qf[t][ks], s[t][sb]);
             }
@@ -1533,13 +1643,12 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnParams p) {
         }
 #pragma unroll
         for (int dn = 0; dn < DH / 16; ++dn) {
-            const bf16x8 vf = *(const bf16x8*)(&Vs[buf][(dn * 64 + lane) * 16]);
+            const bf16x8 vf = *(const bf16x8*)(Vs + (dn * 64 + lane) * 16);
 #pragma unroll
             for (int t = 0; t < RT; ++t) oacc[t][dn] = mfma_16x16x32(pa[t], vf, oacc[t][dn]);
         }
-        if (kb + 1 < nblk) sstore(buf ^ 1);  // that buffer was last read before the previous barrier
-        __syncthreads();
     }
+    vm_wait<0>();   // the repeated tail loads land before the workgroup ends
 
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
