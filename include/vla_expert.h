@@ -80,14 +80,15 @@ extern "C" {
  * its QKV, 8 the norm before gate_up prefetches down; 0 off. Default 7. For measurement; setting it
  * waits for the ctx stream and drops captured graphs. */
 #define VLA_OPT_L2_PREFETCH 6
-/* Large batches: 2 runs the requests as two halves at once, each half a child context (the same
- * weights, its own buffers, graph and stream) forked from and joined back to the ctx stream with
- * events, so that one half's kernel ramps and tails overlap the other's; 0 runs the batch as one. The
- * default splits bf16 weights when each half has at least 1024 rows (batch * horizon / 2). Each request's result
- * differs from the unsplit run only by the order of fp32 sums in the modulation GEMM (whose row count
- * is steps * requests, so a half can take the weight-streaming kernel where the whole batch takes the
- * tiled one), i.e. within rounding. vla_get_option gives the mode in use. Setting any option rebuilds
- * the halves at the next call. */
+/* Large batches: n = 2..4 runs the requests as n parts at once (request ranges [B i / n, B (i+1) / n)),
+ * each part a child context (the same weights, its own buffers, graph and stream) forked from and joined
+ * back to the ctx stream with events, so that one part's kernel ramps and tails overlap another's; 0 runs
+ * the batch as one. Parts of at most 64 rows are not made (the option then runs the batch as one). The
+ * default uses two parts when each half has at least 1024 rows (batch * horizon / 2). A request's result
+ * can differ from the unsplit run only by the order of fp32 sums in the modulation GEMM (whose row count
+ * is steps * requests, so a part can take the weight-streaming kernel where the whole batch takes the
+ * tiled one), i.e. within rounding. vla_get_option gives the number of parts in use (0: none). Setting
+ * any option rebuilds the parts at the next call. */
 #define VLA_OPT_SPLIT_BATCH 8
 
 typedef struct vla_ctx vla_ctx;

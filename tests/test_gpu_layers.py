@@ -205,14 +205,15 @@ def test_create_destroy_cycles_release_device_memory():
 
 
 def test_batch_split_into_concurrent_halves():
-    """VLA_OPT_SPLIT_BATCH = 2 runs the requests as two halves on two streams
-    (child contexts borrowing the weights): 43 requests (halves of 21 and 22),
-    warped per-request schedules and padded prefixes with per-request valid
-    lengths. Each mode repeats bitwise over two calls; the two modes differ
-    only through the fp32 summation order of the modulation GEMM (its row
-    count is steps x requests: 63 rows take the weight-streaming kernel,
-    129 the tiled one), far inside the bf16 gates, and sampled requests of
-    the split run meet the oracle's gates."""
+    """VLA_OPT_SPLIT_BATCH = n runs the requests as n parts on n streams
+    (child contexts borrowing the weights): 43 requests (parts of 21 + 22,
+    14 + 14 + 15 and 10 + 11 + 11 + 11), warped per-request schedules and
+    padded prefixes with per-request valid lengths. Each mode repeats
+    bitwise over two calls; the modes differ only through the fp32 summation
+    order of the modulation GEMM (its row count is steps x requests, so a
+    small part can take the weight-streaming kernel where the whole batch
+    takes the tiled one), far inside the bf16 gates, and sampled requests of
+    the two-part run meet the oracle's gates."""
     import torch
     from vla_flow_matching_denoise_amd import binding as B
     from vla_flow_matching_denoise_amd.expert import to_device
@@ -223,7 +224,7 @@ def test_batch_split_into_concurrent_halves():
     try:
         ex = case.expert
         outs = {}
-        for mode in (0, 2, 0, 2):
+        for mode in (0, 2, 3, 4, 0, 2, 3, 4):
             ex.set_option(B.VLA_OPT_SPLIT_BATCH, mode)
             assert ex.get_option(B.VLA_OPT_SPLIT_BATCH) == mode
             a = ex.denoise(case.pk, case.pv, case.x0, case.ts, cfg.n_steps, prefix_valid=valid).clone()
@@ -232,10 +233,11 @@ def test_batch_split_into_concurrent_halves():
             if mode in outs:
                 assert torch.equal(outs[mode][0], a) and torch.equal(outs[mode][1], b)
             outs[mode] = (a, b)
-        for i in (0, 1):
-            m = metrics(outs[2][i].cpu().numpy(), outs[0][i].cpu().numpy())
-            say(f"[split] halves vs one batch, call {i}: {m}")
-            assert m["cos"] >= 1 - 1e-8 and m["maxabs_over_rms"] <= 2e-3, m
+        for mode in (2, 3, 4):
+            for i in (0, 1):
+                m = metrics(outs[mode][i].cpu().numpy(), outs[0][i].cpu().numpy())
+                say(f"[split] {mode} parts vs one batch, call {i}: {m}")
+                assert m["cos"] >= 1 - 1e-8 and m["maxabs_over_rms"] <= 2e-3, m
         assert not torch.equal(outs[0][0], outs[0][1])     # the valid lengths did matter
     finally:
         case.close()

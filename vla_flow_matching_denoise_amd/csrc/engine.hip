@@ -234,7 +234,7 @@ struct vla_ctx {
     int l2_prefetch = 7;  // VLA_OPT_L2_PREFETCH bits
     // large batches: the requests split into halves run as two child contexts
     // (borrowing this context's weights) on two streams at once
-    int split = -1;                    // VLA_OPT_SPLIT_BATCH: 0 or 2; -1 until set (then automatic)
+    int split = -1;                    // VLA_OPT_SPLIT_BATCH: 0 or 2..4 parts; -1 until set (then automatic)
     std::vector<vla_ctx*> parts;       // the child contexts, created on first use
     std::vector<int> part_b0;          // first request of each part
     hipEvent_t fork_ev = nullptr, join_ev = nullptr;
@@ -1314,13 +1314,17 @@ int create_buffers(vla_ctx* c) {
 namespace {
 
 // Rows of each part when a batch of B requests is split in two.
-bool split_wanted(const vla_ctx* c) {
-    if (c->borrowed || c->d.batch < 2 || c->persist_ok) return false;
+// Number of parts the batch runs as (0: not split).
+int split_parts(const vla_ctx* c) {
+    if (c->borrowed || c->d.batch < 2 || c->persist_ok) return 0;
     const long half_rows = (long)(c->d.batch / 2) * c->d.horizon;
-    // automatic: bf16 weights with at least 1024 rows per half (the batched
-    // E4M3 tier measured no faster split: 66.7-67.3 vs 66.3-66.4 ms at batch 64)
-    const int mode = c->split >= 0 ? c->split : (half_rows >= 1024 && !c->w8 ? 2 : 0);
-    return mode == 2 && half_rows > 64;  // each part keeps the many-row kernels (and their weight layout)
+    // automatic: two parts when each half has at least 1024 rows (batch 64,
+    // horizon 50: 71.7 vs 75.2 ms per call with bf16 weights, 60.6 vs
+    // 63.4 ms with E4M3; three or four parts measured slower)
+    const int n = c->split >= 0 ? c->split : (half_rows >= 1024 ? 2 : 0);
+    if (n < 2 || c->d.batch < n) return 0;
+    // each part keeps the many-row kernels (and their weight layout)
+    return (long)(c->d.batch / n) * c->d.horizon > 64 ? n : 0;
 }
 
 // A child context for requests [b0, b0 + nb): the parent's dims with batch
@@ -1381,15 +1385,18 @@ void drop_parts(vla_ctx* c) {
 static int denoise_enqueue(vla_ctx* c, const void* prefix_k, const void* prefix_v, const int* prefix_valid,
                            const float* noise, const float* t_schedule, int n_steps, float* out_actions) {
     int rc;
-    if (split_wanted(c)) {
-        // two halves of the requests at once, each on its own stream, forked
-        // from and joined back to this context's stream with events
+    if (const int np = split_parts(c)) {
+        // parts of the requests at once, each on its own stream, forked from
+        // and joined back to this context's stream with events
         if (c->parts.empty()) {
             HIPC(hipStreamSynchronize(c->stream));
-            const int B = c->d.batch, h0 = B / 2;
-            if ((rc = create_part(c, 0, h0)) || (rc = create_part(c, h0, B - h0))) {
-                drop_parts(c);
-                return rc;
+            const int B = c->d.batch;
+            for (int i = 0; i < np; ++i) {
+                const int b0 = (int)((long)B * i / np), b1 = (int)((long)B * (i + 1) / np);
+                if ((rc = create_part(c, b0, b1 - b0))) {
+                    drop_parts(c);
+                    return rc;
+                }
             }
             if (!c->fork_ev) HIPC(hipEventCreateWithFlags(&c->fork_ev, hipEventDisableTiming));
             if (!c->join_ev) HIPC(hipEventCreateWithFlags(&c->join_ev, hipEventDisableTiming));
@@ -1596,8 +1603,8 @@ int vla_set_option(vla_ctx* c, int option, int value) {
         drop_parts(c);
     }
     if (option == VLA_OPT_SPLIT_BATCH) {
-        if (value != 0 && value != 2) {
-            set_err("VLA_OPT_SPLIT_BATCH takes 0 or 2, not %d", value);
+        if (value != 0 && (value < 2 || value > 4)) {
+            set_err("VLA_OPT_SPLIT_BATCH takes 0 or 2..4, not %d", value);
             return VLA_ERR_ARG;
         }
         c->split = value;
@@ -1657,7 +1664,7 @@ int vla_get_option(const vla_ctx* c, int option, int* value) {
         case VLA_OPT_PERSISTENT: *value = c->use_persist ? 1 : 0; return VLA_OK;
         case VLA_OPT_GEMM_TILE: *value = c->gemm_tile; return VLA_OK;
         case VLA_OPT_L2_PREFETCH: *value = c->l2_prefetch; return VLA_OK;
-        case VLA_OPT_SPLIT_BATCH: *value = split_wanted(c) ? 2 : 0; return VLA_OK;
+        case VLA_OPT_SPLIT_BATCH: *value = split_parts(c); return VLA_OK;
         case VLA_OPT_PERSISTENT_ACTIVE: *value = (c->persist_ok && c->use_persist) ? 1 : 0; return VLA_OK;
         case VLA_OPT_PERSISTENT_STATUS: {
             int e = 0;
