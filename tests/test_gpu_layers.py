@@ -5,7 +5,8 @@ live context.
   large as the residual) at the first, middle and last layer and the first
   and last Euler step, for the LingBot batch-1 workload (weight-streaming
   GEMMs, the key-split attention) and the batch-64 workload (tiled GEMMs, the
-  row-tile attention; sampled requests on per-request warped schedules).
+  row-tile attention; sampled requests on per-request warped schedules), and
+  at batch 32, the shapes of one half of the split batch-64 call.
   Gate: the layer's change to the residual, cosine >= 0.9995 and max-abs <=
   2e-2 x its RMS.
 * The whole 36-layer gate-open loop (2 Euler steps).  Its tolerance is
@@ -37,12 +38,15 @@ def _inputs(cfg, schedule="uniform", n_steps=None, seed=0):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("cfg_id,requests", [(2, (0,)), (5, (0, 37, 63))])
-def test_gate_open_layer_stages_first_middle_last(cfg_id, requests):
+@pytest.mark.parametrize("cfg_id,batch,requests", [(2, None, (0,)), (5, None, (0, 37, 63)), (5, 32, (0, 31))])
+def test_gate_open_layer_stages_first_middle_last(cfg_id, batch, requests):
+    """Batch 32 (1600 rows) is one half of the split batch-64 call: its tile
+    shapes (256x128 QKV, 128x64 O and down, the 8-wave row attention) differ
+    from those of 3200 rows in one launch."""
     import torch
     from vla_flow_matching_denoise_amd import binding as B
     from vla_flow_matching_denoise_amd.expert import to_device
-    cfg = synth.config(cfg_id)
+    cfg = synth.config(cfg_id) if batch is None else synth.config(cfg_id).replace(batch=batch)
     pk, pv, x0, ts = _inputs(cfg, schedule="warped" if cfg.batch > 1 else "uniform")
     raw = synth.apply_variant(weights(2), "gate_open", cfg)
     say(f"[layers cfg{cfg_id}] gate-open stages, batch {cfg.batch}")

@@ -1046,6 +1046,13 @@ struct Gemm8Shape {
     static_assert(S >= 2, "tile too large for two LDS stages");
 };
 
+// Chunk permutation of an FP8 A row (128 bytes, 8 chunks of 16): chunk c of
+// row r sits at c ^ a8_swz(r). Each lane reads chunks 2 (l / 16) and
+// 2 (l / 16) + 1 of row l % 16; with the bf16 kernel's (r >> 1) those reads
+// ran at half the LDS rate (two-way conflicts, measured); taking row bit 3
+// into bit 0 makes both reads conflict-free.
+VLA_DEV int a8_swz(int r) { return (r & 6) | ((r >> 3) & 1); }
+
 VLA_DEV i32x8 frag32(const uint8_t* lo, const uint8_t* hi) {
     const u32x4 a = *(const u32x4*)lo, b = *(const u32x4*)hi;
     return (i32x8){(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
@@ -1086,16 +1093,16 @@ void gemm8_kernel(GemmParams p) {
     const uint32_t lbase = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds;
     const uint8_t* A = (const uint8_t*)p.A + (size_t)kt0 * GEMM8_KT;
 
-    // A in the stage as MT rows of 128 bytes (128 inputs) with the 16-byte
-    // chunk swizzle of gemm_kernel: load j fills rows 8j .. 8j + 7 from whole
-    // 128-byte lines (rows past M read row M-1, never stored); chunk c of B =
-    // half c%2 of the fragment of column block c/2
+    // A in the stage as MT rows of 128 bytes (128 inputs), chunks permuted by
+    // a8_swz: load j fills rows 8j .. 8j + 7 from whole 128-byte lines (rows
+    // past M read row M-1, never stored); chunk c of B = half c%2 of the
+    // fragment of column block c/2
     const uint8_t* asrc[LA];
     uint32_t adst[LA];
 #pragma unroll
     for (int i = 0; i < LA; ++i) {
         const int j = (wave * LA + i) % ACH, r = j * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        const int c = (lane & 7) ^ a8_swz(r & 15);
         const int row = min(m0 + r, p.M - 1);
         asrc[i] = A + (size_t)row * p.lda + c * 16;
         adst[i] = (uint32_t)j * 1024;
@@ -1141,8 +1148,8 @@ void gemm8_kernel(GemmParams p) {
             bf[fn] = frag32(st + (ACH + cb) * 1024 + lane * 16, st + (ACH + cb + 1) * 1024 + lane * 16);
         }
         const uint8_t* arow = st + (wm * FM * 16 + (lane & 15)) * 128;
-        const int a_lo = ((2 * (lane >> 4)) ^ ((lane & 15) >> 1)) << 4;
-        const int a_hi = ((2 * (lane >> 4) + 1) ^ ((lane & 15) >> 1)) << 4;
+        const int a_lo = ((2 * (lane >> 4)) ^ a8_swz(lane & 15)) << 4;
+        const int a_hi = ((2 * (lane >> 4) + 1) ^ a8_swz(lane & 15)) << 4;
         af[0] = frag32(arow + a_lo, arow + a_hi);
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
