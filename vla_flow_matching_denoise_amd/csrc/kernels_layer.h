@@ -715,27 +715,21 @@ VLA_DEV void vm_wait() {
 // c ^ ((r / RPB) % CPR) (RPB rows per 256 bytes, i.e. per pass over the 64
 // banks): one DMA load (1 KiB) fills RPL whole rows, each from contiguous
 // global bytes, and the 16 lanes that read one MFMA fragment (16 rows, one
-// chunk) meet 16 distinct bank groups. Stages as many as fit in the LDS
-// budget, at most GEMM_SMAX (one workgroup per CU).
-#ifndef VLA_GEMM_KT
-#define VLA_GEMM_KT 64
-#endif
-#ifndef VLA_GEMM_SMAX
-#define VLA_GEMM_SMAX 3
-#endif
-#ifndef VLA_GEMM_LDS
-#define VLA_GEMM_LDS 147456
-#endif
+// chunk) meet 16 distinct bank groups. Stages: as many as fit in
+// GEMM_LDS_BUDGET, at most GEMM_SMAX (one workgroup per CU). The code takes
+// 32- or 64-deep stages; 64 is used (32-deep stages make the A rows 64-byte
+// half lines, which the DMA path moves at about 60 % of the rate).
+constexpr int GEMM_STAGE_KT = 64, GEMM_SMAX = 3, GEMM_LDS_BUDGET = 147456;
 template <int MT, int NT, bool W8>
 struct GemmShape {
-    static constexpr int KT = W8 ? 64 : VLA_GEMM_KT;             // inputs per stage
+    static constexpr int KT = W8 ? 64 : GEMM_STAGE_KT;           // inputs per stage
     static constexpr int KS = KT / 32;                           // MFMA k-steps per stage
     static constexpr int RB = KT * 2, CPR = RB / 16, RPL = 64 / CPR, RPB = 256 / RB;
     static constexpr int AF = MT / RPL;                          // A loads per stage (1 KiB each)
     static constexpr int BBYTES = NT / 16 * KS * (W8 ? 512 : 1024);
     static constexpr int BCH = BBYTES / 1024;                    // 1 KiB DMA chunks of B per stage
     static constexpr int STAGE = AF * 1024 + BBYTES;
-    static constexpr int S = VLA_GEMM_LDS / STAGE >= VLA_GEMM_SMAX ? VLA_GEMM_SMAX : VLA_GEMM_LDS / STAGE;
+    static constexpr int S = GEMM_LDS_BUDGET / STAGE >= GEMM_SMAX ? GEMM_SMAX : GEMM_LDS_BUDGET / STAGE;
     static constexpr int LA = (AF + GEMM_WAVES - 1) / GEMM_WAVES;   // DMA loads per wave and stage
     static constexpr int LB = (BCH + GEMM_WAVES - 1) / GEMM_WAVES;
     static constexpr int LPW = LA + LB;
