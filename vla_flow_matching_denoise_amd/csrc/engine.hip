@@ -232,8 +232,8 @@ struct vla_ctx {
     // batch <= 64 rows: idle workgroups of the attention and norm kernels
     // prefetch the next skinny GEMMs' weights into the right XCD's L2
     int l2_prefetch = 7;  // VLA_OPT_L2_PREFETCH bits
-    // large batches: the requests split into halves run as two child contexts
-    // (borrowing this context's weights) on two streams at once
+    // large batches: the requests split into parts run as child contexts
+    // (borrowing this context's weights), each on its own stream, at once
     int split = -1;                    // VLA_OPT_SPLIT_BATCH: 0 or 2..4 parts; -1 until set (then automatic)
     std::vector<vla_ctx*> parts;       // the child contexts, created on first use
     std::vector<int> part_b0;          // first request of each part
@@ -1313,7 +1313,6 @@ int create_buffers(vla_ctx* c) {
 
 namespace {
 
-// Rows of each part when a batch of B requests is split in two.
 // Number of parts the batch runs as (0: not split).
 int split_parts(const vla_ctx* c) {
     if (c->borrowed || c->d.batch < 2 || c->persist_ok) return 0;
