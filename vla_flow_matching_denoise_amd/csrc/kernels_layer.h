@@ -1250,6 +1250,7 @@ struct AttnParams {
 // by more than ATT_SLACK (log2 units), so most blocks skip the rescale; the
 // unnormalised weights stay below 2^ATT_SLACK, well inside bf16 and fp32.
 constexpr float ATT_SLACK = 8.0f;
+constexpr int ATT_PF_SLEEPS = 3;   // prefetch slices of attn_kernel: s_sleep(16) rounds before their loads
 
 template <int DH, int AT_WAVES>
 __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
@@ -1264,6 +1265,12 @@ __global__ __launch_bounds__(AT_WAVES * 64) void attn_kernel(AttnParams p) {
     const int g = blockIdx.y, b = blockIdx.z;
     const int nb = gridDim.z - p.pf_slices;
     if (b >= nb) {  // slices past the requests prefetch the next GEMMs' weights
+        // after ~1.3 us (3 x 1024 clocks asleep), so that the attention
+        // workgroups' own first loads are not queued behind the weight
+        // stream (batch-1 call 13.80 -> 13.53 ms; longer delays cost more
+        // than they gain)
+#pragma unroll
+        for (int i = 0; i < ATT_PF_SLEEPS; ++i) __builtin_amdgcn_s_sleep(16);
         const int per_slice = gridDim.x * gridDim.y;
         const int lin = per_slice * b + gridDim.x * g + blockIdx.x;
         int xcd, rank, per_xcd;
