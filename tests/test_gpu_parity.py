@@ -237,19 +237,25 @@ def test_single_layer_stage(cfg_id):
 
 # small grids take the key-split kernel; (2, 12) and (1, 130) have enough
 # 16-row tiles (>= 512) to take the 64-rows-per-workgroup kernel (d_h 128 / 64)
-# (cfg, batch, prefix): few rows take the 8-wave kernel (prefix 280 with
-# T = 16 and prefix 320 with T = 50 give 10 and 12 key blocks: some waves
-# take two, and the last block is partly padding); many rows take the
-# row-tile kernel
-@pytest.mark.parametrize("cfg_id,batch,prefix", [(1, 1, None), (2, 1, None), (3, 1, None), (2, 3, None),
-                                                 (2, 12, None), (1, 130, None), (1, 1, 280), (2, 1, 320)])
-def test_attention_stage(cfg_id, batch, prefix):
+# (cfg, batch, prefix, horizon): few rows take the 8-wave kernel (prefix 280
+# with T = 16 and prefix 320 with T = 50 give 10 and 12 key blocks: some
+# waves take two, and the last block is partly padding); many rows take the
+# row-tile kernels, 8 waves of 16 rows when a KV group has more than 64 rows
+# (head dim 128: 12 requests of 400 rows; head dim 64: 64 requests of 100
+# rows), else 4 waves (head dim 64: 130 requests of 32 rows; head dim 128:
+# 64 requests of T = 8, 64 rows)
+@pytest.mark.parametrize("cfg_id,batch,prefix,horizon", [
+    (1, 1, None, None), (2, 1, None, None), (3, 1, None, None), (2, 3, None, None), (2, 12, None, None),
+    (1, 130, None, None), (1, 1, 280, None), (2, 1, 320, None), (1, 64, None, 50), (2, 64, None, 8)])
+def test_attention_stage(cfg_id, batch, prefix, horizon):
     import torch
     from vla_flow_matching_denoise_amd import binding as B
     from vla_flow_matching_denoise_amd.expert import Expert, dims_from_config, to_device
     cfg = synth.config(cfg_id).replace(n_layers=2, batch=batch)
     if prefix is not None:
         cfg = cfg.replace(prefix_len=prefix)
+    if horizon is not None:
+        cfg = cfg.replace(horizon=horizon)
     raw = synth.make_weights(cfg.replace(n_layers=2), seed=0)
     pk, pv = synth.make_prefix(cfg)
     rng = np.random.default_rng(11)
@@ -331,6 +337,28 @@ def test_batch64_sampled_requests_warped():
     for b in (0, 37, 63):
         ref = run_oracle(cfg.replace(batch=1), W, pk[b:b + 1], pv[b:b + 1], x0[b:b + 1], ts[b:b + 1])
         _gate_bf16(metrics(out[b:b + 1], ref), f"cfg5 request {b}")
+
+
+@pytest.mark.parametrize("split", [0, 2])
+def test_head_dim_64_many_rows_sampled_requests(split):
+    """Head dim 64, 100 query rows per KV group, 64 requests (M = 3200): as one
+    batch the attention takes the 8-wave row-tile kernel (896 workgroups); in
+    two parts of 32 requests the few-row kernel. Warped per-request
+    schedules; requests sampled for the oracle."""
+    from vla_flow_matching_denoise_amd import binding as B
+    cfg = synth.config(1).replace(horizon=50, batch=64, n_steps=3)
+    pk, pv, x0, ts = _inputs(cfg, schedule="warped")
+    say(f"[dh64 rows] batch 64, T = 50, parts {split}")
+    case = GpuCase(cfg, weights(1), pk, pv, x0, ts)
+    try:
+        case.expert.set_option(B.VLA_OPT_SPLIT_BATCH, split)
+        out = case.run()
+    finally:
+        case.close()
+    W = decoded(1)
+    for b in (0, 29, 63):
+        ref = run_oracle(cfg.replace(batch=1), W, pk[b:b + 1], pv[b:b + 1], x0[b:b + 1], ts[b:b + 1])
+        _gate_bf16(metrics(out[b:b + 1], ref), f"dh64 rows parts {split} request {b}")
 
 
 def test_fp8_tier_end_to_end():
