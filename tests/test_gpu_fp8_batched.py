@@ -103,6 +103,59 @@ def test_fp8_batched_end_to_end():
     assert m["cos"] >= FP8_COS, m
 
 
+@pytest.mark.parametrize("intermediate", [6144, 16512])
+def test_fp8_batched_long_activation_rows(intermediate):
+    """SwiGLU widths past the wave-per-row quantization (4096 inputs): the
+    down projection's input rows take the workgroup-per-row kernel, and rows
+    past 16384 inputs the part of it that reads them twice. One gate-open
+    layer, tiny widths otherwise (hidden 256, 4/2 heads of 64), 8 requests
+    of 16 rows. For 16512 inputs the result must also sit much closer to the
+    oracle than the same layer with the down projection's last 128 inputs
+    dropped does (those move the layer by ~8 % of its RMS change, E4M3 code
+    flips of the GPU's own rounded activations by about a quarter of that)."""
+    import torch
+    from vla_flow_matching_denoise_amd import binding as B
+    from vla_flow_matching_denoise_amd.expert import Expert, dims_from_config, to_device
+    cfg = synth.config(1).replace(weight_dtype="fp8_e4m3", intermediate=intermediate, batch=8)
+    raw = synth.apply_variant(synth.make_weights(cfg, seed=3), "gate_open", cfg)
+    pk, pv = synth.make_prefix(cfg, seed=4)
+    ts = synth.make_schedule(cfg.n_steps, cfg.batch, "warped")
+    h_in = np.random.default_rng(8).standard_normal((cfg.m_rows, cfg.hidden)).astype(np.float32)
+    layer, step, T = 1, 3, cfg.horizon
+    Wd = oracle.decode_weights(raw)
+    Wt = dict(Wd)
+    Wt["wd"] = list(Wd["wd"])
+    Wt["wd"][layer] = Wd["wd"][layer].copy()
+    Wt["wd"][layer][:, 16384:] = 0.0
+    d = oracle.ExpertDims.from_config(cfg)
+    fpk, fpv = oracle.decode_bf16(pk), oracle.decode_bf16(pv)
+    want = np.empty((cfg.batch, T, cfg.hidden))
+    want_cut = np.empty_like(want)
+    for b in range(cfg.batch):
+        c = oracle.time_condition(float(ts[b, step]), Wd, d)
+        mod = oracle.modulation(c, Wd["mod_w"][layer], Wd["mod_b"][layer], 6)
+        hb = h_in[b * T:(b + 1) * T].astype(np.float64)
+        want[b] = oracle.expert_layer(hb, Wd, layer, mod, fpk[b, layer], fpv[b, layer], d, act_quant=True) - hb
+        want_cut[b] = oracle.expert_layer(hb, Wt, layer, mod, fpk[b, layer], fpv[b, layer], d, act_quant=True) - hb
+    say(f"[fp8 long rows] SwiGLU {intermediate}, batch 8 (M = 128), one gate-open layer")
+    ex = Expert(raw, dims_from_config(cfg))
+    try:
+        dpk, dpv, dts, hi = (to_device(a) for a in (pk, pv, ts, h_in))
+        ho = torch.empty_like(hi)
+        B.vla_test_layer(ex.ctx, dpk.data_ptr(), dpv.data_ptr(), dts.data_ptr(), cfg.n_steps, step, layer,
+                         hi.data_ptr(), ho.data_ptr())
+        got = (ho.cpu().numpy() - h_in).reshape(cfg.batch, T, -1)
+    finally:
+        ex.close()
+    assert np.all(np.isfinite(got))
+    _gate_q(metrics(got, want), f"fp8 long rows I={intermediate}")
+    if intermediate > 16384:
+        err = float(np.sqrt(np.mean((got - want) ** 2)))
+        gap = float(np.sqrt(np.mean((want_cut - want) ** 2)))
+        say(f"  rms error {err:.3e}; the last 128 inputs move the layer by {gap:.3e}")
+        assert err < 0.5 * gap
+
+
 def test_fp8_batch64_sampled_requests():
     """LingBot-shaped E4M3 expert at batch 64 (M = 3200), 2 steps; three
     requests checked against the oracle."""

@@ -86,9 +86,11 @@ __global__ void pack_weight_kernel(const uint8_t* __restrict__ src, int R, int K
 }
 
 // ---------------------------------------------------------------------------
-// Per-token E4M3 activations: row r of a bf16 [M][K] matrix (K <= 16384, a
-// multiple of 8) becomes codes q = RNE(x * 448 / max|x_r|) with the row
-// scale max|x_r| / 448 (1 for an all-zero row), so x ~ q * scale.
+// Per-token E4M3 activations: row r of a bf16 [M][K] matrix (K a multiple of
+// 8) becomes codes q = RNE(x * 448 / max|x_r|) with the row scale
+// max|x_r| / 448 (1 for an all-zero row), so x ~ q * scale. The first 16384
+// inputs of a row stay in registers between the maximum and the conversion;
+// inputs past them (longer rows) are read a second time.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ src, int K,
                                                          uint8_t* __restrict__ dst, float* __restrict__ scale) {
@@ -110,6 +112,12 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
             }
         }
     }
+    for (int c = (tid + 2048) * 8; c < K; c += 2048) {
+        const u32x4 w = *(const u32x4*)(sr + c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            amax = fmaxf(amax, fmaxf(fabsf(__uint_as_float(w[j] << 16)), fabsf(__uint_as_float(w[j] & 0xffff0000u))));
+    }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
     if ((tid & 63) == 0) red[tid >> 6] = amax;
@@ -126,6 +134,19 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
             q[1] = f32x4_to_e4m3x4(v[i][4] * inv, v[i][5] * inv, v[i][6] * inv, v[i][7] * inv);
             *(u32x2*)(dst + (size_t)row * K + c) = q;
         }
+    }
+    for (int c = (tid + 2048) * 8; c < K; c += 2048) {
+        const u32x4 w = *(const u32x4*)(sr + c);
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[2 * j] = __uint_as_float(w[j] << 16) * inv;
+            x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u) * inv;
+        }
+        u32x2 q;
+        q[0] = f32x4_to_e4m3x4(x[0], x[1], x[2], x[3]);
+        q[1] = f32x4_to_e4m3x4(x[4], x[5], x[6], x[7]);
+        *(u32x2*)(dst + (size_t)row * K + c) = q;
     }
 }
 
