@@ -259,6 +259,57 @@ def traffic_from(fetch_dir, write_dir, cmd_fetch, cmd_write):
     print("\n".join(lines))
 
 
+WAVES_SUMMARY = os.path.join(ROOT, "profiles", "layer_kernels_lingbot_b1_wave_states.txt")
+WAVE_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_SCA",
+                 "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAVES", "GRBM_GUI_ACTIVE")
+
+
+def waits_from(pmc_dir, cmd):
+    """Summary of where the waves of each batch-1 layer kernel family spend
+    their time (bench.py --counter-run under rocprofv3 --pmc <WAVE_COUNTERS>):
+    the share of wave-resident cycles spent waiting (on memory, barriers or
+    dependencies: SQ_WAIT_ANY), waiting to issue (SQ_WAIT_INST_ANY), and
+    executing instructions, with the VALU (MFMA included), LDS and scalar
+    parts of the latter;
+    the wave counters are quad-cycles summed over the shader engines, so
+    their ratios need no scaling. Also the mean resident waves per CU while
+    the kernel ran (wave cycles over GRBM_GUI_ACTIVE / 8, per 256 CUs)."""
+    rows = _counter_rows(pmc_dir)
+    res = {}
+    for fam, (kname, which, per_layer) in TRAFFIC_KERNELS.items():
+        v = {}
+        for c in WAVE_COUNTERS:
+            vals = _per_dispatch(rows, c, lambda k, kname=kname: kname in k)[which::per_layer]
+            if not vals:
+                raise SystemExit(f"{c}: no dispatches of {kname}")
+            v[c] = (float(np.mean(vals)), len(vals))
+        res[fam] = v
+    lines = [
+        "# Wave states per launch of each kernel family of one expert layer, LingBot-shaped batch-1",
+        "# workload (M = 50 rows): shares of the waves' resident cycles (all SQ wave counters are",
+        "# quad-cycles summed over the shader engines). wait = SQ_WAIT_ANY (waiting on memory, barriers",
+        "# or dependencies), issue_wait = SQ_WAIT_INST_ANY, active = SQ_ACTIVE_INST_ANY with its VALU",
+        "# (MFMA included), LDS and scalar (SQ_ACTIVE_INST_SCA) parts; waves_per_cu = SQ_WAVE_CYCLES x 4",
+        "# / (GRBM_GUI_ACTIVE / 8) / 256.",
+        "# The attention launch includes its weight read-ahead workgroups (their waves wait on loads).",
+        "# O and down share one kernel instance: launches alternate O, down within a layer.",
+        f"# command: {cmd}",
+        "# summary: python bench.py --waits-from <pmc dir>",
+        "# family | dispatches | waves | wait | issue_wait | active | active_valu | active_lds | active_scalar | waves_per_cu",
+    ]
+    for fam, v in res.items():
+        wc = max(v["SQ_WAVE_CYCLES"][0], 1.0)
+        fr = lambda c: v[c][0] / wc
+        kcyc = max(v["GRBM_GUI_ACTIVE"][0] / XCDS, 1.0)
+        lines.append(f"{fam} | {v['SQ_WAVE_CYCLES'][1]} | {v['SQ_WAVES'][0]:.0f} | {fr('SQ_WAIT_ANY'):.3f} | "
+                     f"{fr('SQ_WAIT_INST_ANY'):.3f} | {fr('SQ_ACTIVE_INST_ANY'):.3f} | {fr('SQ_ACTIVE_INST_VALU'):.3f} | "
+                     f"{fr('SQ_ACTIVE_INST_LDS'):.3f} | {fr('SQ_ACTIVE_INST_SCA'):.3f} | "
+                     f"{v['SQ_WAVE_CYCLES'][0] * 4 / kcyc / 256:.2f}")
+    with open(WAVES_SUMMARY, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 MFMA_SUMMARY = os.path.join(ROOT, "profiles", "gemm_attention_lingbot_b64_mfma_counters.txt")
 MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F8", "SQ_VALU_MFMA_BUSY_CYCLES",
                  "SQ_BUSY_CU_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "GRBM_GUI_ACTIVE")
@@ -643,12 +694,17 @@ def main():
     ap.add_argument("--traffic-cmds", nargs=2, metavar=("FETCH_CMD", "WRITE_CMD"), default=("?", "?"))
     ap.add_argument("--mfma-from", metavar="PMC_DIR", help="write the batch-64 MFMA counter summary")
     ap.add_argument("--mfma-cmd", default="?")
+    ap.add_argument("--waits-from", metavar="PMC_DIR", help="write the batch-1 wave-state counter summary")
+    ap.add_argument("--waits-cmd", default="?")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(*args.traffic_from, *args.traffic_cmds)
         return
     if args.mfma_from:
         mfma_from(args.mfma_from, args.mfma_cmd)
+        return
+    if args.waits_from:
+        waits_from(args.waits_from, args.waits_cmd)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
