@@ -187,6 +187,7 @@ struct vla_ctx {
     vla_dims d{};
     int device = 0;
     int ncu = 256;      // compute units of the device (tile rounds of the tiled GEMM)
+    bool w_nt = false;  // weight-streaming GEMMs read weights non-temporally (a linear outgrows the L2)
     int gemm_tile = 0;  // VLA_OPT_GEMM_TILE
     hipStream_t own_stream = nullptr;
     hipStream_t stream = nullptr;
@@ -499,14 +500,14 @@ int launch_tiled8_t(int epi, const GemmParams& p, dim3 grid, hipStream_t s) {
     return VLA_OK;
 }
 
-template <int WF>
+template <int WF, bool WNT = false>
 int launch_skinny_t(int epi, const GemmParams& p, dim3 grid, hipStream_t s) {
     switch (epi) {
-        case EPI_BIAS_F32: VLA_LAUNCH((skinny_gemm_kernel<WF, EPI_BIAS_F32>), grid, dim3(512), 0, s, p); break;
-        case EPI_RESID: VLA_LAUNCH((skinny_gemm_kernel<WF, EPI_RESID>), grid, dim3(512), 0, s, p); break;
-        case EPI_QKV_ROPE: VLA_LAUNCH((skinny_gemm_kernel<WF, EPI_QKV_ROPE>), grid, dim3(512), 0, s, p); break;
-        case EPI_SWIGLU: VLA_LAUNCH((skinny_gemm_kernel<WF, EPI_SWIGLU>), grid, dim3(512), 0, s, p); break;
-        case EPI_PARTIAL: VLA_LAUNCH((skinny_gemm_kernel<WF, EPI_PARTIAL>), grid, dim3(512), 0, s, p); break;
+        case EPI_BIAS_F32: VLA_LAUNCH((skinny_gemm_kernel<WF, EPI_BIAS_F32, WNT>), grid, dim3(512), 0, s, p); break;
+        case EPI_RESID: VLA_LAUNCH((skinny_gemm_kernel<WF, EPI_RESID, WNT>), grid, dim3(512), 0, s, p); break;
+        case EPI_QKV_ROPE: VLA_LAUNCH((skinny_gemm_kernel<WF, EPI_QKV_ROPE, WNT>), grid, dim3(512), 0, s, p); break;
+        case EPI_SWIGLU: VLA_LAUNCH((skinny_gemm_kernel<WF, EPI_SWIGLU, WNT>), grid, dim3(512), 0, s, p); break;
+        case EPI_PARTIAL: VLA_LAUNCH((skinny_gemm_kernel<WF, EPI_PARTIAL, WNT>), grid, dim3(512), 0, s, p); break;
         default: set_err("bad skinny epilogue %d", epi); return VLA_ERR_ARG;
     }
     HIPC(hipGetLastError());
@@ -535,6 +536,9 @@ int launch_gemm(vla_ctx* c, const Linear& lin, const GemmCfg& cfg, bool w8, int 
             p.bscale = lin.bscale;
             return launch_skinny_t<2>(epi, p, grid, c->stream);
         }
+        if (c->w_nt)
+            return w8 ? launch_skinny_t<1, true>(epi, p, grid, c->stream)
+                      : launch_skinny_t<0, true>(epi, p, grid, c->stream);
         return w8 ? launch_skinny_t<1>(epi, p, grid, c->stream) : launch_skinny_t<0>(epi, p, grid, c->stream);
     }
     if (lin.fmt == 2) {
@@ -1136,6 +1140,20 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
     c->a8 = c->w8 && c->M > 64 && H % 128 == 0 && c->qd % 128 == 0 && I % 128 == 0;
     HIPC(hipGetDevice(&c->device));
     HIPC(hipDeviceGetAttribute(&c->ncu, hipDeviceAttributeMultiprocessorCount, c->device));
+    {
+        // Weights read with the non-temporal hint when the largest linear
+        // alone exceeds the L2 of all XCDs together (the reported L2 is one
+        // XCD's; 32 CUs per XCD): such a stream otherwise evicts everything
+        // that is used again. Measured on the two batch-1 models: the
+        // V2-shaped loop (gate_up 37.7 MB) 94.4 -> 92.5 ms per call with it;
+        // the LingBot-shaped loop (gate_up 16.8 MB) 13.50 -> 13.56 ms.
+        int l2 = 0;
+        HIPC(hipDeviceGetAttribute(&l2, hipDeviceAttributeL2CacheSize, c->device));
+        const double wb = c->w8 ? 1.0 : 2.0;
+        const double largest = wb * std::max(std::max((double)(c->qd + 2 * c->kvd) * H, (double)H * c->qd),
+                                             (double)2 * I * H);
+        c->w_nt = largest > (double)l2 * std::max(1, c->ncu / 32);
+    }
     // graphs are captured on this stream; work runs on `stream`, the legacy
     // default stream until vla_set_stream names another
     HIPC(hipStreamCreateWithFlags(&c->own_stream, hipStreamNonBlocking));
@@ -1336,6 +1354,7 @@ int create_part(vla_ctx* c, int b0, int nb) {
     k->borrowed = true;
     k->device = c->device;
     k->ncu = c->ncu;
+    k->w_nt = c->w_nt;
     k->gemm_tile = c->gemm_tile;
     k->l2_prefetch = c->l2_prefetch;
     k->use_graph = c->use_graph;

@@ -563,8 +563,11 @@ VLA_DEV bf16x8 e2m1x8_to_bf16x8(uint32_t w, uint32_t e) {
 }
 
 // WF: weight format, 0 bf16, 1 E4M3 (fp32 scale per output row), 2 MXFP4
-// (E2M1 codes, E8M0 scale per 32 inputs).
-template <int WF, int EPI>
+// (E2M1 codes, E8M0 scale per 32 inputs). WNT: bf16 / E4M3 weights read
+// with the non-temporal hint, for models whose single linears outgrow the
+// L2: their streamed weights then stop evicting the lines that are used
+// again (code, activations, weights read ahead for the next linear).
+template <int WF, int EPI, bool WNT = false>
 __global__ __launch_bounds__(512) void skinny_gemm_kernel(GemmParams p) {
     constexpr bool W8 = WF == 1;
     __shared__ __attribute__((aligned(16))) float red[2][SK_WAVES][4][64][4];
@@ -601,7 +604,9 @@ __global__ __launch_bounds__(512) void skinny_gemm_kernel(GemmParams p) {
                     dst[i][0] = *(const uint32_t*)((const uint8_t*)p.W + (frag * 64 + lane) * 4);
                     dst[i][1] = p.bscale[frag * 16 + (lane & 15)];
                 } else {
-                    dst[i] = *(const wvec*)((const uint8_t*)p.W + (frag * 64 + lane) * (W8 ? 8 : 16));
+                    const wvec* src = (const wvec*)((const uint8_t*)p.W + (frag * 64 + lane) * (W8 ? 8 : 16));
+                    if constexpr (WNT) dst[i] = __builtin_nontemporal_load(src);
+                    else dst[i] = *src;
                 }
             }
     };
