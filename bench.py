@@ -58,11 +58,11 @@ CALL_TARGET = {"hbm": 0.70, "mfma": 0.50}   # batch-1 HBM and batch-64 bf16 MFMA
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "layer_kernels_lingbot_b1_counters.txt")
 # kernel family -> (kernel name in the trace, which of that name's launches per layer)
 TRAFFIC_KERNELS = {
-    "qkv_rope_gemm": ("skinny_gemm_kernel<0, 2>", 0, 1),
+    "qkv_rope_gemm": ("skinny_gemm_kernel<0, 2, false>", 0, 1),
     "gqa_attention": ("attn_kernel<", 0, 1),
-    "o_proj_gemm": ("skinny_gemm_kernel<0, 4>", 0, 2),
-    "gate_up_swiglu_gemm": ("skinny_gemm_kernel<0, 3>", 0, 1),
-    "down_gemm": ("skinny_gemm_kernel<0, 4>", 1, 2),
+    "o_proj_gemm": ("skinny_gemm_kernel<0, 4, false>", 0, 2),
+    "gate_up_swiglu_gemm": ("skinny_gemm_kernel<0, 3, false>", 0, 1),
+    "down_gemm": ("skinny_gemm_kernel<0, 4, false>", 1, 2),
 }
 KERNEL_SOURCES = ("vla_flow_matching_denoise_amd/csrc/common.h", "vla_flow_matching_denoise_amd/csrc/kernels_layer.h")
 COPY_BYTES = 256 << 20
