@@ -90,6 +90,12 @@ extern "C" {
  * tiled one), i.e. within rounding. vla_get_option gives the number of parts in use (0: none). Setting
  * any option rebuilds the parts at the next call. */
 #define VLA_OPT_SPLIT_BATCH 8
+/* With batch*horizon <= 64, the weight-streaming GEMMs read bf16 / E4M3 weights with the non-temporal
+ * hint (1) or plainly (0). The default is 1 exactly when the largest block linear's weights exceed the
+ * L2 of all XCDs together: a stream that size otherwise evicts the lines that are used again (code,
+ * activations, weights read ahead for the next linear). Results do not depend on it. Setting it waits for
+ * the ctx stream and drops captured graphs; vla_get_option gives the setting in use. */
+#define VLA_OPT_WEIGHT_NT 9
 
 typedef struct vla_ctx vla_ctx;
 

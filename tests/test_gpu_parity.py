@@ -315,12 +315,48 @@ def test_v2_b1_end_to_end():
     raw = synth.make_weights(cfg, seed=0)
     case = GpuCase(cfg, raw, pk, pv, x0, ts)
     try:
+        from vla_flow_matching_denoise_amd import binding as B
+        # gate_up's 37.7 MB of weights exceed the 32 MB of L2: non-temporal weight reads by default
+        assert case.expert.get_option(B.VLA_OPT_WEIGHT_NT) == 1
         out = case.run()
     finally:
         case.close()
     say("[cfg3] GPU done; oracle")
     ref = run_oracle(cfg, oracle.decode_weights(raw), pk, pv, x0, ts)
     _gate_bf16(metrics(out, ref), "cfg3")
+
+
+@pytest.mark.parametrize("weight_dtype", ["bf16", "fp8_e4m3"])
+def test_weight_nt_option_bitwise(weight_dtype):
+    """VLA_OPT_WEIGHT_NT changes only how the weight-streaming GEMMs read
+    their weights (the non-temporal hint, or plain loads): on the tiny
+    expert with bf16 and with E4M3 weights the output is bitwise the same
+    either way, and the default is plain loads there (its largest linear is
+    far below the L2)."""
+    from vla_flow_matching_denoise_amd import binding as B
+    cfg = synth.config(1)
+    wd = None if weight_dtype == "bf16" else weight_dtype
+    if wd:
+        cfg = cfg.replace(weight_dtype=wd)
+    pk, pv, x0, ts = _inputs(cfg)
+    say(f"[weight nt] tiny expert, {weight_dtype} weights")
+    case = GpuCase(cfg, weights(1, weight_dtype=wd), pk, pv, x0, ts)
+    try:
+        ex = case.expert
+        assert ex.get_option(B.VLA_OPT_WEIGHT_NT) == 0
+        plain = case.run()
+        ex.set_option(B.VLA_OPT_WEIGHT_NT, 1)
+        assert ex.get_option(B.VLA_OPT_WEIGHT_NT) == 1
+        nt = case.run()
+        ex.set_option(B.VLA_OPT_WEIGHT_NT, 0)
+        again = case.run()
+        with pytest.raises(B.VlaError):
+            ex.set_option(B.VLA_OPT_WEIGHT_NT, 2)
+        assert ex.get_option(B.VLA_OPT_WEIGHT_NT) == 0
+    finally:
+        case.close()
+    assert np.all(np.isfinite(plain))
+    assert np.array_equal(plain, nt) and np.array_equal(plain, again)
 
 
 def test_batch64_sampled_requests_warped():

@@ -30,6 +30,7 @@ VLA_OPT_PERSISTENT_STATUS = 4
 VLA_OPT_GEMM_TILE = 5
 VLA_OPT_L2_PREFETCH = 6
 VLA_OPT_SPLIT_BATCH = 8
+VLA_OPT_WEIGHT_NT = 9
 
 # every symbol include/vla_expert.h declares
 EXPORTED = (

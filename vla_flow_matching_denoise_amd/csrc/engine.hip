@@ -1648,6 +1648,18 @@ int vla_set_option(vla_ctx* c, int option, int value) {
         c->graphs.clear();
         return VLA_OK;
     }
+    if (option == VLA_OPT_WEIGHT_NT) {
+        if (value != 0 && value != 1) {
+            set_err("VLA_OPT_WEIGHT_NT takes 0 or 1, not %d", value);
+            return VLA_ERR_ARG;
+        }
+        HIPC(hipSetDevice(c->device));
+        HIPC(hipStreamSynchronize(c->stream));
+        c->w_nt = value != 0;
+        for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second);  // they hold the old kernels
+        c->graphs.clear();
+        return VLA_OK;
+    }
     if (option == VLA_OPT_GEMM_TILE) {
         if (value < 0 || value > 4) {
             set_err("VLA_OPT_GEMM_TILE takes 0..4, not %d", value);
@@ -1681,6 +1693,7 @@ int vla_get_option(const vla_ctx* c, int option, int* value) {
         case VLA_OPT_USE_GRAPH: *value = c->use_graph ? 1 : 0; return VLA_OK;
         case VLA_OPT_PERSISTENT: *value = c->use_persist ? 1 : 0; return VLA_OK;
         case VLA_OPT_GEMM_TILE: *value = c->gemm_tile; return VLA_OK;
+        case VLA_OPT_WEIGHT_NT: *value = c->w_nt ? 1 : 0; return VLA_OK;
         case VLA_OPT_L2_PREFETCH: *value = c->l2_prefetch; return VLA_OK;
         case VLA_OPT_SPLIT_BATCH: *value = split_parts(c); return VLA_OK;
         case VLA_OPT_PERSISTENT_ACTIVE: *value = (c->persist_ok && c->use_persist) ? 1 : 0; return VLA_OK;
