@@ -77,8 +77,9 @@ extern "C" {
 /* With batch*horizon <= 64, workgroups appended to the attention and norm kernels (on CUs those leave
  * idle) load the next weight-streaming GEMMs' weights into the L2 of the XCD that will read them. Bits:
  * 1 the attention prefetches O, 2 the attention prefetches gate_up, 4 the norm before a layer prefetches
- * its QKV, 8 the norm before gate_up prefetches down; 0 off. Default 7. For measurement; setting it
- * waits for the ctx stream and drops captured graphs. */
+ * its QKV, 8 the norm before gate_up prefetches down; 0 off. Default 7, or 0 when the largest block
+ * linear outgrows the L2 (VLA_OPT_WEIGHT_NT on by default). For measurement; setting it waits for the
+ * ctx stream and drops captured graphs. */
 #define VLA_OPT_L2_PREFETCH 6
 /* Large batches: n = 2..4 runs the requests as n parts at once (request ranges [B i / n, B (i+1) / n)),
  * each part a child context (the same weights, its own buffers, graph and stream) forked from and joined

@@ -316,8 +316,10 @@ def test_v2_b1_end_to_end():
     case = GpuCase(cfg, raw, pk, pv, x0, ts)
     try:
         from vla_flow_matching_denoise_amd import binding as B
-        # gate_up's 37.7 MB of weights exceed the 32 MB of L2: non-temporal weight reads by default
+        # gate_up's 37.7 MB of weights exceed the 32 MB of L2: non-temporal weight
+        # reads and no L2 read-ahead by default
         assert case.expert.get_option(B.VLA_OPT_WEIGHT_NT) == 1
+        assert case.expert.get_option(B.VLA_OPT_L2_PREFETCH) == 0
         out = case.run()
     finally:
         case.close()
@@ -344,6 +346,7 @@ def test_weight_nt_option_bitwise(weight_dtype):
     try:
         ex = case.expert
         assert ex.get_option(B.VLA_OPT_WEIGHT_NT) == 0
+        assert ex.get_option(B.VLA_OPT_L2_PREFETCH) == 7
         plain = case.run()
         ex.set_option(B.VLA_OPT_WEIGHT_NT, 1)
         assert ex.get_option(B.VLA_OPT_WEIGHT_NT) == 1

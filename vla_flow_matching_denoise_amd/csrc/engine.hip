@@ -1153,6 +1153,13 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
         const double largest = wb * std::max(std::max((double)(c->qd + 2 * c->kvd) * H, (double)H * c->qd),
                                              (double)2 * I * H);
         c->w_nt = largest > (double)l2 * std::max(1, c->ncu / 32);
+        // Reading weights ahead into the L2 helps only while the lines stay
+        // there until their GEMM runs; with a linear larger than all of the
+        // L2 they do not, and the read-ahead only competes with the running
+        // kernels' loads (V2-shaped loop 92.5 -> 90.0 ms per call without
+        // it; the LingBot-shaped loop 13.55 ms with the default, 14.31 ms
+        // without).
+        if (c->w_nt) c->l2_prefetch = 0;
     }
     // graphs are captured on this stream; work runs on `stream`, the legacy
     // default stream until vla_set_stream names another
