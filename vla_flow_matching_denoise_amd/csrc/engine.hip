@@ -1141,24 +1141,22 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
     HIPC(hipGetDevice(&c->device));
     HIPC(hipDeviceGetAttribute(&c->ncu, hipDeviceAttributeMultiprocessorCount, c->device));
     {
-        // Weights read with the non-temporal hint when the largest linear
-        // alone exceeds the L2 of all XCDs together (the reported L2 is one
-        // XCD's; 32 CUs per XCD): such a stream otherwise evicts everything
-        // that is used again. Measured on the two batch-1 models: the
-        // V2-shaped loop (gate_up 37.7 MB) 94.4 -> 92.5 ms per call with it;
-        // the LingBot-shaped loop (gate_up 16.8 MB) 13.50 -> 13.56 ms.
+        // Weights read with the non-temporal hint, and no L2 read-ahead, for
+        // the E4M3 tiers and wherever the largest linear alone exceeds the L2
+        // of all XCDs together (the reported L2 is one XCD's; 32 CUs per
+        // XCD). Measured per call, plain reads with the read-ahead against
+        // non-temporal reads without it: V2-shaped loop (gate_up 37.7 MB)
+        // 94.4 -> 89.9 ms; E4M3 weights 34.46 -> 32.23 ms; E4M3 + MXFP4
+        // gate_up 13.62 -> 12.64 ms; the bf16 LingBot-shaped loop (gate_up
+        // 16.8 MB) is faster as it was, 13.54 ms against 13.59 (non-temporal
+        // reads) and 14.31 (no read-ahead). A read-ahead into the L2 pays only
+        // while its lines stay there until their GEMM runs.
         int l2 = 0;
         HIPC(hipDeviceGetAttribute(&l2, hipDeviceAttributeL2CacheSize, c->device));
         const double wb = c->w8 ? 1.0 : 2.0;
         const double largest = wb * std::max(std::max((double)(c->qd + 2 * c->kvd) * H, (double)H * c->qd),
                                              (double)2 * I * H);
-        c->w_nt = largest > (double)l2 * std::max(1, c->ncu / 32);
-        // Reading weights ahead into the L2 helps only while the lines stay
-        // there until their GEMM runs; with a linear larger than all of the
-        // L2 they do not, and the read-ahead only competes with the running
-        // kernels' loads (V2-shaped loop 92.5 -> 90.0 ms per call without
-        // it; the LingBot-shaped loop 13.55 ms with the default, 14.31 ms
-        // without).
+        c->w_nt = c->w8 || largest > (double)l2 * std::max(1, c->ncu / 32);
         if (c->w_nt) c->l2_prefetch = 0;
     }
     // graphs are captured on this stream; work runs on `stream`, the legacy
