@@ -187,7 +187,7 @@ struct vla_ctx {
     vla_dims d{};
     int device = 0;
     int ncu = 256;      // compute units of the device (tile rounds of the tiled GEMM)
-    bool w_nt = false;  // weight-streaming GEMMs read weights non-temporally (a linear outgrows the L2)
+    bool w_nt = false;  // weight-streaming GEMMs read weights non-temporally (VLA_OPT_WEIGHT_NT)
     int gemm_tile = 0;  // VLA_OPT_GEMM_TILE
     hipStream_t own_stream = nullptr;
     hipStream_t stream = nullptr;
