@@ -1,0 +1,53 @@
+"""Host-side checks of bench.py's bookkeeping (no GPU).
+
+* The per-call algorithmic bytes and flops that the call rooflines divide by
+  agree with the figures derived independently from the workload shapes:
+  13.01 / 129.4 / 16.32 / 18.96 GB and 0.673 / 6.84 / 1.68 / 43.05 TFLOP per
+  call for the LingBot batch-1, V2-shaped, E4M3-weight and batch-64
+  workloads (weights streamed once per Euler step, the prefix K/V read once
+  per step, modulation and time-MLP weights once per call).
+* The kernel-name patterns by which the counter summaries pick a layer's
+  kernel families out of a rocprofv3 trace match the kernels in the
+  committed batch-1 kernel statistics, and the committed traffic summary
+  holds a figure for every family.
+"""
+import csv
+import os
+
+import pytest
+
+import bench
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.parametrize("cfg_id, gbytes, tflop", [(2, 13.01, 0.673), (3, 129.4, 6.84), (4, 16.32, 1.68),
+                                                    (5, 18.96, 43.05)])
+def test_call_work_matches_the_workload_figures(cfg_id, gbytes, tflop):
+    by, fl = bench.call_work(synth.config(cfg_id))
+    assert by / 1e9 == pytest.approx(gbytes, rel=2e-3)
+    assert fl / 1e12 == pytest.approx(tflop, rel=2e-3)
+
+
+def _profiled_kernel_names():
+    path = os.path.join(ROOT, "profiles", "denoise_loop_lingbot_b1_kernel_stats.txt")
+    with open(path) as fh:
+        rows = [line for line in fh if not line.startswith("#")]
+    return [r["Name"] for r in csv.DictReader(rows)]
+
+
+def test_counter_kernel_patterns_match_the_profiled_kernels():
+    names = _profiled_kernel_names()
+    assert names, "no kernels in the committed batch-1 kernel statistics"
+    for fam, (pattern, which, per_layer) in bench.TRAFFIC_KERNELS.items():
+        assert any(pattern in n for n in names), (fam, pattern)
+        assert 0 <= which < per_layer
+
+
+def test_traffic_summary_has_every_family():
+    with open(bench.TRAFFIC_SUMMARY) as fh:
+        text = fh.read()
+    assert "source_sha256_16:" in text
+    for fam in bench.TRAFFIC_KERNELS:
+        assert f"traffic_bytes_per_launch.{fam}:" in text, fam
