@@ -77,9 +77,9 @@ extern "C" {
 /* With batch*horizon <= 64, workgroups appended to the attention and norm kernels (on CUs those leave
  * idle) load the next weight-streaming GEMMs' weights into the L2 of the XCD that will read them. Bits:
  * 1 the attention prefetches O, 2 the attention prefetches gate_up, 4 the norm before a layer prefetches
- * its QKV, 8 the norm before gate_up prefetches down; 0 off. Default 7, or 0 where VLA_OPT_WEIGHT_NT is
- * on by default (E4M3 weights, or a linear larger than the L2). For measurement; setting it waits for the
- * ctx stream and drops captured graphs. */
+ * its QKV, 8 the norm before gate_up prefetches down; 0 off. Default 4 for bf16 weights whose largest
+ * block linear fits the L2 of all XCDs together, else 0 (measured fastest with the non-temporal weight
+ * reads). For measurement; setting it waits for the ctx stream and drops captured graphs. */
 #define VLA_OPT_L2_PREFETCH 6
 /* Large batches: n = 2..4 runs the requests as n parts at once (request ranges [B i / n, B (i+1) / n)),
  * each part a child context (the same weights, its own buffers, graph and stream) forked from and joined
@@ -92,11 +92,9 @@ extern "C" {
  * any option rebuilds the parts at the next call. */
 #define VLA_OPT_SPLIT_BATCH 8
 /* With batch*horizon <= 64, the weight-streaming GEMMs read bf16 / E4M3 weights with the non-temporal
- * hint (1) or plainly (0). The default is 1 for the E4M3 weight tiers and wherever the largest block
- * linear's weights exceed the L2 of all XCDs together (a stream that size otherwise evicts the lines that
- * are used again); such contexts also start with VLA_OPT_L2_PREFETCH 0 (measured faster on those
- * models). Results do not depend on it. Setting it waits for the ctx stream and drops captured graphs;
- * vla_get_option gives the setting in use. */
+ * hint (1, the default: measured faster on every batch-1 model) or plainly (0); MXFP4 gate_up weights are
+ * read plainly. Results do not depend on it. Setting it waits for the ctx stream and drops captured
+ * graphs; vla_get_option gives the setting in use. */
 #define VLA_OPT_WEIGHT_NT 9
 
 typedef struct vla_ctx vla_ctx;

@@ -316,8 +316,8 @@ def test_v2_b1_end_to_end():
     case = GpuCase(cfg, raw, pk, pv, x0, ts)
     try:
         from vla_flow_matching_denoise_amd import binding as B
-        # gate_up's 37.7 MB of weights exceed the 32 MB of L2: non-temporal weight
-        # reads and no L2 read-ahead by default
+        # gate_up's 37.7 MB of weights exceed the 32 MB of L2: no L2 read-ahead
+        # by default (and, as everywhere, non-temporal weight reads)
         assert case.expert.get_option(B.VLA_OPT_WEIGHT_NT) == 1
         assert case.expert.get_option(B.VLA_OPT_L2_PREFETCH) == 0
         out = case.run()
@@ -333,8 +333,8 @@ def test_weight_nt_option_bitwise(weight_dtype):
     """VLA_OPT_WEIGHT_NT changes only how the weight-streaming GEMMs read
     their weights (the non-temporal hint, or plain loads): on the tiny
     expert with bf16 and with E4M3 weights the output is bitwise the same
-    either way. The defaults: plain reads and the L2 read-ahead for bf16
-    weights of this size, non-temporal reads without read-ahead for E4M3."""
+    either way. The defaults: non-temporal reads; the QKV read-ahead alone
+    for bf16 weights of this size (they fit the L2), none for E4M3."""
     from vla_flow_matching_denoise_amd import binding as B
     cfg = synth.config(1)
     wd = None if weight_dtype == "bf16" else weight_dtype
@@ -345,9 +345,8 @@ def test_weight_nt_option_bitwise(weight_dtype):
     case = GpuCase(cfg, weights(1, weight_dtype=wd), pk, pv, x0, ts)
     try:
         ex = case.expert
-        default_nt = 0 if weight_dtype == "bf16" else 1
-        assert ex.get_option(B.VLA_OPT_WEIGHT_NT) == default_nt
-        assert ex.get_option(B.VLA_OPT_L2_PREFETCH) == (0 if default_nt else 7)
+        assert ex.get_option(B.VLA_OPT_WEIGHT_NT) == 1
+        assert ex.get_option(B.VLA_OPT_L2_PREFETCH) == (4 if weight_dtype == "bf16" else 0)
         ex.set_option(B.VLA_OPT_WEIGHT_NT, 0)
         plain = case.run()
         ex.set_option(B.VLA_OPT_WEIGHT_NT, 1)

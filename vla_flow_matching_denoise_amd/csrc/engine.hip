@@ -187,7 +187,7 @@ struct vla_ctx {
     vla_dims d{};
     int device = 0;
     int ncu = 256;      // compute units of the device (tile rounds of the tiled GEMM)
-    bool w_nt = false;  // weight-streaming GEMMs read weights non-temporally (VLA_OPT_WEIGHT_NT)
+    bool w_nt = true;   // weight-streaming GEMMs read weights non-temporally (VLA_OPT_WEIGHT_NT)
     int gemm_tile = 0;  // VLA_OPT_GEMM_TILE
     hipStream_t own_stream = nullptr;
     hipStream_t stream = nullptr;
@@ -1141,23 +1141,24 @@ int create_impl(vla_ctx* c, const vla_weights* w) {
     HIPC(hipGetDevice(&c->device));
     HIPC(hipDeviceGetAttribute(&c->ncu, hipDeviceAttributeMultiprocessorCount, c->device));
     {
-        // Weights read with the non-temporal hint, and no L2 read-ahead, for
-        // the E4M3 tiers and wherever the largest linear alone exceeds the L2
-        // of all XCDs together (the reported L2 is one XCD's; 32 CUs per
-        // XCD). Measured per call, plain reads with the read-ahead against
-        // non-temporal reads without it: V2-shaped loop (gate_up 37.7 MB)
-        // 94.4 -> 89.9 ms; E4M3 weights 34.46 -> 32.23 ms; E4M3 + MXFP4
-        // gate_up 13.62 -> 12.64 ms; the bf16 LingBot-shaped loop (gate_up
-        // 16.8 MB) is faster as it was, 13.54 ms against 13.59 (non-temporal
-        // reads) and 14.31 (no read-ahead). A read-ahead into the L2 pays only
-        // while its lines stay there until their GEMM runs.
+        // Weights are read with the non-temporal hint. The L2 read-ahead keeps
+        // only the norm's read-ahead of the next layer's QKV weights, and only
+        // for bf16 weights whose largest linear fits the L2 of all XCDs
+        // together (the reported L2 is one XCD's; 32 CUs per XCD); otherwise
+        // it is off. Measured per call against plain reads with read-ahead
+        // bits 7 (the earlier default): bf16 LingBot-shaped loop 13.50 ->
+        // 13.10 ms (13.26 without read-ahead); V2-shaped loop (gate_up 37.7
+        // MB, larger than the L2) 94.4 -> 90.0 ms (92.4 with the QKV
+        // read-ahead); E4M3 weights 34.46 -> 32.23 ms; E4M3 + MXFP4 gate_up
+        // 13.62 -> 12.64 ms.
         int l2 = 0;
         HIPC(hipDeviceGetAttribute(&l2, hipDeviceAttributeL2CacheSize, c->device));
         const double wb = c->w8 ? 1.0 : 2.0;
         const double largest = wb * std::max(std::max((double)(c->qd + 2 * c->kvd) * H, (double)H * c->qd),
                                              (double)2 * I * H);
-        c->w_nt = c->w8 || largest > (double)l2 * std::max(1, c->ncu / 32);
-        if (c->w_nt) c->l2_prefetch = 0;
+        const bool fits_l2 = largest <= (double)l2 * std::max(1, c->ncu / 32);
+        c->w_nt = true;
+        c->l2_prefetch = !c->w8 && fits_l2 ? 4 : 0;
     }
     // graphs are captured on this stream; work runs on `stream`, the legacy
     // default stream until vla_set_stream names another
