@@ -58,11 +58,11 @@ CALL_TARGET = {"hbm": 0.70, "mfma": 0.50}   # batch-1 HBM and batch-64 bf16 MFMA
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "layer_kernels_lingbot_b1_counters.txt")
 # kernel family -> (kernel name in the trace, which of that name's launches per layer)
 TRAFFIC_KERNELS = {
-    "qkv_rope_gemm": ("skinny_gemm_kernel<0, 2, false>", 0, 1),
+    "qkv_rope_gemm": ("skinny_gemm_kernel<0, 2, true>", 0, 1),
     "gqa_attention": ("attn_kernel<", 0, 1),
-    "o_proj_gemm": ("skinny_gemm_kernel<0, 4, false>", 0, 2),
-    "gate_up_swiglu_gemm": ("skinny_gemm_kernel<0, 3, false>", 0, 1),
-    "down_gemm": ("skinny_gemm_kernel<0, 4, false>", 1, 2),
+    "o_proj_gemm": ("skinny_gemm_kernel<0, 4, true>", 0, 2),
+    "gate_up_swiglu_gemm": ("skinny_gemm_kernel<0, 3, true>", 0, 1),
+    "down_gemm": ("skinny_gemm_kernel<0, 4, true>", 1, 2),
 }
 KERNEL_SOURCES = ("vla_flow_matching_denoise_amd/csrc/common.h", "vla_flow_matching_denoise_amd/csrc/kernels_layer.h")
 COPY_BYTES = 256 << 20
@@ -236,9 +236,9 @@ def traffic_from(fetch_dir, write_dir, cmd_fetch, cmd_write):
         "# Two rocprofv3 counter runs of `python bench.py --counter-run`, each scaled by the",
         "# counter's reading for a plain device copy of 256 MiB (read 256 MiB, write 256 MiB).",
         "# O and down share one kernel instance: launches alternate O, down within a layer.",
-        "# The attention launch's extra workgroups load the O and gate_up weights (~21 MB) into L2",
-        "# ahead of those GEMMs, and the norm before a layer the layer's QKV weights: those fetches",
-        "# count against the launch that issues them (attention, resnorm), not the GEMM that uses them.",
+        "# Defaults of the run: weights read non-temporally; the only L2 read-ahead is the norm before a",
+        "# layer loading that layer's QKV weights (~5.2 MB), whose fetches count against the norm launch",
+        "# (resnorm, not listed), not the QKV GEMM that uses them.",
         f"# fetch command: {cmd_fetch}",
         f"# write command: {cmd_write}",
         f"# summary: python bench.py --traffic-from <fetch dir> <write dir>",
@@ -742,10 +742,11 @@ def main():
     dom, roof, worst = dominant(kr, "hbm")
     roof["traffic"] = recorded_traffic(dom)
     worst["traffic"] = recorded_traffic(worst["kernel"])
-    for r in (roof, worst):
-        if r["kernel"] == "gqa_attention":
-            r["traffic_note"] = ("includes the O and gate_up weights (about 21 MB) that the launch's idle "
-                                 "workgroups load into L2 for the next GEMMs")
+    if ex.get_option(B.VLA_OPT_L2_PREFETCH) & 3:  # the attention launch reads O / gate_up weights ahead
+        for r in (roof, worst):
+            if r["kernel"] == "gqa_attention":
+                r["traffic_note"] = ("includes the O and gate_up weights that the launch's idle workgroups "
+                                     "load into L2 for the next GEMMs")
     persistent = None
     if not args.no_extra:
         # the opt-in persistent single-launch path on the same workload
