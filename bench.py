@@ -291,7 +291,8 @@ def waits_from(pmc_dir, cmd):
         "# or dependencies), issue_wait = SQ_WAIT_INST_ANY, active = SQ_ACTIVE_INST_ANY with its VALU",
         "# (MFMA included), LDS and scalar (SQ_ACTIVE_INST_SCA) parts; waves_per_cu = SQ_WAVE_CYCLES x 4",
         "# / (GRBM_GUI_ACTIVE / 8) / 256.",
-        "# The attention launch includes its weight read-ahead workgroups (their waves wait on loads).",
+        "# Launches that read weights ahead into L2 (the norms' QKV read-ahead by default) include",
+        "# those read-ahead workgroups (their waves wait on loads).",
         "# O and down share one kernel instance: launches alternate O, down within a layer.",
         f"# command: {cmd}",
         "# summary: python bench.py --waits-from <pmc dir>",
