@@ -887,6 +887,54 @@ def main():
         result["cpu_baseline"] = cpu_baselines(raw, raw4)
 
     print(json.dumps(result), flush=True)
+    try:  # the line is out; a problem found here is reported, never raised
+        for problem in check_line(result):
+            log(f"[bench] report line: {problem}")
+    except Exception as e:  # noqa: BLE001
+        log(f"[bench] report line check failed: {e!r}")
+
+
+def check_line(d) -> list:
+    """Problems with a bench report line (an empty list when it is well formed):
+    the keys and types the report contract asks for, a fraction that is not
+    achieved / peak, a value that does not follow from the time per step."""
+    problems = []
+    want = {"metric": str, "value": (int, float), "unit": str, "n_gpus": int, "steps": int, "warmup": int,
+            "ms_per_step": (int, float), "higher_is_better": bool, "scaling": str, "dtype": str, "data": str,
+            "config": dict, "roofline": dict, "cpu_baseline": dict}
+    for k, t in want.items():
+        if k not in d:
+            problems.append(f"missing {k}")
+        elif not isinstance(d[k], t) or (t == int and isinstance(d[k], bool)):
+            problems.append(f"{k} has type {type(d[k]).__name__}")
+    if "vs_baseline" not in d:
+        problems.append("missing vs_baseline")
+    if problems:
+        return problems
+    if d["scaling"] not in ("weak", "strong"):
+        problems.append(f"scaling {d['scaling']!r}")
+    if not isinstance(d["config"].get("workload"), str):
+        problems.append("config has no workload name")
+    roof = d["roofline"]
+    for k in ("bound", "achieved", "peak", "unit", "frac"):
+        if k not in roof:
+            problems.append(f"roofline misses {k}")
+    if "traffic" not in roof:
+        problems.append("roofline misses traffic (null when unmeasured)")
+    if all(k in roof for k in ("achieved", "peak", "frac")) and roof["peak"]:
+        if abs(roof["achieved"] / roof["peak"] - roof["frac"]) > 1e-3:
+            problems.append("roofline frac is not achieved / peak")
+    if roof.get("bound") not in ("hbm", "mfma", "alu"):
+        problems.append(f"roofline bound {roof.get('bound')!r}")
+    cpu = d["cpu_baseline"]
+    for k in ("value", "unit", "cores", "kind", "sample"):
+        if k not in cpu:
+            problems.append(f"cpu_baseline misses {k}")
+    if d["ms_per_step"] > 0 and d["n_gpus"] == 1:
+        steps_per_call = d["config"].get("euler_steps", 1) * d["config"].get("batch", 1)
+        if abs(steps_per_call / (d["ms_per_step"] / 1e3) - d["value"]) > 1e-2 * d["value"]:
+            problems.append("value does not follow from ms_per_step")
+    return problems
 
 
 if __name__ == "__main__":

@@ -10,6 +10,10 @@
   kernel families out of a rocprofv3 trace match the kernels in the
   committed batch-1 kernel statistics, and the committed traffic summary
   holds a figure for every family.
+* The report-line check that bench.py runs on its own JSON line accepts a
+  well-formed line and names each kind of defect (missing keys, wrong
+  types, a roofline fraction that is not achieved / peak, a value that does
+  not follow from the time per step).
 """
 import csv
 import os
@@ -51,3 +55,38 @@ def test_traffic_summary_has_every_family():
     assert "source_sha256_16:" in text
     for fam in bench.TRAFFIC_KERNELS:
         assert f"traffic_bytes_per_launch.{fam}:" in text, fam
+
+
+def _good_line():
+    # the shape of a report line (figures of a batch-1 call of 13.04 ms)
+    return {"metric": bench.METRIC, "value": 766.98, "unit": "denoise_steps/s", "n_gpus": 1, "steps": 30,
+            "warmup": 5, "ms_per_step": 13.0381, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "lingbot_b1", "batch": 1, "euler_steps": 10},
+            "roofline": {"bound": "hbm", "achieved": 1888.29, "peak": 8000.0, "unit": "GB/s", "frac": 0.236,
+                         "traffic": 18314000},
+            "cpu_baseline": {"value": 7.84, "unit": "denoise_steps/s", "cores": 16, "kind": "oracle",
+                             "sample": "17 Euler steps"}}
+
+
+def test_report_line_check_accepts_a_well_formed_line():
+    assert bench.check_line(_good_line()) == []
+
+
+@pytest.mark.parametrize("edit, expect", [
+    (lambda d: d.pop("roofline"), "missing roofline"),
+    (lambda d: d.pop("vs_baseline"), "missing vs_baseline"),
+    (lambda d: d.update(n_gpus=True), "n_gpus has type bool"),
+    (lambda d: d.update(scaling="linear"), "scaling"),
+    (lambda d: d["config"].pop("workload"), "workload"),
+    (lambda d: d["roofline"].pop("traffic"), "traffic"),
+    (lambda d: d["roofline"].update(frac=0.5), "achieved / peak"),
+    (lambda d: d["roofline"].update(bound="latency"), "bound"),
+    (lambda d: d["cpu_baseline"].pop("cores"), "cores"),
+    (lambda d: d.update(value=700.0), "ms_per_step"),
+])
+def test_report_line_check_names_each_problem(edit, expect):
+    d = _good_line()
+    edit(d)
+    problems = bench.check_line(d)
+    assert any(expect in p for p in problems), problems
