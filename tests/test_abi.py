@@ -137,3 +137,44 @@ def test_header_constants_match_the_binding():
             assert getattr(B, name, None) == value, (path, name, value)
             seen += 1
     assert seen >= 10
+
+
+def _header_struct_fields(path, name):
+    """(field, kind) of `typedef struct name { ... } name;` in a header, kind
+    one of int32 / float / pointer."""
+    text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+    m = re.search(r"typedef struct %s \{(.*?)\} %s;" % (name, name), text, flags=re.S)
+    assert m, name
+    fields = []
+    for decl in m.group(1).split(";"):
+        decl = " ".join(decl.split())
+        if not decl:
+            continue
+        field = re.findall(r"[A-Za-z_]\w*", decl)[-1]
+        kind = "pointer" if "*" in decl else ("float" if decl.startswith("float") else "int32")
+        if kind == "int32":
+            assert decl.startswith("int32_t"), decl
+        fields.append((field, kind))
+    return fields
+
+
+def _ctypes_fields(cls):
+    kinds = {ctypes.c_int32: "int32", ctypes.c_float: "float"}
+    return [(n, kinds.get(t, "pointer" if (t is ctypes.c_void_p or hasattr(t, "contents")) else repr(t)))
+            for n, t in cls._fields_]
+
+
+@pytest.mark.parametrize("header, struct, cls", [
+    ("vla_expert.h", "vla_dims", "VlaDims"),
+    ("vla_expert.h", "vla_weights", "VlaWeights"),
+    ("vla_prefill.h", "vla_backbone_dims", "VlaBackboneDims"),
+    ("vla_prefill.h", "vla_backbone_weights", "VlaBackboneWeights"),
+])
+def test_binding_structs_match_the_header_layouts(header, struct, cls):
+    """The binding's ctypes structures list the header structs' fields in the
+    same order with the same kinds, so the C library reads what Python
+    wrote."""
+    from vla_flow_matching_denoise_amd import binding as B
+    want = _header_struct_fields(os.path.join(ROOT, "include", header), struct)
+    got = _ctypes_fields(getattr(B, cls))
+    assert got == want
