@@ -6,9 +6,10 @@ benchmark's CPU-baseline leg may import it.  The HIP library never calls it,
 and the two share no code; both consume the seeded inputs of ``synth``.
 
 Pins (what fixes each function independently of itself) live in
-``tests/test_oracle_pins.py``.  Parity unpinned: the end-to-end output at the
-real model sizes rests only on the definitions here plus those pins, since the
-pages print no worked numerical example of the expert.
+``tests/test_oracle_pins.py``; every function here has at least one.  The
+pages print no worked numerical example of the expert, so the end-to-end
+output at the real model sizes is fixed by these pinned functions, not by a
+printed value.
 """
 from .denoise import *  # noqa: F401,F403
 from .denoise import __all__  # noqa: F401
